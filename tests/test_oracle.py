@@ -1,0 +1,256 @@
+"""Pins of the CPU fp64 oracle against things other than itself.
+
+Each test fixes a part of the definition a plausible mistake would break:
+ - dense causal indices == torch scaled_dot_product_attention (scale, sign,
+   operand order, inclusive diagonal, GQA head mapping, softmax);
+ - pure-Python brute force on tiny sparse inputs (index -> token set,
+   counts truncation, -1 padding, varlen offsets);
+ - closed forms at t = 0 and q = 0 (lse in natural-log units, |M_t|);
+ - the lse gradient identity d lse / d q = scale * softmax-weighted keys;
+ - v -> a v + b equivariance (rows of P sum to one);
+ - invariance to entry order, to entries past the count and to repeats;
+ - the block-level causal example of the block-sparse mask page.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import nsa_inputs as ni
+import oracle
+from oracle import brute
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def small(pattern, counts_mode="full", seqlens=(40,), Hq=4, Hkv=2, D=8, bs=8, S=4, seed=7,
+          varlen=False, dtype="f32"):
+    return ni.make_workload("t", dtype, list(seqlens), Hq, Hkv, D, bs, S, pattern, counts_mode, seed,
+                            varlen=varlen)
+
+
+def run(w, **kw):
+    return oracle.fwd(w.q, w.k, w.v, w.block_indices, w.block_counts, w.block_size, w.scale,
+                      cu_seqlens=w.cu_seqlens, **kw)
+
+
+# --------------------------------------------------------------------------
+# dense special case == library attention
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("T,Hq,Hkv,D,bs", [(96, 4, 2, 16, 16), (90, 4, 4, 8, 16), (70, 8, 1, 32, 32),
+                                           (33, 2, 2, 8, 8)])
+def test_dense_indices_equal_causal_sdpa(T, Hq, Hkv, D, bs):
+    nb = (T + bs - 1) // bs
+    w = ni.make_workload("dense", "f32", [T, T], Hq, Hkv, D, bs, nb, "dense", "full", seed=3)
+    out, lse = run(w)
+    q = torch.from_numpy(w.q).double().permute(0, 2, 1, 3)   # B H T D
+    k = torch.from_numpy(w.k).double().permute(0, 2, 1, 3)
+    v = torch.from_numpy(w.v).double().permute(0, 2, 1, 3)
+    ref = torch.nn.functional.scaled_dot_product_attention(q, k, v, is_causal=True, scale=w.scale,
+                                                           enable_gqa=True)
+    ref = ref.permute(0, 2, 1, 3).reshape(2 * T, Hq, D).numpy()
+    np.testing.assert_allclose(out, ref, rtol=0, atol=1e-12)
+    # lse against torch.logsumexp of the library's own score matrix
+    G = Hq // Hkv
+    kk = k.repeat_interleave(G, dim=1)
+    sc = torch.matmul(q, kk.transpose(-1, -2)) * w.scale
+    causal = torch.ones(T, T, dtype=torch.bool).tril()
+    sc = sc.masked_fill(~causal, -math.inf)
+    ref_lse = torch.logsumexp(sc, dim=-1).permute(0, 2, 1).reshape(2 * T, Hq).numpy()
+    np.testing.assert_allclose(lse, ref_lse, rtol=0, atol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# brute force on tiny inputs
+# --------------------------------------------------------------------------
+CASES = [
+    dict(pattern="shuffled", counts_mode="uniform", seqlens=(40,), Hq=4, Hkv=1, D=8, bs=8, S=4),
+    dict(pattern="local_random", counts_mode="full", seqlens=(48, 48), Hq=4, Hkv=2, D=8, bs=4, S=6),
+    dict(pattern="local_random", counts_mode="uniform", seqlens=(37,), Hq=2, Hkv=2, D=4, bs=4, S=6),
+    dict(pattern="sink_local_random", counts_mode="full", seqlens=(64,), Hq=8, Hkv=2, D=8, bs=4, S=8),
+    dict(pattern="local_random", counts_mode="uniform", seqlens=(13, 30, 5), Hq=4, Hkv=2, D=8, bs=4, S=6,
+         varlen=True),
+]
+
+
+@pytest.mark.parametrize("case", CASES)
+def test_oracle_matches_brute_force(case):
+    w = small(**case)
+    out, lse = run(w)
+    bout, blse = brute.fwd(w.q, w.k, w.v, w.block_indices, w.block_counts, w.block_size, w.scale,
+                           cu_seqlens=w.cu_seqlens)
+    bout, blse = np.array(bout), np.array(blse)
+    assert np.array_equal(np.isinf(lse), np.isinf(blse))
+    np.testing.assert_allclose(out, bout, rtol=0, atol=1e-12)
+    fin = np.isfinite(blse)
+    np.testing.assert_allclose(lse[fin], blse[fin], rtol=0, atol=1e-12)
+
+
+def test_brute_force_with_hostile_entries():
+    """-1 padding inside the count, blocks beyond own, blocks past the end,
+    counts above S and below zero, repeated entries."""
+    w = small("local_random", "full", seqlens=(32,), Hq=2, Hkv=1, D=4, bs=4, S=5, seed=11)
+    rng = np.random.default_rng(0)
+    bi = rng.integers(-3, 12, size=w.block_indices.shape).astype(np.int32)
+    bc = rng.integers(-2, 8, size=w.block_counts.shape).astype(np.int32)
+    w.block_indices, w.block_counts = bi, bc
+    out, lse = run(w)
+    bout, blse = brute.fwd(w.q, w.k, w.v, bi, bc, w.block_size, w.scale)
+    bout, blse = np.array(bout), np.array(blse)
+    assert np.array_equal(np.isinf(lse), np.isinf(blse))
+    np.testing.assert_allclose(out, bout, rtol=0, atol=1e-12)
+    fin = np.isfinite(blse)
+    np.testing.assert_allclose(lse[fin], blse[fin], rtol=0, atol=1e-12)
+    assert (~fin).any() and fin.any()
+
+
+# --------------------------------------------------------------------------
+# closed forms
+# --------------------------------------------------------------------------
+def test_first_token_closed_form():
+    w = small("local_random", "full", seqlens=(24, 24), Hq=4, Hkv=2, D=8, bs=8, S=3)
+    out, lse = run(w)
+    G = w.G
+    for b in range(2):
+        x = b * w.T
+        for hq in range(w.Hq):
+            h = hq // G
+            assert np.array_equal(out[x, hq], w.v[b, 0, h].astype(np.float64))
+            exp_lse = w.scale * float(np.dot(w.q[b, 0, hq].astype(np.float64), w.k[b, 0, h].astype(np.float64)))
+            assert abs(lse[x, hq] - exp_lse) < 1e-12
+
+
+@pytest.mark.parametrize("pattern,counts_mode", [("shuffled", "uniform"), ("sink_local_random", "full"),
+                                                 ("local_random", "uniform")])
+def test_zero_query_counts_and_mean(pattern, counts_mode):
+    w = small(pattern, counts_mode, seqlens=(64,), Hq=4, Hkv=2, D=8, bs=8, S=4)
+    w.q[:] = 0.0
+    out, lse = run(w)
+    G = w.G
+    for t in range(w.T):
+        for hq in range(w.Hq):
+            h = hq // G
+            keys = brute.visible_keys(list(w.block_indices[0, t, h]), w.block_counts[0, t, h], w.S,
+                                      w.block_size, t, w.T)
+            assert abs(lse[t, hq] - math.log(len(keys))) < 1e-12
+            mean = np.mean([w.v[0, s, h].astype(np.float64) for s in sorted(keys)], axis=0)
+            np.testing.assert_allclose(out[t, hq], mean, rtol=0, atol=1e-12)
+
+
+def test_lse_gradient_identity():
+    """d lse / d q[d] = scale * sum_s p_s k_s[d]: the oracle's output with v := k."""
+    w = small("sink_local_random", "full", seqlens=(48,), Hq=2, Hkv=1, D=6, bs=4, S=6)
+    wk = small("sink_local_random", "full", seqlens=(48,), Hq=2, Hkv=1, D=6, bs=4, S=6)
+    wk.v = wk.k.copy()
+    outk, _ = run(wk)
+    eps = 1e-4
+    for t in (5, 17, 47):
+        for d in range(w.D):
+            wp = small("sink_local_random", "full", seqlens=(48,), Hq=2, Hkv=1, D=6, bs=4, S=6)
+            wm = small("sink_local_random", "full", seqlens=(48,), Hq=2, Hkv=1, D=6, bs=4, S=6)
+            # q +/- eps e_d, with the step measured on the float32 values actually used
+            wp.q[0, t, 0, d] += np.float32(eps)
+            wm.q[0, t, 0, d] -= np.float32(eps)
+            dq = float(wp.q[0, t, 0, d]) - float(wm.q[0, t, 0, d])
+            _, lp = run(wp)
+            _, lm = run(wm)
+            fd = (lp[t, 0] - lm[t, 0]) / dq
+            assert abs(fd - w.scale * outk[t, 0, d]) < 1e-6
+
+
+def test_affine_equivariance_in_v():
+    w = small("sink_local_random", "full", seqlens=(64,), Hq=4, Hkv=2, D=8, bs=8, S=4)
+    w.v = (np.round(w.v * 4) / 4).astype(np.float32)   # dyadic values: 2 v + 0.5 is exact in float32
+    out, _ = run(w)
+    w.v = (np.float32(2.0) * w.v + np.float32(0.5)).astype(np.float32)
+    out2, _ = run(w)
+    np.testing.assert_allclose(out2, 2.0 * out + 0.5, rtol=0, atol=1e-12)
+    w.v[:] = 1.0
+    ones, _ = run(w)
+    np.testing.assert_allclose(ones, 1.0, rtol=0, atol=1e-14)
+
+
+# --------------------------------------------------------------------------
+# invariances of the index contract
+# --------------------------------------------------------------------------
+def test_entry_order_garbage_and_repeats_invariance():
+    w = small("local_random", "uniform", seqlens=(64,), Hq=4, Hkv=2, D=8, bs=8, S=6)
+    out, lse = run(w)
+    rng = np.random.default_rng(5)
+    bi = w.block_indices.copy()
+    n = np.clip(w.block_counts, 0, w.S)
+    for t in range(w.T):
+        for h in range(w.Hkv):
+            k = int(n[0, t, h])
+            bi[0, t, h, :k] = rng.permutation(bi[0, t, h, :k])
+            bi[0, t, h, k:] = rng.integers(-5, 50, size=w.S - k)
+    w2 = small("local_random", "uniform", seqlens=(64,), Hq=4, Hkv=2, D=8, bs=8, S=6)
+    w2.block_indices = bi
+    out2, lse2 = run(w2)
+    assert np.array_equal(out, out2) and np.array_equal(lse, lse2)
+    # repeating a listed block inside the count changes nothing (set semantics)
+    bi3 = w.block_indices.copy()
+    bc3 = w.block_counts.copy()
+    for t in range(w.T):
+        for h in range(w.Hkv):
+            k = int(n[0, t, h])
+            if k < w.S:
+                bi3[0, t, h, k] = bi3[0, t, h, 0]
+                bc3[0, t, h] = k + 1
+    w3 = small("local_random", "uniform", seqlens=(64,), Hq=4, Hkv=2, D=8, bs=8, S=6)
+    w3.block_indices, w3.block_counts = bi3, bc3
+    out3, lse3 = run(w3)
+    assert np.array_equal(out, out3) and np.array_equal(lse, lse3)
+
+
+def test_empty_rows():
+    w = small("local_random", "full", seqlens=(32,), Hq=2, Hkv=1, D=4, bs=8, S=4)
+    w.block_counts[0, 3, 0] = 0
+    w.block_indices[0, 9, 0, :] = -1
+    w.block_indices[0, 10, 0, :] = 3          # only a future block (own = 1)
+    out, lse = run(w)
+    for t in (3, 9, 10):
+        assert np.all(out[t] == 0.0) and np.all(np.isneginf(lse[t]))
+    assert np.all(np.isfinite(np.delete(lse, [3, 9, 10], axis=0)))
+
+
+def test_varlen_equals_per_sequence():
+    lens = [13, 30, 5, 17]
+    w = small("local_random", "uniform", seqlens=lens, Hq=4, Hkv=2, D=8, bs=4, S=6, varlen=True)
+    out, lse = run(w)
+    cu = w.cu_seqlens
+    for i, L in enumerate(lens):
+        a, b = cu[i], cu[i + 1]
+        o1, l1 = oracle.fwd(w.q[:, a:b], w.k[:, a:b], w.v[:, a:b], w.block_indices[:, a:b],
+                            w.block_counts[:, a:b], w.block_size, w.scale)
+        assert np.array_equal(o1, out[a:b]) and np.array_equal(l1, lse[a:b])
+
+
+def test_token_subset_matches_full_run():
+    w = small("sink_local_random", "full", seqlens=(64, 64), Hq=4, Hkv=2, D=8, bs=8, S=4)
+    out, lse = run(w)
+    toks = np.array([0, 5, 63, 64, 100, 127])
+    o2, l2 = run(w, tokens=toks)
+    assert np.array_equal(o2, out[toks]) and np.array_equal(l2, lse[toks])
+
+
+def test_block_level_causal_example():
+    """Page example: causal mask over 4 blocks, query block i attends [0, i+1)."""
+    g = json.load(open(os.path.join(GOLDEN, "causal_4_blocks.json")))
+    nb, bs = g["num_blocks"], 4
+    T = nb * bs
+    w = ni.make_workload("ex", "f32", [T], 1, 1, nb, bs, nb, "dense", "full", seed=1)
+    w.q[:] = 0.0
+    # v[s, d] = 1 iff key s is in block d: out[t, d] > 0 iff block d is visible to t
+    w.v[:] = 0.0
+    for s in range(T):
+        w.v[0, s, 0, s // bs] = 1.0
+    out, _ = run(w)
+    for i, (lo, hi) in enumerate(g["attend_bounds"]):
+        seen = set()
+        for t in range(i * bs, (i + 1) * bs):
+            seen |= {d for d in range(nb) if out[t, 0, d] > 0}
+        assert seen == set(range(lo, hi))

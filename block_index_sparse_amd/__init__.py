@@ -1,0 +1,191 @@
+"""Python binding of the MI355X native sparse attention forward (``libnsa.so``).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI of ``include/nsa.h``.  PyTorch supplies device
+memory and the current HIP stream.  If the library has not been built the
+calls raise; there is no fallback path.
+
+Call contract (ejKernel ``native_sparse_attention`` API page, "Parameters"):
+``fwd(q, k, v, block_indices, block_counts, block_size, scale=None,
+cu_seqlens=None) -> (out, lse)`` with q ``[B, T, Hq, D]``, k/v
+``[B, T, Hkv, D]`` (bf16 or fp32, on the GPU), ``block_indices
+[B, T, Hkv, S]`` int32, ``block_counts [B, T, Hkv]`` int32 or a Python int
+(broadcast), ``scale`` defaulting to 1/sqrt(D), and an optional
+``cu_seqlens [N+1]`` int32 for packed sequences (then B == 1).
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+__all__ = ["fwd", "workspace_size", "schedule", "load_library", "library_path", "NsaError",
+           "DTYPE_F32", "DTYPE_BF16"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "_build", "libnsa.so")
+_lib = None
+
+DTYPE_F32, DTYPE_BF16 = 0, 1
+
+
+class NsaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+
+
+class NsaDims(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("seqlen", ctypes.c_int32),
+                ("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("num_selected", ctypes.c_int32),
+                ("dtype", ctypes.c_int32)]
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load ``libnsa.so`` (built by ``block_index_sparse_amd.build``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"native library missing: {_LIB_PATH}; build it with "
+                           "`python -m block_index_sparse_amd.build` (no fallback path exists)")
+    lib = ctypes.CDLL(_LIB_PATH)
+    p, i32, sz, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t, ctypes.c_float
+    dp = ctypes.POINTER(NsaDims)
+    lib.nsa_fwd_workspace_size.restype = sz
+    lib.nsa_fwd_workspace_size.argtypes = [dp, i32, i32]
+    lib.nsa_fwd.restype = ctypes.c_int
+    lib.nsa_fwd.argtypes = [dp, p, p, p, p, p, i32, f32, p, p, p, sz, p]
+    lib.nsa_fwd_varlen.restype = ctypes.c_int
+    lib.nsa_fwd_varlen.argtypes = [dp, p, p, p, p, p, p, i32, i32, f32, p, p, p, sz, p]
+    lib.nsa_fwd_schedule.restype = ctypes.c_int
+    lib.nsa_fwd_schedule.argtypes = [dp, p, p, p, i32, i32, p, sz, p, ctypes.POINTER(sz),
+                                     ctypes.POINTER(i32)]
+    lib.nsa_status_string.restype = ctypes.c_char_p
+    lib.nsa_status_string.argtypes = [ctypes.c_int]
+    lib.nsa_abi_version.restype = i32
+    lib.nsa_abi_version.argtypes = []
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != 0:
+        lib = load_library()
+        raise NsaError(status, lib.nsa_status_string(status).decode())
+
+
+def _dims(B, T, Hq, Hkv, D, S, dtype_code) -> NsaDims:
+    return NsaDims(B, T, Hq, Hkv, D, S, dtype_code)
+
+
+def workspace_size(B, T, Hq, Hkv, D, S, block_size, dtype="bf16", num_seqs=0) -> int:
+    code = DTYPE_BF16 if dtype in ("bf16", "bfloat16") else DTYPE_F32
+    d = _dims(B, T, Hq, Hkv, D, S, code)
+    return int(load_library().nsa_fwd_workspace_size(ctypes.byref(d), int(block_size), int(num_seqs)))
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _stream(torch, device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _prepare(q, k, v, block_indices, block_counts, cu_seqlens):
+    import torch
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be [B, T, H, D]")
+    B, T, Hq, D = q.shape
+    if k.shape[:2] != (B, T) or v.shape != k.shape or k.shape[3] != D:
+        raise ValueError("k and v must be [B, T, Hkv, D] matching q")
+    if q.dtype != k.dtype or q.dtype != v.dtype:
+        raise ValueError("q, k, v must share a dtype")
+    if q.dtype == torch.bfloat16:
+        code = DTYPE_BF16
+    elif q.dtype == torch.float32:
+        code = DTYPE_F32
+    else:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    if not (q.is_cuda and k.is_cuda and v.is_cuda):
+        raise ValueError("q, k, v must be GPU tensors")
+    Hkv = k.shape[2]
+    if block_indices.dim() != 4 or tuple(block_indices.shape[:3]) != (B, T, Hkv):
+        raise ValueError("block_indices must be [B, T, Hkv, S]")
+    S = block_indices.shape[3]
+    bi = block_indices.to(device=q.device, dtype=torch.int32).contiguous()
+    if isinstance(block_counts, int):
+        bc = torch.full((B, T, Hkv), block_counts, dtype=torch.int32, device=q.device)
+    else:
+        if tuple(block_counts.shape) != (B, T, Hkv):
+            raise ValueError("block_counts must be [B, T, Hkv] or an int")
+        bc = block_counts.to(device=q.device, dtype=torch.int32).contiguous()
+    cu = None
+    if cu_seqlens is not None:
+        cu = cu_seqlens.to(device=q.device, dtype=torch.int32).contiguous()
+        if B != 1:
+            raise ValueError("cu_seqlens needs B == 1")
+    return (q.contiguous(), k.contiguous(), v.contiguous(), bi, bc, cu, B, T, Hq, Hkv, D, S, code)
+
+
+def fwd(q, k, v, block_indices, block_counts, block_size: int = 64, scale: float | None = None,
+        cu_seqlens=None, out=None, lse=None, workspace=None, return_lse: bool = True):
+    """Native sparse attention forward on the GPU.  Returns (out, lse)."""
+    import torch
+    lib = load_library()
+    q, k, v, bi, bc, cu, B, T, Hq, Hkv, D, S, code = _prepare(q, k, v, block_indices, block_counts,
+                                                               cu_seqlens)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    nseq = 0 if cu is None else cu.numel() - 1
+    dims = _dims(B, T, Hq, Hkv, D, S, code)
+    need = int(lib.nsa_fwd_workspace_size(ctypes.byref(dims), int(block_size), int(nseq)))
+    if need == 0:
+        # let the library name the problem
+        need = 256
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and return_lse:
+        lse = torch.empty((B, T, Hq), dtype=torch.float32, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = _stream(torch, q.device)
+    if cu is None:
+        status = lib.nsa_fwd(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(bi), _ptr(bc),
+                             int(block_size), float(scale), _ptr(out), _ptr(lse), _ptr(workspace),
+                             ws_bytes, st)
+    else:
+        status = lib.nsa_fwd_varlen(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(bi), _ptr(bc),
+                                    _ptr(cu), int(nseq), int(block_size), float(scale), _ptr(out),
+                                    _ptr(lse), _ptr(workspace), ws_bytes, st)
+    _check(status)
+    return out, lse
+
+
+def schedule(block_indices, block_counts, Hq, D, block_size, dtype="bf16", cu_seqlens=None):
+    """Run only the work scheduler; returns the work list (int32 tensor)."""
+    import torch
+    lib = load_library()
+    B, T, Hkv, S = block_indices.shape
+    code = DTYPE_BF16 if dtype in ("bf16", "bfloat16") else DTYPE_F32
+    dims = _dims(B, T, Hq, Hkv, D, S, code)
+    bi = block_indices.to(dtype=torch.int32).contiguous()
+    bc = block_counts.to(dtype=torch.int32).contiguous()
+    cu = None if cu_seqlens is None else cu_seqlens.to(dtype=torch.int32).contiguous()
+    nseq = 0 if cu is None else cu.numel() - 1
+    need = int(lib.nsa_fwd_workspace_size(ctypes.byref(dims), int(block_size), int(nseq)))
+    ws = torch.empty(max(need, 256), dtype=torch.uint8, device=bi.device)
+    off = ctypes.c_size_t(0)
+    n = ctypes.c_int32(0)
+    status = lib.nsa_fwd_schedule(ctypes.byref(dims), _ptr(bi), _ptr(bc), _ptr(cu), int(nseq),
+                                  int(block_size), _ptr(ws), ws.numel(), _stream(torch, bi.device),
+                                  ctypes.byref(off), ctypes.byref(n))
+    _check(status)
+    return ws[off.value: off.value + 4 * n.value].view(torch.int32).clone()

@@ -1,0 +1,202 @@
+// C ABI of the native sparse attention forward: argument checks, work
+// tiling, workspace layout and launches.  See include/nsa.h for the contract.
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+
+#include "../../include/nsa.h"
+#include "nsa_internal.h"
+
+namespace {
+
+using nsa::Plan;
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Derive tiling and workspace layout.  Returns NSA_SUCCESS or an error.
+nsa_status make_plan(const nsa_dims* d, int32_t block_size, int32_t num_seqs, bool varlen, Plan* p) {
+  if (!d) return NSA_ERROR_INVALID_VALUE;
+  if (d->batch <= 0 || d->seqlen <= 0 || d->num_q_heads <= 0 || d->num_kv_heads <= 0 ||
+      d->head_dim <= 0 || d->num_selected <= 0 || block_size <= 0)
+    return NSA_ERROR_INVALID_VALUE;
+  if (d->num_q_heads % d->num_kv_heads) return NSA_ERROR_INVALID_VALUE;
+  if (varlen && (d->batch != 1 || num_seqs <= 0)) return NSA_ERROR_INVALID_VALUE;
+  if (d->dtype != NSA_DTYPE_F32 && d->dtype != NSA_DTYPE_BF16) return NSA_ERROR_NOT_SUPPORTED;
+  if (d->head_dim != 64 && d->head_dim != 128) return NSA_ERROR_NOT_SUPPORTED;
+  if (block_size != 32 && block_size != 64 && block_size != 128) return NSA_ERROR_NOT_SUPPORTED;
+  const int64_t rows = (int64_t)d->batch * d->seqlen;
+  if (rows * d->num_q_heads * d->head_dim > INT64_C(1) << 40 || rows > INT32_MAX / 2)
+    return NSA_ERROR_NOT_SUPPORTED;
+
+  Plan& P = *p;
+  P = Plan{};
+  P.B = d->batch;
+  P.T = d->seqlen;
+  P.Hq = d->num_q_heads;
+  P.Hkv = d->num_kv_heads;
+  P.D = d->head_dim;
+  P.S = d->num_selected;
+  P.bs = block_size;
+  P.G = P.Hq / P.Hkv;
+  P.varlen = varlen;
+  P.num_seqs = varlen ? num_seqs : P.B;
+  P.bf16 = d->dtype == NSA_DTYPE_BF16;
+  if (P.G <= 16) {
+    P.nt = 1;
+    P.tpt = 16 / P.G;
+    P.tpi = P.nt * P.tpt;
+  } else if (P.G == 32 || P.G == 64) {
+    P.nt = P.G / 16;
+    P.tpt = 1;
+    P.tpi = 1;
+  } else {
+    return NSA_ERROR_NOT_SUPPORTED;
+  }
+  P.ncols = P.tpi * P.G;
+  if ((int64_t)P.tpi * P.S > 64 * nsa::kMaxEntriesPerLane) {
+    // fewer tokens per item when the rows are long
+    if (P.G <= 16 && P.S <= 64 * nsa::kMaxEntriesPerLane) {
+      P.tpt = (64 * nsa::kMaxEntriesPerLane) / P.S;
+      if (P.tpt < 1) P.tpt = 1;
+      P.tpi = P.tpt;
+      P.ncols = P.tpi * P.G;
+    } else {
+      return NSA_ERROR_NOT_SUPPORTED;
+    }
+  }
+  if (P.tpi > 32) return NSA_ERROR_NOT_SUPPORTED;
+  const int64_t Ttot = rows;
+  const int64_t n_tiles =
+      varlen ? Ttot / P.tpi + P.num_seqs : (int64_t)P.B * ((P.T + P.tpi - 1) / P.tpi);
+  const int64_t nb_max = (P.T + P.bs - 1) / P.bs;  // a sequence is at most T long
+  const int64_t n_items = n_tiles * P.Hkv;
+  if (n_items > INT32_MAX / 2) return NSA_ERROR_NOT_SUPPORTED;
+  P.n_tiles = (int32_t)n_tiles;
+  P.n_items = (int32_t)n_items;
+  P.nb_max = (int32_t)nb_max;
+  const int64_t umax = std::min<int64_t>((int64_t)P.tpi * P.S, nb_max);
+  P.umax = (int32_t)(umax < 1 ? 1 : umax);
+  P.n_chunks = (int32_t)((n_items + nsa::kChunk - 1) / nsa::kChunk);
+
+  size_t off = 0;
+  P.off_tile_start = off;
+  off = align_up(off + sizeof(int32_t) * (P.num_seqs + 1), 256);
+  P.off_hdr = off;
+  off = align_up(off + sizeof(nsa::ItemHeader) * n_items, 256);
+  P.off_bucket = off;
+  off = align_up(off + sizeof(int32_t) * n_items, 256);
+  P.off_lists = off;
+  off = align_up(off + sizeof(nsa::BlockEntry) * n_items * P.umax, 256);
+  P.off_hist = off;
+  off = align_up(off + sizeof(int32_t) * (size_t)nsa::kNumBuckets * P.n_chunks, 256);
+  P.off_off = off;
+  off = align_up(off + sizeof(int32_t) * (size_t)nsa::kNumBuckets * P.n_chunks, 256);
+  P.off_total = off;
+  off = align_up(off + sizeof(int32_t) * nsa::kNumBuckets, 256);
+  P.off_worklist = off;
+  off = align_up(off + sizeof(int32_t) * n_items, 256);
+  P.bytes = off;
+  return NSA_SUCCESS;
+}
+
+bool log_enabled() {
+  static int v = -1;
+  if (v < 0) {
+    const char* e = getenv("NSA_LOG");
+    v = (e && e[0] && e[0] != '0') ? 1 : 0;
+  }
+  return v == 1;
+}
+
+nsa_status run(const nsa_dims* d, const void* q, const void* k, const void* v,
+               const int32_t* block_indices, const int32_t* block_counts, const int32_t* cu_seqlens,
+               int32_t num_seqs, bool varlen, int32_t block_size, float scale, void* out, float* lse,
+               void* workspace, size_t workspace_bytes, void* stream) {
+  Plan p;
+  nsa_status st = make_plan(d, block_size, num_seqs, varlen, &p);
+  if (st != NSA_SUCCESS) return st;
+  if (!q || !k || !v || !block_indices || !block_counts || !out || !workspace)
+    return NSA_ERROR_INVALID_VALUE;
+  if (varlen && !cu_seqlens) return NSA_ERROR_INVALID_VALUE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
+      (reinterpret_cast<uintptr_t>(workspace) & 255u))
+    return NSA_ERROR_INVALID_VALUE;
+  if (!std::isfinite(scale)) return NSA_ERROR_INVALID_VALUE;
+  if (workspace_bytes < p.bytes) return NSA_ERROR_WORKSPACE_TOO_SMALL;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  char* ws = reinterpret_cast<char*>(workspace);
+  if (log_enabled())
+    fprintf(stderr, "[nsa] %s D=%d bs=%d G=%d nt=%d tpi=%d items=%d umax=%d ws=%zu\n",
+            p.bf16 ? "bf16" : "f32", p.D, p.bs, p.G, p.nt, p.tpi, p.n_items, p.umax, p.bytes);
+  if (nsa::launch_schedule(p, block_indices, block_counts, cu_seqlens, ws, s) != hipSuccess)
+    return NSA_ERROR_LAUNCH_FAILED;
+  if (nsa::launch_fwd(p, q, k, v, scale, out, lse, ws, s) != hipSuccess)
+    return NSA_ERROR_LAUNCH_FAILED;
+  return NSA_SUCCESS;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t nsa_fwd_workspace_size(const nsa_dims* dims, int32_t block_size, int32_t num_seqs) {
+  Plan p;
+  if (make_plan(dims, block_size, num_seqs, num_seqs > 0, &p) != NSA_SUCCESS) return 0;
+  return p.bytes;
+}
+
+nsa_status nsa_fwd(const nsa_dims* dims, const void* q, const void* k, const void* v,
+                   const int32_t* block_indices, const int32_t* block_counts, int32_t block_size,
+                   float scale, void* out, float* lse, void* workspace, size_t workspace_bytes,
+                   void* stream) {
+  return run(dims, q, k, v, block_indices, block_counts, nullptr, 0, false, block_size, scale, out,
+             lse, workspace, workspace_bytes, stream);
+}
+
+nsa_status nsa_fwd_varlen(const nsa_dims* dims, const void* q, const void* k, const void* v,
+                          const int32_t* block_indices, const int32_t* block_counts,
+                          const int32_t* cu_seqlens, int32_t num_seqs, int32_t block_size,
+                          float scale, void* out, float* lse, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  return run(dims, q, k, v, block_indices, block_counts, cu_seqlens, num_seqs, true, block_size,
+             scale, out, lse, workspace, workspace_bytes, stream);
+}
+
+nsa_status nsa_fwd_schedule(const nsa_dims* dims, const int32_t* block_indices,
+                            const int32_t* block_counts, const int32_t* cu_seqlens,
+                            int32_t num_seqs, int32_t block_size, void* workspace,
+                            size_t workspace_bytes, void* stream, size_t* list_offset,
+                            int32_t* list_len) {
+  const bool varlen = cu_seqlens != nullptr;
+  Plan p;
+  nsa_status st = make_plan(dims, block_size, varlen ? num_seqs : 0, varlen, &p);
+  if (st != NSA_SUCCESS) return st;
+  if (!block_indices || !block_counts || !workspace || !list_offset || !list_len)
+    return NSA_ERROR_INVALID_VALUE;
+  if (reinterpret_cast<uintptr_t>(workspace) & 255u) return NSA_ERROR_INVALID_VALUE;
+  if (workspace_bytes < p.bytes) return NSA_ERROR_WORKSPACE_TOO_SMALL;
+  if (nsa::launch_schedule(p, block_indices, block_counts, cu_seqlens,
+                           reinterpret_cast<char*>(workspace),
+                           reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
+    return NSA_ERROR_LAUNCH_FAILED;
+  *list_offset = p.off_worklist;
+  *list_len = p.n_items;
+  return NSA_SUCCESS;
+}
+
+const char* nsa_status_string(nsa_status status) {
+  switch (status) {
+    case NSA_SUCCESS: return "NSA_SUCCESS";
+    case NSA_ERROR_INVALID_VALUE: return "NSA_ERROR_INVALID_VALUE";
+    case NSA_ERROR_NOT_SUPPORTED: return "NSA_ERROR_NOT_SUPPORTED";
+    case NSA_ERROR_WORKSPACE_TOO_SMALL: return "NSA_ERROR_WORKSPACE_TOO_SMALL";
+    case NSA_ERROR_LAUNCH_FAILED: return "NSA_ERROR_LAUNCH_FAILED";
+  }
+  return "NSA_UNKNOWN_STATUS";
+}
+
+int32_t nsa_abi_version(void) { return NSA_ABI_VERSION; }
+
+}  // extern "C"

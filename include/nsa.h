@@ -1,0 +1,130 @@
+/*
+ * nsa.h -- C ABI of the MI355X (gfx950) native sparse attention forward.
+ *
+ * The operation (ejKernel "native_sparse_attention" API page: the module
+ * description, and "Parameters" of `run` / `native_sparse_attention`): every
+ * query token's group of query heads attends only to the key/value blocks
+ * listed in its row of `block_indices`, truncated to `block_counts` entries,
+ * each block being `block_size` consecutive keys.  Scores are scale * q.k,
+ * normalised by a softmax over the visible keys, and the output is the
+ * probability-weighted sum of the values.  Inside the query's own block only
+ * keys at or before the query position are visible (causal, inclusive
+ * diagonal: the causal block rule of the ejKernel block-sparse mask page).
+ *
+ * Conventions shared by every entry point:
+ *  - All tensor pointers are DEVICE pointers owned by the caller; the
+ *    library allocates nothing, keeps no pointer after a call returns and
+ *    holds no global state.  Work is enqueued asynchronously on `stream`
+ *    (a hipStream_t; NULL means the default stream).
+ *  - Tensors are contiguous row-major with the last dimension fastest:
+ *      q   [B, T, Hq,  D]      (dtype)
+ *      k,v [B, T, Hkv, D]      (dtype)
+ *      block_indices [B, T, Hkv, S]  int32, block ids relative to the
+ *                                     sequence start
+ *      block_counts  [B, T, Hkv]     int32
+ *      out [B, T, Hq,  D]      (dtype, rounded once from fp32)
+ *      lse [B, T, Hq]          float32, natural log of the softmax
+ *                              denominator: log sum_s exp(scale * q.k_s)
+ *    q, k, v and out must be 16-byte aligned.
+ *  - Query head hq uses kv head hq / (Hq / Hkv).
+ *  - Only entries i < clamp(block_counts, 0, S) are read.  Entries that are
+ *    negative, beyond the query's own block or beyond the sequence
+ *    contribute nothing; a block listed twice counts once.  Index contents
+ *    are never an error.  A row with no visible key gets out = 0 and
+ *    lse = -inf.
+ *  - Host-detectable argument errors return synchronously before anything is
+ *    enqueued; a failed launch returns NSA_ERROR_LAUNCH_FAILED.
+ *  - The workspace is caller-owned device memory of at least
+ *    nsa_fwd_workspace_size() bytes, 256-byte aligned; its contents need no
+ *    initialisation and are overwritten.  Two calls that share a workspace
+ *    must be ordered on one stream.
+ */
+#ifndef NSA_H
+#define NSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define NSA_ABI_VERSION 1
+
+typedef enum {
+  NSA_SUCCESS = 0,
+  NSA_ERROR_INVALID_VALUE = 1,      /* null pointer, bad size, misalignment, non-finite scale */
+  NSA_ERROR_NOT_SUPPORTED = 2,      /* head_dim, block_size, group size or dtype not built */
+  NSA_ERROR_WORKSPACE_TOO_SMALL = 3,
+  NSA_ERROR_LAUNCH_FAILED = 4
+} nsa_status;
+
+typedef enum { NSA_DTYPE_F32 = 0, NSA_DTYPE_BF16 = 1 } nsa_dtype;
+
+typedef struct {
+  int32_t batch;        /* B; must be 1 for the varlen entry point            */
+  int32_t seqlen;       /* T; total packed tokens for the varlen entry point  */
+  int32_t num_q_heads;  /* Hq, a multiple of num_kv_heads                     */
+  int32_t num_kv_heads; /* Hkv                                                */
+  int32_t head_dim;     /* D: 64 or 128                                       */
+  int32_t num_selected; /* S, last dimension of block_indices (1..1024)       */
+  nsa_dtype dtype;      /* dtype of q, k, v and out                           */
+} nsa_dims;
+
+/*
+ * Bytes of workspace nsa_fwd / nsa_fwd_varlen need for these dims.
+ * num_seqs = 0 for the fixed-length entry point, else the number of packed
+ * sequences.  Returns 0 if the dims are invalid or not supported.
+ */
+size_t nsa_fwd_workspace_size(const nsa_dims* dims, int32_t block_size, int32_t num_seqs);
+
+/*
+ * Fixed-length forward: B independent sequences of length T.
+ *  block_size: 32, 64 or 128.
+ *  scale: softmax scale applied to q.k (finite).
+ *  lse: may be NULL (then not written).
+ */
+nsa_status nsa_fwd(const nsa_dims* dims, const void* q, const void* k, const void* v,
+                   const int32_t* block_indices, const int32_t* block_counts,
+                   int32_t block_size, float scale, void* out, float* lse,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Variable-length forward (the `cu_seqlens` argument of the same page):
+ * dims->batch == 1, dims->seqlen = total packed tokens, and the sequences
+ * are packed back to back.  cu_seqlens [num_seqs + 1] int32 DEVICE array,
+ * cu_seqlens[0] = 0, non-decreasing, cu_seqlens[num_seqs] = T (a contract
+ * the device does not check).  Block j of a sequence starting at bos covers
+ * tokens [bos + j*block_size, bos + (j+1)*block_size) clipped to the
+ * sequence; keys never come from another sequence.
+ */
+nsa_status nsa_fwd_varlen(const nsa_dims* dims, const void* q, const void* k, const void* v,
+                          const int32_t* block_indices, const int32_t* block_counts,
+                          const int32_t* cu_seqlens, int32_t num_seqs,
+                          int32_t block_size, float scale, void* out, float* lse,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Runs only the work scheduler of a forward call with the same arguments
+ * and copies nothing back: afterwards the workspace holds, at byte offset
+ * *list_offset, *list_len int32 work-item ids in processing order (a
+ * permutation of 0 .. *list_len - 1).  For tests of the scheduler; cu_seqlens
+ * may be NULL (fixed length).
+ */
+nsa_status nsa_fwd_schedule(const nsa_dims* dims, const int32_t* block_indices,
+                            const int32_t* block_counts, const int32_t* cu_seqlens,
+                            int32_t num_seqs, int32_t block_size, void* workspace,
+                            size_t workspace_bytes, void* stream, size_t* list_offset,
+                            int32_t* list_len);
+
+/* Human-readable name of a status code (static storage). */
+const char* nsa_status_string(nsa_status status);
+
+/* NSA_ABI_VERSION of the built library. */
+int32_t nsa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NSA_H */

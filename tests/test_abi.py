@@ -1,0 +1,80 @@
+"""The C-ABI library loads, exports every symbol include/nsa.h declares and
+rejects bad arguments before launching anything (runs without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_index_sparse_amd as nsa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "nsa.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(nsa_[a-z_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = nsa.load_library()
+    names = declared_functions()
+    assert {"nsa_fwd", "nsa_fwd_varlen", "nsa_fwd_workspace_size", "nsa_status_string",
+            "nsa_abi_version", "nsa_fwd_schedule"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.nsa_abi_version() == 1
+
+
+def test_status_strings():
+    lib = nsa.load_library()
+    for code, name in enumerate(["NSA_SUCCESS", "NSA_ERROR_INVALID_VALUE", "NSA_ERROR_NOT_SUPPORTED",
+                                 "NSA_ERROR_WORKSPACE_TOO_SMALL", "NSA_ERROR_LAUNCH_FAILED"]):
+        assert lib.nsa_status_string(code).decode() == name
+
+
+def _call(dims, bs=64, scale=1.0, ptr=256, ws_bytes=1 << 40, varlen=False, nseq=0, nulls=()):
+    lib = nsa.load_library()
+    p = [ctypes.c_void_p(None if i in nulls else ptr) for i in range(8)]
+    if varlen:
+        return lib.nsa_fwd_varlen(ctypes.byref(dims), p[0], p[1], p[2], p[3], p[4], p[5], nseq, bs,
+                                  scale, p[6], None, p[7], ws_bytes, None)
+    return lib.nsa_fwd(ctypes.byref(dims), p[0], p[1], p[2], p[3], p[4], bs, scale, p[6], None, p[7],
+                       ws_bytes, None)
+
+
+def D(B=1, T=128, Hq=16, Hkv=1, Dh=128, S=4, dt=1):
+    return nsa.NsaDims(B, T, Hq, Hkv, Dh, S, dt)
+
+
+@pytest.mark.parametrize("dims,kw,code", [
+    (D(Hkv=3), {}, 1),                    # Hq % Hkv != 0
+    (D(T=0), {}, 1),
+    (D(S=0), {}, 1),
+    (D(Dh=96), {}, 2),
+    (D(), {"bs": 48}, 2),
+    (D(dt=7), {}, 2),
+    (D(Hq=48, Hkv=1), {}, 2),             # G = 48 not built
+    (D(), {"scale": float("nan")}, 1),
+    (D(), {"scale": float("inf")}, 1),
+    (D(), {"nulls": (0,)}, 1),
+    (D(), {"nulls": (6,)}, 1),
+    (D(), {"nulls": (7,)}, 1),
+    (D(), {"ptr": 264}, 1),               # misaligned
+    (D(), {"ws_bytes": 16}, 3),
+    (D(B=2), {"varlen": True, "nseq": 2}, 1),   # varlen needs B == 1
+    (D(), {"varlen": True, "nseq": 0}, 1),
+    (D(), {"varlen": True, "nseq": 1, "nulls": (5,)}, 1),  # cu_seqlens NULL
+])
+def test_bad_arguments_are_rejected(dims, kw, code):
+    assert _call(dims, **kw) == code
+
+
+def test_workspace_sizes():
+    assert nsa.workspace_size(1, 32768, 64, 4, 128, 16, 64) > 0
+    assert nsa.workspace_size(1, 256, 4, 1, 64, 4, 32, "f32") > 0
+    assert nsa.workspace_size(1, 256, 4, 1, 96, 4, 32, "f32") == 0
+    a = nsa.workspace_size(1, 30000, 32, 2, 128, 16, 64, num_seqs=8)
+    b = nsa.workspace_size(1, 30000, 32, 2, 128, 16, 64, num_seqs=100)
+    assert 0 < a < b

@@ -1,0 +1,196 @@
+"""Benchmark of the native sparse attention forward on one MI355X.
+
+A step is one whole forward call (scheduler + attention kernel) over the
+seeded long-context workload: B=1, T=32768, Hq=64, Hkv=4 (GQA group 16),
+D=128, block_size=64, S=16 (one sink block, three local blocks, twelve random
+earlier blocks per token and kv head), bf16 inputs, inputs resident in HBM.
+
+value = useful TFLOP/s = 4 * D * sum over (token, query head) of the visible
+keys |M_t|, divided by the time per step.  The roofline entry describes the
+attention kernel alone (its duration is measured with HIP events recorded on
+the launch stream around that kernel inside every timed step).  The CPU
+baseline times the fp64 oracle on a bounded token sample of the same
+workload on the host's cores.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 3] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "sparse-attn fwd useful TFLOP/s + % of bf16 MFMA peak, T=32k 1 GPU"
+PEAK_BF16_TFLOPS = 2516.6   # 256 CUs x 4096 dense bf16 FLOP/clk/CU x 2.4 GHz
+PEAK_F32_TFLOPS = 157.3     # dense fp32 matrix peak
+PEAK_HBM_GBS = 8000.0
+
+
+def visible_keys_per_row(w) -> np.ndarray:
+    """|M_t| for every (packed token, kv head): keys of the distinct listed
+    blocks 0 <= j <= own, the own block cut at the token's position."""
+    B, T, Hkv, S = w.block_indices.shape
+    bi = w.block_indices.reshape(-1, Hkv, S).astype(np.int64)
+    n = np.clip(w.block_counts.reshape(-1, Hkv), 0, S)
+    if w.cu_seqlens is None:
+        pos = np.tile(np.arange(T), B)
+    else:
+        pos = np.concatenate([np.arange(L) for L in w.seqlens])
+    own = pos // w.block_size
+    keep = (np.arange(S)[None, None, :] < n[..., None]) & (bi >= 0) & (bi <= own[:, None, None])
+    vals = np.where(keep, bi, -1)
+    vals = np.sort(vals, axis=-1)
+    first = np.ones_like(vals, dtype=bool)
+    first[..., 1:] = vals[..., 1:] != vals[..., :-1]
+    distinct = first & (vals >= 0)
+    full = distinct & (vals < own[:, None, None])
+    diag = distinct & (vals == own[:, None, None])
+    part = (pos - own * w.block_size + 1)[:, None]
+    return full.sum(-1) * w.block_size + diag.sum(-1) * part
+
+
+def useful_flops(w, rows=None) -> int:
+    m = visible_keys_per_row(w)
+    if rows is not None:
+        m = m[rows]
+    return int(4 * w.D * w.G * int(m.sum()))
+
+
+def algorithmic_bytes(w) -> int:
+    """q, k, v, out, lse, indices and counts, each moved once."""
+    el = 2 if w.dtype == "bf16" else 4
+    ntok = w.B * w.T
+    return int(ntok * w.Hq * w.D * el * 2 + 2 * ntok * w.Hkv * w.D * el + ntok * w.Hq * 4
+               + w.block_indices.nbytes + w.block_counts.nbytes)
+
+
+def cpu_baseline(w, seconds_target=12.0, seed=0):
+    """Time the fp64 oracle on a seeded token sample sized to ~seconds_target."""
+    import oracle
+    rng = np.random.default_rng(seed)
+    total = w.B * w.T
+    threads = oracle.max_threads()
+    n = 32
+    used = 0.0
+    rows = None
+    while True:
+        rows = np.sort(rng.choice(total, size=min(n, total), replace=False))
+        t0 = time.perf_counter()
+        oracle.fwd_workload(w, tokens=rows)
+        used = time.perf_counter() - t0
+        if used >= seconds_target / 4 or n >= total:
+            break
+        n = min(total, int(n * max(2.0, seconds_target / 4 / max(used, 1e-3))))
+    fl = useful_flops(w, rows)
+    return {"value": fl / used / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{len(rows)} of {total} tokens (seeded uniform sample, all {w.Hq} query heads), "
+                      f"{used:.2f} s fp64 on {threads} OpenMP threads",
+            "seconds": used, "tokens": int(len(rows))}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only (asked for {args.gpus}); "
+              "the path has no multi-GPU mode", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import block_index_sparse_amd as nsa
+    import nsa_inputs as ni
+
+    dev = torch.device("cuda:0")
+    t0 = time.perf_counter()
+    w = ni.make_config(args.config)
+    gen_s = time.perf_counter() - t0
+    print(f"[bench] {w.name}: generated in {gen_s:.1f} s", file=sys.stderr, flush=True)
+    q, k, v, bi, bc, cu = ni.to_torch(w, dev)
+    flop = useful_flops(w)
+    f = nsa.Forward(q, k, v, bi, bc, w.block_size, w.scale, cu_seqlens=cu)
+    torch.cuda.synchronize()
+
+    for _ in range(args.warmup):
+        f.schedule()
+        f.execute()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    e_start, e_stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    e_start.record()
+    for i in range(K):
+        f.schedule()
+        ev[i][0].record()
+        f.execute()
+        ev[i][1].record()
+    e_stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    step_ms = e_start.elapsed_time(e_stop) / K
+    kern_ms = [a.elapsed_time(b) for a, b in ev]
+    kern_avg = float(np.mean(kern_ms))
+
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+    value = flop / (step_ms * 1e-3) / 1e12
+    achieved = flop / (kern_avg * 1e-3) / 1e12
+    props = torch.cuda.get_device_properties(dev)
+    line = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": w.name, "B": w.B, "T": w.T, "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D,
+            "block_size": w.block_size, "S": w.S, "varlen_seqs": None if w.cu_seqlens is None else len(w.seqlens),
+            "useful_flop_per_step": flop, "pct_of_bf16_mfma_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+            "input_sha256": w.digest()[:16], "device": props.name or "gfx950", "cus": props.multi_processor_count,
+            "wall_s_timed": round(wall, 4),
+        },
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "fwd_bf16_kernel" if w.dtype == "bf16" else "fwd_f32_kernel",
+            "achieved": round(achieved, 3),
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4),
+            "traffic": None,
+            "kernel_ms_avg": round(kern_avg, 4),
+            "kernel_ms_min": round(float(np.min(kern_ms)), 4),
+            "algorithmic_flop_per_launch": flop,
+            "algorithmic_bytes_per_launch": algorithmic_bytes(w),
+        },
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a token sample", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(w, seconds_target=args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

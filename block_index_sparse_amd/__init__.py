@@ -19,7 +19,7 @@ import ctypes
 import math
 import os
 
-__all__ = ["fwd", "workspace_size", "schedule", "load_library", "library_path", "NsaError",
+__all__ = ["fwd", "Forward", "workspace_size", "schedule", "load_library", "library_path", "NsaError",
            "DTYPE_F32", "DTYPE_BF16"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -66,6 +66,8 @@ def load_library():
     lib.nsa_fwd_schedule.restype = ctypes.c_int
     lib.nsa_fwd_schedule.argtypes = [dp, p, p, p, i32, i32, p, sz, p, ctypes.POINTER(sz),
                                      ctypes.POINTER(i32)]
+    lib.nsa_fwd_execute.restype = ctypes.c_int
+    lib.nsa_fwd_execute.argtypes = [dp, p, p, p, i32, i32, f32, p, p, p, sz, p]
     lib.nsa_status_string.restype = ctypes.c_char_p
     lib.nsa_status_string.argtypes = [ctypes.c_int]
     lib.nsa_abi_version.restype = i32
@@ -134,39 +136,81 @@ def _prepare(q, k, v, block_indices, block_counts, cu_seqlens):
     return (q.contiguous(), k.contiguous(), v.contiguous(), bi, bc, cu, B, T, Hq, Hkv, D, S, code)
 
 
+class Forward:
+    """A prepared forward call: device buffers and ctypes arguments are built
+    once, so repeated calls cost one C call each.
+
+    ``run()`` is ``nsa_fwd`` / ``nsa_fwd_varlen``; ``schedule()`` and
+    ``execute()`` are its two halves (``nsa_fwd_schedule`` then
+    ``nsa_fwd_execute``).  All launch on torch's current stream of q's device.
+    """
+
+    def __init__(self, q, k, v, block_indices, block_counts, block_size: int = 64,
+                 scale: float | None = None, cu_seqlens=None, out=None, lse=None, workspace=None,
+                 return_lse: bool = True):
+        import torch
+        self.lib = load_library()
+        (self.q, self.k, self.v, self.bi, self.bc, self.cu, B, T, Hq, Hkv, D, S,
+         code) = _prepare(q, k, v, block_indices, block_counts, cu_seqlens)
+        self.scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+        self.block_size = int(block_size)
+        self.nseq = 0 if self.cu is None else self.cu.numel() - 1
+        self.dims = _dims(B, T, Hq, Hkv, D, S, code)
+        need = int(self.lib.nsa_fwd_workspace_size(ctypes.byref(self.dims), self.block_size, self.nseq))
+        need = max(need, 256)  # an unsupported shape is reported by the call itself
+        if workspace is None or workspace.numel() * workspace.element_size() < need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=self.q.device)
+        self.workspace = workspace
+        self.out = torch.empty_like(self.q) if out is None else out
+        self.lse = lse if lse is not None else (
+            torch.empty((B, T, Hq), dtype=torch.float32, device=self.q.device) if return_lse else None)
+        self.ws_bytes = workspace.numel() * workspace.element_size()
+        self.stream = _stream(torch, self.q.device)
+        self._p = {n: _ptr(getattr(self, n)) for n in ("q", "k", "v", "bi", "bc", "cu", "out", "lse",
+                                                        "workspace")}
+
+    def run(self):
+        P, L = self._p, self.lib
+        if self.cu is None:
+            st = L.nsa_fwd(ctypes.byref(self.dims), P["q"], P["k"], P["v"], P["bi"], P["bc"],
+                           self.block_size, self.scale, P["out"], P["lse"], P["workspace"],
+                           self.ws_bytes, self.stream)
+        else:
+            st = L.nsa_fwd_varlen(ctypes.byref(self.dims), P["q"], P["k"], P["v"], P["bi"], P["bc"],
+                                  P["cu"], self.nseq, self.block_size, self.scale, P["out"], P["lse"],
+                                  P["workspace"], self.ws_bytes, self.stream)
+        _check(st)
+        return self.out, self.lse
+
+    def schedule(self):
+        """Scheduler only; returns (byte offset, length) of the work list."""
+        P = self._p
+        off = ctypes.c_size_t(0)
+        n = ctypes.c_int32(0)
+        _check(self.lib.nsa_fwd_schedule(ctypes.byref(self.dims), P["bi"], P["bc"], P["cu"], self.nseq,
+                                         self.block_size, P["workspace"], self.ws_bytes, self.stream,
+                                         ctypes.byref(off), ctypes.byref(n)))
+        return off.value, n.value
+
+    def execute(self):
+        P = self._p
+        _check(self.lib.nsa_fwd_execute(ctypes.byref(self.dims), P["q"], P["k"], P["v"], self.nseq,
+                                        self.block_size, self.scale, P["out"], P["lse"], P["workspace"],
+                                        self.ws_bytes, self.stream))
+        return self.out, self.lse
+
+    def work_list(self):
+        """Run the scheduler and return a copy of the work list (int32)."""
+        import torch
+        off, n = self.schedule()
+        return self.workspace[off: off + 4 * n].view(torch.int32).clone()
+
+
 def fwd(q, k, v, block_indices, block_counts, block_size: int = 64, scale: float | None = None,
         cu_seqlens=None, out=None, lse=None, workspace=None, return_lse: bool = True):
     """Native sparse attention forward on the GPU.  Returns (out, lse)."""
-    import torch
-    lib = load_library()
-    q, k, v, bi, bc, cu, B, T, Hq, Hkv, D, S, code = _prepare(q, k, v, block_indices, block_counts,
-                                                               cu_seqlens)
-    if scale is None:
-        scale = 1.0 / math.sqrt(D)
-    nseq = 0 if cu is None else cu.numel() - 1
-    dims = _dims(B, T, Hq, Hkv, D, S, code)
-    need = int(lib.nsa_fwd_workspace_size(ctypes.byref(dims), int(block_size), int(nseq)))
-    if need == 0:
-        # let the library name the problem
-        need = 256
-    if workspace is None or workspace.numel() * workspace.element_size() < need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    if out is None:
-        out = torch.empty_like(q)
-    if lse is None and return_lse:
-        lse = torch.empty((B, T, Hq), dtype=torch.float32, device=q.device)
-    ws_bytes = workspace.numel() * workspace.element_size()
-    st = _stream(torch, q.device)
-    if cu is None:
-        status = lib.nsa_fwd(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(bi), _ptr(bc),
-                             int(block_size), float(scale), _ptr(out), _ptr(lse), _ptr(workspace),
-                             ws_bytes, st)
-    else:
-        status = lib.nsa_fwd_varlen(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(bi), _ptr(bc),
-                                    _ptr(cu), int(nseq), int(block_size), float(scale), _ptr(out),
-                                    _ptr(lse), _ptr(workspace), ws_bytes, st)
-    _check(status)
-    return out, lse
+    return Forward(q, k, v, block_indices, block_counts, block_size, scale, cu_seqlens, out, lse,
+                   workspace, return_lse).run()
 
 
 def schedule(block_indices, block_counts, Hq, D, block_size, dtype="bf16", cu_seqlens=None):

@@ -101,6 +101,17 @@ nsa_status make_plan(const nsa_dims* d, int32_t block_size, int32_t num_seqs, bo
   return NSA_SUCCESS;
 }
 
+nsa_status check_tensors(const Plan& p, const void* q, const void* k, const void* v, const void* out,
+                         const void* workspace, size_t workspace_bytes, float scale) {
+  if (!q || !k || !v || !out || !workspace) return NSA_ERROR_INVALID_VALUE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
+      (reinterpret_cast<uintptr_t>(workspace) & 255u))
+    return NSA_ERROR_INVALID_VALUE;
+  if (!std::isfinite(scale)) return NSA_ERROR_INVALID_VALUE;
+  if (workspace_bytes < p.bytes) return NSA_ERROR_WORKSPACE_TOO_SMALL;
+  return NSA_SUCCESS;
+}
+
 bool log_enabled() {
   static int v = -1;
   if (v < 0) {
@@ -117,14 +128,10 @@ nsa_status run(const nsa_dims* d, const void* q, const void* k, const void* v,
   Plan p;
   nsa_status st = make_plan(d, block_size, num_seqs, varlen, &p);
   if (st != NSA_SUCCESS) return st;
-  if (!q || !k || !v || !block_indices || !block_counts || !out || !workspace)
-    return NSA_ERROR_INVALID_VALUE;
+  if (!block_indices || !block_counts) return NSA_ERROR_INVALID_VALUE;
   if (varlen && !cu_seqlens) return NSA_ERROR_INVALID_VALUE;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
-      (reinterpret_cast<uintptr_t>(workspace) & 255u))
-    return NSA_ERROR_INVALID_VALUE;
-  if (!std::isfinite(scale)) return NSA_ERROR_INVALID_VALUE;
-  if (workspace_bytes < p.bytes) return NSA_ERROR_WORKSPACE_TOO_SMALL;
+  st = check_tensors(p, q, k, v, out, workspace, workspace_bytes, scale);
+  if (st != NSA_SUCCESS) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   char* ws = reinterpret_cast<char*>(workspace);
   if (log_enabled())
@@ -173,16 +180,29 @@ nsa_status nsa_fwd_schedule(const nsa_dims* dims, const int32_t* block_indices,
   Plan p;
   nsa_status st = make_plan(dims, block_size, varlen ? num_seqs : 0, varlen, &p);
   if (st != NSA_SUCCESS) return st;
-  if (!block_indices || !block_counts || !workspace || !list_offset || !list_len)
-    return NSA_ERROR_INVALID_VALUE;
+  if (!block_indices || !block_counts || !workspace) return NSA_ERROR_INVALID_VALUE;
   if (reinterpret_cast<uintptr_t>(workspace) & 255u) return NSA_ERROR_INVALID_VALUE;
   if (workspace_bytes < p.bytes) return NSA_ERROR_WORKSPACE_TOO_SMALL;
   if (nsa::launch_schedule(p, block_indices, block_counts, cu_seqlens,
                            reinterpret_cast<char*>(workspace),
                            reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
     return NSA_ERROR_LAUNCH_FAILED;
-  *list_offset = p.off_worklist;
-  *list_len = p.n_items;
+  if (list_offset) *list_offset = p.off_worklist;
+  if (list_len) *list_len = p.n_items;
+  return NSA_SUCCESS;
+}
+
+nsa_status nsa_fwd_execute(const nsa_dims* dims, const void* q, const void* k, const void* v,
+                           int32_t num_seqs, int32_t block_size, float scale, void* out,
+                           float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  Plan p;
+  nsa_status st = make_plan(dims, block_size, num_seqs, num_seqs > 0, &p);
+  if (st != NSA_SUCCESS) return st;
+  st = check_tensors(p, q, k, v, out, workspace, workspace_bytes, scale);
+  if (st != NSA_SUCCESS) return st;
+  if (nsa::launch_fwd(p, q, k, v, scale, out, lse, reinterpret_cast<char*>(workspace),
+                      reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
+    return NSA_ERROR_LAUNCH_FAILED;
   return NSA_SUCCESS;
 }
 

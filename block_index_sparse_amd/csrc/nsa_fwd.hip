@@ -103,6 +103,16 @@ __device__ __forceinline__ void column_of(int n, int c, int G, int tpt, int ntok
   }
 }
 
+// A scheduled header is used only if it stays inside the tensors; a
+// workspace that does not hold a matching schedule then cannot make the
+// kernel touch memory outside its arguments.
+__device__ __forceinline__ bool header_ok(ItemHeader& hd, const FwdArgs& a) {
+  if (hd.ntok <= 0 || hd.ntok > 32 || hd.pos0 < 0 || hd.tok0 < hd.pos0) return false;
+  if (hd.tok0 + hd.ntok > a.Ttot) return false;
+  hd.nunion = min(max(hd.nunion, 0), a.umax);
+  return true;
+}
+
 __device__ __forceinline__ uint32_t tile_token_mask(int n, int G, int tpt) {
   return G <= 16 ? (((1u << tpt) - 1u) << (n * tpt)) : 1u;
 }
@@ -135,8 +145,9 @@ __global__ void __launch_bounds__(256, 2) fwd_bf16_kernel(FwdArgs a) {
   const int pos = xcd_remap(blockIdx.x, gridDim.x) * kWaves + wave;
   if (pos >= a.n_items) return;
   const int item = a.worklist[pos];
-  const ItemHeader hd = a.hdr[item];
-  if (hd.ntok <= 0) return;
+  if (item < 0 || item >= a.n_items) return;
+  ItemHeader hd = a.hdr[item];
+  if (!header_ok(hd, a)) return;
   const int h = item / a.n_tiles;
   const int bos = hd.tok0 - hd.pos0;
   const int tmin = hd.pos0;
@@ -175,6 +186,7 @@ __global__ void __launch_bounds__(256, 2) fwd_bf16_kernel(FwdArgs a) {
   const int nsteps_per_block = a.bs / KB;
   for (int u = 0; u < hd.nunion; u++) {
     const BlockEntry be = list[u];
+    if (be.block < 0 || be.block > tmax / a.bs) continue;
     bool act[NT];
     bool sel[NT];
 #pragma unroll
@@ -331,8 +343,9 @@ __global__ void __launch_bounds__(256, 2) fwd_f32_kernel(FwdArgs a) {
   const int pos = xcd_remap(blockIdx.x, gridDim.x) * kWaves + wave;
   if (pos >= a.n_items) return;
   const int item = a.worklist[pos];
-  const ItemHeader hd = a.hdr[item];
-  if (hd.ntok <= 0) return;
+  if (item < 0 || item >= a.n_items) return;
+  ItemHeader hd = a.hdr[item];
+  if (!header_ok(hd, a)) return;
   const int h = item / a.n_tiles;
   const int bos = hd.tok0 - hd.pos0;
   const int tmin = hd.pos0;
@@ -365,6 +378,7 @@ __global__ void __launch_bounds__(256, 2) fwd_f32_kernel(FwdArgs a) {
   const int nsteps_per_block = a.bs / KB;
   for (int u = 0; u < hd.nunion; u++) {
     const BlockEntry be = list[u];
+    if (be.block < 0 || be.block > tmax / a.bs) continue;
     bool act[NT], sel[NT];
 #pragma unroll
     for (int n = 0; n < NT; n++) {

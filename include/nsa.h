@@ -105,17 +105,37 @@ nsa_status nsa_fwd_varlen(const nsa_dims* dims, const void* q, const void* k, co
                           void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * Runs only the work scheduler of a forward call with the same arguments
- * and copies nothing back: afterwards the workspace holds, at byte offset
- * *list_offset, *list_len int32 work-item ids in processing order (a
- * permutation of 0 .. *list_len - 1).  For tests of the scheduler; cu_seqlens
- * may be NULL (fixed length).
+ * The two halves of a forward call.  nsa_fwd(...) is exactly
+ * nsa_fwd_schedule(...) followed by nsa_fwd_execute(...) on the same stream.
+ *
+ * nsa_fwd_schedule reads block_indices / block_counts (and cu_seqlens when
+ * not NULL: varlen, num_seqs sequences; NULL: fixed length, num_seqs
+ * ignored) and writes into the workspace each work item's merged block
+ * list and the longest-first order of the items.  A sparsity pattern known
+ * ahead of time may be indexed once and used many times (module description
+ * of the page), so a schedule stays valid for any number of nsa_fwd_execute
+ * calls with the same dims, block_size and num_seqs while the indices are
+ * unchanged.
+ * If list_offset / list_len are not NULL they receive the byte offset in
+ * the workspace of the int32 work list (processing order, a permutation of
+ * 0 .. *list_len - 1) and its length, for inspection.
+ *
+ * nsa_fwd_execute runs the attention kernel from a schedule previously
+ * written into `workspace` (num_seqs = 0 for fixed length).  It does not
+ * read the indices.  With a workspace that does not hold a schedule for the
+ * same dims, block_size and num_seqs the results are undefined, but the
+ * kernel still reads and writes only inside q, k, v, out, lse and the
+ * workspace (every scheduled value is range-checked before use).
  */
 nsa_status nsa_fwd_schedule(const nsa_dims* dims, const int32_t* block_indices,
                             const int32_t* block_counts, const int32_t* cu_seqlens,
                             int32_t num_seqs, int32_t block_size, void* workspace,
                             size_t workspace_bytes, void* stream, size_t* list_offset,
                             int32_t* list_len);
+
+nsa_status nsa_fwd_execute(const nsa_dims* dims, const void* q, const void* k, const void* v,
+                           int32_t num_seqs, int32_t block_size, float scale, void* out,
+                           float* lse, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Human-readable name of a status code (static storage). */
 const char* nsa_status_string(nsa_status status);

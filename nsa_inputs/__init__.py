@@ -45,7 +45,7 @@ import numpy as np
 __all__ = [
     "Workload", "make_config", "make_workload", "CONFIG_NAMES",
     "uniform", "normal", "hash_u64", "to_bf16_bits", "bf16_bits_to_f32",
-    "sha256_arrays", "varlen_lengths",
+    "sha256_arrays", "varlen_lengths", "to_torch",
 ]
 
 _GOLDEN = np.uint64(0x9E3779B97F4A7C15)
@@ -336,6 +336,22 @@ def varlen_lengths(seed: int, n_seqs: int = 8, lo: int = 512, hi: int = 8192, ma
         attempt += 1
         if attempt > 100000:
             raise RuntimeError("rejection sampling did not converge")
+
+
+def to_torch(w: Workload, device="cuda"):
+    """Device copies (q, k, v, block_indices, block_counts, cu_seqlens) of a
+    workload as torch tensors; bf16 values are moved as their bit patterns."""
+    import torch
+    if w.dtype == "bf16":
+        def t(bits):
+            return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(device)
+        q, k, v = t(w.q_bits), t(w.k_bits), t(w.v_bits)
+    else:
+        q, k, v = (torch.from_numpy(np.ascontiguousarray(a)).to(device) for a in (w.q, w.k, w.v))
+    bi = torch.from_numpy(np.ascontiguousarray(w.block_indices)).to(device)
+    bc = torch.from_numpy(np.ascontiguousarray(w.block_counts)).to(device)
+    cu = None if w.cu_seqlens is None else torch.from_numpy(w.cu_seqlens).to(device)
+    return q, k, v, bi, bc, cu
 
 
 def make_workload(name, dtype, seqlens, Hq, Hkv, D, block_size, S, pattern, counts_mode,

@@ -8,19 +8,8 @@ F32_ATOL = 1e-5
 
 
 def to_device(w, device="cuda"):
-    import torch
-    if w.dtype == "bf16":
-        def t(bits):
-            return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(device)
-        q, k, v = t(w.q_bits), t(w.k_bits), t(w.v_bits)
-    else:
-        q = torch.from_numpy(np.ascontiguousarray(w.q)).to(device)
-        k = torch.from_numpy(np.ascontiguousarray(w.k)).to(device)
-        v = torch.from_numpy(np.ascontiguousarray(w.v)).to(device)
-    bi = torch.from_numpy(np.ascontiguousarray(w.block_indices)).to(device)
-    bc = torch.from_numpy(np.ascontiguousarray(w.block_counts)).to(device)
-    cu = None if w.cu_seqlens is None else torch.from_numpy(w.cu_seqlens).to(device)
-    return q, k, v, bi, bc, cu
+    import nsa_inputs as ni
+    return ni.to_torch(w, device)
 
 
 def run_gpu(w, device="cuda", **kw):

@@ -1,0 +1,25 @@
+"""The benchmark's useful-FLOP count: |M_t| per row equals the oracle's
+exp(lse) with q = 0 (every visible key then weighs exactly 1)."""
+import numpy as np
+import pytest
+
+import nsa_inputs as ni
+import oracle
+from bench import visible_keys_per_row, useful_flops
+
+
+@pytest.mark.parametrize("pattern,counts,varlen,lens", [
+    ("shuffled", "uniform", False, [100, 100]),
+    ("sink_local_random", "full", False, [300]),
+    ("local_random", "uniform", True, [40, 1, 77, 130]),
+])
+def test_visible_key_count_matches_oracle(pattern, counts, varlen, lens):
+    w = ni.make_workload("cnt", "f32", lens, 4, 2, 8, 16, 6, pattern, counts, seed=9, varlen=varlen)
+    w.block_indices[..., -1] = w.block_indices[..., 0]    # a repeat past or inside the count
+    w.q[:] = 0
+    _, lse = oracle.fwd_workload(w)
+    m = visible_keys_per_row(w)                            # [tokens, Hkv]
+    exp = np.round(np.exp(lse)).astype(np.int64)          # [tokens, Hq]
+    G = w.G
+    assert np.array_equal(np.repeat(m, G, axis=1), exp)
+    assert useful_flops(w) == 4 * w.D * int(exp.sum())

@@ -4,7 +4,7 @@
 #include <cstdio>
 #include <cstdlib>
 
-#include "../../include/nsa.h"
+#include "nsa.h"
 #include "nsa_internal.h"
 
 namespace {
@@ -43,60 +43,63 @@ nsa_status make_plan(const nsa_dims* d, int32_t block_size, int32_t num_seqs, bo
   P.varlen = varlen;
   P.num_seqs = varlen ? num_seqs : P.B;
   P.bf16 = d->dtype == NSA_DTYPE_BF16;
+  // head groups of at most 16 heads (one MFMA column tile)
   if (P.G <= 16) {
-    P.nt = 1;
-    P.tpt = 16 / P.G;
-    P.tpi = P.nt * P.tpt;
-  } else if (P.G == 32 || P.G == 64) {
-    P.nt = P.G / 16;
-    P.tpt = 1;
-    P.tpi = 1;
+    P.gv = P.G;
+    P.gpk = 1;
+  } else if (P.G % 16 == 0 && P.G <= 1024) {
+    P.gv = 16;
+    P.gpk = P.G / 16;
   } else {
     return NSA_ERROR_NOT_SUPPORTED;
   }
-  P.ncols = P.tpi * P.G;
-  if ((int64_t)P.tpi * P.S > 64 * nsa::kMaxEntriesPerLane) {
-    // fewer tokens per item when the rows are long
-    if (P.G <= 16 && P.S <= 64 * nsa::kMaxEntriesPerLane) {
-      P.tpt = (64 * nsa::kMaxEntriesPerLane) / P.S;
-      if (P.tpt < 1) P.tpt = 1;
-      P.tpi = P.tpt;
-      P.ncols = P.tpi * P.G;
-    } else {
-      return NSA_ERROR_NOT_SUPPORTED;
-    }
-  }
-  if (P.tpi > 32) return NSA_ERROR_NOT_SUPPORTED;
+  P.hv = P.Hkv * P.gpk;
+  // tokens per 16-column tile: the largest power of two with tpt * gv <= 16
+  P.tpt = 1;
+  while (P.tpt * 2 * P.gv <= 16) P.tpt *= 2;
+  P.ntpw = P.bf16 ? 1 : ((P.tpt * 2 * nsa::kConsumers <= nsa::kMaxTileTokens) ? 2 : 1);
+  P.tpw = P.tpt * P.ntpw;
+  P.tq = nsa::kConsumers * P.tpw;
+  P.kb = P.bs < 64 ? P.bs : 64;
+  P.nsb = P.bs / P.kb;
   const int64_t Ttot = rows;
   const int64_t n_tiles =
-      varlen ? Ttot / P.tpi + P.num_seqs : (int64_t)P.B * ((P.T + P.tpi - 1) / P.tpi);
+      varlen ? Ttot / P.tq + P.num_seqs : (int64_t)P.B * ((P.T + P.tq - 1) / P.tq);
   const int64_t nb_max = (P.T + P.bs - 1) / P.bs;  // a sequence is at most T long
-  const int64_t n_items = n_tiles * P.Hkv;
+  if (nb_max > (int64_t)nsa::kMaxBitmapWords * 32) return NSA_ERROR_NOT_SUPPORTED;
+  const int64_t n_items = n_tiles * P.hv;
   if (n_items > INT32_MAX / 2) return NSA_ERROR_NOT_SUPPORTED;
+  int64_t umax = std::min<int64_t>((int64_t)P.tq * P.S, nb_max);
+  if (umax < 1) umax = 1;
+  if (umax > nsa::kMaxUnion) return NSA_ERROR_NOT_SUPPORTED;
   P.n_tiles = (int32_t)n_tiles;
   P.n_items = (int32_t)n_items;
   P.nb_max = (int32_t)nb_max;
-  const int64_t umax = std::min<int64_t>((int64_t)P.tpi * P.S, nb_max);
-  P.umax = (int32_t)(umax < 1 ? 1 : umax);
+  P.umax = (int32_t)umax;
+  P.umax_units = (int32_t)((umax * P.nsb + 15) / 16 * 16);
   P.n_chunks = (int32_t)((n_items + nsa::kChunk - 1) / nsa::kChunk);
+  int cus = nsa::device_cu_count();
+  if (cus <= 0) cus = 256;
+  const int64_t wg = std::min<int64_t>(n_items, cus);
+  P.nwg = (int32_t)((wg + nsa::kXcds - 1) / nsa::kXcds * nsa::kXcds);
 
   size_t off = 0;
-  P.off_tile_start = off;
-  off = align_up(off + sizeof(int32_t) * (P.num_seqs + 1), 256);
-  P.off_hdr = off;
-  off = align_up(off + sizeof(nsa::ItemHeader) * n_items, 256);
-  P.off_bucket = off;
-  off = align_up(off + sizeof(int32_t) * n_items, 256);
-  P.off_lists = off;
-  off = align_up(off + sizeof(nsa::BlockEntry) * n_items * P.umax, 256);
-  P.off_hist = off;
-  off = align_up(off + sizeof(int32_t) * (size_t)nsa::kNumBuckets * P.n_chunks, 256);
-  P.off_off = off;
-  off = align_up(off + sizeof(int32_t) * (size_t)nsa::kNumBuckets * P.n_chunks, 256);
-  P.off_total = off;
-  off = align_up(off + sizeof(int32_t) * nsa::kNumBuckets, 256);
-  P.off_worklist = off;
-  off = align_up(off + sizeof(int32_t) * n_items, 256);
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = align_up(off + bytes, 256);
+    return at;
+  };
+  P.off_tile_start = take(sizeof(int32_t) * (P.num_seqs + 1));
+  P.off_hdr = take(sizeof(nsa::ItemHeader) * n_items);
+  P.off_bucket = take(sizeof(int32_t) * n_items);
+  P.off_blocks = take(sizeof(int32_t) * n_items * P.umax);
+  P.off_masks = take(sizeof(uint32_t) * nsa::kMaxMaskWords * n_items * P.umax);
+  P.off_units = take(sizeof(uint32_t) * n_items * P.umax_units);
+  P.off_hist = take(sizeof(int32_t) * (size_t)nsa::kNumBuckets * P.n_chunks);
+  P.off_off = take(sizeof(int32_t) * (size_t)nsa::kNumBuckets * P.n_chunks);
+  P.off_total = take(sizeof(int32_t) * nsa::kNumBuckets);
+  P.off_worklist = take(sizeof(int32_t) * n_items);
+  P.off_err = take(sizeof(int32_t) * 4);
   P.bytes = off;
   return NSA_SUCCESS;
 }
@@ -135,8 +138,9 @@ nsa_status run(const nsa_dims* d, const void* q, const void* k, const void* v,
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   char* ws = reinterpret_cast<char*>(workspace);
   if (log_enabled())
-    fprintf(stderr, "[nsa] %s D=%d bs=%d G=%d nt=%d tpi=%d items=%d umax=%d ws=%zu\n",
-            p.bf16 ? "bf16" : "f32", p.D, p.bs, p.G, p.nt, p.tpi, p.n_items, p.umax, p.bytes);
+    fprintf(stderr, "[nsa] %s D=%d bs=%d G=%d gv=%d tpt=%d ntpw=%d tq=%d items=%d umax=%d nwg=%d ws=%zu\n",
+            p.bf16 ? "bf16" : "f32", p.D, p.bs, p.G, p.gv, p.tpt, p.ntpw, p.tq, p.n_items, p.umax,
+            p.nwg, p.bytes);
   if (nsa::launch_schedule(p, block_indices, block_counts, cu_seqlens, ws, s) != hipSuccess)
     return NSA_ERROR_LAUNCH_FAILED;
   if (nsa::launch_fwd(p, q, k, v, scale, out, lse, ws, s) != hipSuccess)

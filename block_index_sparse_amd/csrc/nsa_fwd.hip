@@ -1,36 +1,45 @@
 // Native sparse attention forward kernels for gfx950 (CDNA4).
 //
 // Operation (ejKernel native_sparse_attention API page, module description
-// and "Parameters"): for each query token, the G query heads of kv head h
+// and "Parameters"): for each query token, the query heads of kv head h
 // attend to the keys of the blocks listed for (token, h), causal inside the
 // token's own block; softmax(scale * q.k) weighted sum of v, plus the
 // log-sum-exp of the scores.
 //
-// Mapping onto the matrix cores.  One wave owns one work item (a tile of
-// consecutive tokens of one sequence and one kv head) and walks the item's
-// merged block list in ascending block order.  The MFMA "N" dimension (16
-// columns) holds query heads -- the G heads of one token, or 16/G tokens x G
-// heads when G < 16 -- so one gathered K/V block feeds every head of the GQA
-// group.  The products are computed transposed:
+// bf16 kernel: persistent workgroups of 12 waves, one per CU.
+//  * 4 loader waves stream the K and V rows of each item's merged block list
+//    (ascending block order, `kb` keys per unit) into a ring of R LDS slots
+//    with direct-to-LDS 16-byte loads (global_load_lds_dwordx4).  A slot is
+//    refilled only when every attention wave has released it; a loader
+//    publishes its share of a unit as soon as its own loads have landed.
+//  * 8 attention waves each own a fixed set of the item's tokens and walk
+//    the same unit sequence without any barrier: a wave waits only for the
+//    unit's data, computes its own tokens that selected the block, releases
+//    the slot and moves on, so tokens with different block lists do not
+//    hold each other up.  A gathered block feeds every token of the item
+//    that listed it, and every query head of those tokens.
+//  * Matrix work, per 16 query columns (the G heads of one token, or 16/G
+//    tokens x G heads when G < 16):
+//        S^T (keys x cols) = K (keys x D) . Q^T (D x cols)     A = K rows
+//        O^T (D x cols)   += V^T (D x keys) . P^T (keys x cols)
+//    with v_mfma_f32_16x16x32_bf16.  In this orientation the fp32 S^T
+//    accumulator layout (lane = column, four consecutive keys per lane group)
+//    is exactly the B-operand layout of P^T, so P stays in registers.  K
+//    fragments are ds_read_b128 from the slot; V^T fragments come from
+//    ds_read_b64_tr_b16, the gfx950 transposing LDS read (lanes 4r..4r+3 of a
+//    16-lane group supply row r of a 4 x 16 tile, lane i receives column i).
+//    Both slot halves are XOR-swizzled by 16-byte chunk so these reads are
+//    free of bank conflicts.
+//  * fp32 online softmax in the log2 domain: scores scaled by scale*log2(e),
+//    v_exp_f32 for 2^x, running max and normaliser per column (the
+//    (output, max, normaliser) carry of a flash-attention block step, as in
+//    `flash_attention_block` on the ejKernel ragged-decode page), causal
+//    mask evaluated only on units that reach past a wave's first token.
+//  * Every wait is a bounded spin: a wave that waits too long records an
+//    error word in the workspace and leaves, so the grid always drains.
 //
-//   S^T (keys x cols) = K (keys x D) . Q^T (D x cols)       A = K rows, B = Q
-//   O^T (D x cols)   += V^T (D x keys) . P^T (keys x cols)  A = V^T, B = P^T
-//
-// With this orientation the fp32 accumulator layout of S^T (lane = column,
-// four consecutive keys per lane group) is exactly the B-operand layout P^T
-// needs, so P never leaves its registers: it is exponentiated, rounded to
-// bf16 and fed back to the PV product in place.  V^T fragments come from a
-// per-wave LDS copy of the block through ds_read_b64_tr_b16, the gfx950
-// transposing LDS read (lanes 4r..4r+3 of each 16-lane group supply row r of
-// a 4x16 tile and lane i receives column i).  K fragments are 16-byte global
-// loads straight into the A-operand registers.
-//
-// Softmax: fp32 online softmax in the log2 domain (scores pre-multiplied by
-// scale*log2(e), v_exp_f32 for 2^x), running max and normaliser per column,
-// cross-lane reductions over the four lane groups, causal mask evaluated only
-// on blocks that reach past the item's first token.  The running state is
-// the (output, max, normaliser) carry of a flash-attention block step (the
-// `flash_attention_block` carry on the ejKernel ragged-decode page).
+// fp32 kernel: one wave per (item, token group) reading K and V straight
+// from global memory, v_mfma_f32_16x16x4_f32, P kept in fp32.
 #include "nsa_internal.h"
 
 namespace nsa {
@@ -41,9 +50,34 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 
 #define NSA_LDS __attribute__((address_space(3)))
+#define NSA_CONST __attribute__((address_space(4)))
+
+// Schedule reads go through the constant address space: with a wave-uniform
+// address they become scalar loads, which keeps the vector-memory counter
+// free for the loader waves' own direct-to-LDS traffic.
+template <typename T>
+__device__ __forceinline__ T ld_const(const T* p, int64_t i) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  return ((const NSA_CONST T*)p)[i];
+#else
+  return p[i];
+#endif
+}
+
+__device__ __forceinline__ uint4 ld_const_mask(const uint4* p, int64_t i) {
+  const uint32_t* w = reinterpret_cast<const uint32_t*>(p) + i * 4;
+  uint4 m;
+  m.x = ld_const(w, 0);
+  m.y = ld_const(w, 1);
+  m.z = ld_const(w, 2);
+  m.w = ld_const(w, 3);
+  return m;
+}
+
+constexpr int kMaxSpin = 1 << 22;        // polls before a wait is declared stuck
+constexpr int32_t kErrStuck = 1;
 
 struct FwdArgs {
   const void* q;
@@ -52,318 +86,625 @@ struct FwdArgs {
   void* out;
   float* lse;
   const ItemHeader* hdr;
-  const BlockEntry* lists;
+  const int32_t* blocks;
+  const uint4* masks;
+  const uint32_t* units;
   const int32_t* worklist;
+  int32_t* err;
   int32_t Ttot;     // packed token rows
-  int32_t Hq, Hkv, G, tpt, n_tiles, n_items, umax, bs;
+  int32_t Hq, Hkv, G, gv, gpk, tpt, tpw, n_tiles, n_items, umax, umax_units, bs, nwg;
   float scale_log2;  // scale * log2(e)
 };
 
-// Workgroups are dispatched round-robin over the 8 XCDs (workgroup i runs
-// on XCD i % 8).  Remap so that each XCD walks consecutive runs of
-// kXcdRun workgroups of the longest-first list: neighbouring items (same kv
-// head, adjacent tokens, shared sink/local blocks) then share one L2.
-constexpr int kXcds = 8;
-constexpr int kXcdRun = 8;
-
-__device__ __forceinline__ int xcd_remap(int wg, int nwg) {
-  const int group = kXcds * kXcdRun;
-  const int full = (nwg / group) * group;
-  if (wg >= full) return wg;
-  const int x = wg % kXcds, k = wg / kXcds;
-  return (k / kXcdRun) * group + x * kXcdRun + (k % kXcdRun);
-}
-
-__device__ __forceinline__ float wave_max_groups(float v) {
-  // reduce over the four 16-lane groups (lanes c, c+16, c+32, c+48)
-  v = fmaxf(v, __shfl_xor(v, 16, 64));
-  v = fmaxf(v, __shfl_xor(v, 32, 64));
-  return v;
-}
-
-__device__ __forceinline__ float wave_sum_groups(float v) {
-  v += __shfl_xor(v, 16, 64);
-  v += __shfl_xor(v, 32, 64);
-  return v;
-}
-
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// Column c of column tile n -> (token offset in item, head in group, valid).
-__device__ __forceinline__ void column_of(int n, int c, int G, int tpt, int ntok, int& tau,
-                                          int& head, bool& valid) {
-  if (G <= 16) {
-    tau = n * tpt + c / G;
-    head = c - (c / G) * G;
-    valid = (c < tpt * G) && (tau < ntok);
-  } else {
-    tau = 0;
-    head = n * 16 + c;
-    valid = true;
-  }
-}
-
-// A scheduled header is used only if it stays inside the tensors; a
-// workspace that does not hold a matching schedule then cannot make the
-// kernel touch memory outside its arguments.
+// A header is used only if it stays inside the tensors: a workspace that does
+// not hold a matching schedule then cannot make the kernels touch memory
+// outside their arguments.
 __device__ __forceinline__ bool header_ok(ItemHeader& hd, const FwdArgs& a) {
-  if (hd.ntok <= 0 || hd.ntok > 32 || hd.pos0 < 0 || hd.tok0 < hd.pos0) return false;
+  if (hd.ntok <= 0 || hd.ntok > kMaxTileTokens || hd.pos0 < 0 || hd.tok0 < hd.pos0) return false;
   if (hd.tok0 + hd.ntok > a.Ttot) return false;
   hd.nunion = min(max(hd.nunion, 0), a.umax);
   return true;
 }
 
-__device__ __forceinline__ uint32_t tile_token_mask(int n, int G, int tpt) {
-  return G <= 16 ? (((1u << tpt) - 1u) << (n * tpt)) : 1u;
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ float max_over_groups(float v) {
+  // lanes c, c+16, c+32, c+48 hold the same column
+  v = fmaxf(v, __shfl_xor(v, 16, 64));
+  v = fmaxf(v, __shfl_xor(v, 32, 64));
+  return v;
 }
 
-// XOR swizzle of 16-byte chunks in the LDS copy of V: rows that one
-// transposing read touches together land on distinct bank groups.
+__device__ __forceinline__ float sum_over_groups(float v) {
+  v += __shfl_xor(v, 16, 64);
+  v += __shfl_xor(v, 32, 64);
+  return v;
+}
+
+// Column c of a 16-column tile whose first token is `tok_base` -> token
+// offset, head inside the group, valid.
+__device__ __forceinline__ void column_of(int c, int gv, int tpt, int tok_base, int ntok, int& tau,
+                                          int& head, bool& valid) {
+  const int lt = c / gv;
+  tau = tok_base + lt;
+  head = c - lt * gv;
+  valid = (lt < tpt) && (tau < ntok);
+}
+
+__device__ __forceinline__ uint32_t mask_bits(const uint4& m, int first, int count) {
+  // `count` bits of the 128-bit token set starting at bit `first` (count is
+  // a power of two <= 32 and first a multiple of it, so the field never
+  // straddles words)
+  const int w = first >> 5;
+  const uint32_t word = w == 0 ? m.x : (w == 1 ? m.y : (w == 2 ? m.z : m.w));
+  const uint32_t sh = word >> (first & 31);
+  return count >= 32 ? sh : (sh & ((1u << count) - 1u));
+}
+
+// 16-byte chunk swizzles of a slot.  K rows are read as ds_read_b128 by
+// 16 consecutive rows, V rows by the transposing read in 4 x 16 tiles.
+template <int D>
+__device__ __forceinline__ int k_swizzle(int row) {
+  constexpr int kRowsPer256 = (256 / (D * 2)) > 0 ? 256 / (D * 2) : 1;
+  constexpr int kChunks = D / 8;
+  return (row / kRowsPer256) & (kChunks - 1);
+}
 template <int D>
 __device__ __forceinline__ int v_swizzle(int row) {
-  constexpr int kRowsPer256 = 256 / (D * 2) > 0 ? 256 / (D * 2) : 1;
-  constexpr int kPairs = D / 16;  // 16-byte chunk pairs per row
+  constexpr int kRowsPer256 = (256 / (D * 2)) > 0 ? 256 / (D * 2) : 1;
+  constexpr int kPairs = D / 16;
   return ((row / kRowsPer256) & (kPairs - 1)) << 1;
 }
 
+// s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Wait until at most `newer` units (SHARE loads each) of this wave are still
+// in flight; loads complete in issue order for the counter.
+template <int SHARE>
+__device__ __forceinline__ void wait_units_older_than(int newer) {
+  switch (newer) {
+    case 0: wait_vmcnt<0>(); break;
+    case 1: wait_vmcnt<(1 * SHARE < 64 ? 1 * SHARE : 0)>(); break;
+    case 2: wait_vmcnt<(2 * SHARE < 64 ? 2 * SHARE : 0)>(); break;
+    case 3: wait_vmcnt<(3 * SHARE < 64 ? 3 * SHARE : 0)>(); break;
+    case 4: wait_vmcnt<(4 * SHARE < 64 ? 4 * SHARE : 0)>(); break;
+    case 5: wait_vmcnt<(5 * SHARE < 64 ? 5 * SHARE : 0)>(); break;
+    case 6: wait_vmcnt<(6 * SHARE < 64 ? 6 * SHARE : 0)>(); break;
+    default: wait_vmcnt<0>(); break;
+  }
+}
+
+// Ring counters live in LDS and are accessed with relaxed atomics; ordering
+// is made explicit so that no wait covers more than it must (an acquire or
+// release at workgroup scope would also drain the loader waves' in-flight
+// direct-to-LDS loads):
+//  * a loader publishes a unit after s_waitcnt vmcnt has retired that unit's
+//    own loads (their data is then in LDS);
+//  * an attention wave releases a slot after an LDS-only release fence
+//    (s_waitcnt lgkmcnt(0): its reads of the slot have returned);
+//  * reads of a slot are issued only after the counter that allows them was
+//    observed (control dependence, plus a compiler fence).
+__device__ __forceinline__ int lds_poll(int* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+// Loader-side counter accesses.  The compiler cannot tell the ring slots
+// (written by direct-to-LDS loads) from the counters, and would retire every
+// in-flight load before touching a counter; written as plain LDS
+// instructions they wait only for themselves.
+__device__ __forceinline__ uint32_t lds_offset(int* p) {
+  return (uint32_t)(uintptr_t)((NSA_LDS int*)p);
+}
+__device__ __forceinline__ int loader_poll(int* p) {
+  int v;
+  asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(lds_offset(p)) : "memory");
+  return __builtin_amdgcn_readfirstlane(v);   // the same value in every lane
+}
+// One increment per wave: only lane 0 adds (every active lane of an LDS
+// atomic would otherwise add its own 1).
+__device__ __forceinline__ void loader_bump(int* p) {
+  if ((threadIdx.x & 63) == 0)
+    asm volatile("ds_add_u32 %0, %1" : : "v"(lds_offset(p)), "v"(1) : "memory");
+}
+__device__ __forceinline__ void lds_release_bump(int* p) {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  if ((threadIdx.x & 63) == 0) __hip_atomic_fetch_add(p, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+// Item of round r for workgroup g: each XCD takes a contiguous stretch of
+// the longest-first list per round, so neighbouring items (same head group,
+// adjacent tokens, shared sink/local blocks) meet in one L2.
+__device__ __forceinline__ int list_position(int g, int round, int nwg) {
+  const int per = nwg / kXcds;
+  return round * nwg + (g % kXcds) * per + g / kXcds;
+}
+
+// Item walk shared by every wave of a workgroup: rounds of the
+// longest-first list, skipping items whose header is out of range.
+struct ItemCursor {
+  int round;
+  int item;
+  ItemHeader hd;
+  bool valid;
+};
+
+__device__ __forceinline__ void next_item(ItemCursor& cs, const FwdArgs& a) {
+  while (true) {
+    const int pos = list_position(blockIdx.x, cs.round, a.nwg);
+    if (pos >= a.n_items) {
+      cs.valid = false;
+      return;
+    }
+    cs.round++;
+    const int item = ld_const(a.worklist, pos);
+    if (item < 0 || item >= a.n_items) continue;
+    const int32_t* hw = reinterpret_cast<const int32_t*>(a.hdr) + (int64_t)item * 4;
+    ItemHeader hd{ld_const(hw, 0), ld_const(hw, 1), ld_const(hw, 2), ld_const(hw, 3)};
+    if (!header_ok(hd, a)) continue;
+    cs.item = item;
+    cs.hd = hd;
+    cs.valid = true;
+    return;
+  }
+}
+
 // ---------------------------------------------------------------------------
-// bf16: D in {64, 128}, KB keys per step in {32, 64}, NT column tiles per item
+// bf16 ring kernel
+//
+// Units: every item contributes nunion * (bs / kb) units, numbered
+// v = (units of earlier items of this workgroup) + u * (bs / kb) + sb, in the
+// same order on every wave; unit v lives in slot v % R.  A unit is "live" if
+// its block is in range and its first key is not past the item's last token.
+// An attention wave reads a unit iff the unit is live, one of the wave's
+// tokens listed the block and the unit's first key is not past the wave's
+// last token; the number of such waves is the unit's participant count.
+//  * ready[s] counts loader publications of slot s (every unit, live or not,
+//    is published by each loader, in order): unit v is readable once
+//    ready[v % R] >= kProducers * (v / R + 1).
+//  * done[s] counts participant releases of slot s: a loader may overwrite
+//    slot s once done[s] has reached the participant total of all earlier
+//    occupants.  A wave can only reach a later occupant after it was
+//    published, which already required every reader of the earlier one to
+//    have released it, so the counts of successive occupants never mix.
+// Waves therefore touch only the units they compute.
 // ---------------------------------------------------------------------------
-template <int D, int KB, int NT>
-__global__ void __launch_bounds__(256, 2) fwd_bf16_kernel(FwdArgs a) {
+template <int D, int KB>
+struct RingCfg {
+  static constexpr int kSlotBytes = 2 * KB * D * 2;              // K then V
+  static constexpr int kR0 = (128 * 1024) / kSlotBytes;
+  static constexpr int R = kR0 > 8 ? 8 : kR0;                    // ring slots
+  static constexpr int kLoadsKV = (KB * D * 2) / 1024;           // 1 KB loads per K (or V) unit
+  static constexpr int SHARE = 2 * kLoadsKV / kProducers;        // loads per loader wave per unit
+  static constexpr int kMaxF0 = 63 / SHARE;
+  static constexpr int kMaxF1 = kMaxF0 < R ? kMaxF0 : R;
+  static constexpr int MAXF = kMaxF1 < 7 ? kMaxF1 : 7;           // units in flight per loader
+  static constexpr int kRowsPerLoad = 1024 / (D * 2);
+  static constexpr int kUnitLoads = 2 * kLoadsKV;                // loads of one whole unit
+  static constexpr int kOwnSlots0 = R / kProducers;              // units in flight per loader
+  static constexpr int kOwnSlots1 = kOwnSlots0 * kUnitLoads <= 63 ? kOwnSlots0 : 63 / kUnitLoads;
+  static constexpr int kOwnSlots = kOwnSlots1 < 1 ? 1 : kOwnSlots1;
+  static_assert(R % kProducers == 0, "slots per loader");
+  static_assert(kUnitLoads <= 63, "one unit must fit the load counter");
+};
+
+template <int D, int KB, int NTPW>
+__global__ void __launch_bounds__(64 * (kConsumers + kProducers), 1) fwd_bf16_ring_kernel(FwdArgs a) {
+  using C = RingCfg<D, KB>;
+  constexpr int R = C::R;
   constexpr int KT = D / 32;   // k-steps of S^T = K Q^T
   constexpr int MT = KB / 16;  // 16-key row tiles of S^T
   constexpr int KQ = KB / 32;  // 32-key k-steps of O^T += V^T P^T
   constexpr int DT = D / 16;   // 16-row tiles of O^T
-  constexpr int CH = D / 8;    // 16-byte chunks per K/V row
-  __shared__ __attribute__((aligned(16))) __bf16 vlds[kWaves][KB * D];
+  constexpr int CH = D / 8;    // 16-byte chunks per row
+
+  __shared__ __attribute__((aligned(1024))) char ring[R][C::kSlotBytes];
+  __shared__ int ready[R];
+  __shared__ int done[R];
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
+  if (threadIdx.x < R) {
+    ready[threadIdx.x] = 0;
+    done[threadIdx.x] = 0;
+  }
+  __syncthreads();
+
+  const int nsb = a.bs / KB;  // units per listed block
+  ItemCursor cs;
+  cs.round = 0;
+  next_item(cs, a);
+
+  if (wave >= kConsumers) {
+    // ------------------------------------------------------------ loader
+    // Loader p owns the units v with v % kProducers == p: it loads all of a
+    // unit's K and V rows and publishes the unit as soon as its own loads
+    // have landed.  It keeps up to R / kProducers of its units in flight.
+    const __bf16* __restrict__ K = reinterpret_cast<const __bf16*>(a.k);
+    const __bf16* __restrict__ V = reinterpret_cast<const __bf16*>(a.v);
+    const int p = wave - kConsumers;
+    int tgt[R];
+#pragma unroll
+    for (int s = 0; s < R; s++) tgt[s] = 0;
+    int v_next = 0;         // next unit of the stream to examine
+    int v_pub = p;          // oldest own unit not yet published
+    int n_fly = 0;          // own units issued and not yet published
+    uint32_t loaded = 0;    // bit i: the i-th oldest unpublished own unit carries loads
+    int spins = 0;
+    int uu = 0;             // unit index inside the current item
+    int nunits = cs.valid ? cs.hd.nunion * nsb : 0;
+    bool stuck = false;
+    bool have = false;      // metadata of unit v_next is loaded
+    int kstart = 0, npart = 0;
+    while (true) {
+      // find the next own unit of the stream
+      while (!have) {
+        while (cs.valid && uu >= nunits) {
+          next_item(cs, a);
+          uu = 0;
+          nunits = cs.valid ? cs.hd.nunion * nsb : 0;
+        }
+        if (!cs.valid) break;
+        if (v_next % kProducers != p) {
+          v_next++;
+          uu++;
+          continue;
+        }
+        const int u = uu / nsb;
+        const int sb = uu - u * nsb;
+        const uint32_t word = ld_const(a.units, (int64_t)cs.item * a.umax_units + uu);
+        npart = (word >> 31) != 0u ? (int)((word >> 24) & 15u) : 0;
+        kstart = (int)(word & 0xFFFFFFu) * a.bs + sb * KB;
+        have = true;
+      }
+      if (have && n_fly < C::kOwnSlots) {
+        const int slot = v_next % R;
+        int t = 0;
+#pragma unroll
+        for (int s = 0; s < R; s++) t = (s == slot) ? tgt[s] : t;
+        if (npart == 0 || loader_poll(&done[slot]) >= t) {
+          __atomic_signal_fence(__ATOMIC_SEQ_CST);
+          if (npart > 0) {
+            const int h = cs.item / a.n_tiles / a.gpk;
+            const int row0 = cs.hd.tok0 - cs.hd.pos0 + kstart;
+            NSA_LDS char* kdst = (NSA_LDS char*)&ring[slot][0];
+            NSA_LDS char* vdst = kdst + KB * D * 2;
+#pragma unroll
+            for (int li = 0; li < 2 * C::kLoadsKV; li++) {
+              const bool isv = li >= C::kLoadsKV;
+              const int ld = isv ? li - C::kLoadsKV : li;   // 1 KB load index within K or V
+              const int r = ld * C::kRowsPerLoad + lane / CH;
+              const int pc = lane % CH;
+              const int lc = pc ^ (isv ? v_swizzle<D>(r) : k_swizzle<D>(r));
+              int grow = row0 + r;
+              grow = grow < a.Ttot ? grow : a.Ttot - 1;
+              const __bf16* src = (isv ? V : K) + ((int64_t)grow * a.Hkv + h) * D + lc * 8;
+              NSA_LDS char* dst = (isv ? vdst : kdst) + ld * 1024;
+              __builtin_amdgcn_global_load_lds(src, (NSA_LDS void*)dst, 16, 0, 0);
+            }
+#pragma unroll
+            for (int s = 0; s < R; s++) tgt[s] += (s == slot) ? npart : 0;
+            loaded |= 1u << n_fly;
+          }
+          n_fly++;
+          v_next++;
+          uu++;
+          have = false;
+          spins = 0;
+          continue;
+        }
+      }
+      if (n_fly > 0) {
+        // publish the oldest own unit once its loads have landed
+        if (loaded & 1u) wait_units_older_than<C::kUnitLoads>(__popc(loaded >> 1));
+        loader_bump(&ready[v_pub % R]);
+        loaded >>= 1;
+        n_fly--;
+        v_pub += kProducers;
+        spins = 0;
+        continue;
+      }
+      if (!have) break;  // stream exhausted and everything published
+      __builtin_amdgcn_s_sleep(1);
+      if (++spins > kMaxSpin) {
+        stuck = true;
+        break;
+      }
+    }
+    if (stuck) atomicOr(a.err, kErrStuck);
+    return;
+  }
+
+  // ------------------------------------------------------------ attention
   const int c = lane & 15;
   const int g = lane >> 4;
-  const int pos = xcd_remap(blockIdx.x, gridDim.x) * kWaves + wave;
-  if (pos >= a.n_items) return;
-  const int item = a.worklist[pos];
-  if (item < 0 || item >= a.n_items) return;
-  ItemHeader hd = a.hdr[item];
-  if (!header_ok(hd, a)) return;
-  const int h = item / a.n_tiles;
-  const int bos = hd.tok0 - hd.pos0;
-  const int tmin = hd.pos0;
-  const int tmax = hd.pos0 + hd.ntok - 1;
+  const int tpw = a.tpw;
+  const int tok_first = wave * tpw;   // this wave's first token inside an item
   const __bf16* __restrict__ Q = reinterpret_cast<const __bf16*>(a.q);
-  const __bf16* __restrict__ K = reinterpret_cast<const __bf16*>(a.k);
-  const __bf16* __restrict__ V = reinterpret_cast<const __bf16*>(a.v);
-  NSA_LDS __bf16* vl = (NSA_LDS __bf16*)(&vlds[wave][0]);
+  __bf16* __restrict__ Out = reinterpret_cast<__bf16*>(a.out);
+  int v_base = 0;
+  bool stuck = false;
+  while (cs.valid && !stuck) {
+    const int item = cs.item;
+    const ItemHeader hd = cs.hd;
+    const int vg = item / a.n_tiles;
+    const int my_ntok = min(max(hd.ntok - tok_first, 0), tpw);
+    const int my_tmin = hd.pos0 + tok_first;
+    const int my_tmax = my_tmin + my_ntok - 1;
+    const int nunits = hd.nunion * nsb;
 
-  int tau[NT], hq[NT], tcol[NT];
-  bool cvalid[NT];
-  bf16x8 qf[NT][KT];
-  f32x4 o[NT][DT];
-  float mrun[NT], lrun[NT];
+    int tau[NTPW], hq[NTPW], tcol[NTPW];
+    uint32_t tvalid[NTPW];
+    bool cvalid[NTPW];
+    bf16x8 qf[NTPW][KT];
+    f32x4 o[NTPW][DT];
+    float mrun[NTPW], lrun[NTPW];
 #pragma unroll
-  for (int n = 0; n < NT; n++) {
-    int head;
-    column_of(n, c, a.G, a.tpt, hd.ntok, tau[n], head, cvalid[n]);
-    hq[n] = h * a.G + head;
-    tcol[n] = hd.pos0 + tau[n];
-    const int64_t qrow = ((int64_t)(hd.tok0 + (cvalid[n] ? tau[n] : 0)) * a.Hq + hq[n]) * D;
+    for (int n = 0; n < NTPW; n++) {
+      int head;
+      column_of(c, a.gv, a.tpt, tok_first + n * a.tpt, hd.ntok, tau[n], head, cvalid[n]);
+      hq[n] = vg * a.gv + head;
+      tcol[n] = hd.pos0 + tau[n];
+      {
+        // tokens of tile n (bits relative to tok_first) that exist
+        const int t0 = n * a.tpt;
+        const int nv = min(max(my_ntok - t0, 0), a.tpt);
+        tvalid[n] = nv >= 32 ? 0xFFFFFFFFu : (((1u << nv) - 1u) << t0);
+      }
+      const int64_t qrow = ((int64_t)(hd.tok0 + (cvalid[n] ? tau[n] : 0)) * a.Hq + hq[n]) * D;
 #pragma unroll
-    for (int kk = 0; kk < KT; kk++) {
-      if (cvalid[n])
-        qf[n][kk] = *reinterpret_cast<const bf16x8*>(Q + qrow + kk * 32 + g * 8);
-      else
-        qf[n][kk] = bf16x8{0, 0, 0, 0, 0, 0, 0, 0};
+      for (int kk = 0; kk < KT; kk++) {
+        if (cvalid[n])
+          qf[n][kk] = *reinterpret_cast<const bf16x8*>(Q + qrow + kk * 32 + g * 8);
+        else
+          qf[n][kk] = bf16x8{0, 0, 0, 0, 0, 0, 0, 0};
+      }
+#pragma unroll
+      for (int dt = 0; dt < DT; dt++) o[n][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      mrun[n] = -INFINITY;
+      lrun[n] = 0.f;
     }
-#pragma unroll
-    for (int dt = 0; dt < DT; dt++) o[n][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    mrun[n] = -INFINITY;
-    lrun[n] = 0.f;
-  }
 
-  const BlockEntry* list = a.lists + (int64_t)item * a.umax;
-  const int nsteps_per_block = a.bs / KB;
-  for (int u = 0; u < hd.nunion; u++) {
-    const BlockEntry be = list[u];
-    if (be.block < 0 || be.block > tmax / a.bs) continue;
-    bool act[NT];
-    bool sel[NT];
+    // find this wave's units 64 at a time: lane i examines unit cbase + i
+    for (int cbase = 0; cbase < nunits && my_ntok > 0 && !stuck; cbase += 64) {
+      const int uu = cbase + lane;
+      int lj = -1;
+      uint32_t lbits = 0u;
+      bool part = false;
+      if (uu < nunits) {
+        const int u = uu / nsb;
+        const int sb = uu - u * nsb;
+        const uint32_t word = a.units[(int64_t)item * a.umax_units + uu];
+        lj = (int)(word & 0xFFFFFFu);
+        const int ks = lj * a.bs + sb * KB;
+        if ((word >> 31) != 0u && ks <= my_tmax) {
+          const uint4 mk = a.masks[(int64_t)item * a.umax + u];
+          lbits = mask_bits(mk, tok_first, tpw);
+          part = lbits != 0u;
+        }
+      }
+      uint64_t todo = __ballot(part);
+      while (todo != 0ull && !stuck) {
+        const int b = __builtin_ctzll(todo);
+        todo &= todo - 1ull;
+        const int uu_b = cbase + b;
+        const int j = __builtin_amdgcn_readlane(lj, b);
+        const uint32_t mine = (uint32_t)__builtin_amdgcn_readlane((int)lbits, b);
+        const int kstart = j * a.bs + (uu_b % nsb) * KB;
+        const int v = v_base + uu_b;
+        const int slot = v % R;
+        const int need = v / R + 1;
+        int spins = 0;
+        while (lds_poll(&ready[slot]) < need) {
+          __builtin_amdgcn_s_sleep(1);
+          if (++spins > kMaxSpin) {
+            stuck = true;
+            break;
+          }
+        }
+        if (stuck) break;
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        const bool diag = (kstart + KB - 1) > my_tmin;
+        NSA_LDS const char* kl = (NSA_LDS const char*)&ring[slot][0];
+        NSA_LDS const char* vl = kl + KB * D * 2;
+        // all K fragments of the unit first (one LDS round trip for the whole
+        // QK^T), then the MFMAs
+        bf16x8 kf[MT][KT];
 #pragma unroll
-    for (int n = 0; n < NT; n++) {
-      act[n] = (be.tokmask & tile_token_mask(n, a.G, a.tpt)) != 0u;
-      sel[n] = cvalid[n] && ((be.tokmask >> tau[n]) & 1u);
+        for (int mt = 0; mt < MT; mt++) {
+          const int row = mt * 16 + c;
+#pragma unroll
+          for (int kk = 0; kk < KT; kk++) {
+            const int pc = (kk * 4 + g) ^ k_swizzle<D>(row);
+            kf[mt][kk] = *(NSA_LDS const bf16x8*)(kl + row * (D * 2) + pc * 16);
+          }
+        }
+#pragma unroll
+        for (int n = 0; n < NTPW; n++) {
+          const uint32_t tbits = mine & (((1u << a.tpt) - 1u) << (n * a.tpt));
+          if (tbits == 0u) continue;
+          const bool sel = cvalid[n] && ((mine >> (tau[n] - tok_first)) & 1u);
+          // S^T = K Q^T
+          f32x4 s[MT];
+#pragma unroll
+          for (int mt = 0; mt < MT; mt++) {
+            s[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < KT; kk++)
+              s[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[mt][kk], qf[n][kk], s[mt], 0, 0, 0);
+          }
+          // mask (only where some column of the tile must not see some key),
+          // online softmax in the log2 domain.  Lane (c, g) holds keys
+          // 16*mt + 4*g + jj of column c.
+          const bool need_mask = diag || (tbits != tvalid[n]);
+          if (need_mask) {
+#pragma unroll
+            for (int mt = 0; mt < MT; mt++) {
+#pragma unroll
+              for (int jj = 0; jj < 4; jj++) {
+                const int kp = kstart + mt * 16 + g * 4 + jj;
+                if (!sel || kp > tcol[n]) s[mt][jj] = -INFINITY;
+              }
+            }
+          }
+          float mx = -INFINITY;
+          const float sc = a.scale_log2;
+          if (sc >= 0.f) {
+#pragma unroll
+            for (int mt = 0; mt < MT; mt++) mx = fmaxf(mx, fmaxf(fmaxf(s[mt][0], s[mt][1]), fmaxf(s[mt][2], s[mt][3])));
+            mx = max_over_groups(mx) * sc;
+          } else {
+#pragma unroll
+            for (int mt = 0; mt < MT; mt++) {
+#pragma unroll
+              for (int jj = 0; jj < 4; jj++) {
+                if (s[mt][jj] != -INFINITY) mx = fmaxf(mx, s[mt][jj] * sc);
+              }
+            }
+            mx = max_over_groups(mx);
+          }
+          // The running max moves only when a score exceeds it by more than
+          // 2^8: p = 2^(x - m) then stays <= 256, exact enough in fp32 and
+          // bf16, and the O rescale is skipped on most units.
+          const bool raise = mx > mrun[n] + 8.f;
+          const float mnew = raise ? mx : mrun[n];
+          const float muse = (mnew == -INFINITY) ? 0.f : mnew;
+          float rs = 0.f;
+#pragma unroll
+          for (int mt = 0; mt < MT; mt++) {
+#pragma unroll
+            for (int jj = 0; jj < 4; jj++) {
+              const float x = s[mt][jj];
+              const float pv = fast_exp2(sc >= 0.f ? __builtin_fmaf(x, sc, -muse)
+                                                   : (x == -INFINITY ? -INFINITY : x * sc - muse));
+              s[mt][jj] = pv;
+              rs += pv;
+            }
+          }
+          rs = sum_over_groups(rs);
+          if (__ballot(raise) != 0ull) {
+            const float alpha = raise ? fast_exp2(mrun[n] - muse) : 1.f;
+            lrun[n] *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < DT; dt++) o[n][dt] *= alpha;
+          }
+          lrun[n] += rs;
+          mrun[n] = mnew;
+          bf16x8 pf[KQ];
+#pragma unroll
+          for (int kq = 0; kq < KQ; kq++) {
+#pragma unroll
+            for (int jj = 0; jj < 4; jj++) {
+              pf[kq][jj] = (__bf16)s[2 * kq][jj];
+              pf[kq][4 + jj] = (__bf16)s[2 * kq + 1][jj];
+            }
+          }
+          // O^T += V^T P^T, V^T fragments in two batches of DT/2 row tiles
+#pragma unroll
+          for (int hb = 0; hb < 2; hb++) {
+            bf16x8 vf[DT / 2][KQ];
+#pragma unroll
+            for (int dd = 0; dd < DT / 2; dd++) {
+              const int dt = hb * (DT / 2) + dd;
+#pragma unroll
+              for (int kq = 0; kq < KQ; kq++) {
+#pragma unroll
+                for (int half = 0; half < 2; half++) {
+                  const int key = kq * 32 + half * 16 + g * 4 + (c >> 2);
+                  const int d0 = dt * 16 + (c & 3) * 4;
+                  const int pc = (d0 >> 3) ^ v_swizzle<D>(key);
+                  const s16x4 t = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                      (NSA_LDS s16x4*)(vl + key * (D * 2) + pc * 16 + (d0 & 7) * 2));
+                  const bf16x4 tb = __builtin_bit_cast(bf16x4, t);
+#pragma unroll
+                  for (int e = 0; e < 4; e++) vf[dd][kq][half * 4 + e] = tb[e];
+                }
+              }
+            }
+#pragma unroll
+            for (int dd = 0; dd < DT / 2; dd++) {
+              const int dt = hb * (DT / 2) + dd;
+#pragma unroll
+              for (int kq = 0; kq < KQ; kq++)
+                o[n][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[dd][kq], pf[kq], o[n][dt], 0, 0, 0);
+            }
+          }
+        }
+        lds_release_bump(&done[slot]);
+      }
     }
-    for (int sb = 0; sb < nsteps_per_block; sb++) {
-      const int kstart = be.block * a.bs + sb * KB;  // first key (sequence-relative)
-      if (kstart > tmax) break;
-      const bool diag = (kstart + KB - 1) > tmin;
-      const int row0 = bos + kstart;
+    if (stuck) break;
 
-      // ---- stage V[row0 .. row0+KB) into this wave's LDS (swizzled rows)
+    // epilogue: out = O / l (bf16, round to nearest even), lse = ln 2 * (m + log2 l)
 #pragma unroll
-      for (int it = 0; it < KB * CH / 64; it++) {
-        const int qd = it * 64 + lane;
-        const int r = qd / CH;
-        const int ch = qd - r * CH;
-        const int grow = min(row0 + r, a.Ttot - 1);
-        const i32x4 val = *reinterpret_cast<const i32x4*>(V + ((int64_t)grow * a.Hkv + h) * D + ch * 8);
-        *reinterpret_cast<NSA_LDS i32x4*>(vl + r * D + ((ch ^ v_swizzle<D>(r)) * 8)) = val;
-      }
-
-      // ---- K fragments: A operand rows = keys 16*mt + c, k = 32*kk + 8*g .. +7
-      bf16x8 kf[MT][KT];
-#pragma unroll
-      for (int mt = 0; mt < MT; mt++) {
-        const int grow = min(row0 + mt * 16 + c, a.Ttot - 1);
-        const __bf16* kp = K + ((int64_t)grow * a.Hkv + h) * D + g * 8;
-#pragma unroll
-        for (int kk = 0; kk < KT; kk++) kf[mt][kk] = *reinterpret_cast<const bf16x8*>(kp + kk * 32);
-      }
-
-      bf16x8 pf[NT][KQ];
-#pragma unroll
-      for (int n = 0; n < NT; n++) {
-        if (!act[n]) continue;
-        f32x4 s[MT];
-#pragma unroll
-        for (int mt = 0; mt < MT; mt++) {
-          s[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int kk = 0; kk < KT; kk++)
-            s[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[mt][kk], qf[n][kk], s[mt], 0, 0, 0);
-        }
-        // scale + masks; lane (c, g) holds keys 16*mt + 4*g + jj of column c
-        float mx = -INFINITY;
-#pragma unroll
-        for (int mt = 0; mt < MT; mt++) {
-#pragma unroll
-          for (int jj = 0; jj < 4; jj++) {
-            float x = s[mt][jj] * a.scale_log2;
-            const int kp = kstart + mt * 16 + g * 4 + jj;
-            if (!sel[n] || (diag && kp > tcol[n])) x = -INFINITY;
-            s[mt][jj] = x;
-            mx = fmaxf(mx, x);
-          }
-        }
-        mx = wave_max_groups(mx);
-        const float mnew = fmaxf(mrun[n], mx);
-        const float muse = (mnew == -INFINITY) ? 0.f : mnew;
-        const float alpha = fast_exp2(mrun[n] - muse);
-        float rs = 0.f;
-#pragma unroll
-        for (int mt = 0; mt < MT; mt++) {
-#pragma unroll
-          for (int jj = 0; jj < 4; jj++) {
-            const float pv = fast_exp2(s[mt][jj] - muse);
-            s[mt][jj] = pv;
-            rs += pv;
-          }
-        }
-        rs = wave_sum_groups(rs);
-        lrun[n] = lrun[n] * alpha + rs;
-        mrun[n] = mnew;
-#pragma unroll
-        for (int dt = 0; dt < DT; dt++) o[n][dt] *= alpha;
-#pragma unroll
-        for (int kq = 0; kq < KQ; kq++) {
-          bf16x8 pk;
-#pragma unroll
-          for (int jj = 0; jj < 4; jj++) {
-            pk[jj] = (__bf16)s[2 * kq][jj];
-            pk[4 + jj] = (__bf16)s[2 * kq + 1][jj];
-          }
-          pf[n][kq] = pk;
-        }
-      }
-
-      // ---- O^T += V^T P^T ; V^T fragments through the transposing LDS read
+    for (int n = 0; n < NTPW; n++) {
+      if (!cvalid[n]) continue;
+      const float l = lrun[n];
+      const float inv = l > 0.f ? 1.f / l : 0.f;
+      const int64_t orow = ((int64_t)(hd.tok0 + tau[n]) * a.Hq + hq[n]) * D;
 #pragma unroll
       for (int dt = 0; dt < DT; dt++) {
+        bf16x4 ov;
 #pragma unroll
-        for (int kq = 0; kq < KQ; kq++) {
-          bf16x8 vf;
-#pragma unroll
-          for (int half = 0; half < 2; half++) {
-            const int key = kq * 32 + half * 16 + g * 4 + (c >> 2);
-            const int d0 = dt * 16 + (c & 3) * 4;
-            const int chk = d0 >> 3;
-            const int addr = key * D + ((chk ^ v_swizzle<D>(key)) << 3) + (d0 & 7);
-            const s16x4 t = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                reinterpret_cast<NSA_LDS s16x4*>(vl + addr));
-            const bf16x4 tb = __builtin_bit_cast(bf16x4, t);
-#pragma unroll
-            for (int e = 0; e < 4; e++) vf[half * 4 + e] = tb[e];
-          }
-#pragma unroll
-          for (int n = 0; n < NT; n++) {
-            if (!act[n]) continue;
-            o[n][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[n][kq], o[n][dt], 0, 0, 0);
-          }
-        }
+        for (int jj = 0; jj < 4; jj++) ov[jj] = (__bf16)(o[n][dt][jj] * inv);
+        *reinterpret_cast<bf16x4*>(Out + orow + dt * 16 + g * 4) = ov;
+      }
+      if (a.lse && g == 0) {
+        const float lv = l > 0.f ? (mrun[n] + __log2f(l)) * 0.69314718055994530942f : -INFINITY;
+        a.lse[(int64_t)(hd.tok0 + tau[n]) * a.Hq + hq[n]] = lv;
       }
     }
+    v_base += nunits;
+    next_item(cs, a);
   }
-
-  // ---- epilogue: out = O / l (bf16, round to nearest even), lse = ln 2 * (m + log2 l)
-  __bf16* __restrict__ Out = reinterpret_cast<__bf16*>(a.out);
-#pragma unroll
-  for (int n = 0; n < NT; n++) {
-    if (!cvalid[n]) continue;
-    const float l = lrun[n];
-    const float inv = l > 0.f ? 1.f / l : 0.f;
-    const int64_t orow = ((int64_t)(hd.tok0 + tau[n]) * a.Hq + hq[n]) * D;
-#pragma unroll
-    for (int dt = 0; dt < DT; dt++) {
-      bf16x4 ov;
-#pragma unroll
-      for (int jj = 0; jj < 4; jj++) ov[jj] = (__bf16)(o[n][dt][jj] * inv);
-      *reinterpret_cast<bf16x4*>(Out + orow + dt * 16 + g * 4) = ov;
-    }
-    if (a.lse && g == 0) {
-      const float lv = l > 0.f ? (mrun[n] + __log2f(l)) * 0.69314718055994530942f : -INFINITY;
-      a.lse[(int64_t)(hd.tok0 + tau[n]) * a.Hq + hq[n]] = lv;
-    }
-  }
+  if (stuck) atomicOr(a.err, kErrStuck);
 }
 
 // ---------------------------------------------------------------------------
-// fp32: same walk, v_mfma_f32_16x16x4_f32 (fp32 products, fp32 accumulation),
-// P stays fp32; V^T fragments are single fp32 elements read from global.
+// fp32: one wave per (item, token group of `tpw` tokens), no LDS
 // ---------------------------------------------------------------------------
-template <int D, int KB, int NT>
+template <int D, int KB, int NTPW>
 __global__ void __launch_bounds__(256, 2) fwd_f32_kernel(FwdArgs a) {
   constexpr int KT = D / 4;
   constexpr int MT = KB / 16;
   constexpr int DT = D / 16;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
   const int c = lane & 15;
   const int g = lane >> 4;
-  const int pos = xcd_remap(blockIdx.x, gridDim.x) * kWaves + wave;
+  const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);   // global wave id
+  const int pos = gw / kConsumers;
+  const int part = gw % kConsumers;
   if (pos >= a.n_items) return;
   const int item = a.worklist[pos];
   if (item < 0 || item >= a.n_items) return;
   ItemHeader hd = a.hdr[item];
   if (!header_ok(hd, a)) return;
-  const int h = item / a.n_tiles;
+  const int vg = item / a.n_tiles;
+  const int h = vg / a.gpk;
+  const int tpw = a.tpw;
+  const int tok_first = part * tpw;
+  const int my_ntok = min(max(hd.ntok - tok_first, 0), tpw);
+  if (my_ntok == 0) return;
+  const int my_tmin = hd.pos0 + tok_first;
+  const int my_tmax = my_tmin + my_ntok - 1;
   const int bos = hd.tok0 - hd.pos0;
-  const int tmin = hd.pos0;
-  const int tmax = hd.pos0 + hd.ntok - 1;
   const float* __restrict__ Q = reinterpret_cast<const float*>(a.q);
   const float* __restrict__ K = reinterpret_cast<const float*>(a.k);
   const float* __restrict__ V = reinterpret_cast<const float*>(a.v);
 
-  int tau[NT], hq[NT], tcol[NT];
-  bool cvalid[NT];
-  float qf[NT][KT];
-  f32x4 o[NT][DT];
-  float mrun[NT], lrun[NT];
+  int tau[NTPW], hq[NTPW], tcol[NTPW];
+  bool cvalid[NTPW];
+  float qf[NTPW][KT];
+  f32x4 o[NTPW][DT];
+  float mrun[NTPW], lrun[NTPW];
 #pragma unroll
-  for (int n = 0; n < NT; n++) {
+  for (int n = 0; n < NTPW; n++) {
     int head;
-    column_of(n, c, a.G, a.tpt, hd.ntok, tau[n], head, cvalid[n]);
-    hq[n] = h * a.G + head;
+    column_of(c, a.gv, a.tpt, tok_first + n * a.tpt, hd.ntok, tau[n], head, cvalid[n]);
+    hq[n] = vg * a.gv + head;
     tcol[n] = hd.pos0 + tau[n];
     const int64_t qrow = ((int64_t)(hd.tok0 + (cvalid[n] ? tau[n] : 0)) * a.Hq + hq[n]) * D;
 #pragma unroll
@@ -373,30 +714,27 @@ __global__ void __launch_bounds__(256, 2) fwd_f32_kernel(FwdArgs a) {
     mrun[n] = -INFINITY;
     lrun[n] = 0.f;
   }
-
-  const BlockEntry* list = a.lists + (int64_t)item * a.umax;
-  const int nsteps_per_block = a.bs / KB;
   for (int u = 0; u < hd.nunion; u++) {
-    const BlockEntry be = list[u];
-    if (be.block < 0 || be.block > tmax / a.bs) continue;
-    bool act[NT], sel[NT];
-#pragma unroll
-    for (int n = 0; n < NT; n++) {
-      act[n] = (be.tokmask & tile_token_mask(n, a.G, a.tpt)) != 0u;
-      sel[n] = cvalid[n] && ((be.tokmask >> tau[n]) & 1u);
-    }
-    for (int sb = 0; sb < nsteps_per_block; sb++) {
-      const int kstart = be.block * a.bs + sb * KB;
-      if (kstart > tmax) break;
-      const bool diag = (kstart + KB - 1) > tmin;
+    const int j = a.blocks[(int64_t)item * a.umax + u];
+    if (j < 0 || j > my_tmax / a.bs) continue;
+    const uint4 mk = a.masks[(int64_t)item * a.umax + u];
+    const uint32_t mine = mask_bits(mk, tok_first, tpw);
+    if (mine == 0u) continue;
+    for (int sb = 0; sb < a.bs / KB; sb++) {
+      const int kstart = j * a.bs + sb * KB;
+      if (kstart > my_tmax) break;
+      const bool diag = (kstart + KB - 1) > my_tmin;
       const int row0 = bos + kstart;
 #pragma unroll
-      for (int n = 0; n < NT; n++) {
-        if (!act[n]) continue;
+      for (int n = 0; n < NTPW; n++) {
+        const uint32_t tbits = (mine >> (n * a.tpt)) & ((1u << a.tpt) - 1u);
+        if (tbits == 0u) continue;
+        const bool sel = cvalid[n] && ((mine >> (tau[n] - tok_first)) & 1u);
         f32x4 s[MT];
 #pragma unroll
         for (int mt = 0; mt < MT; mt++) {
-          const int grow = min(row0 + mt * 16 + c, a.Ttot - 1);
+          int grow = row0 + mt * 16 + c;
+          grow = grow < a.Ttot ? grow : a.Ttot - 1;
           const float* kp = K + ((int64_t)grow * a.Hkv + h) * D + g;
           s[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -410,12 +748,12 @@ __global__ void __launch_bounds__(256, 2) fwd_f32_kernel(FwdArgs a) {
           for (int jj = 0; jj < 4; jj++) {
             float x = s[mt][jj] * a.scale_log2;
             const int kp = kstart + mt * 16 + g * 4 + jj;
-            if (!sel[n] || (diag && kp > tcol[n])) x = -INFINITY;
+            if (!sel || (diag && kp > tcol[n])) x = -INFINITY;
             s[mt][jj] = x;
             mx = fmaxf(mx, x);
           }
         }
-        mx = wave_max_groups(mx);
+        mx = max_over_groups(mx);
         const float mnew = fmaxf(mrun[n], mx);
         const float muse = (mnew == -INFINITY) ? 0.f : mnew;
         const float alpha = fast_exp2(mrun[n] - muse);
@@ -429,7 +767,7 @@ __global__ void __launch_bounds__(256, 2) fwd_f32_kernel(FwdArgs a) {
             rs += pv;
           }
         }
-        rs = wave_sum_groups(rs);
+        rs = sum_over_groups(rs);
         lrun[n] = lrun[n] * alpha + rs;
         mrun[n] = mnew;
 #pragma unroll
@@ -439,7 +777,8 @@ __global__ void __launch_bounds__(256, 2) fwd_f32_kernel(FwdArgs a) {
           for (int mt = 0; mt < MT; mt++) {
 #pragma unroll
             for (int jj = 0; jj < 4; jj++) {
-              const int grow = min(row0 + mt * 16 + g * 4 + jj, a.Ttot - 1);
+              int grow = row0 + mt * 16 + g * 4 + jj;
+              grow = grow < a.Ttot ? grow : a.Ttot - 1;
               const float vv = V[((int64_t)grow * a.Hkv + h) * D + dt * 16 + c];
               acc = __builtin_amdgcn_mfma_f32_16x16x4f32(vv, s[mt][jj], acc, 0, 0, 0);
             }
@@ -449,17 +788,16 @@ __global__ void __launch_bounds__(256, 2) fwd_f32_kernel(FwdArgs a) {
       }
     }
   }
-
   float* __restrict__ Out = reinterpret_cast<float*>(a.out);
 #pragma unroll
-  for (int n = 0; n < NT; n++) {
+  for (int n = 0; n < NTPW; n++) {
     if (!cvalid[n]) continue;
     const float l = lrun[n];
     const float inv = l > 0.f ? 1.f / l : 0.f;
     const int64_t orow = ((int64_t)(hd.tok0 + tau[n]) * a.Hq + hq[n]) * D;
 #pragma unroll
     for (int dt = 0; dt < DT; dt++) {
-      f32x4 ov = o[n][dt] * inv;
+      const f32x4 ov = o[n][dt] * inv;
       *reinterpret_cast<f32x4*>(Out + orow + dt * 16 + g * 4) = ov;
     }
     if (a.lse && g == 0) {
@@ -472,30 +810,35 @@ __global__ void __launch_bounds__(256, 2) fwd_f32_kernel(FwdArgs a) {
 typedef void (*KernelFn)(FwdArgs);
 
 template <int D, int KB>
-KernelFn pick_nt(bool bf16, int nt) {
+KernelFn pick_ntpw(bool bf16, int ntpw) {
   if (bf16) {
-    switch (nt) {
-      case 1: return fwd_bf16_kernel<D, KB, 1>;
-      case 2: return fwd_bf16_kernel<D, KB, 2>;
-      case 4: return fwd_bf16_kernel<D, KB, 4>;
+    switch (ntpw) {
+      case 1: return fwd_bf16_ring_kernel<D, KB, 1>;
+      case 2: return fwd_bf16_ring_kernel<D, KB, 2>;
     }
   } else {
-    switch (nt) {
+    switch (ntpw) {
       case 1: return fwd_f32_kernel<D, KB, 1>;
       case 2: return fwd_f32_kernel<D, KB, 2>;
-      case 4: return fwd_f32_kernel<D, KB, 4>;
     }
   }
   return nullptr;
 }
 
-KernelFn pick(bool bf16, int D, int KB, int nt) {
-  if (D == 64) return KB == 32 ? pick_nt<64, 32>(bf16, nt) : pick_nt<64, 64>(bf16, nt);
-  if (D == 128) return KB == 32 ? pick_nt<128, 32>(bf16, nt) : pick_nt<128, 64>(bf16, nt);
+KernelFn pick(bool bf16, int D, int KB, int ntpw) {
+  if (D == 64) return KB == 32 ? pick_ntpw<64, 32>(bf16, ntpw) : pick_ntpw<64, 64>(bf16, ntpw);
+  if (D == 128) return KB == 32 ? pick_ntpw<128, 32>(bf16, ntpw) : pick_ntpw<128, 64>(bf16, ntpw);
   return nullptr;
 }
 
 }  // namespace
+
+int device_cu_count() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  return n;
+}
 
 hipError_t launch_fwd(const Plan& p, const void* q, const void* k, const void* v, float scale,
                       void* out, float* lse, char* ws, hipStream_t stream) {
@@ -506,23 +849,34 @@ hipError_t launch_fwd(const Plan& p, const void* q, const void* k, const void* v
   a.out = out;
   a.lse = lse;
   a.hdr = reinterpret_cast<const ItemHeader*>(ws + p.off_hdr);
-  a.lists = reinterpret_cast<const BlockEntry*>(ws + p.off_lists);
+  a.blocks = reinterpret_cast<const int32_t*>(ws + p.off_blocks);
+  a.masks = reinterpret_cast<const uint4*>(ws + p.off_masks);
+  a.units = reinterpret_cast<const uint32_t*>(ws + p.off_units);
+  a.umax_units = p.umax_units;
   a.worklist = reinterpret_cast<const int32_t*>(ws + p.off_worklist);
+  a.err = reinterpret_cast<int32_t*>(ws + p.off_err);
   a.Ttot = p.B * p.T;
   a.Hq = p.Hq;
   a.Hkv = p.Hkv;
   a.G = p.G;
+  a.gv = p.gv;
+  a.gpk = p.gpk;
   a.tpt = p.tpt;
+  a.tpw = p.tpw;
   a.n_tiles = p.n_tiles;
   a.n_items = p.n_items;
   a.umax = p.umax;
   a.bs = p.bs;
+  a.nwg = p.nwg;
   a.scale_log2 = scale * 1.4426950408889634f;
-  const int KB = p.bs < 64 ? p.bs : 64;
-  KernelFn fn = pick(p.bf16, p.D, KB, p.nt);
+  KernelFn fn = pick(p.bf16, p.D, p.kb, p.ntpw);
   if (!fn) return hipErrorInvalidValue;
-  const int nwg = (p.n_items + kWaves - 1) / kWaves;
-  hipLaunchKernelGGL(fn, dim3(nwg), dim3(64 * kWaves), 0, stream, a);
+  if (p.bf16) {
+    hipLaunchKernelGGL(fn, dim3(p.nwg), dim3(64 * (kConsumers + kProducers)), 0, stream, a);
+  } else {
+    const int waves = p.n_items * kConsumers;
+    hipLaunchKernelGGL(fn, dim3((waves + 3) / 4), dim3(256), 0, stream, a);
+  }
   return hipGetLastError();
 }
 

@@ -55,7 +55,7 @@ def D(B=1, T=128, Hq=16, Hkv=1, Dh=128, S=4, dt=1):
     (D(Dh=96), {}, 2),
     (D(), {"bs": 48}, 2),
     (D(dt=7), {}, 2),
-    (D(Hq=48, Hkv=1), {}, 2),             # G = 48 not built
+    (D(Hq=24, Hkv=1), {}, 2),             # G = 24: neither <= 16 nor a multiple of 16
     (D(), {"scale": float("nan")}, 1),
     (D(), {"scale": float("inf")}, 1),
     (D(), {"nulls": (0,)}, 1),

@@ -59,7 +59,7 @@ nsa_status make_plan(const nsa_dims* d, int32_t block_size, int32_t num_seqs, bo
   while (P.tpt * 2 * P.gv <= 16) P.tpt *= 2;
   P.ntpw = P.bf16 ? 1 : ((P.tpt * 2 * nsa::kConsumers <= nsa::kMaxTileTokens) ? 2 : 1);
   P.tpw = P.tpt * P.ntpw;
-  P.tq = nsa::kConsumers * P.tpw;
+  P.tq = std::min(nsa::kConsumers * P.tpw, nsa::kMaxTileTokens) / P.tpw * P.tpw;
   P.kb = P.bs < 64 ? P.bs : 64;
   P.nsb = P.bs / P.kb;
   const int64_t Ttot = rows;

@@ -108,16 +108,27 @@ __device__ __forceinline__ bool header_ok(ItemHeader& hd, const FwdArgs& a) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Lanes c, c+16, c+32, c+48 hold the same column.  v_permlane16_swap /
+// v_permlane32_swap (gfx950) exchange 16-lane rows between two registers in
+// the VALU: with both operands = v, the pair returned holds v of the lane
+// itself and of its partner 16 (resp. 32) lanes away.
+__device__ __forceinline__ float xor16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float((threadIdx.x & 16) ? r[0] : r[1]);
+}
+__device__ __forceinline__ float xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
+}
 __device__ __forceinline__ float max_over_groups(float v) {
-  // lanes c, c+16, c+32, c+48 hold the same column
-  v = fmaxf(v, __shfl_xor(v, 16, 64));
-  v = fmaxf(v, __shfl_xor(v, 32, 64));
+  v = fmaxf(v, xor16(v));
+  v = fmaxf(v, xor32(v));
   return v;
 }
 
 __device__ __forceinline__ float sum_over_groups(float v) {
-  v += __shfl_xor(v, 16, 64);
-  v += __shfl_xor(v, 32, 64);
+  v += xor16(v);
+  v += xor32(v);
   return v;
 }
 
@@ -293,6 +304,7 @@ struct RingCfg {
 
 template <int D, int KB, int NTPW>
 __global__ void __launch_bounds__(64 * (kConsumers + kProducers), 1) fwd_bf16_ring_kernel(FwdArgs a) {
+  static_assert(64 * (kConsumers + kProducers) <= 1024, "workgroup size");
   using C = RingCfg<D, KB>;
   constexpr int R = C::R;
   constexpr int KT = D / 32;   // k-steps of S^T = K Q^T
@@ -510,31 +522,36 @@ __global__ void __launch_bounds__(64 * (kConsumers + kProducers), 1) fwd_bf16_ri
         const bool diag = (kstart + KB - 1) > my_tmin;
         NSA_LDS const char* kl = (NSA_LDS const char*)&ring[slot][0];
         NSA_LDS const char* vl = kl + KB * D * 2;
-        // all K fragments of the unit first (one LDS round trip for the whole
-        // QK^T), then the MFMAs
-        bf16x8 kf[MT][KT];
-#pragma unroll
-        for (int mt = 0; mt < MT; mt++) {
-          const int row = mt * 16 + c;
-#pragma unroll
-          for (int kk = 0; kk < KT; kk++) {
-            const int pc = (kk * 4 + g) ^ k_swizzle<D>(row);
-            kf[mt][kk] = *(NSA_LDS const bf16x8*)(kl + row * (D * 2) + pc * 16);
-          }
-        }
 #pragma unroll
         for (int n = 0; n < NTPW; n++) {
           const uint32_t tbits = mine & (((1u << a.tpt) - 1u) << (n * a.tpt));
           if (tbits == 0u) continue;
           const bool sel = cvalid[n] && ((mine >> (tau[n] - tok_first)) & 1u);
-          // S^T = K Q^T
+          // S^T = K Q^T; K fragments read from the slot half a unit at a time
+          // (one LDS round trip per half), then the MFMAs
           f32x4 s[MT];
 #pragma unroll
-          for (int mt = 0; mt < MT; mt++) {
-            s[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+          for (int mt = 0; mt < MT; mt++) s[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int kk = 0; kk < KT; kk++)
-              s[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[mt][kk], qf[n][kk], s[mt], 0, 0, 0);
+          for (int hh = 0; hh < 2; hh++) {
+            constexpr int MH = MT / 2;
+            bf16x8 kf[MH][KT];
+#pragma unroll
+            for (int mm = 0; mm < MH; mm++) {
+              const int row = (hh * MH + mm) * 16 + c;
+#pragma unroll
+              for (int kk = 0; kk < KT; kk++) {
+                const int pc = (kk * 4 + g) ^ k_swizzle<D>(row);
+                kf[mm][kk] = *(NSA_LDS const bf16x8*)(kl + row * (D * 2) + pc * 16);
+              }
+            }
+#pragma unroll
+            for (int mm = 0; mm < MH; mm++) {
+#pragma unroll
+              for (int kk = 0; kk < KT; kk++)
+                s[hh * MH + mm] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[mm][kk], qf[n][kk],
+                                                                          s[hh * MH + mm], 0, 0, 0);
+            }
           }
           // mask (only where some column of the tile must not see some key),
           // online softmax in the log2 domain.  Lane (c, g) holds keys

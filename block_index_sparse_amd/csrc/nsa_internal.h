@@ -25,7 +25,7 @@ constexpr int kMaxMaskWords = 4;    // token bit set of one list entry: up to 12
 constexpr int kMaxTileTokens = 32 * kMaxMaskWords;
 constexpr int kMaxBitmapWords = 2048;   // blocks per sequence the planner can merge: 65536
 constexpr int kMaxUnion = 2048;         // entries of one item's merged list
-constexpr int kConsumers = 8;       // attention waves per forward workgroup
+constexpr int kConsumers = 12;      // attention waves per forward workgroup
 constexpr int kProducers = 4;       // loader waves per forward workgroup
 constexpr int kXcds = 8;            // XCDs of an MI355X
 
@@ -53,7 +53,7 @@ struct Plan {
   int32_t tpt;               // tokens per 16-column MFMA tile
   int32_t ntpw;              // column tiles per attention wave
   int32_t tpw;               // tokens per attention wave
-  int32_t tq;                // tokens per item (kConsumers * tpw)
+  int32_t tq;                // tokens per item (at most kConsumers * tpw and 128)
   int32_t kb;                // keys per streamed unit (min(bs, 64))
   int32_t nsb;               // streamed units per listed block (bs / kb)
   int32_t umax_units;        // unit-table stride per item (umax * nsb rounded up to 16)

@@ -13,10 +13,19 @@ baseline times the fp64 oracle on a bounded token sample of the same
 workload on the host's cores.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 3] [--no-cpu-baseline]
+
+HBM traffic of the attention kernel comes from two rocprofv3 counter runs
+(FETCH_SIZE, then WRITE_SIZE) of this script, each scaled by what the same
+counter reads for a plain copy kernel of known size (``--calibrate-copy``);
+``--traffic-summary`` turns the four runs into ``profiles/`` JSON, which is
+reported while the kernel sources still hash to what was profiled.
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import math
 import os
@@ -33,6 +42,93 @@ METRIC = "sparse-attn fwd useful TFLOP/s + % of bf16 MFMA peak, T=32k 1 GPU"
 PEAK_BF16_TFLOPS = 2516.6   # 256 CUs x 4096 dense bf16 FLOP/clk/CU x 2.4 GHz
 PEAK_F32_TFLOPS = 157.3     # dense fp32 matrix peak
 PEAK_HBM_GBS = 8000.0
+COPY_BYTES = 1 << 30         # bytes read (and written) by the calibration copy
+CSRC = os.path.join(ROOT, "block_index_sparse_amd", "csrc")
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def kernel_source_digest() -> str:
+    """sha256 over the sources that decide what the attention kernel does: the
+    kernel, its shared header and the host code that sizes its tiles."""
+    h = hashlib.sha256()
+    for f in ("nsa_fwd.hip", "nsa_internal.h", "nsa_api.hip"):
+        h.update(f.encode())
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def traffic_path(workload: str) -> str:
+    return os.path.join(PROFILES, f"nsa_fwd_traffic_{workload}.json")
+
+
+def read_traffic(workload: str):
+    """HBM bytes per launch from the committed counter summary, or None when
+    there is none or the kernel sources changed since it was taken."""
+    p = traffic_path(workload)
+    if not os.path.exists(p):
+        return None
+    with open(p) as fh:
+        t = json.load(fh)
+    if t.get("kernel_source_sha256") != kernel_source_digest():
+        return None
+    return t["traffic_bytes_per_launch"]
+
+
+def _pmc_rows(run_dir: str, counter: str):
+    files = glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {run_dir}")
+    out = []
+    for f in files:
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] == counter:
+                    out.append((r["Kernel_Name"], float(r["Counter_Value"])))
+    return out
+
+
+def _mean_for(rows, needle: str, skip: str = "\0") -> tuple:
+    vals = [v for n, v in rows if needle in n and skip not in n]
+    if not vals:
+        raise SystemExit(f"no dispatch of a kernel named like {needle!r}")
+    return float(np.mean(vals)), len(vals)
+
+
+def traffic_summary(workload: str, fetch_dir: str, write_dir: str, copy_fetch_dir: str,
+                    copy_write_dir: str, kernel: str):
+    """Write profiles/nsa_fwd_traffic_<workload>.json from four --pmc runs."""
+    copy_kib = COPY_BYTES / 1024.0
+    cf, _ = _mean_for(_pmc_rows(copy_fetch_dir, "FETCH_SIZE"), "elementwise", skip="Fill")
+    cw, _ = _mean_for(_pmc_rows(copy_write_dir, "WRITE_SIZE"), "elementwise", skip="Fill")
+    kf, nf = _mean_for(_pmc_rows(fetch_dir, "FETCH_SIZE"), kernel)
+    kw, nw = _mean_for(_pmc_rows(write_dir, "WRITE_SIZE"), kernel)
+    ff, fw = copy_kib / cf, copy_kib / cw
+    res = {
+        "workload": workload, "kernel": kernel,
+        "kernel_source_sha256": kernel_source_digest(),
+        "fetch_kib_per_launch_raw": kf, "write_kib_per_launch_raw": kw, "launches": [nf, nw],
+        "copy_bytes": COPY_BYTES, "copy_fetch_kib_raw": cf, "copy_write_kib_raw": cw,
+        "fetch_scale": ff, "write_scale": fw,
+        "fetch_bytes_per_launch": kf * 1024 * ff, "write_bytes_per_launch": kw * 1024 * fw,
+        "traffic_bytes_per_launch": kf * 1024 * ff + kw * 1024 * fw,
+    }
+    with open(traffic_path(workload), "w") as fh:
+        json.dump(res, fh, indent=1)
+        fh.write("\n")
+    print(json.dumps(res))
+
+
+def calibrate_copy():
+    """A plain elementwise copy of COPY_BYTES (x * 1 into a second buffer)."""
+    import torch
+    dev = torch.device("cuda:0")
+    src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev)   # contents irrelevant
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": COPY_BYTES, "launches": 3}), flush=True)
 
 
 def visible_keys_per_row(w) -> np.ndarray:
@@ -87,9 +183,9 @@ def cpu_baseline(w, seconds_target=12.0, seed=0):
         t0 = time.perf_counter()
         oracle.fwd_workload(w, tokens=rows)
         used = time.perf_counter() - t0
-        if used >= seconds_target / 4 or n >= total:
+        if used >= seconds_target * 0.6 or n >= total:
             break
-        n = min(total, int(n * max(2.0, seconds_target / 4 / max(used, 1e-3))))
+        n = min(total, int(n * min(8.0, max(1.2, seconds_target / max(used, 1e-3)))))
     fl = useful_flops(w, rows)
     return {"value": fl / used / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"{len(rows)} of {total} tokens (seeded uniform sample, all {w.Hq} query heads), "
@@ -105,11 +201,26 @@ def main():
     ap.add_argument("--config", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run the copy kernel used to scale the traffic counters")
+    ap.add_argument("--traffic-summary", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR",
+                                                           "COPY_WRITE_DIR"),
+                    help="write the traffic summary of --config from four rocprofv3 --pmc runs")
     args = ap.parse_args()
+    if args.traffic_summary:
+        import nsa_inputs as ni
+        name = ni.CONFIG_NAMES[args.config]
+        kern = "fwd_f32_kernel" if args.config == 0 else "fwd_bf16_ring_kernel"
+        traffic_summary(name, *args.traffic_summary, kernel=kern)
+        return
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only (asked for {args.gpus}); "
               "the path has no multi-GPU mode", file=sys.stderr)
         sys.exit(2)
+
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
 
     import torch
     import block_index_sparse_amd as nsa
@@ -174,12 +285,12 @@ def main():
         },
         "roofline": {
             "bound": "mfma",
-            "kernel": "fwd_bf16_kernel" if w.dtype == "bf16" else "fwd_f32_kernel",
+            "kernel": "fwd_bf16_ring_kernel" if w.dtype == "bf16" else "fwd_f32_kernel",
             "achieved": round(achieved, 3),
             "peak": peak,
             "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4),
-            "traffic": None,
+            "traffic": read_traffic(w.name),
             "kernel_ms_avg": round(kern_avg, 4),
             "kernel_ms_min": round(float(np.min(kern_ms)), 4),
             "algorithmic_flop_per_launch": flop,

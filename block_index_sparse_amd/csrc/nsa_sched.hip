@@ -66,6 +66,8 @@ struct PlanArgs {
   int32_t T, Hkv, S, bs, gpk, tq, num_seqs, n_tiles, n_items, umax, n_chunks;
   int32_t max_pairs;    // tq * min(S, blocks per sequence): the heaviest possible item
   int32_t kb, nsb, umax_units, tpw;
+  int32_t nbw;          // bitmap words per wave: ceil(blocks per sequence / 32)
+  int32_t wave_words;   // LDS words per wave: 2 * nbw + kMaxMaskWords * umax
 };
 
 // Token bits [first, first + count) of a 128-bit set (count a power of two
@@ -75,31 +77,41 @@ __device__ __forceinline__ uint32_t field(const uint32_t* m, int first, int coun
   return count >= 32 ? sh : (sh & ((1u << count) - 1u));
 }
 
-// Block-wide exclusive scan of one value per thread (256 threads).
-__device__ int32_t block_exclusive_scan(int32_t v, int32_t* part, int32_t* total) {
-  part[threadIdx.x] = v;
-  __syncthreads();
-  for (int o = 1; o < 256; o <<= 1) {
-    const int32_t add = threadIdx.x >= (unsigned)o ? part[threadIdx.x - o] : 0;
-    __syncthreads();
-    part[threadIdx.x] += add;
-    __syncthreads();
-  }
-  const int32_t incl = part[threadIdx.x];
-  *total = part[255];
-  __syncthreads();
-  return incl - v;
+// LDS operations of one wave complete in issue order, so ordering the
+// compiler's view is all a wave needs between its own LDS writes and reads.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
 }
 
-// One workgroup (256 threads) per item.
-__global__ void __launch_bounds__(256) plan_kernel(PlanArgs a) {
-  __shared__ uint32_t bitmap[kMaxBitmapWords];
-  __shared__ int32_t wbase[kMaxBitmapWords];
-  __shared__ uint32_t tmask[kMaxUnion][kMaxMaskWords];
-  __shared__ int32_t part[256];
-  __shared__ int32_t red[256];
+__device__ __forceinline__ int32_t wave_inclusive_scan(int32_t v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int32_t t = __shfl_up(v, o, 64);
+    if (lane >= o) v += t;
+  }
+  return v;
+}
 
-  const int32_t item = blockIdx.x;
+__device__ __forceinline__ int32_t wave_sum(int32_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// One wave per item (blockDim.x / 64 items per workgroup, each wave with its
+// own slice of the dynamic LDS; the waves never synchronise with each other).
+__global__ void __launch_bounds__(256) plan_kernel(PlanArgs a) {
+  extern __shared__ uint32_t plan_lds[];
+  const int32_t lane = threadIdx.x & 63;
+  const int32_t wv = threadIdx.x >> 6;
+  const int32_t item = blockIdx.x * (int32_t)(blockDim.x >> 6) + wv;
+  if (item >= a.n_items) return;
+  uint32_t* bitmap = plan_lds + (size_t)wv * a.wave_words;
+  int32_t* wbase = reinterpret_cast<int32_t*>(bitmap + a.nbw);
+  uint32_t* tmask = bitmap + 2 * a.nbw;   // [umax][kMaxMaskWords]
+
   const int32_t vg = item / a.n_tiles;
   const int32_t tile = item - vg * a.n_tiles;
   const int32_t h = vg / a.gpk;
@@ -107,7 +119,7 @@ __global__ void __launch_bounds__(256) plan_kernel(PlanArgs a) {
   const int32_t chunk = item / kChunk;
 
   if (tile >= total_tiles) {
-    if (threadIdx.x == 0) {
+    if (lane == 0) {
       a.hdr[item] = ItemHeader{0, 0, 0, 0};
       a.bucket[item] = 0;
       atomicAdd(&a.hist[chunk], 1);  // bucket 0 row
@@ -127,12 +139,12 @@ __global__ void __launch_bounds__(256) plan_kernel(PlanArgs a) {
   const int32_t ntok = min(a.tq, len - pos0);
   const int32_t tok0 = bos + pos0;
   const int32_t own_hi = (pos0 + ntok - 1) / a.bs;
-  const int32_t nwords = own_hi / 32 + 1;   // host guarantees <= kMaxBitmapWords
+  const int32_t nwords = own_hi / 32 + 1;   // host guarantees <= nbw
   const int32_t nent = ntok * a.S;
 
-  for (int32_t w = threadIdx.x; w < nwords; w += 256) bitmap[w] = 0;
-  __syncthreads();
-  for (int32_t e = threadIdx.x; e < nent; e += 256) {
+  for (int32_t w = lane; w < nwords; w += 64) bitmap[w] = 0;
+  wave_lds_sync();
+  for (int32_t e = lane; e < nent; e += 64) {
     const int32_t tau = e / a.S;
     const int32_t i = e - tau * a.S;
     const int64_t row = (int64_t)(tok0 + tau) * a.Hkv + h;
@@ -143,27 +155,29 @@ __global__ void __launch_bounds__(256) plan_kernel(PlanArgs a) {
       if (idx >= 0 && idx <= (pos0 + tau) / a.bs) atomicOr(&bitmap[idx >> 5], 1u << (idx & 31));
     }
   }
-  __syncthreads();
-  // compact ids: exclusive prefix of set bits over the words
-  const int32_t per = (nwords + 255) / 256;
+  wave_lds_sync();
+  // merged-list position of the first block of every bitmap word: each lane
+  // counts a contiguous run of words, then a wave scan
+  const int32_t per = (nwords + 63) / 64;
   int32_t mine = 0;
   for (int32_t k = 0; k < per; k++) {
-    const int32_t w = threadIdx.x * per + k;
+    const int32_t w = lane * per + k;
     if (w < nwords) mine += __popc(bitmap[w]);
   }
-  int32_t U;
-  int32_t run = block_exclusive_scan(mine, part, &U);
+  const int32_t incl = wave_inclusive_scan(mine);
+  const int32_t U = __shfl(incl, 63, 64);
+  int32_t run = incl - mine;
   for (int32_t k = 0; k < per; k++) {
-    const int32_t w = threadIdx.x * per + k;
+    const int32_t w = lane * per + k;
     if (w < nwords) {
       wbase[w] = run;
       run += __popc(bitmap[w]);
     }
   }
-  for (int32_t c = threadIdx.x; c < U; c += 256)
-    for (int m = 0; m < kMaxMaskWords; m++) tmask[c][m] = 0;
-  __syncthreads();
-  for (int32_t e = threadIdx.x; e < nent; e += 256) {
+  for (int32_t c = lane; c < U * kMaxMaskWords; c += 64) tmask[c] = 0;
+  wave_lds_sync();
+  // token set of every merged entry
+  for (int32_t e = lane; e < nent; e += 64) {
     const int32_t tau = e / a.S;
     const int32_t i = e - tau * a.S;
     const int64_t row = (int64_t)(tok0 + tau) * a.Hkv + h;
@@ -174,58 +188,46 @@ __global__ void __launch_bounds__(256) plan_kernel(PlanArgs a) {
       if (idx >= 0 && idx <= (pos0 + tau) / a.bs) {
         const int32_t w = idx >> 5;
         const int32_t cid = wbase[w] + __popc(bitmap[w] & ((1u << (idx & 31)) - 1u));
-        atomicOr(&tmask[cid][tau >> 5], 1u << (tau & 31));
+        atomicOr(&tmask[cid * kMaxMaskWords + (tau >> 5)], 1u << (tau & 31));
       }
     }
   }
-  __syncthreads();
+  wave_lds_sync();
+  // emit the list: lane-strided over the candidate blocks 0 .. 32 * nwords - 1
   int32_t pairs = 0;
   const int64_t lbase = (int64_t)item * a.umax;
-  for (int32_t w = threadIdx.x; w < nwords; w += 256) {
-    uint32_t bits = bitmap[w];
-    int32_t cid = wbase[w];
-    while (bits) {
-      const int32_t b = __ffs(bits) - 1;
-      bits &= bits - 1u;
-      a.blocks[lbase + cid] = w * 32 + b;
-      uint4 mk;
-      mk.x = tmask[cid][0];
-      mk.y = tmask[cid][1];
-      mk.z = tmask[cid][2];
-      mk.w = tmask[cid][3];
-      a.masks[lbase + cid] = mk;
-      pairs += __popc(mk.x) + __popc(mk.y) + __popc(mk.z) + __popc(mk.w);
-      // unit words: which attention waves read each key sub-block
-      const int32_t blk = w * 32 + b;
-      for (int32_t sb = 0; sb < a.nsb; sb++) {
-        const int32_t kstart = blk * a.bs + sb * a.kb;
-        uint32_t word = 0u;
-        if (kstart <= pos0 + ntok - 1) {
-          int32_t np = 0;
-          for (int32_t wv = 0; wv < kConsumers; wv++) {
-            const int32_t first = wv * a.tpw;
-            if (first >= ntok) break;
-            const int32_t last_pos = pos0 + min(first + a.tpw, ntok) - 1;
-            if (field(tmask[cid], first, a.tpw) != 0u && kstart <= last_pos) np++;
-          }
-          word = unit_word(blk, np);
+  for (int32_t blk = lane; blk < nwords * 32; blk += 64) {
+    const int32_t w = blk >> 5;
+    const uint32_t bits = bitmap[w];
+    if (((bits >> (blk & 31)) & 1u) == 0u) continue;
+    const int32_t cid = wbase[w] + __popc(bits & ((1u << (blk & 31)) - 1u));
+    const uint32_t* tm = tmask + cid * kMaxMaskWords;
+    a.blocks[lbase + cid] = blk;
+    a.masks[lbase + cid] = uint4{tm[0], tm[1], tm[2], tm[3]};
+    pairs += __popc(tm[0]) + __popc(tm[1]) + __popc(tm[2]) + __popc(tm[3]);
+    // unit words: which attention waves read each key sub-block
+    for (int32_t sb = 0; sb < a.nsb; sb++) {
+      const int32_t kstart = blk * a.bs + sb * a.kb;
+      uint32_t word = 0u;
+      if (kstart <= pos0 + ntok - 1) {
+        int32_t np = 0;
+        for (int32_t wc = 0; wc < kConsumers; wc++) {
+          const int32_t first = wc * a.tpw;
+          if (first >= ntok) break;
+          const int32_t last_pos = pos0 + min(first + a.tpw, ntok) - 1;
+          if (field(tm, first, a.tpw) != 0u && kstart <= last_pos) np++;
         }
-        a.units[(int64_t)item * a.umax_units + cid * a.nsb + sb] = word;
+        word = unit_word(blk, np);
       }
-      cid++;
+      a.units[(int64_t)item * a.umax_units + cid * a.nsb + sb] = word;
     }
   }
   // weight = (block, token) pairs, scaled so the heaviest possible item lands
   // in the top bucket
-  red[threadIdx.x] = pairs;
-  __syncthreads();
-  for (int o = 128; o > 0; o >>= 1) {
-    if (threadIdx.x < (unsigned)o) red[threadIdx.x] += red[threadIdx.x + o];
-    __syncthreads();
-  }
-  if (threadIdx.x == 0) {
+  pairs = wave_sum(pairs);
+  if (lane == 0) {
     a.hdr[item] = ItemHeader{tok0, pos0, ntok, U};
-    const int64_t wgt = ((int64_t)red[0] * (kNumBuckets - 1) + a.max_pairs - 1) / a.max_pairs;
+    const int64_t wgt = ((int64_t)pairs * (kNumBuckets - 1) + a.max_pairs - 1) / a.max_pairs;
     const int32_t b = wgt < kNumBuckets ? (int32_t)wgt : kNumBuckets - 1;
     a.bucket[item] = b;
     atomicAdd(&a.hist[(int64_t)b * a.n_chunks + chunk], 1);
@@ -324,7 +326,12 @@ hipError_t launch_schedule(const Plan& p, const int32_t* block_indices, const in
   a.nsb = p.nsb;
   a.umax_units = p.umax_units;
   a.tpw = p.tpw;
-  plan_kernel<<<p.n_items, 256, 0, stream>>>(a);
+  a.nbw = (p.nb_max + 31) / 32;
+  a.wave_words = 2 * a.nbw + kMaxMaskWords * p.umax;
+  const size_t wave_bytes = sizeof(uint32_t) * (size_t)a.wave_words;
+  int waves = (int)((64 * 1024) / wave_bytes);   // items per workgroup
+  waves = waves < 1 ? 1 : (waves > 4 ? 4 : waves);
+  plan_kernel<<<(p.n_items + waves - 1) / waves, 64 * waves, wave_bytes * waves, stream>>>(a);
   int32_t* off = reinterpret_cast<int32_t*>(ws + p.off_off);
   int32_t* total = reinterpret_cast<int32_t*>(ws + p.off_total);
   scan_kernel<<<kNumBuckets, 256, 0, stream>>>(hist, off, total, p.n_chunks);

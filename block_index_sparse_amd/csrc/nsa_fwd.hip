@@ -318,7 +318,7 @@ __global__ void __launch_bounds__(64 * (kConsumers + kProducers), 1) fwd_bf16_ri
   __shared__ int done[R];
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: scalar control flow
   if (threadIdx.x < R) {
     ready[threadIdx.x] = 0;
     done[threadIdx.x] = 0;

@@ -176,18 +176,23 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 // Wait until at most `newer` units (SHARE loads each) of this wave are still
 // in flight; loads complete in issue order for the counter.
-template <int SHARE>
+// With EXTRA > 0, additionally allow EXTRA loads issued after the awaited
+// ones (the V rows that follow a unit's K rows).  A count that would not fit
+// the counter falls back to waiting for everything.
+template <int SHARE, int EXTRA = 0>
 __device__ __forceinline__ void wait_units_older_than(int newer) {
+#define NSA_W(k) wait_vmcnt<(EXTRA + (k) * SHARE < 64 ? EXTRA + (k) * SHARE : 0)>()
   switch (newer) {
-    case 0: wait_vmcnt<0>(); break;
-    case 1: wait_vmcnt<(1 * SHARE < 64 ? 1 * SHARE : 0)>(); break;
-    case 2: wait_vmcnt<(2 * SHARE < 64 ? 2 * SHARE : 0)>(); break;
-    case 3: wait_vmcnt<(3 * SHARE < 64 ? 3 * SHARE : 0)>(); break;
-    case 4: wait_vmcnt<(4 * SHARE < 64 ? 4 * SHARE : 0)>(); break;
-    case 5: wait_vmcnt<(5 * SHARE < 64 ? 5 * SHARE : 0)>(); break;
-    case 6: wait_vmcnt<(6 * SHARE < 64 ? 6 * SHARE : 0)>(); break;
+    case 0: NSA_W(0); break;
+    case 1: NSA_W(1); break;
+    case 2: NSA_W(2); break;
+    case 3: NSA_W(3); break;
+    case 4: NSA_W(4); break;
+    case 5: NSA_W(5); break;
+    case 6: NSA_W(6); break;
     default: wait_vmcnt<0>(); break;
   }
+#undef NSA_W
 }
 
 // Ring counters live in LDS and are accessed with relaxed atomics; ordering
@@ -305,6 +310,7 @@ struct RingCfg {
 template <int D, int KB, int NTPW>
 __global__ void __launch_bounds__(64 * (kConsumers + kProducers), 1) fwd_bf16_ring_kernel(FwdArgs a) {
   static_assert(64 * (kConsumers + kProducers) <= 1024, "workgroup size");
+  static_assert(NTPW == 1, "the ring kernel runs one 16-column tile per attention wave");
   using C = RingCfg<D, KB>;
   constexpr int R = C::R;
   constexpr int KT = D / 32;   // k-steps of S^T = K Q^T
@@ -314,12 +320,14 @@ __global__ void __launch_bounds__(64 * (kConsumers + kProducers), 1) fwd_bf16_ri
   constexpr int CH = D / 8;    // 16-byte chunks per row
 
   __shared__ __attribute__((aligned(1024))) char ring[R][C::kSlotBytes];
+  __shared__ int ready_k[R];
   __shared__ int ready[R];
   __shared__ int done[R];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: scalar control flow
   if (threadIdx.x < R) {
+    ready_k[threadIdx.x] = 0;
     ready[threadIdx.x] = 0;
     done[threadIdx.x] = 0;
   }
@@ -351,6 +359,7 @@ __global__ void __launch_bounds__(64 * (kConsumers + kProducers), 1) fwd_bf16_ri
     bool stuck = false;
     bool have = false;      // metadata of unit v_next is loaded
     int kstart = 0, npart = 0;
+    bool kpub = false;      // K rows of the oldest unpublished own unit are published
     while (true) {
       // find the next own unit of the stream
       while (!have) {
@@ -410,9 +419,23 @@ __global__ void __launch_bounds__(64 * (kConsumers + kProducers), 1) fwd_bf16_ri
         }
       }
       if (n_fly > 0) {
-        // publish the oldest own unit once its loads have landed
-        if (loaded & 1u) wait_units_older_than<C::kUnitLoads>(__popc(loaded >> 1));
+        // publish the oldest own unit: its K rows once they have landed (the
+        // loads issued after them are its V rows and the newer units), then
+        // its V rows
+        if (!kpub && (loaded & 1u)) {
+          wait_units_older_than<C::kUnitLoads, C::kLoadsKV>(__popc(loaded >> 1));
+          loader_bump(&ready_k[v_pub % R]);
+          kpub = true;
+          spins = 0;
+          continue;
+        }
+        if (loaded & 1u) {
+          wait_units_older_than<C::kUnitLoads>(__popc(loaded >> 1));
+        } else {
+          loader_bump(&ready_k[v_pub % R]);   // nothing was loaded: both at once
+        }
         loader_bump(&ready[v_pub % R]);
+        kpub = false;
         loaded >>= 1;
         n_fly--;
         v_pub += kProducers;
@@ -510,7 +533,7 @@ __global__ void __launch_bounds__(64 * (kConsumers + kProducers), 1) fwd_bf16_ri
         const int slot = v % R;
         const int need = v / R + 1;
         int spins = 0;
-        while (lds_poll(&ready[slot]) < need) {
+        while (lds_poll(&ready_k[slot]) < need) {
           __builtin_amdgcn_s_sleep(1);
           if (++spins > kMaxSpin) {
             stuck = true;
@@ -522,135 +545,158 @@ __global__ void __launch_bounds__(64 * (kConsumers + kProducers), 1) fwd_bf16_ri
         const bool diag = (kstart + KB - 1) > my_tmin;
         NSA_LDS const char* kl = (NSA_LDS const char*)&ring[slot][0];
         NSA_LDS const char* vl = kl + KB * D * 2;
+        constexpr int n = 0;   // one 16-column tile per attention wave
+        const uint32_t tbits = mine;
+        const bool sel = cvalid[n] && ((mine >> (tau[n] - tok_first)) & 1u);
+        // S^T = K Q^T; K fragments read from the slot half a unit at a time
+        // (one LDS round trip per half), then the MFMAs
+        f32x4 s[MT];
 #pragma unroll
-        for (int n = 0; n < NTPW; n++) {
-          const uint32_t tbits = mine & (((1u << a.tpt) - 1u) << (n * a.tpt));
-          if (tbits == 0u) continue;
-          const bool sel = cvalid[n] && ((mine >> (tau[n] - tok_first)) & 1u);
-          // S^T = K Q^T; K fragments read from the slot half a unit at a time
-          // (one LDS round trip per half), then the MFMAs
-          f32x4 s[MT];
+        for (int mt = 0; mt < MT; mt++) s[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int mt = 0; mt < MT; mt++) s[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int hh = 0; hh < 2; hh++) {
+          constexpr int MH = MT / 2;
+          bf16x8 kf[MH][KT];
 #pragma unroll
-          for (int hh = 0; hh < 2; hh++) {
-            constexpr int MH = MT / 2;
-            bf16x8 kf[MH][KT];
+          for (int mm = 0; mm < MH; mm++) {
+            const int row = (hh * MH + mm) * 16 + c;
 #pragma unroll
-            for (int mm = 0; mm < MH; mm++) {
-              const int row = (hh * MH + mm) * 16 + c;
-#pragma unroll
-              for (int kk = 0; kk < KT; kk++) {
-                const int pc = (kk * 4 + g) ^ k_swizzle<D>(row);
-                kf[mm][kk] = *(NSA_LDS const bf16x8*)(kl + row * (D * 2) + pc * 16);
-              }
-            }
-#pragma unroll
-            for (int mm = 0; mm < MH; mm++) {
-#pragma unroll
-              for (int kk = 0; kk < KT; kk++)
-                s[hh * MH + mm] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[mm][kk], qf[n][kk],
-                                                                          s[hh * MH + mm], 0, 0, 0);
+            for (int kk = 0; kk < KT; kk++) {
+              const int pc = (kk * 4 + g) ^ k_swizzle<D>(row);
+              kf[mm][kk] = *(NSA_LDS const bf16x8*)(kl + row * (D * 2) + pc * 16);
             }
           }
-          // mask (only where some column of the tile must not see some key),
-          // online softmax in the log2 domain.  Lane (c, g) holds keys
-          // 16*mt + 4*g + jj of column c.
-          const bool need_mask = diag || (tbits != tvalid[n]);
-          if (need_mask) {
 #pragma unroll
-            for (int mt = 0; mt < MT; mt++) {
+          for (int mm = 0; mm < MH; mm++) {
 #pragma unroll
-              for (int jj = 0; jj < 4; jj++) {
-                const int kp = kstart + mt * 16 + g * 4 + jj;
-                if (!sel || kp > tcol[n]) s[mt][jj] = -INFINITY;
+            for (int kk = 0; kk < KT; kk++)
+              s[hh * MH + mm] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[mm][kk], qf[n][kk],
+                                                                        s[hh * MH + mm], 0, 0, 0);
+          }
+        }
+        // V^T fragments, a quarter of the row tiles at a time (lane (c, g)
+        // reads keys 4g + c/4 of each 16-key half, columns 4 (c % 4) .. + 3)
+        constexpr int DQ = DT / 4;
+        auto read_v = [&](bf16x8 (&vf)[DQ][KQ], int qb) {
+#pragma unroll
+          for (int dd = 0; dd < DQ; dd++) {
+            const int dt = qb * DQ + dd;
+#pragma unroll
+            for (int kq = 0; kq < KQ; kq++) {
+#pragma unroll
+              for (int half = 0; half < 2; half++) {
+                const int key = kq * 32 + half * 16 + g * 4 + (c >> 2);
+                const int d0 = dt * 16 + (c & 3) * 4;
+                const int pc = (d0 >> 3) ^ v_swizzle<D>(key);
+                const s16x4 t = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (NSA_LDS s16x4*)(vl + key * (D * 2) + pc * 16 + (d0 & 7) * 2));
+                const bf16x4 tb = __builtin_bit_cast(bf16x4, t);
+#pragma unroll
+                for (int e = 0; e < 4; e++) vf[dd][kq][half * 4 + e] = tb[e];
               }
             }
           }
-          float mx = -INFINITY;
-          const float sc = a.scale_log2;
-          if (sc >= 0.f) {
-#pragma unroll
-            for (int mt = 0; mt < MT; mt++) mx = fmaxf(mx, fmaxf(fmaxf(s[mt][0], s[mt][1]), fmaxf(s[mt][2], s[mt][3])));
-            mx = max_over_groups(mx) * sc;
-          } else {
-#pragma unroll
-            for (int mt = 0; mt < MT; mt++) {
-#pragma unroll
-              for (int jj = 0; jj < 4; jj++) {
-                if (s[mt][jj] != -INFINITY) mx = fmaxf(mx, s[mt][jj] * sc);
-              }
-            }
-            mx = max_over_groups(mx);
-          }
-          // The running max moves only when a score exceeds it by more than
-          // 2^8: p = 2^(x - m) then stays <= 256, exact enough in fp32 and
-          // bf16, and the O rescale is skipped on most units.
-          const bool raise = mx > mrun[n] + 8.f;
-          const float mnew = raise ? mx : mrun[n];
-          const float muse = (mnew == -INFINITY) ? 0.f : mnew;
-          float rs = 0.f;
+        };
+        // mask (only where some column of the tile must not see some key),
+        // online softmax in the log2 domain.  Lane (c, g) holds keys
+        // 16*mt + 4*g + jj of column c.
+        const bool need_mask = diag || (tbits != tvalid[n]);
+        if (need_mask) {
 #pragma unroll
           for (int mt = 0; mt < MT; mt++) {
 #pragma unroll
             for (int jj = 0; jj < 4; jj++) {
-              const float x = s[mt][jj];
-              const float pv = fast_exp2(sc >= 0.f ? __builtin_fmaf(x, sc, -muse)
-                                                   : (x == -INFINITY ? -INFINITY : x * sc - muse));
-              s[mt][jj] = pv;
-              rs += pv;
-            }
-          }
-          rs = sum_over_groups(rs);
-          if (__ballot(raise) != 0ull) {
-            const float alpha = raise ? fast_exp2(mrun[n] - muse) : 1.f;
-            lrun[n] *= alpha;
-#pragma unroll
-            for (int dt = 0; dt < DT; dt++) o[n][dt] *= alpha;
-          }
-          lrun[n] += rs;
-          mrun[n] = mnew;
-          bf16x8 pf[KQ];
-#pragma unroll
-          for (int kq = 0; kq < KQ; kq++) {
-#pragma unroll
-            for (int jj = 0; jj < 4; jj++) {
-              pf[kq][jj] = (__bf16)s[2 * kq][jj];
-              pf[kq][4 + jj] = (__bf16)s[2 * kq + 1][jj];
-            }
-          }
-          // O^T += V^T P^T, V^T fragments in two batches of DT/2 row tiles
-#pragma unroll
-          for (int hb = 0; hb < 2; hb++) {
-            bf16x8 vf[DT / 2][KQ];
-#pragma unroll
-            for (int dd = 0; dd < DT / 2; dd++) {
-              const int dt = hb * (DT / 2) + dd;
-#pragma unroll
-              for (int kq = 0; kq < KQ; kq++) {
-#pragma unroll
-                for (int half = 0; half < 2; half++) {
-                  const int key = kq * 32 + half * 16 + g * 4 + (c >> 2);
-                  const int d0 = dt * 16 + (c & 3) * 4;
-                  const int pc = (d0 >> 3) ^ v_swizzle<D>(key);
-                  const s16x4 t = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                      (NSA_LDS s16x4*)(vl + key * (D * 2) + pc * 16 + (d0 & 7) * 2));
-                  const bf16x4 tb = __builtin_bit_cast(bf16x4, t);
-#pragma unroll
-                  for (int e = 0; e < 4; e++) vf[dd][kq][half * 4 + e] = tb[e];
-                }
-              }
-            }
-#pragma unroll
-            for (int dd = 0; dd < DT / 2; dd++) {
-              const int dt = hb * (DT / 2) + dd;
-#pragma unroll
-              for (int kq = 0; kq < KQ; kq++)
-                o[n][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[dd][kq], pf[kq], o[n][dt], 0, 0, 0);
+              const int kp = kstart + mt * 16 + g * 4 + jj;
+              if (!sel || kp > tcol[n]) s[mt][jj] = -INFINITY;
             }
           }
         }
+        float mx = -INFINITY;
+        const float sc = a.scale_log2;
+        if (sc >= 0.f) {
+#pragma unroll
+          for (int mt = 0; mt < MT; mt++) mx = fmaxf(mx, fmaxf(fmaxf(s[mt][0], s[mt][1]), fmaxf(s[mt][2], s[mt][3])));
+          mx = max_over_groups(mx) * sc;
+        } else {
+#pragma unroll
+          for (int mt = 0; mt < MT; mt++) {
+#pragma unroll
+            for (int jj = 0; jj < 4; jj++) {
+              if (s[mt][jj] != -INFINITY) mx = fmaxf(mx, s[mt][jj] * sc);
+            }
+          }
+          mx = max_over_groups(mx);
+        }
+        // The running max moves only when a score exceeds it by more than
+        // 2^8: p = 2^(x - m) then stays <= 256, exact enough in fp32 and
+        // bf16, and the O rescale is skipped on most units.
+        const bool raise = mx > mrun[n] + 8.f;
+        const float mnew = raise ? mx : mrun[n];
+        const float muse = (mnew == -INFINITY) ? 0.f : mnew;
+        float rs = 0.f;
+#pragma unroll
+        for (int mt = 0; mt < MT; mt++) {
+#pragma unroll
+          for (int jj = 0; jj < 4; jj++) {
+            const float x = s[mt][jj];
+            const float pv = fast_exp2(sc >= 0.f ? __builtin_fmaf(x, sc, -muse)
+                                                 : (x == -INFINITY ? -INFINITY : x * sc - muse));
+            s[mt][jj] = pv;
+            rs += pv;
+          }
+        }
+        rs = sum_over_groups(rs);
+        if (__ballot(raise) != 0ull) {
+          const float alpha = raise ? fast_exp2(mrun[n] - muse) : 1.f;
+          lrun[n] *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < DT; dt++) o[n][dt] *= alpha;
+        }
+        lrun[n] += rs;
+        mrun[n] = mnew;
+        bf16x8 pf[KQ];
+#pragma unroll
+        for (int kq = 0; kq < KQ; kq++) {
+#pragma unroll
+          for (int jj = 0; jj < 4; jj++) {
+            pf[kq][jj] = (__bf16)s[2 * kq][jj];
+            pf[kq][4 + jj] = (__bf16)s[2 * kq + 1][jj];
+          }
+        }
+        // O^T += V^T P^T, one quarter of the row tiles at a time; the reads
+        // of the next quarter are issued before the MFMAs of the current one,
+        // and the slot is released as soon as the last reads have returned
+        auto pv = [&](bf16x8 (&vf)[DQ][KQ], int qb) {
+#pragma unroll
+          for (int dd = 0; dd < DQ; dd++) {
+#pragma unroll
+            for (int kq = 0; kq < KQ; kq++)
+              o[n][qb * DQ + dd] =
+                  __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[dd][kq], pf[kq], o[n][qb * DQ + dd], 0, 0, 0);
+          }
+        };
+        // the V rows of the unit may land after its K rows (they were issued
+        // after them): wait for them only now, after the softmax
+        spins = 0;
+        while (lds_poll(&ready[slot]) < need) {
+          __builtin_amdgcn_s_sleep(1);
+          if (++spins > kMaxSpin) {
+            stuck = true;
+            break;
+          }
+        }
+        if (stuck) break;
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        bf16x8 va[DQ][KQ], vb[DQ][KQ];
+        read_v(va, 0);
+        read_v(vb, 1);
+        pv(va, 0);
+        read_v(va, 2);
+        pv(vb, 1);
+        read_v(vb, 3);
         lds_release_bump(&done[slot]);
+        pv(va, 2);
+        pv(vb, 3);
       }
     }
     if (stuck) break;
@@ -829,10 +875,7 @@ typedef void (*KernelFn)(FwdArgs);
 template <int D, int KB>
 KernelFn pick_ntpw(bool bf16, int ntpw) {
   if (bf16) {
-    switch (ntpw) {
-      case 1: return fwd_bf16_ring_kernel<D, KB, 1>;
-      case 2: return fwd_bf16_ring_kernel<D, KB, 2>;
-    }
+    if (ntpw == 1) return fwd_bf16_ring_kernel<D, KB, 1>;
   } else {
     switch (ntpw) {
       case 1: return fwd_f32_kernel<D, KB, 1>;

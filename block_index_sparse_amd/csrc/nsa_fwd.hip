@@ -307,7 +307,10 @@ struct RingCfg {
   static_assert(kUnitLoads <= 63, "one unit must fit the load counter");
 };
 
-template <int D, int KB, int NTPW>
+// kPosScale: the softmax scale is > 0, so max(scale * s) = scale * max(s) and
+// masked scores (-inf) stay -inf through the scaling FMA; otherwise each
+// score is scaled and tested on its own.
+template <int D, int KB, int NTPW, bool kPosScale>
 __global__ void __launch_bounds__(64 * (kConsumers + kProducers), 1) fwd_bf16_ring_kernel(FwdArgs a) {
   static_assert(64 * (kConsumers + kProducers) <= 1024, "workgroup size");
   static_assert(NTPW == 1, "the ring kernel runs one 16-column tile per attention wave");
@@ -613,7 +616,7 @@ __global__ void __launch_bounds__(64 * (kConsumers + kProducers), 1) fwd_bf16_ri
         }
         float mx = -INFINITY;
         const float sc = a.scale_log2;
-        if (sc >= 0.f) {
+        if constexpr (kPosScale) {
 #pragma unroll
           for (int mt = 0; mt < MT; mt++) mx = fmaxf(mx, fmaxf(fmaxf(s[mt][0], s[mt][1]), fmaxf(s[mt][2], s[mt][3])));
           mx = max_over_groups(mx) * sc;
@@ -622,7 +625,8 @@ __global__ void __launch_bounds__(64 * (kConsumers + kProducers), 1) fwd_bf16_ri
           for (int mt = 0; mt < MT; mt++) {
 #pragma unroll
             for (int jj = 0; jj < 4; jj++) {
-              if (s[mt][jj] != -INFINITY) mx = fmaxf(mx, s[mt][jj] * sc);
+              s[mt][jj] = s[mt][jj] == -INFINITY ? -INFINITY : s[mt][jj] * sc;
+              mx = fmaxf(mx, s[mt][jj]);
             }
           }
           mx = max_over_groups(mx);
@@ -633,18 +637,18 @@ __global__ void __launch_bounds__(64 * (kConsumers + kProducers), 1) fwd_bf16_ri
         const bool raise = mx > mrun[n] + 8.f;
         const float mnew = raise ? mx : mrun[n];
         const float muse = (mnew == -INFINITY) ? 0.f : mnew;
-        float rs = 0.f;
+        float rsum[4] = {0.f, 0.f, 0.f, 0.f};   // four partial sums: a short dependency chain
 #pragma unroll
         for (int mt = 0; mt < MT; mt++) {
 #pragma unroll
           for (int jj = 0; jj < 4; jj++) {
-            const float x = s[mt][jj];
-            const float pv = fast_exp2(sc >= 0.f ? __builtin_fmaf(x, sc, -muse)
-                                                 : (x == -INFINITY ? -INFINITY : x * sc - muse));
+            const float pv = kPosScale ? fast_exp2(__builtin_fmaf(s[mt][jj], sc, -muse))
+                                       : fast_exp2(s[mt][jj] - muse);
             s[mt][jj] = pv;
-            rs += pv;
+            rsum[jj] += pv;
           }
         }
+        float rs = (rsum[0] + rsum[1]) + (rsum[2] + rsum[3]);
         rs = sum_over_groups(rs);
         if (__ballot(raise) != 0ull) {
           const float alpha = raise ? fast_exp2(mrun[n] - muse) : 1.f;
@@ -873,9 +877,9 @@ __global__ void __launch_bounds__(256, 2) fwd_f32_kernel(FwdArgs a) {
 typedef void (*KernelFn)(FwdArgs);
 
 template <int D, int KB>
-KernelFn pick_ntpw(bool bf16, int ntpw) {
+KernelFn pick_ntpw(bool bf16, int ntpw, bool pos_scale) {
   if (bf16) {
-    if (ntpw == 1) return fwd_bf16_ring_kernel<D, KB, 1>;
+    if (ntpw == 1) return pos_scale ? fwd_bf16_ring_kernel<D, KB, 1, true> : fwd_bf16_ring_kernel<D, KB, 1, false>;
   } else {
     switch (ntpw) {
       case 1: return fwd_f32_kernel<D, KB, 1>;
@@ -885,9 +889,10 @@ KernelFn pick_ntpw(bool bf16, int ntpw) {
   return nullptr;
 }
 
-KernelFn pick(bool bf16, int D, int KB, int ntpw) {
-  if (D == 64) return KB == 32 ? pick_ntpw<64, 32>(bf16, ntpw) : pick_ntpw<64, 64>(bf16, ntpw);
-  if (D == 128) return KB == 32 ? pick_ntpw<128, 32>(bf16, ntpw) : pick_ntpw<128, 64>(bf16, ntpw);
+KernelFn pick(bool bf16, int D, int KB, int ntpw, bool pos_scale) {
+  if (D == 64) return KB == 32 ? pick_ntpw<64, 32>(bf16, ntpw, pos_scale) : pick_ntpw<64, 64>(bf16, ntpw, pos_scale);
+  if (D == 128)
+    return KB == 32 ? pick_ntpw<128, 32>(bf16, ntpw, pos_scale) : pick_ntpw<128, 64>(bf16, ntpw, pos_scale);
   return nullptr;
 }
 
@@ -929,7 +934,7 @@ hipError_t launch_fwd(const Plan& p, const void* q, const void* k, const void* v
   a.bs = p.bs;
   a.nwg = p.nwg;
   a.scale_log2 = scale * 1.4426950408889634f;
-  KernelFn fn = pick(p.bf16, p.D, p.kb, p.ntpw);
+  KernelFn fn = pick(p.bf16, p.D, p.kb, p.ntpw, a.scale_log2 > 0.f);
   if (!fn) return hipErrorInvalidValue;
   if (p.bf16) {
     hipLaunchKernelGGL(fn, dim3(p.nwg), dim3(64 * (kConsumers + kProducers)), 0, stream, a);

@@ -61,6 +61,21 @@ def test_hostile_entries_and_duplicates():
     assert np.isneginf(ref_l).any()
 
 
+@pytest.mark.parametrize("dtype,scale", [("bf16", -0.3), ("bf16", 0.0), ("bf16", 2.5), ("f32", -0.125),
+                                         ("f32", 0.0)])
+def test_any_finite_scale(dtype, scale):
+    """Negative, zero and large softmax scales (the bf16 kernel takes a
+    separate path when the scale is not positive).  fp32 stays at the
+    magnitude of 1/sqrt(D): its 1e-5 bar is absolute, and fp32 rounding of
+    the scores grows with the scale."""
+    _say(f"[parity] scale {scale} {dtype}")
+    w = ni.make_workload(f"scale_{scale}", dtype, [230], 16, 1, 128 if dtype == "bf16" else 64, 64, 5,
+                         "sink_local_random", "uniform", seed=23, scale=float(np.float32(scale)))
+    out, lse = run_gpu(w)
+    ref_o, ref_l = oracle.fwd_workload(w)
+    compare(w, out, lse, ref_o, ref_l, what=f"scale {scale} {dtype}")
+
+
 @pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4])
 def test_named_workload_full_size(cfg):
     _say(f"[parity] config {cfg}: generating")

@@ -40,6 +40,8 @@
 //
 // fp32 kernel: one wave per (item, token group) reading K and V straight
 // from global memory, v_mfma_f32_16x16x4_f32, P kept in fp32.
+#include <utility>
+
 #include "nsa_internal.h"
 
 namespace nsa {
@@ -195,6 +197,33 @@ __device__ __forceinline__ void wait_units_older_than(int newer) {
 #undef NSA_W
 }
 
+// A pointer whose value is the same in every lane, held in scalar registers.
+__device__ __forceinline__ const char* uniform_ptr(const char* p) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
+  return (const char*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
+// One direct-to-LDS load of 16 bytes per lane: global address base + off
+// (base uniform, off per lane), LDS address lds + LOFF + 16 * lane.
+template <int LOFF>
+__device__ __forceinline__ void dma_16b(const char* base, uint32_t off, uint32_t lds) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile(
+      "s_add_u32 m0, %2, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, %1"
+      :
+      : "v"(off), "s"(base), "s"(lds), "i"(LOFF)
+      : "memory", "m0", "scc");
+#else
+  (void)base;
+  (void)off;
+  (void)lds;
+#endif
+}
+
 // Ring counters live in LDS and are accessed with relaxed atomics; ordering
 // is made explicit so that no wait covers more than it must (an acquire or
 // release at workgroup scope would also drain the loader waves' in-flight
@@ -346,76 +375,100 @@ __global__ void __launch_bounds__(64 * (kConsumers + kProducers), 1) fwd_bf16_ri
     // Loader p owns the units v with v % kProducers == p: it loads all of a
     // unit's K and V rows and publishes the unit as soon as its own loads
     // have landed.  It keeps up to R / kProducers of its units in flight.
-    const __bf16* __restrict__ K = reinterpret_cast<const __bf16*>(a.k);
-    const __bf16* __restrict__ V = reinterpret_cast<const __bf16*>(a.v);
+    const char* __restrict__ K = reinterpret_cast<const char*>(a.k);
+    const char* __restrict__ V = reinterpret_cast<const char*>(a.v);
     const int p = wave - kConsumers;
-    int tgt[R];
+    const int row_bytes = a.Hkv * D * 2;      // stride between key rows of one kv head
+    // Per-lane byte offsets of the unit's loads from the unit's first row
+    // (load li covers rows 4 li .. 4 li + 3 of K, then of V; lane l writes
+    // the 16 bytes at l * 16 of the load's 1 KB of LDS).  Only the row base
+    // changes between units, so a load is one address add and the LDS base.
+    uint32_t loff[2 * C::kLoadsKV];
 #pragma unroll
-    for (int s = 0; s < R; s++) tgt[s] = 0;
-    int v_next = 0;         // next unit of the stream to examine
+    for (int li = 0; li < 2 * C::kLoadsKV; li++) {
+      const bool isv = li >= C::kLoadsKV;
+      const int ld = isv ? li - C::kLoadsKV : li;
+      const int r = ld * C::kRowsPerLoad + lane / CH;
+      const int lc = (lane % CH) ^ (isv ? v_swizzle<D>(r) : k_swizzle<D>(r));
+      loff[li] = (uint32_t)(r * row_bytes + lc * 16);
+    }
+    constexpr int kOwn = R / kProducers;    // ring slots each loader owns
+    int tgt[kOwn];                          // participant releases owed to each own slot
+#pragma unroll
+    for (int j = 0; j < kOwn; j++) tgt[j] = 0;
+    int v_next = p;         // next own unit (stream index)
     int v_pub = p;          // oldest own unit not yet published
     int n_fly = 0;          // own units issued and not yet published
     uint32_t loaded = 0;    // bit i: the i-th oldest unpublished own unit carries loads
     int spins = 0;
-    int uu = 0;             // unit index inside the current item
-    int nunits = cs.valid ? cs.hd.nunion * nsb : 0;
+    // the item holding v_next: its first stream index, units, kv head, rows
+    int it_v0 = 0;
+    int it_n = cs.valid ? cs.hd.nunion * nsb : 0;
+    int it_h = cs.valid ? __builtin_amdgcn_readfirstlane(cs.item / a.n_tiles / a.gpk) : 0;
     bool stuck = false;
     bool have = false;      // metadata of unit v_next is loaded
     int kstart = 0, npart = 0;
     bool kpub = false;      // K rows of the oldest unpublished own unit are published
     while (true) {
-      // find the next own unit of the stream
-      while (!have) {
-        while (cs.valid && uu >= nunits) {
+      if (!have) {
+        // find the item that holds own unit v_next, then its unit word
+        while (cs.valid && v_next - it_v0 >= it_n) {
+          it_v0 += it_n;
           next_item(cs, a);
-          uu = 0;
-          nunits = cs.valid ? cs.hd.nunion * nsb : 0;
+          it_n = cs.valid ? cs.hd.nunion * nsb : 0;
+          it_h = cs.valid ? __builtin_amdgcn_readfirstlane(cs.item / a.n_tiles / a.gpk) : 0;
         }
-        if (!cs.valid) break;
-        if (v_next % kProducers != p) {
-          v_next++;
-          uu++;
-          continue;
+        if (cs.valid) {
+          const int uu = v_next - it_v0;
+          const uint32_t word = ld_const(a.units, (int64_t)cs.item * a.umax_units + uu);
+          npart = (word >> 31) != 0u ? (int)((word >> 24) & 15u) : 0;
+          kstart = (int)(word & 0xFFFFFFu) * a.bs + (uu & (nsb - 1)) * KB;   // nsb is 1 or 2
+          have = true;
         }
-        const int u = uu / nsb;
-        const int sb = uu - u * nsb;
-        const uint32_t word = ld_const(a.units, (int64_t)cs.item * a.umax_units + uu);
-        npart = (word >> 31) != 0u ? (int)((word >> 24) & 15u) : 0;
-        kstart = (int)(word & 0xFFFFFFu) * a.bs + sb * KB;
-        have = true;
       }
       if (have && n_fly < C::kOwnSlots) {
         const int slot = v_next % R;
+        const int js = (v_next / kProducers) % kOwn;   // which of this loader's slots
         int t = 0;
 #pragma unroll
-        for (int s = 0; s < R; s++) t = (s == slot) ? tgt[s] : t;
+        for (int j = 0; j < kOwn; j++) t = (j == js) ? tgt[j] : t;
         if (npart == 0 || loader_poll(&done[slot]) >= t) {
           __atomic_signal_fence(__ATOMIC_SEQ_CST);
           if (npart > 0) {
-            const int h = cs.item / a.n_tiles / a.gpk;
             const int row0 = cs.hd.tok0 - cs.hd.pos0 + kstart;
             NSA_LDS char* kdst = (NSA_LDS char*)&ring[slot][0];
             NSA_LDS char* vdst = kdst + KB * D * 2;
+            if (row0 + KB <= a.Ttot) {
+              const int64_t rb = ((int64_t)row0 * a.Hkv + it_h) * (D * 2);
+              const char* kb = uniform_ptr(K + rb);
+              const char* vb = uniform_ptr(V + rb);
+              const uint32_t klds = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(uintptr_t)kdst);
+              // scalar row base + 32-bit lane offset; M0 holds the LDS
+              // destination of each load's 1 KB
+              [&]<int... LI>(std::integer_sequence<int, LI...>) {
+                (dma_16b<LI * 1024>(LI >= C::kLoadsKV ? vb : kb, loff[LI], klds), ...);
+              }(std::make_integer_sequence<int, 2 * C::kLoadsKV>{});
+            } else {
+              // the unit runs past the last row: clamp rows (they are masked)
 #pragma unroll
-            for (int li = 0; li < 2 * C::kLoadsKV; li++) {
-              const bool isv = li >= C::kLoadsKV;
-              const int ld = isv ? li - C::kLoadsKV : li;   // 1 KB load index within K or V
-              const int r = ld * C::kRowsPerLoad + lane / CH;
-              const int pc = lane % CH;
-              const int lc = pc ^ (isv ? v_swizzle<D>(r) : k_swizzle<D>(r));
-              int grow = row0 + r;
-              grow = grow < a.Ttot ? grow : a.Ttot - 1;
-              const __bf16* src = (isv ? V : K) + ((int64_t)grow * a.Hkv + h) * D + lc * 8;
-              NSA_LDS char* dst = (isv ? vdst : kdst) + ld * 1024;
-              __builtin_amdgcn_global_load_lds(src, (NSA_LDS void*)dst, 16, 0, 0);
+              for (int li = 0; li < 2 * C::kLoadsKV; li++) {
+                const bool isv = li >= C::kLoadsKV;
+                const int ld = isv ? li - C::kLoadsKV : li;
+                const int r = ld * C::kRowsPerLoad + lane / CH;
+                const int lc = (lane % CH) ^ (isv ? v_swizzle<D>(r) : k_swizzle<D>(r));
+                int grow = row0 + r;
+                grow = grow < a.Ttot ? grow : a.Ttot - 1;
+                const char* src = (isv ? V : K) + ((int64_t)grow * a.Hkv + it_h) * (D * 2) + lc * 16;
+                __builtin_amdgcn_global_load_lds(src, (NSA_LDS void*)((isv ? vdst : kdst) + ld * 1024), 16, 0,
+                                                 0);
+              }
             }
 #pragma unroll
-            for (int s = 0; s < R; s++) tgt[s] += (s == slot) ? npart : 0;
+            for (int j = 0; j < kOwn; j++) tgt[j] += (j == js) ? npart : 0;
             loaded |= 1u << n_fly;
           }
           n_fly++;
-          v_next++;
-          uu++;
+          v_next += kProducers;
           have = false;
           spins = 0;
           continue;

@@ -100,6 +100,23 @@ __device__ __forceinline__ int32_t wave_sum(int32_t v) {
   return v;
 }
 
+constexpr int kPlanBatch = 8;   // index entries per lane loaded before use
+
+// Block listed by entry e of an item (token e / S, position e % S) if the
+// entry is kept, else -1.  The count and the index are loaded independently
+// (the index row is always inside the tensor), so the two loads overlap.
+__device__ __forceinline__ int32_t entry_block(const PlanArgs& a, int32_t e, int32_t nent, int32_t tok0,
+                                               int32_t pos0, int32_t h) {
+  if (e >= nent) return -1;
+  const int32_t tau = e / a.S;
+  const int32_t i = e - tau * a.S;
+  const int64_t row = (int64_t)(tok0 + tau) * a.Hkv + h;
+  int32_t n = a.bc[row];
+  const int32_t idx = a.bi[row * a.S + i];
+  n = n < 0 ? 0 : (n > a.S ? a.S : n);
+  return (i < n && idx >= 0 && idx <= (pos0 + tau) / a.bs) ? idx : -1;
+}
+
 // One wave per item (blockDim.x / 64 items per workgroup, each wave with its
 // own slice of the dynamic LDS; the waves never synchronise with each other).
 __global__ void __launch_bounds__(256) plan_kernel(PlanArgs a) {
@@ -144,16 +161,16 @@ __global__ void __launch_bounds__(256) plan_kernel(PlanArgs a) {
 
   for (int32_t w = lane; w < nwords; w += 64) bitmap[w] = 0;
   wave_lds_sync();
-  for (int32_t e = lane; e < nent; e += 64) {
-    const int32_t tau = e / a.S;
-    const int32_t i = e - tau * a.S;
-    const int64_t row = (int64_t)(tok0 + tau) * a.Hkv + h;
-    int32_t n = a.bc[row];
-    n = n < 0 ? 0 : (n > a.S ? a.S : n);
-    if (i < n) {
-      const int32_t idx = a.bi[row * a.S + i];
-      if (idx >= 0 && idx <= (pos0 + tau) / a.bs) atomicOr(&bitmap[idx >> 5], 1u << (idx & 31));
-    }
+  // Entry e = tau * S + i of the item (token tau, list position i) is kept
+  // iff i < clamp(count, 0, S) and 0 <= idx <= tau's own block; the loads of
+  // kPlanBatch entries per lane are issued before any of them is used.
+  for (int32_t e0 = lane; e0 < nent; e0 += 64 * kPlanBatch) {
+    int32_t keep[kPlanBatch];
+#pragma unroll
+    for (int u = 0; u < kPlanBatch; u++) keep[u] = entry_block(a, e0 + 64 * u, nent, tok0, pos0, h);
+#pragma unroll
+    for (int u = 0; u < kPlanBatch; u++)
+      if (keep[u] >= 0) atomicOr(&bitmap[keep[u] >> 5], 1u << (keep[u] & 31));
   }
   wave_lds_sync();
   // merged-list position of the first block of every bitmap word: each lane
@@ -177,15 +194,15 @@ __global__ void __launch_bounds__(256) plan_kernel(PlanArgs a) {
   for (int32_t c = lane; c < U * kMaxMaskWords; c += 64) tmask[c] = 0;
   wave_lds_sync();
   // token set of every merged entry
-  for (int32_t e = lane; e < nent; e += 64) {
-    const int32_t tau = e / a.S;
-    const int32_t i = e - tau * a.S;
-    const int64_t row = (int64_t)(tok0 + tau) * a.Hkv + h;
-    int32_t n = a.bc[row];
-    n = n < 0 ? 0 : (n > a.S ? a.S : n);
-    if (i < n) {
-      const int32_t idx = a.bi[row * a.S + i];
-      if (idx >= 0 && idx <= (pos0 + tau) / a.bs) {
+  for (int32_t e0 = lane; e0 < nent; e0 += 64 * kPlanBatch) {
+    int32_t keep[kPlanBatch];
+#pragma unroll
+    for (int u = 0; u < kPlanBatch; u++) keep[u] = entry_block(a, e0 + 64 * u, nent, tok0, pos0, h);
+#pragma unroll
+    for (int u = 0; u < kPlanBatch; u++) {
+      if (keep[u] >= 0) {
+        const int32_t idx = keep[u];
+        const int32_t tau = (e0 + 64 * u) / a.S;
         const int32_t w = idx >> 5;
         const int32_t cid = wbase[w] + __popc(bitmap[w] & ((1u << (idx & 31)) - 1u));
         atomicOr(&tmask[cid * kMaxMaskWords + (tau >> 5)], 1u << (tau & 31));

@@ -27,6 +27,7 @@ _LIB_PATH = os.path.join(_HERE, "_build", "libnsa.so")
 _lib = None
 
 DTYPE_F32, DTYPE_BF16 = 0, 1
+DEVICE_WAIT_EXPIRED = 1
 
 
 class NsaError(RuntimeError):
@@ -68,6 +69,8 @@ def load_library():
                                      ctypes.POINTER(i32)]
     lib.nsa_fwd_execute.restype = ctypes.c_int
     lib.nsa_fwd_execute.argtypes = [dp, p, p, p, i32, i32, f32, p, p, p, sz, p]
+    lib.nsa_fwd_device_status.restype = ctypes.c_int
+    lib.nsa_fwd_device_status.argtypes = [dp, i32, i32, p, sz, p, ctypes.POINTER(i32)]
     lib.nsa_status_string.restype = ctypes.c_char_p
     lib.nsa_status_string.argtypes = [ctypes.c_int]
     lib.nsa_abi_version.restype = i32
@@ -198,6 +201,16 @@ class Forward:
                                         self.block_size, self.scale, P["out"], P["lse"], P["workspace"],
                                         self.ws_bytes, self.stream))
         return self.out, self.lse
+
+    def device_status(self) -> int:
+        """Device status word of the runs since the last schedule (0 = all
+        completed; NSA_DEVICE_WAIT_EXPIRED = a bounded wait expired).
+        Synchronises the stream."""
+        st = ctypes.c_int32(0)
+        _check(self.lib.nsa_fwd_device_status(ctypes.byref(self.dims), self.block_size, self.nseq,
+                                              self._p["workspace"], self.ws_bytes, self.stream,
+                                              ctypes.byref(st)))
+        return st.value
 
     def work_list(self):
         """Run the scheduler and return a copy of the work list (int32)."""

@@ -210,6 +210,24 @@ nsa_status nsa_fwd_execute(const nsa_dims* dims, const void* q, const void* k, c
   return NSA_SUCCESS;
 }
 
+nsa_status nsa_fwd_device_status(const nsa_dims* dims, int32_t block_size, int32_t num_seqs,
+                                 const void* workspace, size_t workspace_bytes, void* stream,
+                                 int32_t* status) {
+  Plan p;
+  nsa_status st = make_plan(dims, block_size, num_seqs, num_seqs > 0, &p);
+  if (st != NSA_SUCCESS) return st;
+  if (!workspace || !status) return NSA_ERROR_INVALID_VALUE;
+  if (workspace_bytes < p.bytes) return NSA_ERROR_WORKSPACE_TOO_SMALL;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  int32_t word = 0;
+  if (hipMemcpyAsync(&word, reinterpret_cast<const char*>(workspace) + p.off_err, sizeof(word),
+                     hipMemcpyDeviceToHost, s) != hipSuccess ||
+      hipStreamSynchronize(s) != hipSuccess)
+    return NSA_ERROR_LAUNCH_FAILED;
+  *status = word;
+  return NSA_SUCCESS;
+}
+
 const char* nsa_status_string(nsa_status status) {
   switch (status) {
     case NSA_SUCCESS: return "NSA_SUCCESS";

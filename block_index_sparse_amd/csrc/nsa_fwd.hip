@@ -42,6 +42,7 @@
 // from global memory, v_mfma_f32_16x16x4_f32, P kept in fp32.
 #include <utility>
 
+#include "nsa.h"
 #include "nsa_internal.h"
 
 namespace nsa {
@@ -79,7 +80,7 @@ __device__ __forceinline__ uint4 ld_const_mask(const uint4* p, int64_t i) {
 }
 
 constexpr int kMaxSpin = 1 << 22;        // polls before a wait is declared stuck
-constexpr int32_t kErrStuck = 1;
+constexpr int32_t kErrStuck = NSA_DEVICE_WAIT_EXPIRED;
 
 struct FwdArgs {
   const void* q;
@@ -408,7 +409,8 @@ __global__ void __launch_bounds__(64 * (kConsumers + kProducers), 1) fwd_bf16_ri
     bool stuck = false;
     bool have = false;      // metadata of unit v_next is loaded
     int kstart = 0, npart = 0;
-    bool kpub = false;      // K rows of the oldest unpublished own unit are published
+    int pf_v = -1;          // own unit whose word was requested ahead (pf_word)
+    uint32_t pf_word = 0u;
     while (true) {
       if (!have) {
         // find the item that holds own unit v_next, then its unit word
@@ -420,7 +422,8 @@ __global__ void __launch_bounds__(64 * (kConsumers + kProducers), 1) fwd_bf16_ri
         }
         if (cs.valid) {
           const int uu = v_next - it_v0;
-          const uint32_t word = ld_const(a.units, (int64_t)cs.item * a.umax_units + uu);
+          // the word was usually requested when the previous own unit was issued
+          const uint32_t word = (pf_v == v_next) ? pf_word : ld_const(a.units, (int64_t)cs.item * a.umax_units + uu);
           npart = (word >> 31) != 0u ? (int)((word >> 24) & 15u) : 0;
           kstart = (int)(word & 0xFFFFFFu) * a.bs + (uu & (nsb - 1)) * KB;   // nsb is 1 or 2
           have = true;
@@ -469,6 +472,12 @@ __global__ void __launch_bounds__(64 * (kConsumers + kProducers), 1) fwd_bf16_ri
           }
           n_fly++;
           v_next += kProducers;
+          // request the next own unit's word now; it is used after this
+          // unit's loads have been waited for
+          if (v_next - it_v0 < it_n) {
+            pf_v = v_next;
+            pf_word = ld_const(a.units, (int64_t)cs.item * a.umax_units + (v_next - it_v0));
+          }
           have = false;
           spins = 0;
           continue;
@@ -478,20 +487,14 @@ __global__ void __launch_bounds__(64 * (kConsumers + kProducers), 1) fwd_bf16_ri
         // publish the oldest own unit: its K rows once they have landed (the
         // loads issued after them are its V rows and the newer units), then
         // its V rows
-        if (!kpub && (loaded & 1u)) {
+        if (loaded & 1u) {
           wait_units_older_than<C::kUnitLoads, C::kLoadsKV>(__popc(loaded >> 1));
           loader_bump(&ready_k[v_pub % R]);
-          kpub = true;
-          spins = 0;
-          continue;
-        }
-        if (loaded & 1u) {
           wait_units_older_than<C::kUnitLoads>(__popc(loaded >> 1));
         } else {
           loader_bump(&ready_k[v_pub % R]);   // nothing was loaded: both at once
         }
         loader_bump(&ready[v_pub % R]);
-        kpub = false;
         loaded >>= 1;
         n_fly--;
         v_pub += kProducers;
@@ -566,8 +569,8 @@ __global__ void __launch_bounds__(64 * (kConsumers + kProducers), 1) fwd_bf16_ri
       uint32_t lbits = 0u;
       bool part = false;
       if (uu < nunits) {
-        const int u = uu / nsb;
-        const int sb = uu - u * nsb;
+        const int u = uu >> (nsb - 1);   // nsb is 1 or 2
+        const int sb = uu & (nsb - 1);
         const uint32_t word = a.units[(int64_t)item * a.umax_units + uu];
         lj = (int)(word & 0xFFFFFFu);
         const int ks = lj * a.bs + sb * KB;
@@ -584,7 +587,7 @@ __global__ void __launch_bounds__(64 * (kConsumers + kProducers), 1) fwd_bf16_ri
         const int uu_b = cbase + b;
         const int j = __builtin_amdgcn_readlane(lj, b);
         const uint32_t mine = (uint32_t)__builtin_amdgcn_readlane((int)lbits, b);
-        const int kstart = j * a.bs + (uu_b % nsb) * KB;
+        const int kstart = j * a.bs + (uu_b & (nsb - 1)) * KB;   // nsb is 1 or 2
         const int v = v_base + uu_b;
         const int slot = v % R;
         const int need = v / R + 1;

@@ -137,6 +137,20 @@ nsa_status nsa_fwd_execute(const nsa_dims* dims, const void* q, const void* k, c
                            int32_t num_seqs, int32_t block_size, float scale, void* out,
                            float* lse, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Device status of the forward calls that used `workspace` since the last
+ * nsa_fwd_schedule (or nsa_fwd / nsa_fwd_varlen, which schedule first) on it.
+ * Every wait inside the kernels is bounded; if one expired, bit 0
+ * (NSA_DEVICE_WAIT_EXPIRED) is set and the results of those calls are
+ * incomplete.  0 means every run completed normally.  The dims, block_size
+ * and num_seqs (0 = fixed length) must be those of the calls.  This waits
+ * for `stream` to finish and copies one word to the host.
+ */
+#define NSA_DEVICE_WAIT_EXPIRED 1
+nsa_status nsa_fwd_device_status(const nsa_dims* dims, int32_t block_size, int32_t num_seqs,
+                                 const void* workspace, size_t workspace_bytes, void* stream,
+                                 int32_t* status);
+
 /* Human-readable name of a status code (static storage). */
 const char* nsa_status_string(nsa_status status);
 

@@ -13,9 +13,14 @@ def to_device(w, device="cuda"):
 
 
 def run_gpu(w, device="cuda", **kw):
+    """Forward through the C ABI; also asserts that no bounded wait inside
+    the kernels expired."""
     import block_index_sparse_amd as nsa
     q, k, v, bi, bc, cu = to_device(w, device)
-    return nsa.fwd(q, k, v, bi, bc, w.block_size, w.scale, cu_seqlens=cu, **kw)
+    f = nsa.Forward(q, k, v, bi, bc, w.block_size, w.scale, cu_seqlens=cu, **kw)
+    out, lse = f.run()
+    assert f.device_status() == 0, "a bounded wait inside the kernel expired"
+    return out, lse
 
 
 def compare(w, out, lse, ref_out, ref_lse, rows=None, what=""):

@@ -78,3 +78,16 @@ def test_workspace_sizes():
     a = nsa.workspace_size(1, 30000, 32, 2, 128, 16, 64, num_seqs=8)
     b = nsa.workspace_size(1, 30000, 32, 2, 128, 16, 64, num_seqs=100)
     assert 0 < a < b
+
+
+def test_device_status_rejects_bad_arguments():
+    """Checked on the host before any copy is enqueued."""
+    lib = nsa.load_library()
+    st = ctypes.c_int32(-1)
+    dims = D()
+    ws = ctypes.c_void_p(256)
+    assert lib.nsa_fwd_device_status(ctypes.byref(dims), 64, 0, ws, 1 << 40, None, None) == 1
+    assert lib.nsa_fwd_device_status(ctypes.byref(dims), 64, 0, None, 1 << 40, None, ctypes.byref(st)) == 1
+    assert lib.nsa_fwd_device_status(ctypes.byref(dims), 64, 0, ws, 16, None, ctypes.byref(st)) == 3
+    assert lib.nsa_fwd_device_status(ctypes.byref(D(Dh=96)), 64, 0, ws, 1 << 40, None, ctypes.byref(st)) == 2
+    assert st.value == -1

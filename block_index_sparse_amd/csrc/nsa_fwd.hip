@@ -56,6 +56,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 #define NSA_LDS __attribute__((address_space(3)))
 #define NSA_CONST __attribute__((address_space(4)))
+// Third dword of a raw buffer resource (untyped loads, no swizzle).
+constexpr int kBufferFlags = 0x00020000;
 
 // Schedule reads go through the constant address space: with a wave-uniform
 // address they become scalar loads, which keeps the vector-memory counter
@@ -204,25 +206,6 @@ __device__ __forceinline__ const char* uniform_ptr(const char* p) {
   const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
   const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
   return (const char*)(uintptr_t)(((uint64_t)hi << 32) | lo);
-}
-
-// One direct-to-LDS load of 16 bytes per lane: global address base + off
-// (base uniform, off per lane), LDS address lds + LOFF + 16 * lane.
-template <int LOFF>
-__device__ __forceinline__ void dma_16b(const char* base, uint32_t off, uint32_t lds) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  asm volatile(
-      "s_add_u32 m0, %2, %3\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %0, %1"
-      :
-      : "v"(off), "s"(base), "s"(lds), "i"(LOFF)
-      : "memory", "m0", "scc");
-#else
-  (void)base;
-  (void)off;
-  (void)lds;
-#endif
 }
 
 // Ring counters live in LDS and are accessed with relaxed atomics; ordering
@@ -380,18 +363,20 @@ __global__ void __launch_bounds__(64 * (kConsumers + kProducers), 1) fwd_bf16_ri
     const char* __restrict__ V = reinterpret_cast<const char*>(a.v);
     const int p = wave - kConsumers;
     const int row_bytes = a.Hkv * D * 2;      // stride between key rows of one kv head
-    // Per-lane byte offsets of the unit's loads from the unit's first row
-    // (load li covers rows 4 li .. 4 li + 3 of K, then of V; lane l writes
-    // the 16 bytes at l * 16 of the load's 1 KB of LDS).  Only the row base
-    // changes between units, so a load is one address add and the LDS base.
-    uint32_t loff[2 * C::kLoadsKV];
+    // Per-lane byte offsets of the unit's loads from the unit's first row.
+    // Load ld (of K, or of V) covers rows ld * kRowsPerLoad .. + kRowsPerLoad
+    // - 1, lane l writing the 16 bytes at l * 16 of the load's 1 KB of LDS.
+    // The chunk swizzles repeat every four loads, so load 4 g + j is the
+    // offset of load j plus g groups of rows; only the row base changes
+    // between units.
+    static_assert(C::kLoadsKV % 4 == 0, "loads come in groups of four");
+    const uint32_t grp_bytes = (uint32_t)(4 * C::kRowsPerLoad * row_bytes);
+    uint32_t koff[4], voff[4];
 #pragma unroll
-    for (int li = 0; li < 2 * C::kLoadsKV; li++) {
-      const bool isv = li >= C::kLoadsKV;
-      const int ld = isv ? li - C::kLoadsKV : li;
-      const int r = ld * C::kRowsPerLoad + lane / CH;
-      const int lc = (lane % CH) ^ (isv ? v_swizzle<D>(r) : k_swizzle<D>(r));
-      loff[li] = (uint32_t)(r * row_bytes + lc * 16);
+    for (int j = 0; j < 4; j++) {
+      const int r = j * C::kRowsPerLoad + lane / CH;
+      koff[j] = (uint32_t)(r * row_bytes + ((lane % CH) ^ k_swizzle<D>(r)) * 16);
+      voff[j] = (uint32_t)(r * row_bytes + ((lane % CH) ^ v_swizzle<D>(r)) * 16);
     }
     constexpr int kOwn = R / kProducers;    // ring slots each loader owns
     int tgt[kOwn];                          // participant releases owed to each own slot
@@ -441,43 +426,57 @@ __global__ void __launch_bounds__(64 * (kConsumers + kProducers), 1) fwd_bf16_ri
             const int row0 = cs.hd.tok0 - cs.hd.pos0 + kstart;
             NSA_LDS char* kdst = (NSA_LDS char*)&ring[slot][0];
             NSA_LDS char* vdst = kdst + KB * D * 2;
-            if (row0 + KB <= a.Ttot) {
-              const int64_t rb = ((int64_t)row0 * a.Hkv + it_h) * (D * 2);
-              const char* kb = uniform_ptr(K + rb);
-              const char* vb = uniform_ptr(V + rb);
-              const uint32_t klds = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(uintptr_t)kdst);
-              // scalar row base + 32-bit lane offset; M0 holds the LDS
-              // destination of each load's 1 KB
+            // Direct-to-LDS buffer loads from the unit's first row: a scalar
+            // resource, the group of four loads as scalar offset (or, for a
+            // unit that runs past the last row, in the lane offset, where the
+            // range check applies: those rows read as zero and are masked).
+            const int64_t rb = ((int64_t)row0 * a.Hkv + it_h) * (D * 2);
+            const bool whole = row0 + KB <= a.Ttot;
+            const int64_t left = (int64_t)a.Ttot * a.Hkv * (D * 2) - rb;   // bytes to the tensor's end
+            const int nrec = whole ? 0x7FFFFFFF : (int)(left < 0x7FFFFFFF ? left : 0x7FFFFFFF);
+            const __amdgpu_buffer_rsrc_t rk =
+                __builtin_amdgcn_make_buffer_rsrc((void*)uniform_ptr(K + rb), 0, nrec, kBufferFlags);
+            const __amdgpu_buffer_rsrc_t rv =
+                __builtin_amdgcn_make_buffer_rsrc((void*)uniform_ptr(V + rb), 0, nrec, kBufferFlags);
+            if (whole) {
               [&]<int... LI>(std::integer_sequence<int, LI...>) {
-                (dma_16b<LI * 1024>(LI >= C::kLoadsKV ? vb : kb, loff[LI], klds), ...);
-              }(std::make_integer_sequence<int, 2 * C::kLoadsKV>{});
+                (__builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (NSA_LDS void*)(kdst + LI * 1024), 16, koff[LI % 4],
+                                                          (LI / 4) * grp_bytes, 0, 0),
+                 ...);
+              }(std::make_integer_sequence<int, C::kLoadsKV>{});
             } else {
-              // the unit runs past the last row: clamp rows (they are masked)
-#pragma unroll
-              for (int li = 0; li < 2 * C::kLoadsKV; li++) {
-                const bool isv = li >= C::kLoadsKV;
-                const int ld = isv ? li - C::kLoadsKV : li;
-                const int r = ld * C::kRowsPerLoad + lane / CH;
-                const int lc = (lane % CH) ^ (isv ? v_swizzle<D>(r) : k_swizzle<D>(r));
-                int grow = row0 + r;
-                grow = grow < a.Ttot ? grow : a.Ttot - 1;
-                const char* src = (isv ? V : K) + ((int64_t)grow * a.Hkv + it_h) * (D * 2) + lc * 16;
-                __builtin_amdgcn_global_load_lds(src, (NSA_LDS void*)((isv ? vdst : kdst) + ld * 1024), 16, 0,
-                                                 0);
-              }
+              [&]<int... LI>(std::integer_sequence<int, LI...>) {
+                (__builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (NSA_LDS void*)(kdst + LI * 1024), 16,
+                                                          koff[LI % 4] + (LI / 4) * grp_bytes, 0, 0, 0),
+                 ...);
+              }(std::make_integer_sequence<int, C::kLoadsKV>{});
+            }
+            if (whole) {
+              [&]<int... LI>(std::integer_sequence<int, LI...>) {
+                (__builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (NSA_LDS void*)(vdst + LI * 1024), 16, voff[LI % 4],
+                                                          (LI / 4) * grp_bytes, 0, 0),
+                 ...);
+              }(std::make_integer_sequence<int, C::kLoadsKV>{});
+            } else {
+              [&]<int... LI>(std::integer_sequence<int, LI...>) {
+                (__builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (NSA_LDS void*)(vdst + LI * 1024), 16,
+                                                          voff[LI % 4] + (LI / 4) * grp_bytes, 0, 0, 0),
+                 ...);
+              }(std::make_integer_sequence<int, C::kLoadsKV>{});
             }
 #pragma unroll
             for (int j = 0; j < kOwn; j++) tgt[j] += (j == js) ? npart : 0;
             loaded |= 1u << n_fly;
           }
-          n_fly++;
-          v_next += kProducers;
           // request the next own unit's word now; it is used after this
           // unit's loads have been waited for
-          if (v_next - it_v0 < it_n) {
-            pf_v = v_next;
-            pf_word = ld_const(a.units, (int64_t)cs.item * a.umax_units + (v_next - it_v0));
+          const int vn = v_next + kProducers;
+          if (vn - it_v0 < it_n) {
+            pf_v = vn;
+            pf_word = ld_const(a.units, (int64_t)cs.item * a.umax_units + (vn - it_v0));
           }
+          n_fly++;
+          v_next = vn;
           have = false;
           spins = 0;
           continue;

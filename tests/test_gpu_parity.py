@@ -28,6 +28,8 @@ SMALL = [
     ("bf16_g1_d128_bs64_dense", "bf16", [300, 300], 4, 4, 128, 64, 5, "dense", "full", False),
     ("bf16_g8_d128_bs128", "bf16", [400], 16, 2, 128, 128, 4, "local_random", "uniform", False),
     ("bf16_g32_d128_bs64", "bf16", [150], 64, 2, 128, 64, 3, "local_random", "full", False),
+    ("bf16_g48_d64_bs64", "bf16", [140], 48, 1, 64, 64, 3, "sink_local_random", "uniform", False),
+    ("bf16_g64_d128_bs32", "bf16", [100, 37], 128, 2, 128, 32, 4, "shuffled", "uniform", True),
     ("bf16_g2_d64_bs64", "bf16", [130], 4, 2, 64, 64, 3, "shuffled", "uniform", False),
     ("bf16_g3_d64_bs32", "bf16", [97], 6, 2, 64, 32, 4, "local_random", "uniform", False),
     ("bf16_varlen_g16", "bf16", [65, 1, 200, 64, 129], 32, 2, 128, 64, 5, "local_random", "uniform", True),

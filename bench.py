@@ -29,6 +29,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -53,8 +54,12 @@ def kernel_source_digest() -> str:
     h = hashlib.sha256()
     for f in ("nsa_fwd.hip", "nsa_internal.h", "nsa_api.hip"):
         h.update(f.encode())
-        with open(os.path.join(CSRC, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(CSRC, f)) as fh:
+            text = fh.read()
+        # comments and layout do not change the kernel
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()
 
 

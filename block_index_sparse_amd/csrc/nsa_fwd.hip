@@ -6,13 +6,14 @@
 // token's own block; softmax(scale * q.k) weighted sum of v, plus the
 // log-sum-exp of the scores.
 //
-// bf16 kernel: persistent workgroups of 12 waves, one per CU.
+// bf16 kernel: persistent workgroups of 16 waves, one per CU.
 //  * 4 loader waves stream the K and V rows of each item's merged block list
 //    (ascending block order, `kb` keys per unit) into a ring of R LDS slots
-//    with direct-to-LDS 16-byte loads (global_load_lds_dwordx4).  A slot is
-//    refilled only when every attention wave has released it; a loader
-//    publishes its share of a unit as soon as its own loads have landed.
-//  * 8 attention waves each own a fixed set of the item's tokens and walk
+//    with direct-to-LDS 16-byte buffer loads.  Loader p owns the units
+//    v = p (mod 4), loads all of a unit and publishes its K rows and then its
+//    V rows once they have landed; a slot is refilled only when every
+//    attention wave that reads its occupant has released it.
+//  * 12 attention waves each own a fixed set of the item's tokens and walk
 //    the same unit sequence without any barrier: a wave waits only for the
 //    unit's data, computes its own tokens that selected the block, releases
 //    the slot and moves on, so tokens with different block lists do not
@@ -33,10 +34,11 @@
 //  * fp32 online softmax in the log2 domain: scores scaled by scale*log2(e),
 //    v_exp_f32 for 2^x, running max and normaliser per column (the
 //    (output, max, normaliser) carry of a flash-attention block step, as in
-//    `flash_attention_block` on the ejKernel ragged-decode page), causal
-//    mask evaluated only on units that reach past a wave's first token.
-//  * Every wait is a bounded spin: a wave that waits too long records an
-//    error word in the workspace and leaves, so the grid always drains.
+//    `flash_attention_block` on the ejKernel ragged-decode page); masks are
+//    evaluated only on units that hold a token's own block or that not every
+//    token of the tile selected.
+//  * Every wait is a bounded spin: a wave that waits too long sets the
+//    status word in the workspace and leaves, so the grid always drains.
 //
 // fp32 kernel: one wave per (item, token group) reading K and V straight
 // from global memory, v_mfma_f32_16x16x4_f32, P kept in fp32.
@@ -290,11 +292,13 @@ __device__ __forceinline__ void next_item(ItemCursor& cs, const FwdArgs& a) {
 // its block is in range and its first key is not past the item's last token.
 // An attention wave reads a unit iff the unit is live, one of the wave's
 // tokens listed the block and the unit's first key is not past the wave's
-// last token; the number of such waves is the unit's participant count.
-//  * ready[s] counts loader publications of slot s (every unit, live or not,
-//    is published by each loader, in order): unit v is readable once
-//    ready[v % R] >= kProducers * (v / R + 1).
-//  * done[s] counts participant releases of slot s: a loader may overwrite
+// last token; the number of such waves is the unit's participant count,
+// computed by the scheduler into the unit's word.
+//  * ready_k[s] / ready[s] count publications of the K rows / V rows of the
+//    units of slot s (one each per unit, live or not, in unit order): the K
+//    rows of unit v are readable once ready_k[v % R] >= v / R + 1, its V
+//    rows once ready[v % R] >= v / R + 1.
+//  * done[s] counts participant releases of slot s: the loader may overwrite
 //    slot s once done[s] has reached the participant total of all earlier
 //    occupants.  A wave can only reach a later occupant after it was
 //    published, which already required every reader of the earlier one to

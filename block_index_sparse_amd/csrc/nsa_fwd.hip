@@ -55,6 +55,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 #define NSA_LDS __attribute__((address_space(3)))
 #define NSA_CONST __attribute__((address_space(4)))
@@ -208,6 +209,15 @@ __device__ __forceinline__ const char* uniform_ptr(const char* p) {
   const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
   const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
   return (const char*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
+// Raw buffer resource for the rows from byte `at` of a K or V tensor of
+// `total` bytes: the record count ends at the tensor's end (clamped to the
+// 31-bit range), so loads past it read zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t group_rsrc(const char* base, int64_t at, int64_t total) {
+  int64_t left = total - at;
+  left = left < 0 ? 0 : (left > 0x7FFFFFFF ? 0x7FFFFFFF : left);
+  return __builtin_amdgcn_make_buffer_rsrc((void*)uniform_ptr(base + at), 0, (int)left, kBufferFlags);
 }
 
 // Ring counters live in LDS and are accessed with relaxed atomics; ordering
@@ -386,130 +396,110 @@ __global__ void __launch_bounds__(64 * (kConsumers + kProducers), 1) fwd_bf16_ri
     int tgt[kOwn];                          // participant releases owed to each own slot
 #pragma unroll
     for (int j = 0; j < kOwn; j++) tgt[j] = 0;
-    int v_next = p;         // next own unit (stream index)
-    int v_pub = p;          // oldest own unit not yet published
-    int n_fly = 0;          // own units issued and not yet published
-    uint32_t loaded = 0;    // bit i: the i-th oldest unpublished own unit carries loads
-    int spins = 0;
-    // the item holding v_next: its first stream index, units, kv head, rows
+    // The K rows of the next own unit wait in registers (16 bytes per lane
+    // per 1 KB load), fetched while its slot is still being read; once the
+    // slot is free they are written in with LDS stores, so the consumers can
+    // start on S^T right away, while the V rows travel straight from memory
+    // to LDS behind them.
+    u32x4 kst[C::kLoadsKV];
+    // the item holding the next unit to locate: its first stream index, units, kv head
     int it_v0 = 0;
     int it_n = cs.valid ? cs.hd.nunion * nsb : 0;
     int it_h = cs.valid ? __builtin_amdgcn_readfirstlane(cs.item / a.n_tiles / a.gpk) : 0;
-    bool stuck = false;
-    bool have = false;      // metadata of unit v_next is loaded
-    int kstart = 0, npart = 0;
-    int pf_v = -1;          // own unit whose word was requested ahead (pf_word)
-    uint32_t pf_word = 0u;
-    while (true) {
-      if (!have) {
-        // find the item that holds own unit v_next, then its unit word
-        while (cs.valid && v_next - it_v0 >= it_n) {
-          it_v0 += it_n;
-          next_item(cs, a);
-          it_n = cs.valid ? cs.hd.nunion * nsb : 0;
-          it_h = cs.valid ? __builtin_amdgcn_readfirstlane(cs.item / a.n_tiles / a.gpk) : 0;
-        }
-        if (cs.valid) {
-          const int uu = v_next - it_v0;
-          // the word was usually requested when the previous own unit was issued
-          const uint32_t word = (pf_v == v_next) ? pf_word : ld_const(a.units, (int64_t)cs.item * a.umax_units + uu);
-          npart = (word >> 31) != 0u ? (int)((word >> 24) & 15u) : 0;
-          kstart = (int)(word & 0xFFFFFFu) * a.bs + (uu & (nsb - 1)) * KB;   // nsb is 1 or 2
-          have = true;
-        }
+    // Find own unit v and read its word: participants and the byte offset of
+    // its first row (kv head included).  False once the stream is over.
+    auto locate = [&](int v, int& np, int64_t& rb) -> bool {
+      while (cs.valid && v - it_v0 >= it_n) {
+        it_v0 += it_n;
+        next_item(cs, a);
+        it_n = cs.valid ? cs.hd.nunion * nsb : 0;
+        it_h = cs.valid ? __builtin_amdgcn_readfirstlane(cs.item / a.n_tiles / a.gpk) : 0;
       }
-      if (have && n_fly < C::kOwnSlots) {
-        const int slot = v_next % R;
-        const int js = (v_next / kProducers) % kOwn;   // which of this loader's slots
+      if (!cs.valid) return false;
+      const int uu = v - it_v0;
+      const uint32_t word = ld_const(a.units, (int64_t)cs.item * a.umax_units + uu);
+      np = (word >> 31) != 0u ? (int)((word >> 24) & 15u) : 0;
+      const int kstart = (int)(word & 0xFFFFFFu) * a.bs + (uu & (nsb - 1)) * KB;   // nsb is 1 or 2
+      const int row0 = cs.hd.tok0 - cs.hd.pos0 + kstart;
+      rb = ((int64_t)row0 * a.Hkv + it_h) * (D * 2);
+      return true;
+    };
+    // Buffer loads of a unit: each group of four loads gets a scalar resource
+    // based at its own first row whose record count ends at the tensor's
+    // end, so the rows of a unit that runs past the last row read as zero
+    // (they are masked by causality); the lane offsets stay the four koff /
+    // voff values.
+    const int64_t kv_bytes = (int64_t)a.Ttot * a.Hkv * (D * 2);
+    auto issue_k = [&](int64_t rb) {
+      [&]<int... LI>(std::integer_sequence<int, LI...>) {
+        ((kst[LI] = __builtin_amdgcn_raw_buffer_load_b128(
+              group_rsrc(K, rb + (int64_t)(LI / 4) * grp_bytes, kv_bytes), (int)koff[LI % 4], 0, 0)),
+         ...);
+      }(std::make_integer_sequence<int, C::kLoadsKV>{});
+    };
+    auto issue_v = [&](int64_t rb, NSA_LDS char* vdst) {
+      [&]<int... LI>(std::integer_sequence<int, LI...>) {
+        (__builtin_amdgcn_raw_ptr_buffer_load_lds(group_rsrc(V, rb + (int64_t)(LI / 4) * grp_bytes, kv_bytes),
+                                                  (NSA_LDS void*)(vdst + LI * 1024), 16, voff[LI % 4], 0, 0, 0),
+         ...);
+      }(std::make_integer_sequence<int, C::kLoadsKV>{});
+    };
+    // Each pass places own unit v_cur (its K rows already in registers) and
+    // stages the next one; the first pass has no unit to place.
+    int v_cur = p - kProducers;
+    int np = 0;               // participants of v_cur
+    int64_t rb = 0;           // byte offset of v_cur's first row
+    bool have = true;
+    bool stuck = false;
+    while (have) {
+      const bool real = v_cur >= 0;
+      const int slot = (v_cur + kProducers * R) % R;
+      const int js = ((v_cur + kProducers * R) / kProducers) % kOwn;   // which of this loader's slots
+      if (np > 0) {
         int t = 0;
 #pragma unroll
         for (int j = 0; j < kOwn; j++) t = (j == js) ? tgt[j] : t;
-        if (npart == 0 || loader_poll(&done[slot]) >= t) {
-          __atomic_signal_fence(__ATOMIC_SEQ_CST);
-          if (npart > 0) {
-            const int row0 = cs.hd.tok0 - cs.hd.pos0 + kstart;
-            NSA_LDS char* kdst = (NSA_LDS char*)&ring[slot][0];
-            NSA_LDS char* vdst = kdst + KB * D * 2;
-            // Direct-to-LDS buffer loads from the unit's first row: a scalar
-            // resource, the group of four loads as scalar offset (or, for a
-            // unit that runs past the last row, in the lane offset, where the
-            // range check applies: those rows read as zero and are masked).
-            const int64_t rb = ((int64_t)row0 * a.Hkv + it_h) * (D * 2);
-            const bool whole = row0 + KB <= a.Ttot;
-            const int64_t left = (int64_t)a.Ttot * a.Hkv * (D * 2) - rb;   // bytes to the tensor's end
-            const int nrec = whole ? 0x7FFFFFFF : (int)(left < 0x7FFFFFFF ? left : 0x7FFFFFFF);
-            const __amdgpu_buffer_rsrc_t rk =
-                __builtin_amdgcn_make_buffer_rsrc((void*)uniform_ptr(K + rb), 0, nrec, kBufferFlags);
-            const __amdgpu_buffer_rsrc_t rv =
-                __builtin_amdgcn_make_buffer_rsrc((void*)uniform_ptr(V + rb), 0, nrec, kBufferFlags);
-            if (whole) {
-              [&]<int... LI>(std::integer_sequence<int, LI...>) {
-                (__builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (NSA_LDS void*)(kdst + LI * 1024), 16, koff[LI % 4],
-                                                          (LI / 4) * grp_bytes, 0, 0),
-                 ...);
-              }(std::make_integer_sequence<int, C::kLoadsKV>{});
-            } else {
-              [&]<int... LI>(std::integer_sequence<int, LI...>) {
-                (__builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (NSA_LDS void*)(kdst + LI * 1024), 16,
-                                                          koff[LI % 4] + (LI / 4) * grp_bytes, 0, 0, 0),
-                 ...);
-              }(std::make_integer_sequence<int, C::kLoadsKV>{});
-            }
-            if (whole) {
-              [&]<int... LI>(std::integer_sequence<int, LI...>) {
-                (__builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (NSA_LDS void*)(vdst + LI * 1024), 16, voff[LI % 4],
-                                                          (LI / 4) * grp_bytes, 0, 0),
-                 ...);
-              }(std::make_integer_sequence<int, C::kLoadsKV>{});
-            } else {
-              [&]<int... LI>(std::integer_sequence<int, LI...>) {
-                (__builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (NSA_LDS void*)(vdst + LI * 1024), 16,
-                                                          voff[LI % 4] + (LI / 4) * grp_bytes, 0, 0, 0),
-                 ...);
-              }(std::make_integer_sequence<int, C::kLoadsKV>{});
-            }
+        // the slot's earlier occupants must all have been released
+        int spins = 0;
+        while (loader_poll(&done[slot]) < t) {
+          __builtin_amdgcn_s_sleep(1);
+          if (++spins > kMaxSpin) {
+            stuck = true;
+            break;
+          }
+        }
+        if (stuck) break;
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        NSA_LDS char* kdst = (NSA_LDS char*)&ring[slot][0];
+        NSA_LDS char* dst = kdst + lane * 16;
+        [&]<int... LI>(std::integer_sequence<int, LI...>) {
+          ((*(NSA_LDS u32x4*)(dst + LI * 1024) = kst[LI]), ...);
+        }(std::make_integer_sequence<int, C::kLoadsKV>{});
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");   // the K stores have landed
+        loader_bump(&ready_k[slot]);
+        issue_v(rb, kdst + KB * D * 2);
 #pragma unroll
-            for (int j = 0; j < kOwn; j++) tgt[j] += (j == js) ? npart : 0;
-            loaded |= 1u << n_fly;
-          }
-          // request the next own unit's word now; it is used after this
-          // unit's loads have been waited for
-          const int vn = v_next + kProducers;
-          if (vn - it_v0 < it_n) {
-            pf_v = vn;
-            pf_word = ld_const(a.units, (int64_t)cs.item * a.umax_units + (vn - it_v0));
-          }
-          n_fly++;
-          v_next = vn;
-          have = false;
-          spins = 0;
-          continue;
-        }
+        for (int j = 0; j < kOwn; j++) tgt[j] += (j == js) ? np : 0;
+      } else if (real) {
+        loader_bump(&ready_k[slot]);   // no attention wave reads this unit: nothing to load
       }
-      if (n_fly > 0) {
-        // publish the oldest own unit: its K rows once they have landed (the
-        // loads issued after them are its V rows and the newer units), then
-        // its V rows
-        if (loaded & 1u) {
-          wait_units_older_than<C::kUnitLoads, C::kLoadsKV>(__popc(loaded >> 1));
-          loader_bump(&ready_k[v_pub % R]);
-          wait_units_older_than<C::kUnitLoads>(__popc(loaded >> 1));
+      // stage the next own unit while this one's V rows are in flight
+      int np_n = 0;
+      int64_t rb_n = 0;
+      have = locate(v_cur + kProducers, np_n, rb_n);
+      const bool staged = have && np_n > 0;
+      if (staged) issue_k(rb_n);
+      if (np > 0) {
+        if (staged) {
+          wait_vmcnt<C::kLoadsKV>();   // the V rows, older than the K loads just issued
         } else {
-          loader_bump(&ready_k[v_pub % R]);   // nothing was loaded: both at once
+          wait_vmcnt<0>();
         }
-        loader_bump(&ready[v_pub % R]);
-        loaded >>= 1;
-        n_fly--;
-        v_pub += kProducers;
-        spins = 0;
-        continue;
       }
-      if (!have) break;  // stream exhausted and everything published
-      __builtin_amdgcn_s_sleep(1);
-      if (++spins > kMaxSpin) {
-        stuck = true;
-        break;
-      }
+      if (real) loader_bump(&ready[slot]);
+      v_cur += kProducers;
+      np = np_n;
+      rb = rb_n;
     }
     if (stuck) atomicOr(a.err, kErrStuck);
     return;

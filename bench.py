@@ -285,7 +285,7 @@ def main():
             "workload": w.name, "B": w.B, "T": w.T, "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D,
             "block_size": w.block_size, "S": w.S, "varlen_seqs": None if w.cu_seqlens is None else len(w.seqlens),
             "useful_flop_per_step": flop, "pct_of_bf16_mfma_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
-            "input_sha256": w.digest()[:16], "device": props.name or "gfx950", "cus": props.multi_processor_count,
+            "input_sha256": w.digest()[:16], "device": (getattr(props, "gcnArchName", "") or props.name or "gfx950").split(":")[0], "cus": props.multi_processor_count,
             "wall_s_timed": round(wall, 4),
         },
         "roofline": {

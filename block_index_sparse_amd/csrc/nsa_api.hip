@@ -57,21 +57,34 @@ nsa_status make_plan(const nsa_dims* d, int32_t block_size, int32_t num_seqs, bo
   // tokens per 16-column tile: the largest power of two with tpt * gv <= 16
   P.tpt = 1;
   while (P.tpt * 2 * P.gv <= 16) P.tpt *= 2;
-  P.ntpw = P.bf16 ? 1 : ((P.tpt * 2 * nsa::kConsumers <= nsa::kMaxTileTokens) ? 2 : 1);
+  P.ntpw = P.bf16 ? 1 : ((P.tpt * 2 * nsa::kConsumers <= nsa::kMaxTileTokensF32) ? 2 : 1);
   P.tpw = P.tpt * P.ntpw;
-  P.tq = std::min(nsa::kConsumers * P.tpw, nsa::kMaxTileTokens) / P.tpw * P.tpw;
   P.kb = P.bs < 64 ? P.bs : 64;
   P.nsb = P.bs / P.kb;
+  const int64_t nb_max = (P.T + P.bs - 1) / P.bs;  // a sequence is at most T long
+  if (nb_max > (int64_t)nsa::kMaxBitmapWords * 32) return NSA_ERROR_NOT_SUPPORTED;
+  // Tokens per item: one tile per attention wave (bf16 up to 256 tokens,
+  // fp32 up to 128).  An item wider than 128 tokens is used only where its
+  // merged list and token masks fit the scheduler's 64 KB of LDS per wave;
+  // otherwise the item falls back to 128 tokens.
+  const int64_t nbw = (nb_max + 31) / 32;
+  int64_t umax = 1;
+  auto size_for = [&](int32_t tq) {
+    P.tq = tq;
+    P.mw = (tq + 31) / 32;
+    umax = std::max<int64_t>(1, std::min<int64_t>((int64_t)tq * P.S, nb_max));
+  };
+  size_for(std::min(nsa::kConsumers * P.tpw, P.bf16 ? nsa::kMaxTileTokens : nsa::kMaxTileTokensF32) / P.tpw *
+           P.tpw);
+  if (P.tq > 128 &&
+      (umax > nsa::kMaxUnion || (2 * nbw + (int64_t)P.mw * umax) * (int64_t)sizeof(uint32_t) > 64 * 1024))
+    size_for(std::min(nsa::kConsumers * P.tpw, 128) / P.tpw * P.tpw);
+  if (umax > nsa::kMaxUnion) return NSA_ERROR_NOT_SUPPORTED;
   const int64_t Ttot = rows;
   const int64_t n_tiles =
       varlen ? Ttot / P.tq + P.num_seqs : (int64_t)P.B * ((P.T + P.tq - 1) / P.tq);
-  const int64_t nb_max = (P.T + P.bs - 1) / P.bs;  // a sequence is at most T long
-  if (nb_max > (int64_t)nsa::kMaxBitmapWords * 32) return NSA_ERROR_NOT_SUPPORTED;
   const int64_t n_items = n_tiles * P.hv;
   if (n_items > INT32_MAX / 2) return NSA_ERROR_NOT_SUPPORTED;
-  int64_t umax = std::min<int64_t>((int64_t)P.tq * P.S, nb_max);
-  if (umax < 1) umax = 1;
-  if (umax > nsa::kMaxUnion) return NSA_ERROR_NOT_SUPPORTED;
   P.n_tiles = (int32_t)n_tiles;
   P.n_items = (int32_t)n_items;
   P.nb_max = (int32_t)nb_max;
@@ -93,7 +106,7 @@ nsa_status make_plan(const nsa_dims* d, int32_t block_size, int32_t num_seqs, bo
   P.off_hdr = take(sizeof(nsa::ItemHeader) * n_items);
   P.off_bucket = take(sizeof(int32_t) * n_items);
   P.off_blocks = take(sizeof(int32_t) * n_items * P.umax);
-  P.off_masks = take(sizeof(uint32_t) * nsa::kMaxMaskWords * n_items * P.umax);
+  P.off_masks = take(sizeof(uint32_t) * P.mw * n_items * P.umax);
   P.off_units = take(sizeof(uint32_t) * n_items * P.umax_units);
   P.off_hist = take(sizeof(int32_t) * (size_t)nsa::kNumBuckets * P.n_chunks);
   P.off_off = take(sizeof(int32_t) * (size_t)nsa::kNumBuckets * P.n_chunks);

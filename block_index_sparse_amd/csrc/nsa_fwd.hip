@@ -95,12 +95,12 @@ struct FwdArgs {
   float* lse;
   const ItemHeader* hdr;
   const int32_t* blocks;
-  const uint4* masks;
+  const uint32_t* masks;   // [n_items * umax][mw] token bits of each merged entry
   const uint32_t* units;
   const int32_t* worklist;
   int32_t* err;
   int32_t Ttot;     // packed token rows
-  int32_t Hq, Hkv, G, gv, gpk, tpt, tpw, n_tiles, n_items, umax, umax_units, bs, nwg;
+  int32_t Hq, Hkv, G, gv, gpk, tpt, tpw, tq, mw, n_tiles, n_items, umax, umax_units, bs, nwg;
   float scale_log2;  // scale * log2(e)
 };
 
@@ -108,7 +108,7 @@ struct FwdArgs {
 // not hold a matching schedule then cannot make the kernels touch memory
 // outside their arguments.
 __device__ __forceinline__ bool header_ok(ItemHeader& hd, const FwdArgs& a) {
-  if (hd.ntok <= 0 || hd.ntok > kMaxTileTokens || hd.pos0 < 0 || hd.tok0 < hd.pos0) return false;
+  if (hd.ntok <= 0 || hd.ntok > a.tq || hd.pos0 < 0 || hd.tok0 < hd.pos0) return false;
   if (hd.tok0 + hd.ntok > a.Ttot) return false;
   hd.nunion = min(max(hd.nunion, 0), a.umax);
   return true;
@@ -150,12 +150,10 @@ __device__ __forceinline__ void column_of(int c, int gv, int tpt, int tok_base, 
   valid = (lt < tpt) && (tau < ntok);
 }
 
-__device__ __forceinline__ uint32_t mask_bits(const uint4& m, int first, int count) {
-  // `count` bits of the 128-bit token set starting at bit `first` (count is
-  // a power of two <= 32 and first a multiple of it, so the field never
-  // straddles words)
-  const int w = first >> 5;
-  const uint32_t word = w == 0 ? m.x : (w == 1 ? m.y : (w == 2 ? m.z : m.w));
+// `count` token bits from bit `first` of an entry's token set, given the
+// set's word that holds them (word first / 32: count is a power of two <= 32
+// and first a multiple of it, so the field never straddles words).
+__device__ __forceinline__ uint32_t mask_field(uint32_t word, int first, int count) {
   const uint32_t sh = word >> (first & 31);
   return count >= 32 ? sh : (sh & ((1u << count) - 1u));
 }
@@ -568,8 +566,8 @@ __global__ void __launch_bounds__(64 * (kConsumers + kProducers), 1) fwd_bf16_ri
         lj = (int)(word & 0xFFFFFFu);
         const int ks = lj * a.bs + sb * KB;
         if ((word >> 31) != 0u && ks <= my_tmax) {
-          const uint4 mk = a.masks[(int64_t)item * a.umax + u];
-          lbits = mask_bits(mk, tok_first, tpw);
+          const uint32_t mk = a.masks[((int64_t)item * a.umax + u) * a.mw + (tok_first >> 5)];
+          lbits = mask_field(mk, tok_first, tpw);
           part = lbits != 0u;
         }
       }
@@ -833,8 +831,8 @@ __global__ void __launch_bounds__(256, 2) fwd_f32_kernel(FwdArgs a) {
   for (int u = 0; u < hd.nunion; u++) {
     const int j = a.blocks[(int64_t)item * a.umax + u];
     if (j < 0 || j > my_tmax / a.bs) continue;
-    const uint4 mk = a.masks[(int64_t)item * a.umax + u];
-    const uint32_t mine = mask_bits(mk, tok_first, tpw);
+    const uint32_t mk = a.masks[((int64_t)item * a.umax + u) * a.mw + (tok_first >> 5)];
+    const uint32_t mine = mask_field(mk, tok_first, tpw);
     if (mine == 0u) continue;
     for (int sb = 0; sb < a.bs / KB; sb++) {
       const int kstart = j * a.bs + sb * KB;
@@ -964,7 +962,9 @@ hipError_t launch_fwd(const Plan& p, const void* q, const void* k, const void* v
   a.lse = lse;
   a.hdr = reinterpret_cast<const ItemHeader*>(ws + p.off_hdr);
   a.blocks = reinterpret_cast<const int32_t*>(ws + p.off_blocks);
-  a.masks = reinterpret_cast<const uint4*>(ws + p.off_masks);
+  a.masks = reinterpret_cast<const uint32_t*>(ws + p.off_masks);
+  a.tq = p.tq;
+  a.mw = p.mw;
   a.units = reinterpret_cast<const uint32_t*>(ws + p.off_units);
   a.umax_units = p.umax_units;
   a.worklist = reinterpret_cast<const int32_t*>(ws + p.off_worklist);

@@ -21,8 +21,9 @@ struct ItemHeader {
 
 constexpr int kNumBuckets = 128;    // longest-first weight buckets
 constexpr int kChunk = 64;          // items per scheduler chunk
-constexpr int kMaxMaskWords = 4;    // token bit set of one list entry: up to 128 tokens
+constexpr int kMaxMaskWords = 8;    // token bit set of one list entry: up to 256 tokens
 constexpr int kMaxTileTokens = 32 * kMaxMaskWords;
+constexpr int kMaxTileTokensF32 = 128;   // tokens per item of the fp32 path
 constexpr int kMaxBitmapWords = 2048;   // blocks per sequence the planner can merge: 65536
 constexpr int kMaxUnion = 2048;         // entries of one item's merged list
 constexpr int kConsumers = 12;      // attention waves per forward workgroup
@@ -53,7 +54,8 @@ struct Plan {
   int32_t tpt;               // tokens per 16-column MFMA tile
   int32_t ntpw;              // column tiles per attention wave
   int32_t tpw;               // tokens per attention wave
-  int32_t tq;                // tokens per item (at most kConsumers * tpw and 128)
+  int32_t tq;                // tokens per item (at most kConsumers * tpw)
+  int32_t mw;                // token-mask words per merged-list entry (ceil(tq / 32))
   int32_t kb;                // keys per streamed unit (min(bs, 64))
   int32_t nsb;               // streamed units per listed block (bs / kb)
   int32_t umax_units;        // unit-table stride per item (umax * nsb rounded up to 16)

@@ -60,17 +60,18 @@ struct PlanArgs {
   ItemHeader* hdr;
   int32_t* bucket;
   int32_t* blocks;      // [n_items * umax]
-  uint4* masks;         // [n_items * umax]
+  uint32_t* masks;      // [n_items * umax][mw]
   uint32_t* units;      // [n_items * umax_units]
   int32_t* hist;        // [kNumBuckets][n_chunks]
   int32_t T, Hkv, S, bs, gpk, tq, num_seqs, n_tiles, n_items, umax, n_chunks;
   int32_t max_pairs;    // tq * min(S, blocks per sequence): the heaviest possible item
   int32_t kb, nsb, umax_units, tpw;
+  int32_t mw;           // token-mask words per merged entry
   int32_t nbw;          // bitmap words per wave: ceil(blocks per sequence / 32)
-  int32_t wave_words;   // LDS words per wave: 2 * nbw + kMaxMaskWords * umax
+  int32_t wave_words;   // LDS words per wave: 2 * nbw + mw * umax
 };
 
-// Token bits [first, first + count) of a 128-bit set (count a power of two
+// Token bits [first, first + count) of an entry's token set (count a power of two
 // dividing 32, first a multiple of count).
 __device__ __forceinline__ uint32_t field(const uint32_t* m, int first, int count) {
   const uint32_t sh = m[first >> 5] >> (first & 31);
@@ -127,7 +128,7 @@ __global__ void __launch_bounds__(256) plan_kernel(PlanArgs a) {
   if (item >= a.n_items) return;
   uint32_t* bitmap = plan_lds + (size_t)wv * a.wave_words;
   int32_t* wbase = reinterpret_cast<int32_t*>(bitmap + a.nbw);
-  uint32_t* tmask = bitmap + 2 * a.nbw;   // [umax][kMaxMaskWords]
+  uint32_t* tmask = bitmap + 2 * a.nbw;   // [umax][mw]
 
   const int32_t vg = item / a.n_tiles;
   const int32_t tile = item - vg * a.n_tiles;
@@ -191,7 +192,7 @@ __global__ void __launch_bounds__(256) plan_kernel(PlanArgs a) {
       run += __popc(bitmap[w]);
     }
   }
-  for (int32_t c = lane; c < U * kMaxMaskWords; c += 64) tmask[c] = 0;
+  for (int32_t c = lane; c < U * a.mw; c += 64) tmask[c] = 0;
   wave_lds_sync();
   // token set of every merged entry
   for (int32_t e0 = lane; e0 < nent; e0 += 64 * kPlanBatch) {
@@ -205,7 +206,7 @@ __global__ void __launch_bounds__(256) plan_kernel(PlanArgs a) {
         const int32_t tau = (e0 + 64 * u) / a.S;
         const int32_t w = idx >> 5;
         const int32_t cid = wbase[w] + __popc(bitmap[w] & ((1u << (idx & 31)) - 1u));
-        atomicOr(&tmask[cid * kMaxMaskWords + (tau >> 5)], 1u << (tau & 31));
+        atomicOr(&tmask[cid * a.mw + (tau >> 5)], 1u << (tau & 31));
       }
     }
   }
@@ -218,10 +219,12 @@ __global__ void __launch_bounds__(256) plan_kernel(PlanArgs a) {
     const uint32_t bits = bitmap[w];
     if (((bits >> (blk & 31)) & 1u) == 0u) continue;
     const int32_t cid = wbase[w] + __popc(bits & ((1u << (blk & 31)) - 1u));
-    const uint32_t* tm = tmask + cid * kMaxMaskWords;
+    const uint32_t* tm = tmask + cid * a.mw;
     a.blocks[lbase + cid] = blk;
-    a.masks[lbase + cid] = uint4{tm[0], tm[1], tm[2], tm[3]};
-    pairs += __popc(tm[0]) + __popc(tm[1]) + __popc(tm[2]) + __popc(tm[3]);
+    for (int32_t w2 = 0; w2 < a.mw; w2++) {
+      a.masks[(lbase + cid) * a.mw + w2] = tm[w2];
+      pairs += __popc(tm[w2]);
+    }
     // unit words: which attention waves read each key sub-block
     for (int32_t sb = 0; sb < a.nsb; sb++) {
       const int32_t kstart = blk * a.bs + sb * a.kb;
@@ -324,7 +327,8 @@ hipError_t launch_schedule(const Plan& p, const int32_t* block_indices, const in
   a.hdr = reinterpret_cast<ItemHeader*>(ws + p.off_hdr);
   a.bucket = reinterpret_cast<int32_t*>(ws + p.off_bucket);
   a.blocks = reinterpret_cast<int32_t*>(ws + p.off_blocks);
-  a.masks = reinterpret_cast<uint4*>(ws + p.off_masks);
+  a.masks = reinterpret_cast<uint32_t*>(ws + p.off_masks);
+  a.mw = p.mw;
   a.hist = hist;
   a.T = p.T;
   a.Hkv = p.Hkv;
@@ -344,7 +348,7 @@ hipError_t launch_schedule(const Plan& p, const int32_t* block_indices, const in
   a.umax_units = p.umax_units;
   a.tpw = p.tpw;
   a.nbw = (p.nb_max + 31) / 32;
-  a.wave_words = 2 * a.nbw + kMaxMaskWords * p.umax;
+  a.wave_words = 2 * a.nbw + p.mw * p.umax;
   const size_t wave_bytes = sizeof(uint32_t) * (size_t)a.wave_words;
   int waves = (int)((64 * 1024) / wave_bytes);   // items per workgroup
   waves = waves < 1 ? 1 : (waves > 4 ? 4 : waves);

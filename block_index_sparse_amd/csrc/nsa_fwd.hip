@@ -8,11 +8,13 @@
 //
 // bf16 kernel: persistent workgroups of 16 waves, one per CU.
 //  * 4 loader waves stream the K and V rows of each item's merged block list
-//    (ascending block order, `kb` keys per unit) into a ring of R LDS slots
-//    with direct-to-LDS 16-byte buffer loads.  Loader p owns the units
-//    v = p (mod 4), loads all of a unit and publishes its K rows and then its
-//    V rows once they have landed; a slot is refilled only when every
-//    attention wave that reads its occupant has released it.
+//    (ascending block order, `kb` keys per unit) into a ring of R LDS slots.
+//    Loader p owns the units v = p (mod 4).  It fetches the K rows of its
+//    next unit into registers while that unit's slot is still being read,
+//    stores them into the slot once every attention wave that reads the
+//    occupant has released it, publishes them, and sends the V rows
+//    straight to LDS with 16-byte buffer loads, publishing them once they
+//    have landed.
 //  * 12 attention waves each own a fixed set of the item's tokens and walk
 //    the same unit sequence without any barrier: a wave waits only for the
 //    unit's data, computes its own tokens that selected the block, releases
@@ -72,16 +74,6 @@ __device__ __forceinline__ T ld_const(const T* p, int64_t i) {
 #else
   return p[i];
 #endif
-}
-
-__device__ __forceinline__ uint4 ld_const_mask(const uint4* p, int64_t i) {
-  const uint32_t* w = reinterpret_cast<const uint32_t*>(p) + i * 4;
-  uint4 m;
-  m.x = ld_const(w, 0);
-  m.y = ld_const(w, 1);
-  m.z = ld_const(w, 2);
-  m.w = ld_const(w, 3);
-  return m;
 }
 
 constexpr int kMaxSpin = 1 << 22;        // polls before a wait is declared stuck
@@ -178,27 +170,6 @@ template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
-
-// Wait until at most `newer` units (SHARE loads each) of this wave are still
-// in flight; loads complete in issue order for the counter.
-// With EXTRA > 0, additionally allow EXTRA loads issued after the awaited
-// ones (the V rows that follow a unit's K rows).  A count that would not fit
-// the counter falls back to waiting for everything.
-template <int SHARE, int EXTRA = 0>
-__device__ __forceinline__ void wait_units_older_than(int newer) {
-#define NSA_W(k) wait_vmcnt<(EXTRA + (k) * SHARE < 64 ? EXTRA + (k) * SHARE : 0)>()
-  switch (newer) {
-    case 0: NSA_W(0); break;
-    case 1: NSA_W(1); break;
-    case 2: NSA_W(2); break;
-    case 3: NSA_W(3); break;
-    case 4: NSA_W(4); break;
-    case 5: NSA_W(5); break;
-    case 6: NSA_W(6); break;
-    default: wait_vmcnt<0>(); break;
-  }
-#undef NSA_W
 }
 
 // A pointer whose value is the same in every lane, held in scalar registers.
@@ -319,17 +290,9 @@ struct RingCfg {
   static constexpr int kR0 = (128 * 1024) / kSlotBytes;
   static constexpr int R = kR0 > 8 ? 8 : kR0;                    // ring slots
   static constexpr int kLoadsKV = (KB * D * 2) / 1024;           // 1 KB loads per K (or V) unit
-  static constexpr int SHARE = 2 * kLoadsKV / kProducers;        // loads per loader wave per unit
-  static constexpr int kMaxF0 = 63 / SHARE;
-  static constexpr int kMaxF1 = kMaxF0 < R ? kMaxF0 : R;
-  static constexpr int MAXF = kMaxF1 < 7 ? kMaxF1 : 7;           // units in flight per loader
   static constexpr int kRowsPerLoad = 1024 / (D * 2);
-  static constexpr int kUnitLoads = 2 * kLoadsKV;                // loads of one whole unit
-  static constexpr int kOwnSlots0 = R / kProducers;              // units in flight per loader
-  static constexpr int kOwnSlots1 = kOwnSlots0 * kUnitLoads <= 63 ? kOwnSlots0 : 63 / kUnitLoads;
-  static constexpr int kOwnSlots = kOwnSlots1 < 1 ? 1 : kOwnSlots1;
   static_assert(R % kProducers == 0, "slots per loader");
-  static_assert(kUnitLoads <= 63, "one unit must fit the load counter");
+  static_assert(kLoadsKV <= 16, "a unit's K rows must fit the loader's staging registers");
 };
 
 // kPosScale: the softmax scale is > 0, so max(scale * s) = scale * max(s) and
@@ -368,9 +331,8 @@ __global__ void __launch_bounds__(64 * (kConsumers + kProducers), 1) fwd_bf16_ri
 
   if (wave >= kConsumers) {
     // ------------------------------------------------------------ loader
-    // Loader p owns the units v with v % kProducers == p: it loads all of a
-    // unit's K and V rows and publishes the unit as soon as its own loads
-    // have landed.  It keeps up to R / kProducers of its units in flight.
+    // Loader p owns the units v with v % kProducers == p, and the slots
+    // those units map to; it places its units one after another.
     const char* __restrict__ K = reinterpret_cast<const char*>(a.k);
     const char* __restrict__ V = reinterpret_cast<const char*>(a.v);
     const int p = wave - kConsumers;

@@ -443,20 +443,17 @@ __global__ void __launch_bounds__(64 * (kConsumers + kProducers), 1) fwd_bf16_ri
       } else if (real) {
         loader_bump(&ready_k[slot]);   // no attention wave reads this unit: nothing to load
       }
-      // stage the next own unit while this one's V rows are in flight
+      // Find the next own unit while this one's V rows are in flight, and
+      // stage its K rows only after publishing them: the V loads are the
+      // ones attention waves are about to wait for, so they should not
+      // queue behind the early K loads in the vector-memory path.
       int np_n = 0;
       int64_t rb_n = 0;
       have = locate(v_cur + kProducers, np_n, rb_n);
       const bool staged = have && np_n > 0;
-      if (staged) issue_k(rb_n);
-      if (np > 0) {
-        if (staged) {
-          wait_vmcnt<C::kLoadsKV>();   // the V rows, older than the K loads just issued
-        } else {
-          wait_vmcnt<0>();
-        }
-      }
+      if (np > 0) wait_vmcnt<0>();   // the V rows have landed
       if (real) loader_bump(&ready[slot]);
+      if (staged) issue_k(rb_n);
       v_cur += kProducers;
       np = np_n;
       rb = rb_n;

@@ -118,15 +118,24 @@ __device__ __forceinline__ int32_t entry_block(const PlanArgs& a, int32_t e, int
   return (i < n && idx >= 0 && idx <= (pos0 + tau) / a.bs) ? idx : -1;
 }
 
-// One wave per item (blockDim.x / 64 items per workgroup, each wave with its
-// own slice of the dynamic LDS; the waves never synchronise with each other).
+// kWG false: one wave per item (blockDim.x / 64 items per workgroup, each
+// wave with its own slice of the dynamic LDS; the waves never synchronise
+// with each other).  kWG true: one workgroup of four waves per item, for
+// items with many index entries: the entry passes are spread over all 256
+// threads and one wave forms and writes the merged list.
+template <bool kWG>
 __global__ void __launch_bounds__(256) plan_kernel(PlanArgs a) {
   extern __shared__ uint32_t plan_lds[];
   const int32_t lane = threadIdx.x & 63;
   const int32_t wv = threadIdx.x >> 6;
-  const int32_t item = blockIdx.x * (int32_t)(blockDim.x >> 6) + wv;
+  const int32_t item = kWG ? (int32_t)blockIdx.x : blockIdx.x * (int32_t)(blockDim.x >> 6) + wv;
   if (item >= a.n_items) return;
-  uint32_t* bitmap = plan_lds + (size_t)wv * a.wave_words;
+  const int32_t tid = kWG ? (int32_t)threadIdx.x : lane;   // this thread among the item's threads
+  const int32_t nthr = kWG ? 256 : 64;
+  auto item_sync = [&]() {
+    if constexpr (kWG) __syncthreads(); else wave_lds_sync();
+  };
+  uint32_t* bitmap = plan_lds + (kWG ? (size_t)0 : (size_t)wv * a.wave_words);
   int32_t* wbase = reinterpret_cast<int32_t*>(bitmap + a.nbw);
   uint32_t* tmask = bitmap + 2 * a.nbw;   // [umax][mw]
 
@@ -137,7 +146,7 @@ __global__ void __launch_bounds__(256) plan_kernel(PlanArgs a) {
   const int32_t chunk = item / kChunk;
 
   if (tile >= total_tiles) {
-    if (lane == 0) {
+    if (tid == 0) {
       a.hdr[item] = ItemHeader{0, 0, 0, 0};
       a.bucket[item] = 0;
       atomicAdd(&a.hist[chunk], 1);  // bucket 0 row
@@ -160,22 +169,23 @@ __global__ void __launch_bounds__(256) plan_kernel(PlanArgs a) {
   const int32_t nwords = own_hi / 32 + 1;   // host guarantees <= nbw
   const int32_t nent = ntok * a.S;
 
-  for (int32_t w = lane; w < nwords; w += 64) bitmap[w] = 0;
-  wave_lds_sync();
+  for (int32_t w = tid; w < nwords; w += nthr) bitmap[w] = 0;
+  item_sync();
   // Entry e = tau * S + i of the item (token tau, list position i) is kept
   // iff i < clamp(count, 0, S) and 0 <= idx <= tau's own block; the loads of
   // kPlanBatch entries per lane are issued before any of them is used.
-  for (int32_t e0 = lane; e0 < nent; e0 += 64 * kPlanBatch) {
+  for (int32_t e0 = tid; e0 < nent; e0 += nthr * kPlanBatch) {
     int32_t keep[kPlanBatch];
 #pragma unroll
-    for (int u = 0; u < kPlanBatch; u++) keep[u] = entry_block(a, e0 + 64 * u, nent, tok0, pos0, h);
+    for (int u = 0; u < kPlanBatch; u++) keep[u] = entry_block(a, e0 + nthr * u, nent, tok0, pos0, h);
 #pragma unroll
     for (int u = 0; u < kPlanBatch; u++)
       if (keep[u] >= 0) atomicOr(&bitmap[keep[u] >> 5], 1u << (keep[u] & 31));
   }
-  wave_lds_sync();
+  item_sync();
   // merged-list position of the first block of every bitmap word: each lane
-  // counts a contiguous run of words, then a wave scan
+  // counts a contiguous run of words, then a wave scan (every wave computes
+  // it, the first one stores it)
   const int32_t per = (nwords + 63) / 64;
   int32_t mine = 0;
   for (int32_t k = 0; k < per; k++) {
@@ -185,32 +195,35 @@ __global__ void __launch_bounds__(256) plan_kernel(PlanArgs a) {
   const int32_t incl = wave_inclusive_scan(mine);
   const int32_t U = __shfl(incl, 63, 64);
   int32_t run = incl - mine;
-  for (int32_t k = 0; k < per; k++) {
-    const int32_t w = lane * per + k;
-    if (w < nwords) {
-      wbase[w] = run;
-      run += __popc(bitmap[w]);
+  if (wv == 0 || !kWG) {
+    for (int32_t k = 0; k < per; k++) {
+      const int32_t w = lane * per + k;
+      if (w < nwords) {
+        wbase[w] = run;
+        run += __popc(bitmap[w]);
+      }
     }
   }
-  for (int32_t c = lane; c < U * a.mw; c += 64) tmask[c] = 0;
-  wave_lds_sync();
+  for (int32_t c = tid; c < U * a.mw; c += nthr) tmask[c] = 0;
+  item_sync();
   // token set of every merged entry
-  for (int32_t e0 = lane; e0 < nent; e0 += 64 * kPlanBatch) {
+  for (int32_t e0 = tid; e0 < nent; e0 += nthr * kPlanBatch) {
     int32_t keep[kPlanBatch];
 #pragma unroll
-    for (int u = 0; u < kPlanBatch; u++) keep[u] = entry_block(a, e0 + 64 * u, nent, tok0, pos0, h);
+    for (int u = 0; u < kPlanBatch; u++) keep[u] = entry_block(a, e0 + nthr * u, nent, tok0, pos0, h);
 #pragma unroll
     for (int u = 0; u < kPlanBatch; u++) {
       if (keep[u] >= 0) {
         const int32_t idx = keep[u];
-        const int32_t tau = (e0 + 64 * u) / a.S;
+        const int32_t tau = (e0 + nthr * u) / a.S;
         const int32_t w = idx >> 5;
         const int32_t cid = wbase[w] + __popc(bitmap[w] & ((1u << (idx & 31)) - 1u));
         atomicOr(&tmask[cid * a.mw + (tau >> 5)], 1u << (tau & 31));
       }
     }
   }
-  wave_lds_sync();
+  item_sync();
+  if (kWG && wv != 0) return;   // one wave writes the list
   // emit the list: lane-strided over the candidate blocks 0 .. 32 * nwords - 1
   int32_t pairs = 0;
   const int64_t lbase = (int64_t)item * a.umax;
@@ -350,9 +363,14 @@ hipError_t launch_schedule(const Plan& p, const int32_t* block_indices, const in
   a.nbw = (p.nb_max + 31) / 32;
   a.wave_words = 2 * a.nbw + p.mw * p.umax;
   const size_t wave_bytes = sizeof(uint32_t) * (size_t)a.wave_words;
-  int waves = (int)((64 * 1024) / wave_bytes);   // items per workgroup
-  waves = waves < 1 ? 1 : (waves > 4 ? 4 : waves);
-  plan_kernel<<<(p.n_items + waves - 1) / waves, 64 * waves, wave_bytes * waves, stream>>>(a);
+  if ((int64_t)p.tq * p.S > 64 * 2 * kPlanBatch) {
+    // many index entries per item: a workgroup per item
+    plan_kernel<true><<<p.n_items, 256, wave_bytes, stream>>>(a);
+  } else {
+    int waves = (int)((64 * 1024) / wave_bytes);   // items per workgroup
+    waves = waves < 1 ? 1 : (waves > 4 ? 4 : waves);
+    plan_kernel<false><<<(p.n_items + waves - 1) / waves, 64 * waves, wave_bytes * waves, stream>>>(a);
+  }
   int32_t* off = reinterpret_cast<int32_t*>(ws + p.off_off);
   int32_t* total = reinterpret_cast<int32_t*>(ws + p.off_total);
   scan_kernel<<<kNumBuckets, 256, 0, stream>>>(hist, off, total, p.n_chunks);

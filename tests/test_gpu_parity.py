@@ -34,6 +34,7 @@ SMALL = [
     ("bf16_g3_d64_bs32", "bf16", [97], 6, 2, 64, 32, 4, "local_random", "uniform", False),
     ("bf16_varlen_g16", "bf16", [65, 1, 200, 64, 129], 32, 2, 128, 64, 5, "local_random", "uniform", True),
     ("bf16_varlen_g1_d64_bs32", "bf16", [250, 5, 193, 384], 2, 2, 64, 32, 6, "local_random", "uniform", True),
+    ("bf16_g1_d128_bs64_wide_items", "bf16", [700, 700], 2, 2, 128, 64, 8, "sink_local_random", "uniform", False),
     ("f32_g4_d64_bs32", "f32", [256], 4, 1, 64, 32, 4, "shuffled", "uniform", False),
     ("f32_g2_d128_bs64", "f32", [190, 190], 4, 2, 128, 64, 3, "sink_local_random", "full", False),
     ("f32_g16_d64_bs128", "f32", [300], 16, 1, 64, 128, 3, "local_random", "uniform", False),

@@ -71,11 +71,28 @@ struct PlanArgs {
   int32_t wave_words;   // LDS words per wave: 2 * nbw + mw * umax
 };
 
-// Token bits [first, first + count) of an entry's token set (count a power of two
-// dividing 32, first a multiple of count).
-__device__ __forceinline__ uint32_t field(const uint32_t* m, int first, int count) {
-  const uint32_t sh = m[first >> 5] >> (first & 31);
-  return count >= 32 ? sh : (sh & ((1u << count) - 1u));
+// Attention waves that read a sub-block of an entry: wave wc owns the
+// item's tokens [wc * tpw, wc * tpw + tpw) and reads the sub-block iff one
+// of its tokens listed the block and its last token is at offset >= d (the
+// sub-block's first key relative to the item's first position; the caller
+// emits only sub-blocks with d < ntok, so a partial last wave qualifies
+// whenever its group index does).  Waves below wc_min = d / tpw end too
+// early; each tpw-bit group of the token set is folded to its lowest bit and
+// counted (tpw is a power of two <= 32).
+__device__ __forceinline__ int32_t readers(const uint32_t* tm, int32_t mw, int32_t tpw, int32_t d) {
+  const int32_t first_bit = (d > 0 ? d / tpw : 0) * tpw;   // first bit of wave wc_min
+  const uint32_t lows = tpw >= 32 ? 1u : 0xFFFFFFFFu / ((1u << tpw) - 1u);   // bit 0 of every group
+  int32_t np = 0;
+  for (int32_t w = 0; w < mw; w++) {
+    uint32_t x = tm[w];
+    for (int32_t sh = 1; sh < tpw; sh <<= 1) x |= x >> sh;
+    x &= lows;
+    const int32_t lo = first_bit - 32 * w;                 // keep groups from bit lo on
+    if (lo >= 32) continue;
+    if (lo > 0) x &= 0xFFFFFFFFu << lo;
+    np += __popc(x);
+  }
+  return np;
 }
 
 // LDS operations of one wave complete in issue order, so ordering the
@@ -243,14 +260,7 @@ __global__ void __launch_bounds__(256) plan_kernel(PlanArgs a) {
       const int32_t kstart = blk * a.bs + sb * a.kb;
       uint32_t word = 0u;
       if (kstart <= pos0 + ntok - 1) {
-        int32_t np = 0;
-        for (int32_t wc = 0; wc < kConsumers; wc++) {
-          const int32_t first = wc * a.tpw;
-          if (first >= ntok) break;
-          const int32_t last_pos = pos0 + min(first + a.tpw, ntok) - 1;
-          if (field(tm, first, a.tpw) != 0u && kstart <= last_pos) np++;
-        }
-        word = unit_word(blk, np);
+        word = unit_word(blk, readers(tm, a.mw, a.tpw, kstart - pos0));
       }
       a.units[(int64_t)item * a.umax_units + cid * a.nsb + sb] = word;
     }

@@ -94,6 +94,7 @@ struct FwdArgs {
   int32_t Ttot;     // packed token rows
   int32_t Hq, Hkv, G, gv, gpk, tpt, tpw, tq, mw, n_tiles, n_items, umax, umax_units, bs, nwg;
   float scale_log2;  // scale * log2(e)
+  int32_t split_release;   // attention waves release a slot's K rows after S^T
 };
 
 // A header is used only if it stays inside the tensors: a workspace that does
@@ -277,9 +278,11 @@ __device__ __forceinline__ void next_item(ItemCursor& cs, const FwdArgs& a) {
 //    units of slot s (one each per unit, live or not, in unit order): the K
 //    rows of unit v are readable once ready_k[v % R] >= v / R + 1, its V
 //    rows once ready[v % R] >= v / R + 1.
-//  * done[s] counts participant releases of slot s: the loader may overwrite
-//    slot s once done[s] has reached the participant total of all earlier
-//    occupants.  A wave can only reach a later occupant after it was
+//  * done[s] counts participant releases of slot s after their V reads: the
+//    loader may overwrite slot s once done[s] has reached the participant
+//    total of all earlier occupants.  With split releases (few readers per
+//    unit) done_k[s] also counts releases after the S^T reads, and the K rows
+//    may be replaced as soon as done_k[s] reaches that total.  A wave can only reach a later occupant after it was
 //    published, which already required every reader of the earlier one to
 //    have released it, so the counts of successive occupants never mix.
 // Waves therefore touch only the units they compute.
@@ -313,6 +316,7 @@ __global__ void __launch_bounds__(64 * (kConsumers + kProducers), 1) fwd_bf16_ri
   __shared__ __attribute__((aligned(1024))) char ring[R][C::kSlotBytes];
   __shared__ int ready_k[R];
   __shared__ int ready[R];
+  __shared__ int done_k[R];
   __shared__ int done[R];
 
   const int lane = threadIdx.x & 63;
@@ -320,6 +324,7 @@ __global__ void __launch_bounds__(64 * (kConsumers + kProducers), 1) fwd_bf16_ri
   if (threadIdx.x < R) {
     ready_k[threadIdx.x] = 0;
     ready[threadIdx.x] = 0;
+    done_k[threadIdx.x] = 0;
     done[threadIdx.x] = 0;
   }
   __syncthreads();
@@ -419,9 +424,12 @@ __global__ void __launch_bounds__(64 * (kConsumers + kProducers), 1) fwd_bf16_ri
         int t = 0;
 #pragma unroll
         for (int j = 0; j < kOwn; j++) t = (j == js) ? tgt[j] : t;
-        // the slot's earlier occupants must all have been released
+        // With split releases the K rows may be replaced once the readers of
+        // the slot's earlier occupants have formed S^T, and the V rows once
+        // they have read them; otherwise the whole slot waits for the latter.
+        int* const k_free = a.split_release ? &done_k[slot] : &done[slot];
         int spins = 0;
-        while (loader_poll(&done[slot]) < t) {
+        while (loader_poll(k_free) < t) {
           __builtin_amdgcn_s_sleep(1);
           if (++spins > kMaxSpin) {
             stuck = true;
@@ -437,6 +445,18 @@ __global__ void __launch_bounds__(64 * (kConsumers + kProducers), 1) fwd_bf16_ri
         }(std::make_integer_sequence<int, C::kLoadsKV>{});
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");   // the K stores have landed
         loader_bump(&ready_k[slot]);
+        if (a.split_release) {
+          spins = 0;
+          while (loader_poll(&done[slot]) < t) {
+            __builtin_amdgcn_s_sleep(1);
+            if (++spins > kMaxSpin) {
+              stuck = true;
+              break;
+            }
+          }
+          if (stuck) break;
+          __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        }
         issue_v(rb, kdst + KB * D * 2);
 #pragma unroll
         for (int j = 0; j < kOwn; j++) tgt[j] += (j == js) ? np : 0;
@@ -583,6 +603,7 @@ __global__ void __launch_bounds__(64 * (kConsumers + kProducers), 1) fwd_bf16_ri
                                                                         s[hh * MH + mm], 0, 0, 0);
           }
         }
+        if (a.split_release) lds_release_bump(&done_k[slot]);   // the K reads have returned
         // V^T fragments, a quarter of the row tiles at a time (lane (c, g)
         // reads keys 4g + c/4 of each 16-key half, columns 4 (c % 4) .. + 3)
         constexpr int DQ = DT / 4;
@@ -942,6 +963,9 @@ hipError_t launch_fwd(const Plan& p, const void* q, const void* k, const void* v
   a.bs = p.bs;
   a.nwg = p.nwg;
   a.scale_log2 = scale * 1.4426950408889634f;
+  // Split releases pay where a unit has few readers (one token per wave);
+  // with many readers per unit the second release atomic costs more.
+  a.split_release = p.tpw == 1 ? 1 : 0;
   KernelFn fn = pick(p.bf16, p.D, p.kb, p.ntpw, a.scale_log2 > 0.f);
   if (!fn) return hipErrorInvalidValue;
   if (p.bf16) {

@@ -582,25 +582,33 @@ __global__ void __launch_bounds__(64 * (kConsumers + kProducers), 1) fwd_bf16_ri
         f32x4 s[MT];
 #pragma unroll
         for (int mt = 0; mt < MT; mt++) s[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        // one 16-key row tile of K at a time, two in flight: the reads of
+        // tile mt + 2 are issued before the MFMAs of tile mt + 1
+        auto read_k = [&](bf16x8 (&kf)[KT], int mt) {
+          const int row = mt * 16 + c;
 #pragma unroll
-        for (int hh = 0; hh < 2; hh++) {
-          constexpr int MH = MT / 2;
-          bf16x8 kf[MH][KT];
-#pragma unroll
-          for (int mm = 0; mm < MH; mm++) {
-            const int row = (hh * MH + mm) * 16 + c;
-#pragma unroll
-            for (int kk = 0; kk < KT; kk++) {
-              const int pc = (kk * 4 + g) ^ k_swizzle<D>(row);
-              kf[mm][kk] = *(NSA_LDS const bf16x8*)(kl + row * (D * 2) + pc * 16);
-            }
+          for (int kk = 0; kk < KT; kk++) {
+            const int pc = (kk * 4 + g) ^ k_swizzle<D>(row);
+            kf[kk] = *(NSA_LDS const bf16x8*)(kl + row * (D * 2) + pc * 16);
           }
+        };
+        auto qk = [&](const bf16x8 (&kf)[KT], int mt) {
 #pragma unroll
-          for (int mm = 0; mm < MH; mm++) {
-#pragma unroll
-            for (int kk = 0; kk < KT; kk++)
-              s[hh * MH + mm] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[mm][kk], qf[n][kk],
-                                                                        s[hh * MH + mm], 0, 0, 0);
+          for (int kk = 0; kk < KT; kk++)
+            s[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kk], qf[n][kk], s[mt], 0, 0, 0);
+        };
+        {
+          static_assert(MT == 2 || MT == 4, "units of 32 or 64 keys");
+          bf16x8 ka[KT], kb[KT];
+          read_k(ka, 0);
+          read_k(kb, 1);
+          qk(ka, 0);
+          if constexpr (MT == 4) read_k(ka, 2);
+          qk(kb, 1);
+          if constexpr (MT == 4) {
+            read_k(kb, 3);
+            qk(ka, 2);
+            qk(kb, 3);
           }
         }
         if (a.split_release) lds_release_bump(&done_k[slot]);   // the K reads have returned

@@ -80,6 +80,17 @@ def test_workspace_sizes():
     assert 0 < a < b
 
 
+def test_wide_items_fall_back_where_the_scheduler_cannot_hold_them():
+    """bf16 with one query head per kv head plans 192-token items; where such
+    an item's merged list could exceed the scheduler's 2048 entries (more than
+    2048 blocks per sequence) the plan falls back to 128-token items, so every
+    shape the narrower items support stays supported."""
+    T = 2049 * 64
+    assert nsa.workspace_size(1, T, 2, 2, 64, 16, 64) > 0      # 128 x 16 = 2048 entries fit
+    assert nsa.workspace_size(1, T, 2, 2, 64, 17, 64) == 0     # 128 x 17 > 2048 and 2049 blocks
+    assert nsa.workspace_size(1, 4096, 2, 2, 64, 32, 64) > 0   # 192-token items
+
+
 def test_device_status_rejects_bad_arguments():
     """Checked on the host before any copy is enqueued."""
     lib = nsa.load_library()

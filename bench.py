@@ -260,6 +260,10 @@ def main():
     e_stop.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
+    # outside the timed region: every timed launch must have completed its
+    # bounded waits, or the numbers describe a broken run
+    if f.device_status() != 0:
+        sys.exit("bench: a bounded wait in the forward kernel expired; no result reported")
     step_ms = e_start.elapsed_time(e_stop) / K
     kern_ms = [a.elapsed_time(b) for a, b in ev]
     kern_avg = float(np.mean(kern_ms))

@@ -14,6 +14,10 @@ workload on the host's cores.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 3] [--no-cpu-baseline]
 
+--config 0..4 selects the other named workloads (parity cases, not the
+headline); --config 5 is the same long-context shape with one index row per
+query block (nsa_fwd_qblock).
+
 HBM traffic of the attention kernel comes from two rocprofv3 counter runs
 (FETCH_SIZE, then WRITE_SIZE) of this script, each scaled by what the same
 counter reads for a plain copy kernel of known size (``--calibrate-copy``);
@@ -139,9 +143,14 @@ def calibrate_copy():
 def visible_keys_per_row(w) -> np.ndarray:
     """|M_t| for every (packed token, kv head): keys of the distinct listed
     blocks 0 <= j <= own, the own block cut at the token's position."""
-    B, T, Hkv, S = w.block_indices.shape
-    bi = w.block_indices.reshape(-1, Hkv, S).astype(np.int64)
-    n = np.clip(w.block_counts.reshape(-1, Hkv), 0, S)
+    bi, bc = w.block_indices, w.block_counts
+    if getattr(w, "index_layout", "token") == "query_block":
+        # one row per query block: token t reads row t // block_size
+        qb = np.arange(w.T) // w.block_size
+        bi, bc = bi[:, :, qb, :].transpose(0, 2, 1, 3), bc[:, :, qb].transpose(0, 2, 1)
+    B, T, Hkv, S = bi.shape
+    bi = bi.reshape(-1, Hkv, S).astype(np.int64)
+    n = np.clip(bc.reshape(-1, Hkv), 0, S)
     if w.cu_seqlens is None:
         pos = np.tile(np.arange(T), B)
     else:
@@ -214,7 +223,7 @@ def main():
     args = ap.parse_args()
     if args.traffic_summary:
         import nsa_inputs as ni
-        name = ni.CONFIG_NAMES[args.config]
+        name = ni.workload_name(args.config)
         kern = "fwd_f32_kernel" if args.config == 0 else "fwd_bf16_ring_kernel"
         traffic_summary(name, *args.traffic_summary, kernel=kern)
         return
@@ -238,7 +247,7 @@ def main():
     print(f"[bench] {w.name}: generated in {gen_s:.1f} s", file=sys.stderr, flush=True)
     q, k, v, bi, bc, cu = ni.to_torch(w, dev)
     flop = useful_flops(w)
-    f = nsa.Forward(q, k, v, bi, bc, w.block_size, w.scale, cu_seqlens=cu)
+    f = nsa.Forward(q, k, v, bi, bc, w.block_size, w.scale, cu_seqlens=cu, index_layout=w.index_layout)
     torch.cuda.synchronize()
 
     for _ in range(args.warmup):
@@ -288,6 +297,7 @@ def main():
         "config": {
             "workload": w.name, "B": w.B, "T": w.T, "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D,
             "block_size": w.block_size, "S": w.S, "varlen_seqs": None if w.cu_seqlens is None else len(w.seqlens),
+            "index_layout": w.index_layout,
             "useful_flop_per_step": flop, "pct_of_bf16_mfma_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
             "input_sha256": w.digest()[:16], "device": (getattr(props, "gcnArchName", "") or props.name or "gfx950").split(":")[0], "cus": props.multi_processor_count,
             "wall_s_timed": round(wall, 4),

@@ -12,6 +12,12 @@ cu_seqlens=None) -> (out, lse)`` with q ``[B, T, Hq, D]``, k/v
 [B, T, Hkv, S]`` int32, ``block_counts [B, T, Hkv]`` int32 or a Python int
 (broadcast), ``scale`` defaulting to 1/sqrt(D), and an optional
 ``cu_seqlens [N+1]`` int32 for packed sequences (then B == 1).
+
+``index_layout="query_block"`` takes the layout of the page's
+``block_indices`` description instead: ``block_indices [B, Hkv, NQB, S]`` and
+``block_counts [B, Hkv, NQB]`` (or an int), NQB = ceil(T / block_size), one
+row per query block shared by its tokens (``nsa_fwd_qblock``; fixed-length
+sequences only).
 """
 from __future__ import annotations
 
@@ -64,6 +70,10 @@ def load_library():
     lib.nsa_fwd.argtypes = [dp, p, p, p, p, p, i32, f32, p, p, p, sz, p]
     lib.nsa_fwd_varlen.restype = ctypes.c_int
     lib.nsa_fwd_varlen.argtypes = [dp, p, p, p, p, p, p, i32, i32, f32, p, p, p, sz, p]
+    lib.nsa_fwd_qblock.restype = ctypes.c_int
+    lib.nsa_fwd_qblock.argtypes = [dp, p, p, p, p, p, i32, f32, p, p, p, sz, p]
+    lib.nsa_fwd_schedule_qblock.restype = ctypes.c_int
+    lib.nsa_fwd_schedule_qblock.argtypes = [dp, p, p, i32, p, sz, p, ctypes.POINTER(sz), ctypes.POINTER(i32)]
     lib.nsa_fwd_schedule.restype = ctypes.c_int
     lib.nsa_fwd_schedule.argtypes = [dp, p, p, p, i32, i32, p, sz, p, ctypes.POINTER(sz),
                                      ctypes.POINTER(i32)]
@@ -103,7 +113,10 @@ def _stream(torch, device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
-def _prepare(q, k, v, block_indices, block_counts, cu_seqlens):
+INDEX_LAYOUTS = ("token", "query_block")
+
+
+def _prepare(q, k, v, block_indices, block_counts, cu_seqlens, block_size=64, index_layout="token"):
     import torch
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
         raise ValueError("q, k, v must be [B, T, H, D]")
@@ -121,15 +134,25 @@ def _prepare(q, k, v, block_indices, block_counts, cu_seqlens):
     if not (q.is_cuda and k.is_cuda and v.is_cuda):
         raise ValueError("q, k, v must be GPU tensors")
     Hkv = k.shape[2]
-    if block_indices.dim() != 4 or tuple(block_indices.shape[:3]) != (B, T, Hkv):
-        raise ValueError("block_indices must be [B, T, Hkv, S]")
+    if index_layout == "token":
+        rows, name = (B, T, Hkv), "[B, T, Hkv"
+    elif index_layout == "query_block":
+        if block_size <= 0:
+            raise ValueError("block_size must be positive")
+        if cu_seqlens is not None:
+            raise ValueError("the query_block index layout takes fixed-length sequences only")
+        rows, name = (B, Hkv, (T + block_size - 1) // block_size), "[B, Hkv, ceil(T / block_size)"
+    else:
+        raise ValueError(f"index_layout must be one of {INDEX_LAYOUTS}")
+    if block_indices.dim() != 4 or tuple(block_indices.shape[:3]) != rows:
+        raise ValueError(f"block_indices must be {name}, S]")
     S = block_indices.shape[3]
     bi = block_indices.to(device=q.device, dtype=torch.int32).contiguous()
     if isinstance(block_counts, int):
-        bc = torch.full((B, T, Hkv), block_counts, dtype=torch.int32, device=q.device)
+        bc = torch.full(rows, block_counts, dtype=torch.int32, device=q.device)
     else:
-        if tuple(block_counts.shape) != (B, T, Hkv):
-            raise ValueError("block_counts must be [B, T, Hkv] or an int")
+        if tuple(block_counts.shape) != rows:
+            raise ValueError(f"block_counts must be {name}] or an int")
         bc = block_counts.to(device=q.device, dtype=torch.int32).contiguous()
     cu = None
     if cu_seqlens is not None:
@@ -143,18 +166,20 @@ class Forward:
     """A prepared forward call: device buffers and ctypes arguments are built
     once, so repeated calls cost one C call each.
 
-    ``run()`` is ``nsa_fwd`` / ``nsa_fwd_varlen``; ``schedule()`` and
-    ``execute()`` are its two halves (``nsa_fwd_schedule`` then
-    ``nsa_fwd_execute``).  All launch on torch's current stream of q's device.
+    ``run()`` is ``nsa_fwd`` / ``nsa_fwd_varlen`` / ``nsa_fwd_qblock``;
+    ``schedule()`` and ``execute()`` are its two halves (``nsa_fwd_schedule``
+    or ``nsa_fwd_schedule_qblock``, then ``nsa_fwd_execute``).  All launch on
+    torch's current stream of q's device.
     """
 
     def __init__(self, q, k, v, block_indices, block_counts, block_size: int = 64,
                  scale: float | None = None, cu_seqlens=None, out=None, lse=None, workspace=None,
-                 return_lse: bool = True):
+                 return_lse: bool = True, index_layout: str = "token"):
         import torch
         self.lib = load_library()
         (self.q, self.k, self.v, self.bi, self.bc, self.cu, B, T, Hq, Hkv, D, S,
-         code) = _prepare(q, k, v, block_indices, block_counts, cu_seqlens)
+         code) = _prepare(q, k, v, block_indices, block_counts, cu_seqlens, int(block_size), index_layout)
+        self.qblock = index_layout == "query_block"
         self.scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
         self.block_size = int(block_size)
         self.nseq = 0 if self.cu is None else self.cu.numel() - 1
@@ -174,7 +199,11 @@ class Forward:
 
     def run(self):
         P, L = self._p, self.lib
-        if self.cu is None:
+        if self.qblock:
+            st = L.nsa_fwd_qblock(ctypes.byref(self.dims), P["q"], P["k"], P["v"], P["bi"], P["bc"],
+                                  self.block_size, self.scale, P["out"], P["lse"], P["workspace"],
+                                  self.ws_bytes, self.stream)
+        elif self.cu is None:
             st = L.nsa_fwd(ctypes.byref(self.dims), P["q"], P["k"], P["v"], P["bi"], P["bc"],
                            self.block_size, self.scale, P["out"], P["lse"], P["workspace"],
                            self.ws_bytes, self.stream)
@@ -190,6 +219,11 @@ class Forward:
         P = self._p
         off = ctypes.c_size_t(0)
         n = ctypes.c_int32(0)
+        if self.qblock:
+            _check(self.lib.nsa_fwd_schedule_qblock(ctypes.byref(self.dims), P["bi"], P["bc"], self.block_size,
+                                                    P["workspace"], self.ws_bytes, self.stream,
+                                                    ctypes.byref(off), ctypes.byref(n)))
+            return off.value, n.value
         _check(self.lib.nsa_fwd_schedule(ctypes.byref(self.dims), P["bi"], P["bc"], P["cu"], self.nseq,
                                          self.block_size, P["workspace"], self.ws_bytes, self.stream,
                                          ctypes.byref(off), ctypes.byref(n)))
@@ -220,10 +254,11 @@ class Forward:
 
 
 def fwd(q, k, v, block_indices, block_counts, block_size: int = 64, scale: float | None = None,
-        cu_seqlens=None, out=None, lse=None, workspace=None, return_lse: bool = True):
+        cu_seqlens=None, out=None, lse=None, workspace=None, return_lse: bool = True,
+        index_layout: str = "token"):
     """Native sparse attention forward on the GPU.  Returns (out, lse)."""
     return Forward(q, k, v, block_indices, block_counts, block_size, scale, cu_seqlens, out, lse,
-                   workspace, return_lse).run()
+                   workspace, return_lse, index_layout).run()
 
 
 def schedule(block_indices, block_counts, Hq, D, block_size, dtype="bf16", cu_seqlens=None):

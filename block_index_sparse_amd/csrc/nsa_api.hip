@@ -16,13 +16,15 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // Derive tiling and workspace layout.  Returns NSA_SUCCESS or an error.
-nsa_status make_plan(const nsa_dims* d, int32_t block_size, int32_t num_seqs, bool varlen, Plan* p) {
+nsa_status make_plan(const nsa_dims* d, int32_t block_size, int32_t num_seqs, bool varlen, Plan* p,
+                     bool qblock = false) {
   if (!d) return NSA_ERROR_INVALID_VALUE;
   if (d->batch <= 0 || d->seqlen <= 0 || d->num_q_heads <= 0 || d->num_kv_heads <= 0 ||
       d->head_dim <= 0 || d->num_selected <= 0 || block_size <= 0)
     return NSA_ERROR_INVALID_VALUE;
   if (d->num_q_heads % d->num_kv_heads) return NSA_ERROR_INVALID_VALUE;
   if (varlen && (d->batch != 1 || num_seqs <= 0)) return NSA_ERROR_INVALID_VALUE;
+  if (varlen && qblock) return NSA_ERROR_NOT_SUPPORTED;
   if (d->dtype != NSA_DTYPE_F32 && d->dtype != NSA_DTYPE_BF16) return NSA_ERROR_NOT_SUPPORTED;
   if (d->head_dim != 64 && d->head_dim != 128) return NSA_ERROR_NOT_SUPPORTED;
   if (block_size != 32 && block_size != 64 && block_size != 128) return NSA_ERROR_NOT_SUPPORTED;
@@ -41,6 +43,8 @@ nsa_status make_plan(const nsa_dims* d, int32_t block_size, int32_t num_seqs, bo
   P.bs = block_size;
   P.G = P.Hq / P.Hkv;
   P.varlen = varlen;
+  P.qblock = qblock;
+  P.nqb = (P.T + P.bs - 1) / P.bs;
   P.num_seqs = varlen ? num_seqs : P.B;
   P.bf16 = d->dtype == NSA_DTYPE_BF16;
   // head groups of at most 16 heads (one MFMA column tile)
@@ -140,9 +144,9 @@ bool log_enabled() {
 nsa_status run(const nsa_dims* d, const void* q, const void* k, const void* v,
                const int32_t* block_indices, const int32_t* block_counts, const int32_t* cu_seqlens,
                int32_t num_seqs, bool varlen, int32_t block_size, float scale, void* out, float* lse,
-               void* workspace, size_t workspace_bytes, void* stream) {
+               void* workspace, size_t workspace_bytes, void* stream, bool qblock = false) {
   Plan p;
-  nsa_status st = make_plan(d, block_size, num_seqs, varlen, &p);
+  nsa_status st = make_plan(d, block_size, num_seqs, varlen, &p, qblock);
   if (st != NSA_SUCCESS) return st;
   if (!block_indices || !block_counts) return NSA_ERROR_INVALID_VALUE;
   if (varlen && !cu_seqlens) return NSA_ERROR_INVALID_VALUE;
@@ -151,9 +155,9 @@ nsa_status run(const nsa_dims* d, const void* q, const void* k, const void* v,
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   char* ws = reinterpret_cast<char*>(workspace);
   if (log_enabled())
-    fprintf(stderr, "[nsa] %s D=%d bs=%d G=%d gv=%d tpt=%d ntpw=%d tq=%d items=%d umax=%d nwg=%d ws=%zu\n",
-            p.bf16 ? "bf16" : "f32", p.D, p.bs, p.G, p.gv, p.tpt, p.ntpw, p.tq, p.n_items, p.umax,
-            p.nwg, p.bytes);
+    fprintf(stderr, "[nsa] %s%s D=%d bs=%d G=%d gv=%d tpt=%d ntpw=%d tq=%d items=%d umax=%d nwg=%d ws=%zu\n",
+            p.bf16 ? "bf16" : "f32", p.qblock ? " qblock" : "", p.D, p.bs, p.G, p.gv, p.tpt, p.ntpw, p.tq,
+            p.n_items, p.umax, p.nwg, p.bytes);
   if (nsa::launch_schedule(p, block_indices, block_counts, cu_seqlens, ws, s) != hipSuccess)
     return NSA_ERROR_LAUNCH_FAILED;
   if (nsa::launch_fwd(p, q, k, v, scale, out, lse, ws, s) != hipSuccess)
@@ -186,6 +190,32 @@ nsa_status nsa_fwd_varlen(const nsa_dims* dims, const void* q, const void* k, co
                           size_t workspace_bytes, void* stream) {
   return run(dims, q, k, v, block_indices, block_counts, cu_seqlens, num_seqs, true, block_size,
              scale, out, lse, workspace, workspace_bytes, stream);
+}
+
+nsa_status nsa_fwd_qblock(const nsa_dims* dims, const void* q, const void* k, const void* v,
+                          const int32_t* block_indices, const int32_t* block_counts,
+                          int32_t block_size, float scale, void* out, float* lse, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  return run(dims, q, k, v, block_indices, block_counts, nullptr, 0, false, block_size, scale, out,
+             lse, workspace, workspace_bytes, stream, true);
+}
+
+nsa_status nsa_fwd_schedule_qblock(const nsa_dims* dims, const int32_t* block_indices,
+                                   const int32_t* block_counts, int32_t block_size,
+                                   void* workspace, size_t workspace_bytes, void* stream,
+                                   size_t* list_offset, int32_t* list_len) {
+  Plan p;
+  nsa_status st = make_plan(dims, block_size, 0, false, &p, true);
+  if (st != NSA_SUCCESS) return st;
+  if (!block_indices || !block_counts || !workspace) return NSA_ERROR_INVALID_VALUE;
+  if (reinterpret_cast<uintptr_t>(workspace) & 255u) return NSA_ERROR_INVALID_VALUE;
+  if (workspace_bytes < p.bytes) return NSA_ERROR_WORKSPACE_TOO_SMALL;
+  if (nsa::launch_schedule(p, block_indices, block_counts, nullptr, reinterpret_cast<char*>(workspace),
+                           reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
+    return NSA_ERROR_LAUNCH_FAILED;
+  if (list_offset) *list_offset = p.off_worklist;
+  if (list_len) *list_len = p.n_items;
+  return NSA_SUCCESS;
 }
 
 nsa_status nsa_fwd_schedule(const nsa_dims* dims, const int32_t* block_indices,

@@ -44,6 +44,8 @@ struct Plan {
   int32_t B, T, Hq, Hkv, D, S, bs, G;
   int32_t num_seqs;          // sequences (B for fixed length)
   bool varlen;
+  bool qblock;               // indices per query block: [B, Hkv, nqb, S], counts [B, Hkv, nqb]
+  int32_t nqb;               // query blocks per sequence (qblock layout)
   bool bf16;
   // head groups: G <= 16 -> one group of G heads per kv head; G = 32, 64 ->
   // G/16 groups of 16 heads sharing the kv head

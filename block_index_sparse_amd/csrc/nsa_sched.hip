@@ -69,6 +69,8 @@ struct PlanArgs {
   int32_t mw;           // token-mask words per merged entry
   int32_t nbw;          // bitmap words per wave: ceil(blocks per sequence / 32)
   int32_t wave_words;   // LDS words per wave: 2 * nbw + mw * umax
+  int32_t qblock;       // rows per query block: [B, Hkv, nqb, S] / [B, Hkv, nqb]
+  int32_t nqb;
 };
 
 // Attention waves that read a sub-block of an entry: wave wc owns the
@@ -128,7 +130,11 @@ __device__ __forceinline__ int32_t entry_block(const PlanArgs& a, int32_t e, int
   if (e >= nent) return -1;
   const int32_t tau = e / a.S;
   const int32_t i = e - tau * a.S;
-  const int64_t row = (int64_t)(tok0 + tau) * a.Hkv + h;
+  // row of (token, kv head), or of (sequence, kv head, query block): a token
+  // uses the row of the query block that holds it (fixed length only, so the
+  // sequence is (tok0 - pos0) / T)
+  const int64_t row = a.qblock ? ((int64_t)((tok0 - pos0) / a.T) * a.Hkv + h) * a.nqb + (pos0 + tau) / a.bs
+                               : (int64_t)(tok0 + tau) * a.Hkv + h;
   int32_t n = a.bc[row];
   const int32_t idx = a.bi[row * a.S + i];
   n = n < 0 ? 0 : (n > a.S ? a.S : n);
@@ -372,6 +378,8 @@ hipError_t launch_schedule(const Plan& p, const int32_t* block_indices, const in
   a.tpw = p.tpw;
   a.nbw = (p.nb_max + 31) / 32;
   a.wave_words = 2 * a.nbw + p.mw * p.umax;
+  a.qblock = p.qblock ? 1 : 0;
+  a.nqb = p.nqb;
   const size_t wave_bytes = sizeof(uint32_t) * (size_t)a.wave_words;
   if ((int64_t)p.tq * p.S > 64 * 2 * kPlanBatch) {
     // many index entries per item: a workgroup per item

@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define NSA_ABI_VERSION 1
+#define NSA_ABI_VERSION 2
 
 typedef enum {
   NSA_SUCCESS = 0,
@@ -105,6 +105,26 @@ nsa_status nsa_fwd_varlen(const nsa_dims* dims, const void* q, const void* k, co
                           void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Fixed-length forward with indices shared by the tokens of a query block
+ * (the `block_indices` parameter description of the same page: indices of
+ * key blocks per query block, [batch, num_kv_heads, num_query_blocks, ...],
+ * and `block_counts`, the number of key blocks per query block).
+ *  block_indices [B, Hkv, NQB, S] int32, NQB = ceil(T / block_size);
+ *  block_counts  [B, Hkv, NQB]    int32.
+ * Query token t uses row t / block_size (query blocks have the key blocks'
+ * size).  Everything else -- entries read, skipped and merged, the causal
+ * rule inside the token's own block, q/k/v/out/lse layouts, errors and the
+ * workspace (nsa_fwd_workspace_size with num_seqs = 0) -- is as for
+ * nsa_fwd, so the result equals nsa_fwd with every token's row copied from
+ * its query block's row.  Packed (varlen) sequences are not supported by
+ * this layout.
+ */
+nsa_status nsa_fwd_qblock(const nsa_dims* dims, const void* q, const void* k, const void* v,
+                          const int32_t* block_indices, const int32_t* block_counts,
+                          int32_t block_size, float scale, void* out, float* lse,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * The two halves of a forward call.  nsa_fwd(...) is exactly
  * nsa_fwd_schedule(...) followed by nsa_fwd_execute(...) on the same stream.
  *
@@ -132,6 +152,16 @@ nsa_status nsa_fwd_schedule(const nsa_dims* dims, const int32_t* block_indices,
                             int32_t num_seqs, int32_t block_size, void* workspace,
                             size_t workspace_bytes, void* stream, size_t* list_offset,
                             int32_t* list_len);
+
+/*
+ * Scheduler half of nsa_fwd_qblock: the indices in the query-block layout
+ * described there, otherwise as nsa_fwd_schedule for fixed length.  The
+ * schedule it writes is run by nsa_fwd_execute with num_seqs = 0.
+ */
+nsa_status nsa_fwd_schedule_qblock(const nsa_dims* dims, const int32_t* block_indices,
+                                   const int32_t* block_counts, int32_t block_size,
+                                   void* workspace, size_t workspace_bytes, void* stream,
+                                   size_t* list_offset, int32_t* list_len);
 
 nsa_status nsa_fwd_execute(const nsa_dims* dims, const void* q, const void* k, const void* v,
                            int32_t num_seqs, int32_t block_size, float scale, void* out,

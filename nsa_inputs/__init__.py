@@ -32,6 +32,12 @@ sparse attention forward (ejKernel ``native_sparse_attention`` API page,
 ``run`` / ``native_sparse_attention``), optional ``cu_seqlens``.  The index
 patterns are the readings written down in the design notes (sink / local /
 random blocks, dense causal, varlen relative blocks).
+
+Query-block workloads (``index_layout == "query_block"``) carry the layout of
+the page's ``block_indices`` parameter description instead: one row per
+query block, ``block_indices [B, Hkv, NQB, S]`` and ``block_counts
+[B, Hkv, NQB]``, drawn with the same patterns, the query block playing the
+part of the token's own block.
 """
 from __future__ import annotations
 
@@ -45,7 +51,7 @@ import numpy as np
 __all__ = [
     "Workload", "make_config", "make_workload", "CONFIG_NAMES",
     "uniform", "normal", "hash_u64", "to_bf16_bits", "bf16_bits_to_f32",
-    "sha256_arrays", "varlen_lengths", "to_torch",
+    "sha256_arrays", "varlen_lengths", "to_torch", "make_qblock_workload",
 ]
 
 _GOLDEN = np.uint64(0x9E3779B97F4A7C15)
@@ -160,13 +166,14 @@ class Workload:
     q: np.ndarray
     k: np.ndarray
     v: np.ndarray
-    block_indices: np.ndarray      # int32 [B, T, Hkv, S]
-    block_counts: np.ndarray       # int32 [B, T, Hkv]
+    block_indices: np.ndarray      # int32 [B, T, Hkv, S]  (query_block: [B, Hkv, NQB, S])
+    block_counts: np.ndarray       # int32 [B, T, Hkv]     (query_block: [B, Hkv, NQB])
     cu_seqlens: np.ndarray | None = None   # int32 [N + 1]
     q_bits: np.ndarray | None = None
     k_bits: np.ndarray | None = None
     v_bits: np.ndarray | None = None
     meta: dict = field(default_factory=dict)
+    index_layout: str = "token"    # "token" or "query_block"
 
     @property
     def G(self) -> int:
@@ -419,4 +426,35 @@ def make_config(i: int, seed: int | None = None) -> Workload:
         lens = varlen_lengths(s)
         return make_workload(CONFIG_NAMES[4], "bf16", lens, 32, 2, 128, 64, 16, "local_random", "uniform", s,
                              varlen=True)
+    if i == 5:
+        return make_qblock_workload(EXTRA_NAMES[5], "bf16", 1, 32768, 64, 4, 128, 64, 16, "sink_local_random",
+                                    "full", s, value_scale=0.5)
     raise ValueError(f"no config {i}")
+
+
+# Workloads beyond the five named ones, by number: the long-context shapes
+# with one index row per query block.
+EXTRA_NAMES = {5: "c3q_bf16_qblock_T32768"}
+
+
+def workload_name(i: int) -> str:
+    return CONFIG_NAMES[i] if i < len(CONFIG_NAMES) else EXTRA_NAMES[i]
+
+
+def make_qblock_workload(name, dtype, B, T, Hq, Hkv, D, block_size, S, pattern, counts_mode, seed,
+                         value_scale=1.0, scale=None) -> Workload:
+    """Seeded fixed-length workload whose indices hold one row per query
+    block: ``block_indices [B, Hkv, NQB, S]``, ``block_counts [B, Hkv, NQB]``,
+    NQB = ceil(T / block_size).  The rows are drawn with the token patterns,
+    query block qb taking the part of the own block."""
+    w = make_workload(name, dtype, [T] * B, Hq, Hkv, D, block_size, 1, "dense", "full", seed,
+                      value_scale=value_scale, scale=scale)
+    nqb = (T + block_size - 1) // block_size
+    # one pseudo-token per query block with block size 1: its own block is qb
+    idx, cnt = _build_rows(pattern, [nqb] * B, Hkv, 1, S, seed, counts_mode)
+    w.block_indices = np.ascontiguousarray(idx.reshape(B, nqb, Hkv, S).transpose(0, 2, 1, 3))
+    w.block_counts = np.ascontiguousarray(cnt.reshape(B, nqb, Hkv).transpose(0, 2, 1))
+    w.S = S
+    w.index_layout = "query_block"
+    w.meta.update({"pattern": pattern, "counts_mode": counts_mode, "index_layout": "query_block"})
+    return w

@@ -6,7 +6,8 @@ with the HIP library (``block_index_sparse_amd``) and does not import it.
 
 ``fwd`` wraps ``nsa_oracle.c`` (plain C, fp64, OpenMP over (token, kv head)):
 it materialises each row's token mask from ``block_indices`` /
-``block_counts`` and runs dense masked softmax attention.  ``brute`` holds a
+``block_counts`` and runs dense masked softmax attention.  ``fwd_qblock``
+takes rows per query block and hands every token its query block's row.  ``brute`` holds a
 pure-Python version for tiny inputs.  The definition and the readings it
 takes are in the header of ``nsa_oracle.c``.
 """
@@ -95,8 +96,41 @@ def fwd(q, k, v, block_indices, block_counts, block_size, scale, cu_seqlens=None
     return out, lse
 
 
+def expand_query_block_rows(block_indices, block_counts, T, block_size):
+    """Per-token rows from rows given per query block.
+
+    The ``block_indices`` parameter of the NSA page ("Parameters" of ``run``)
+    lists key blocks for each query block, ``[batch, num_kv_heads,
+    num_query_blocks, ...]``, and ``block_counts`` counts them per query
+    block.  Query block i holds tokens [i * block_size, (i + 1) *
+    block_size), so token t takes row t // block_size.
+    [B, Hkv, NQB, S] -> [B, T, Hkv, S] and [B, Hkv, NQB] -> [B, T, Hkv].
+    """
+    bi = np.asarray(block_indices)
+    bc = np.asarray(block_counts)
+    assert bi.ndim == 4 and bc.shape == bi.shape[:3]
+    qb = np.arange(T) // int(block_size)
+    assert bi.shape[2] > qb[-1], "fewer query-block rows than query blocks"
+    bi_t = bi[:, :, qb, :].transpose(0, 2, 1, 3)
+    bc_t = bc[:, :, qb].transpose(0, 2, 1)
+    return np.ascontiguousarray(bi_t, dtype=np.int32), np.ascontiguousarray(bc_t, dtype=np.int32)
+
+
+def fwd_qblock(q, k, v, block_indices, block_counts, block_size, scale, tokens=None, threads: int = 0):
+    """Oracle forward with rows per query block (fixed-length sequences):
+    every token uses its query block's row, then the per-token definition."""
+    T = np.asarray(q).shape[1]
+    bi, bc = expand_query_block_rows(block_indices, block_counts, T, block_size)
+    return fwd(q, k, v, bi, bc, block_size, scale, tokens=tokens, threads=threads)
+
+
 def fwd_workload(w, tokens=None, threads: int = 0):
     """Oracle forward on an object carrying q, k, v, block_indices,
-    block_counts, block_size, scale and cu_seqlens attributes."""
+    block_counts, block_size, scale and cu_seqlens attributes (and
+    index_layout, "token" unless it says "query_block")."""
+    if getattr(w, "index_layout", "token") == "query_block":
+        assert w.cu_seqlens is None
+        return fwd_qblock(w.q, w.k, w.v, w.block_indices, w.block_counts, w.block_size, w.scale,
+                          tokens=tokens, threads=threads)
     return fwd(w.q, w.k, w.v, w.block_indices, w.block_counts, w.block_size, w.scale,
                cu_seqlens=w.cu_seqlens, tokens=tokens, threads=threads)

@@ -24,13 +24,19 @@ def visible_keys(block_indices_row, count, S, block_size, t, seqlen):
     return keys
 
 
-def fwd(q, k, v, block_indices, block_counts, block_size, scale, cu_seqlens=None):
+def fwd(q, k, v, block_indices, block_counts, block_size, scale, cu_seqlens=None, query_block_rows=False):
     """Arguments as for ``oracle.fwd`` (nested lists or numpy arrays).
-    Returns (out[B*T][Hq][D], lse[B*T][Hq]) as nested Python lists of floats."""
+    Returns (out[B*T][Hq][D], lse[B*T][Hq]) as nested Python lists of floats.
+
+    query_block_rows: block_indices [B][Hkv][NQB][S] and block_counts
+    [B][Hkv][NQB] hold one row per query block (the page's description of
+    ``block_indices``): the token at position t of sequence b reads row
+    [b][h][t // block_size].  Fixed-length sequences only."""
     B, T, Hq, D = len(q), len(q[0]), len(q[0][0]), len(q[0][0][0])
     Hkv = len(k[0][0])
     S = len(block_indices[0][0][0])
     G = Hq // Hkv
+    assert not (query_block_rows and cu_seqlens is not None)
     # flatten tokens
     def tok(a, x):
         return a[x // T][x % T]
@@ -46,8 +52,12 @@ def fwd(q, k, v, block_indices, block_counts, block_size, scale, cu_seqlens=None
             orow_all, lrow_all = [], []
             for hq in range(Hq):
                 h = hq // G
-                keys = visible_keys(list(tok(block_indices, x)[h]), tok(block_counts, x)[h], S,
-                                    block_size, t, L)
+                if query_block_rows:
+                    b = x // T
+                    row, cnt = list(block_indices[b][h][t // block_size]), block_counts[b][h][t // block_size]
+                else:
+                    row, cnt = list(tok(block_indices, x)[h]), tok(block_counts, x)[h]
+                keys = visible_keys(row, cnt, S, block_size, t, L)
                 qv = [float(a) for a in tok(q, x)[hq]]
                 if not keys:
                     orow_all.append([0.0] * D)

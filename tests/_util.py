@@ -17,6 +17,7 @@ def run_gpu(w, device="cuda", **kw):
     the kernels expired."""
     import block_index_sparse_amd as nsa
     q, k, v, bi, bc, cu = to_device(w, device)
+    kw.setdefault("index_layout", getattr(w, "index_layout", "token"))
     f = nsa.Forward(q, k, v, bi, bc, w.block_size, w.scale, cu_seqlens=cu, **kw)
     out, lse = f.run()
     assert f.device_status() == 0, "a bounded wait inside the kernel expired"

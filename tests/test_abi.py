@@ -21,10 +21,10 @@ def test_library_exports_every_declared_symbol():
     lib = nsa.load_library()
     names = declared_functions()
     assert {"nsa_fwd", "nsa_fwd_varlen", "nsa_fwd_workspace_size", "nsa_status_string",
-            "nsa_abi_version", "nsa_fwd_schedule"} <= set(names)
+            "nsa_abi_version", "nsa_fwd_schedule", "nsa_fwd_qblock", "nsa_fwd_schedule_qblock"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.nsa_abi_version() == 1
+    assert lib.nsa_abi_version() == 2
 
 
 def test_status_strings():
@@ -102,3 +102,40 @@ def test_device_status_rejects_bad_arguments():
     assert lib.nsa_fwd_device_status(ctypes.byref(dims), 64, 0, ws, 16, None, ctypes.byref(st)) == 3
     assert lib.nsa_fwd_device_status(ctypes.byref(D(Dh=96)), 64, 0, ws, 1 << 40, None, ctypes.byref(st)) == 2
     assert st.value == -1
+
+
+def _call_qblock(dims, bs=64, scale=1.0, ptr=256, ws_bytes=1 << 40, nulls=()):
+    lib = nsa.load_library()
+    p = [ctypes.c_void_p(None if i in nulls else ptr) for i in range(8)]
+    return lib.nsa_fwd_qblock(ctypes.byref(dims), p[0], p[1], p[2], p[3], p[4], bs, scale, p[6], None, p[7],
+                              ws_bytes, None)
+
+
+@pytest.mark.parametrize("dims,kw,code", [
+    (D(Hkv=3), {}, 1),
+    (D(T=0), {}, 1),
+    (D(Dh=96), {}, 2),
+    (D(), {"bs": 48}, 2),
+    (D(), {"scale": float("nan")}, 1),
+    (D(), {"nulls": (0,)}, 1),
+    (D(), {"nulls": (3,)}, 1),            # block_indices NULL
+    (D(), {"nulls": (4,)}, 1),            # block_counts NULL
+    (D(), {"ptr": 264}, 1),
+    (D(), {"ws_bytes": 16}, 3),
+])
+def test_qblock_bad_arguments_are_rejected(dims, kw, code):
+    assert _call_qblock(dims, **kw) == code
+
+
+def test_qblock_schedule_rejects_bad_arguments():
+    lib = nsa.load_library()
+    off, n = ctypes.c_size_t(0), ctypes.c_int32(-1)
+    p = ctypes.c_void_p(256)
+    args = lambda dims, bi=p, ws=p, wsb=1 << 40: lib.nsa_fwd_schedule_qblock(
+        ctypes.byref(dims), bi, p, 64, ws, wsb, None, ctypes.byref(off), ctypes.byref(n))
+    assert args(D(), bi=None) == 1
+    assert args(D(), ws=None) == 1
+    assert args(D(), ws=ctypes.c_void_p(264)) == 1
+    assert args(D(), wsb=16) == 3
+    assert args(D(Dh=96)) == 2
+    assert n.value == -1

@@ -23,3 +23,12 @@ def test_visible_key_count_matches_oracle(pattern, counts, varlen, lens):
     G = w.G
     assert np.array_equal(np.repeat(m, G, axis=1), exp)
     assert useful_flops(w) == 4 * w.D * int(exp.sum())
+
+
+def test_visible_key_count_query_block_rows():
+    w = ni.make_qblock_workload("cntq", "f32", 2, 90, 4, 2, 8, 16, 5, "sink_local_random", "uniform", seed=3)
+    w.q[:] = 0
+    _, lse = oracle.fwd_workload(w)
+    m = visible_keys_per_row(w)
+    exp = np.round(np.exp(lse)).astype(np.int64)
+    assert np.array_equal(np.repeat(m, w.G, axis=1), exp)

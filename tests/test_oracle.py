@@ -254,3 +254,60 @@ def test_block_level_causal_example():
         for t in range(i * bs, (i + 1) * bs):
             seen |= {d for d in range(nb) if out[t, 0, d] > 0}
         assert seen == set(range(lo, hi))
+
+
+# --------------------------------------------------------------------------
+# rows per query block (the page's description of block_indices)
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("B,T,Hq,Hkv,D,bs,S,pattern,counts_mode", [
+    (2, 37, 4, 2, 8, 8, 4, "sink_local_random", "uniform"),
+    (1, 40, 4, 1, 8, 4, 6, "local_random", "full"),
+    (2, 24, 2, 2, 4, 8, 3, "shuffled", "uniform"),
+])
+def test_query_block_rows_match_brute_force(B, T, Hq, Hkv, D, bs, S, pattern, counts_mode):
+    """The brute force reads the row [b][h][t // bs] itself; the oracle expands
+    the rows to tokens and runs the per-token definition."""
+    w = ni.make_qblock_workload("qb", "f32", B, T, Hq, Hkv, D, bs, S, pattern, counts_mode, seed=5)
+    assert w.block_indices.shape == (B, Hkv, (T + bs - 1) // bs, S)
+    out, lse = oracle.fwd_workload(w)
+    bout, blse = brute.fwd(w.q, w.k, w.v, w.block_indices, w.block_counts, bs, w.scale,
+                           query_block_rows=True)
+    bout, blse = np.array(bout), np.array(blse)
+    assert np.array_equal(np.isinf(lse), np.isinf(blse))
+    np.testing.assert_allclose(out, bout, rtol=0, atol=1e-12)
+    fin = np.isfinite(blse)
+    np.testing.assert_allclose(lse[fin], blse[fin], rtol=0, atol=1e-12)
+
+
+def test_query_block_rows_hostile_entries():
+    """Negative entries, blocks past the query block or the sequence, repeats
+    and counts outside [0, S], all in query-block rows."""
+    w = ni.make_qblock_workload("qb", "f32", 2, 29, 2, 1, 4, 4, 5, "local_random", "full", seed=9)
+    rng = np.random.default_rng(1)
+    w.block_indices = rng.integers(-3, 10, size=w.block_indices.shape).astype(np.int32)
+    w.block_counts = rng.integers(-2, 8, size=w.block_counts.shape).astype(np.int32)
+    out, lse = oracle.fwd_workload(w)
+    bout, blse = brute.fwd(w.q, w.k, w.v, w.block_indices, w.block_counts, 4, w.scale,
+                           query_block_rows=True)
+    bout, blse = np.array(bout), np.array(blse)
+    assert np.array_equal(np.isinf(lse), np.isinf(blse))
+    np.testing.assert_allclose(out, bout, rtol=0, atol=1e-12)
+    fin = np.isfinite(blse)
+    np.testing.assert_allclose(lse[fin], blse[fin], rtol=0, atol=1e-12)
+    assert (~fin).any() and fin.any()
+
+
+def test_query_block_dense_rows_equal_causal_sdpa():
+    """Every query block listing all blocks up to itself is dense causal
+    attention (the library routine, not the oracle's formula)."""
+    B, T, Hq, Hkv, D, bs = 2, 50, 4, 2, 16, 8
+    nqb = (T + bs - 1) // bs
+    w = ni.make_qblock_workload("qbd", "f32", B, T, Hq, Hkv, D, bs, nqb, "dense", "full", seed=4)
+    assert (w.block_counts == np.arange(1, nqb + 1)[None, None, :]).all()
+    out, _ = oracle.fwd_workload(w)
+    q = torch.from_numpy(w.q).double().permute(0, 2, 1, 3)
+    k = torch.from_numpy(w.k).double().permute(0, 2, 1, 3)
+    v = torch.from_numpy(w.v).double().permute(0, 2, 1, 3)
+    ref = torch.nn.functional.scaled_dot_product_attention(q, k, v, is_causal=True, scale=w.scale,
+                                                           enable_gqa=True)
+    np.testing.assert_allclose(out, ref.permute(0, 2, 1, 3).reshape(B * T, Hq, D).numpy(), rtol=0, atol=1e-12)

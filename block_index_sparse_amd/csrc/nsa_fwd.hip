@@ -9,12 +9,12 @@
 // bf16 kernel: persistent workgroups of 16 waves, one per CU.
 //  * 4 loader waves stream the K and V rows of each item's merged block list
 //    (ascending block order, `kb` keys per unit) into a ring of R LDS slots.
-//    Loader p owns the units v = p (mod 4).  It fetches the K rows of its
-//    next unit into registers while that unit's slot is still being read,
-//    stores them into the slot once every attention wave that reads the
-//    occupant has released it, publishes them, and sends the V rows
-//    straight to LDS with 16-byte buffer loads, publishing them once they
-//    have landed.
+//    Loader p owns the units v = p (mod 4).  It fetches the V rows of its
+//    next unit into registers a unit ahead; once every attention wave that
+//    reads the slot's occupant has released its K rows it sends the new K
+//    rows straight to LDS with 16-byte buffer loads and publishes them when
+//    they have landed, and once the V rows are released too it stores the
+//    staged V rows and publishes them.
 //  * 12 attention waves each own a fixed set of the item's tokens and walk
 //    the same unit sequence without any barrier: a wave waits only for the
 //    unit's data, computes its own tokens that selected the block, releases
@@ -361,12 +361,12 @@ __global__ void __launch_bounds__(64 * (kConsumers + kProducers), 1) fwd_bf16_ri
     int tgt[kOwn];                          // participant releases owed to each own slot
 #pragma unroll
     for (int j = 0; j < kOwn; j++) tgt[j] = 0;
-    // The K rows of the next own unit wait in registers (16 bytes per lane
-    // per 1 KB load), fetched while its slot is still being read; once the
-    // slot is free they are written in with LDS stores, so the consumers can
-    // start on S^T right away, while the V rows travel straight from memory
-    // to LDS behind them.
-    u32x4 kst[C::kLoadsKV];
+    // The V rows of the next own unit wait in registers (16 bytes per lane
+    // per 1 KB load), fetched a whole unit ahead; the K rows go straight
+    // from memory to LDS as soon as the slot's K half is free (its readers
+    // have formed S^T), so their latency overlaps the earlier occupant's
+    // softmax and PV, and the V half, freed last, only waits for the stores.
+    u32x4 vst[C::kLoadsKV];
     // the item holding the next unit to locate: its first stream index, units, kv head
     int it_v0 = 0;
     int it_n = cs.valid ? cs.hd.nunion * nsb : 0;
@@ -395,88 +395,83 @@ __global__ void __launch_bounds__(64 * (kConsumers + kProducers), 1) fwd_bf16_ri
     // (they are masked by causality); the lane offsets stay the four koff /
     // voff values.
     const int64_t kv_bytes = (int64_t)a.Ttot * a.Hkv * (D * 2);
-    auto issue_k = [&](int64_t rb) {
+    auto issue_k = [&](int64_t rb, NSA_LDS char* kdst) {
       [&]<int... LI>(std::integer_sequence<int, LI...>) {
-        ((kst[LI] = __builtin_amdgcn_raw_buffer_load_b128(
-              group_rsrc(K, rb + (int64_t)(LI / 4) * grp_bytes, kv_bytes), (int)koff[LI % 4], 0, 0)),
+        (__builtin_amdgcn_raw_ptr_buffer_load_lds(group_rsrc(K, rb + (int64_t)(LI / 4) * grp_bytes, kv_bytes),
+                                                  (NSA_LDS void*)(kdst + LI * 1024), 16, koff[LI % 4], 0, 0, 0),
          ...);
       }(std::make_integer_sequence<int, C::kLoadsKV>{});
     };
-    auto issue_v = [&](int64_t rb, NSA_LDS char* vdst) {
+    auto issue_v = [&](int64_t rb) {
       [&]<int... LI>(std::integer_sequence<int, LI...>) {
-        (__builtin_amdgcn_raw_ptr_buffer_load_lds(group_rsrc(V, rb + (int64_t)(LI / 4) * grp_bytes, kv_bytes),
-                                                  (NSA_LDS void*)(vdst + LI * 1024), 16, voff[LI % 4], 0, 0, 0),
+        ((vst[LI] = __builtin_amdgcn_raw_buffer_load_b128(
+              group_rsrc(V, rb + (int64_t)(LI / 4) * grp_bytes, kv_bytes), (int)voff[LI % 4], 0, 0)),
          ...);
       }(std::make_integer_sequence<int, C::kLoadsKV>{});
     };
-    // Each pass places own unit v_cur (its K rows already in registers) and
-    // stages the next one; the first pass has no unit to place.
-    int v_cur = p - kProducers;
+    // Bounded wait until the release counter reaches t; false if it expired.
+    auto wait_free = [&](int* ctr, int t) -> bool {
+      int spins = 0;
+      while (loader_poll(ctr) < t) {
+        __builtin_amdgcn_s_sleep(1);
+        if (++spins > kMaxSpin) return false;
+      }
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      return true;
+    };
+    // Each pass places own unit v_cur (its V rows already in registers):
+    // K loads into the slot, the next unit's word, K landed -> publish K,
+    // V half free -> store V -> publish V, then stage the next unit's V rows.
+    int v_cur = p;
     int np = 0;               // participants of v_cur
     int64_t rb = 0;           // byte offset of v_cur's first row
-    bool have = true;
+    bool have = locate(v_cur, np, rb);
+    if (have && np > 0) issue_v(rb);
     bool stuck = false;
     while (have) {
-      const bool real = v_cur >= 0;
-      const int slot = (v_cur + kProducers * R) % R;
-      const int js = ((v_cur + kProducers * R) / kProducers) % kOwn;   // which of this loader's slots
+      const int slot = v_cur % R;
+      const int js = (v_cur / kProducers) % kOwn;   // which of this loader's slots
+      int t = 0;
+#pragma unroll
+      for (int j = 0; j < kOwn; j++) t = (j == js) ? tgt[j] : t;
+      NSA_LDS char* kdst = (NSA_LDS char*)&ring[slot][0];
       if (np > 0) {
-        int t = 0;
-#pragma unroll
-        for (int j = 0; j < kOwn; j++) t = (j == js) ? tgt[j] : t;
-        // With split releases the K rows may be replaced once the readers of
-        // the slot's earlier occupants have formed S^T, and the V rows once
-        // they have read them; otherwise the whole slot waits for the latter.
-        int* const k_free = a.split_release ? &done_k[slot] : &done[slot];
-        int spins = 0;
-        while (loader_poll(k_free) < t) {
-          __builtin_amdgcn_s_sleep(1);
-          if (++spins > kMaxSpin) {
-            stuck = true;
-            break;
-          }
+        // With split releases the K half may be refilled once the readers of
+        // the slot's earlier occupants have formed S^T; otherwise the whole
+        // slot waits for their V reads.
+        if (!wait_free(a.split_release ? &done_k[slot] : &done[slot], t)) {
+          stuck = true;
+          break;
         }
-        if (stuck) break;
-        __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        NSA_LDS char* kdst = (NSA_LDS char*)&ring[slot][0];
-        NSA_LDS char* dst = kdst + lane * 16;
-        [&]<int... LI>(std::integer_sequence<int, LI...>) {
-          ((*(NSA_LDS u32x4*)(dst + LI * 1024) = kst[LI]), ...);
-        }(std::make_integer_sequence<int, C::kLoadsKV>{});
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");   // the K stores have landed
-        loader_bump(&ready_k[slot]);
-        if (a.split_release) {
-          spins = 0;
-          while (loader_poll(&done[slot]) < t) {
-            __builtin_amdgcn_s_sleep(1);
-            if (++spins > kMaxSpin) {
-              stuck = true;
-              break;
-            }
-          }
-          if (stuck) break;
-          __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        }
-        issue_v(rb, kdst + KB * D * 2);
-#pragma unroll
-        for (int j = 0; j < kOwn; j++) tgt[j] += (j == js) ? np : 0;
-      } else if (real) {
-        loader_bump(&ready_k[slot]);   // no attention wave reads this unit: nothing to load
+        issue_k(rb, kdst);
       }
-      // Find the next own unit while this one's V rows are in flight, and
-      // stage its K rows only after publishing them: the V loads are the
-      // ones attention waves are about to wait for, so they should not
-      // queue behind the early K loads in the vector-memory path.
       int np_n = 0;
       int64_t rb_n = 0;
-      have = locate(v_cur + kProducers, np_n, rb_n);
-      const bool staged = have && np_n > 0;
-      if (np > 0) wait_vmcnt<0>();   // the V rows have landed
-      if (real) loader_bump(&ready[slot]);
-      if (staged) issue_k(rb_n);
+      const bool have_n = locate(v_cur + kProducers, np_n, rb_n);
+      if (np > 0) {
+        wait_vmcnt<0>();   // the K rows (and this unit's staged V rows) have landed
+        loader_bump(&ready_k[slot]);
+        if (a.split_release && !wait_free(&done[slot], t)) {
+          stuck = true;
+          break;
+        }
+        NSA_LDS char* dst = kdst + KB * D * 2 + lane * 16;
+        [&]<int... LI>(std::integer_sequence<int, LI...>) {
+          ((*(NSA_LDS u32x4*)(dst + LI * 1024) = vst[LI]), ...);
+        }(std::make_integer_sequence<int, C::kLoadsKV>{});
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");   // the V stores have landed
+        loader_bump(&ready[slot]);
+#pragma unroll
+        for (int j = 0; j < kOwn; j++) tgt[j] += (j == js) ? np : 0;
+      } else {
+        loader_bump(&ready_k[slot]);   // no attention wave reads this unit: nothing to load
+        loader_bump(&ready[slot]);
+      }
+      if (have_n && np_n > 0) issue_v(rb_n);
       v_cur += kProducers;
       np = np_n;
       rb = rb_n;
+      have = have_n;
     }
     if (stuck) atomicOr(a.err, kErrStuck);
     return;

@@ -16,7 +16,9 @@ workload on the host's cores.
 
 --config 0..4 selects the other named workloads (parity cases, not the
 headline); --config 5 is the same long-context shape with one index row per
-query block (nsa_fwd_qblock).
+query block (nsa_fwd_qblock).  --decode measures the decode step
+(nsa_decode: 128 sequences' newest tokens against a bf16 cache of 8192 rows,
+Hq=64, Hkv=4, D=128, bs=64, S=16) against the HBM roofline.
 
 HBM traffic of the attention kernel comes from two rocprofv3 counter runs
 (FETCH_SIZE, then WRITE_SIZE) of this script, each scaled by what the same
@@ -207,6 +209,87 @@ def cpu_baseline(w, seconds_target=12.0, seed=0):
             "seconds": used, "tokens": int(len(rows))}
 
 
+METRIC_DECODE = "sparse-attn decode step: useful HBM GB/s + % of HBM peak, 1 GPU"
+
+
+def decode_visible_keys(w) -> np.ndarray:
+    """|M| for every (sequence, kv head) of a decode workload: keys of the
+    distinct listed blocks 0 <= j <= own, the own block cut at t = len - 1."""
+    S = w.block_indices.shape[-1]
+    t = np.clip(w.seq_lens.astype(np.int64), 0, w.Smax) - 1                  # [B]
+    own = np.where(t >= 0, t // w.block_size, -1)[:, None, None]
+    n = np.clip(w.block_counts, 0, S)[..., None]
+    bi = w.block_indices.astype(np.int64)
+    keep = (np.arange(S)[None, None, :] < n) & (bi >= 0) & (bi <= own)
+    vals = np.sort(np.where(keep, bi, -1), axis=-1)
+    first = np.ones_like(vals, dtype=bool)
+    first[..., 1:] = vals[..., 1:] != vals[..., :-1]
+    distinct = first & (vals >= 0)
+    part = (t - np.maximum(own[:, 0, 0], 0) * w.block_size + 1)[:, None]
+    return ((distinct & (vals < own)).sum(-1) * w.block_size + (distinct & (vals == own)).sum(-1) * part)
+
+
+def decode_algorithmic_bytes(w, m) -> int:
+    """K and V rows of the visible keys once per kv head, q, out, lse, the
+    index rows and the lengths."""
+    return int(int(m.sum()) * w.D * 2 * 2 + 2 * w.B * w.Hq * w.D * 2 + w.B * w.Hq * 4
+               + w.block_indices.nbytes + w.block_counts.nbytes + w.seq_lens.nbytes)
+
+
+def decode_bench(args):
+    import torch
+    import block_index_sparse_amd as nsa
+    import nsa_inputs as ni
+    dev = torch.device("cuda:0")
+    t0 = time.perf_counter()
+    w = ni.make_decode_config()
+    print(f"[bench] {w.name}: generated in {time.perf_counter() - t0:.1f} s", file=sys.stderr, flush=True)
+    q, k, v, sl, bi, bc = ni.decode_to_torch(w, dev)
+    out = torch.empty_like(q)
+    lse = torch.empty((w.B, w.Hq), dtype=torch.float32, device=dev)
+    m = decode_visible_keys(w)
+    flop = int(4 * w.D * w.G * int(m.sum()))
+    nbytes = decode_algorithmic_bytes(w, m)
+
+    call = nsa.Decode(q, k, v, sl, bi, bc, w.block_size, w.scale, out=out, lse=lse).run
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    K = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    torch.cuda.synchronize()
+    for i in range(K):
+        ev[i][0].record()
+        call()
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(b) for a, b in ev]
+    avg = float(np.mean(ms))
+    gbs = nbytes / (avg * 1e-3) / 1e9
+    line = {
+        "metric": METRIC_DECODE, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(avg, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "Smax": w.Smax, "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D,
+                   "block_size": w.block_size, "S": w.S, "useful_flop_per_step": flop,
+                   "useful_tflops": round(flop / (avg * 1e-3) / 1e12, 3), "input_sha256": w.digest()[:16]},
+        "roofline": {"bound": "hbm", "kernel": "decode_bf16_kernel", "achieved": round(gbs, 1),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                     "traffic": read_traffic(w.name), "kernel_ms_avg": round(avg, 4),
+                     "kernel_ms_min": round(float(np.min(ms)), 4), "algorithmic_bytes_per_launch": nbytes},
+    }
+    if not args.no_cpu_baseline:
+        import oracle.decode as odec
+        t1 = time.perf_counter()
+        odec.decode_workload(w)
+        sec = time.perf_counter() - t1
+        line["cpu_baseline"] = {"value": round(nbytes / sec / 1e9, 3), "unit": "GB/s", "cores": 1,
+                                "kind": "oracle", "sample": f"all {w.B} sequences, numpy fp64, {sec:.2f} s",
+                                "seconds": sec}
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -214,6 +297,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--decode", action="store_true", help="measure the decode step instead")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run the copy kernel used to scale the traffic counters")
@@ -234,6 +318,9 @@ def main():
 
     if args.calibrate_copy:
         calibrate_copy()
+        return
+    if args.decode:
+        decode_bench(args)
         return
 
     import torch

@@ -25,7 +25,7 @@ import ctypes
 import math
 import os
 
-__all__ = ["fwd", "Forward", "workspace_size", "schedule", "load_library", "library_path", "NsaError",
+__all__ = ["fwd", "Forward", "decode", "Decode", "workspace_size", "schedule", "load_library", "library_path", "NsaError",
            "DTYPE_F32", "DTYPE_BF16"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -74,6 +74,8 @@ def load_library():
     lib.nsa_fwd_qblock.argtypes = [dp, p, p, p, p, p, i32, f32, p, p, p, sz, p]
     lib.nsa_fwd_schedule_qblock.restype = ctypes.c_int
     lib.nsa_fwd_schedule_qblock.argtypes = [dp, p, p, i32, p, sz, p, ctypes.POINTER(sz), ctypes.POINTER(i32)]
+    lib.nsa_decode.restype = ctypes.c_int
+    lib.nsa_decode.argtypes = [dp, p, p, p, p, p, p, i32, f32, p, p, p]
     lib.nsa_fwd_schedule.restype = ctypes.c_int
     lib.nsa_fwd_schedule.argtypes = [dp, p, p, p, i32, i32, p, sz, p, ctypes.POINTER(sz),
                                      ctypes.POINTER(i32)]
@@ -281,3 +283,64 @@ def schedule(block_indices, block_counts, Hq, D, block_size, dtype="bf16", cu_se
                                   ctypes.byref(off), ctypes.byref(n))
     _check(status)
     return ws[off.value: off.value + 4 * n.value].view(torch.int32).clone()
+
+
+class Decode:
+    """A prepared decode step (``nsa_decode``): the newest token of each
+    sequence, q ``[B, Hq, D]`` bf16, against its cache ``k_cache, v_cache
+    [B, Smax, Hkv, D]`` bf16 holding ``seq_lens [B]`` (int32) keys, with the
+    selected blocks ``block_indices [B, Hkv, S]`` and ``block_counts
+    [B, Hkv]`` (or an int).  Arguments are checked and marshalled once;
+    ``run()`` is one C call on torch's current stream and returns
+    (out [B, Hq, D], lse [B, Hq])."""
+
+    def __init__(self, q, k_cache, v_cache, seq_lens, block_indices, block_counts, block_size: int = 64,
+                 scale: float | None = None, out=None, lse=None, return_lse: bool = True):
+        import torch
+        self.lib = load_library()
+        if q.dim() != 3 or k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
+            raise ValueError("q must be [B, Hq, D] and k_cache, v_cache [B, Smax, Hkv, D]")
+        B, Hq, D = q.shape
+        _, Smax, Hkv, Dk = k_cache.shape
+        if k_cache.shape[0] != B or Dk != D:
+            raise ValueError("cache shape does not match q")
+        if not (q.dtype == k_cache.dtype == v_cache.dtype == torch.bfloat16):
+            raise ValueError("decode takes bf16 q, k_cache, v_cache")
+        if not (q.is_cuda and k_cache.is_cuda and v_cache.is_cuda):
+            raise ValueError("q and the cache must be GPU tensors")
+        if block_indices.dim() != 3 or tuple(block_indices.shape[:2]) != (B, Hkv):
+            raise ValueError("block_indices must be [B, Hkv, S]")
+        S = block_indices.shape[2]
+        dev = q.device
+        self.bi = block_indices.to(device=dev, dtype=torch.int32).contiguous()
+        if isinstance(block_counts, int):
+            self.bc = torch.full((B, Hkv), block_counts, dtype=torch.int32, device=dev)
+        else:
+            if tuple(block_counts.shape) != (B, Hkv):
+                raise ValueError("block_counts must be [B, Hkv] or an int")
+            self.bc = block_counts.to(device=dev, dtype=torch.int32).contiguous()
+        self.sl = seq_lens.to(device=dev, dtype=torch.int32).contiguous()
+        if tuple(self.sl.shape) != (B,):
+            raise ValueError("seq_lens must be [B]")
+        self.q, self.k, self.v = q.contiguous(), k_cache.contiguous(), v_cache.contiguous()
+        self.out = torch.empty_like(self.q) if out is None else out
+        self.lse = lse if lse is not None else (
+            torch.empty((B, Hq), dtype=torch.float32, device=dev) if return_lse else None)
+        self.dims = _dims(B, Smax, Hq, Hkv, D, S, DTYPE_BF16)
+        self.scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+        self.block_size = int(block_size)
+        self.stream = _stream(torch, dev)
+        self._p = [_ptr(getattr(self, n)) for n in ("q", "k", "v", "sl", "bi", "bc", "out", "lse")]
+
+    def run(self):
+        q, k, v, sl, bi, bc, out, lse = self._p
+        _check(self.lib.nsa_decode(ctypes.byref(self.dims), q, k, v, sl, bi, bc, self.block_size, self.scale,
+                                   out, lse, self.stream))
+        return self.out, self.lse
+
+
+def decode(q, k_cache, v_cache, seq_lens, block_indices, block_counts, block_size: int = 64,
+           scale: float | None = None, out=None, lse=None, return_lse: bool = True):
+    """Decode step on the GPU (see ``Decode``).  Returns (out, lse)."""
+    return Decode(q, k_cache, v_cache, seq_lens, block_indices, block_counts, block_size, scale, out, lse,
+                  return_lse).run()

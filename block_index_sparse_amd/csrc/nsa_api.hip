@@ -271,6 +271,50 @@ nsa_status nsa_fwd_device_status(const nsa_dims* dims, int32_t block_size, int32
   return NSA_SUCCESS;
 }
 
+nsa_status nsa_decode(const nsa_dims* d, const void* q, const void* k, const void* v,
+                      const int32_t* seq_lens, const int32_t* block_indices,
+                      const int32_t* block_counts, int32_t block_size, float scale, void* out,
+                      float* lse, void* stream) {
+  if (!d) return NSA_ERROR_INVALID_VALUE;
+  if (d->batch <= 0 || d->seqlen <= 0 || d->num_q_heads <= 0 || d->num_kv_heads <= 0 ||
+      d->head_dim <= 0 || d->num_selected <= 0 || block_size <= 0)
+    return NSA_ERROR_INVALID_VALUE;
+  if (d->num_q_heads % d->num_kv_heads) return NSA_ERROR_INVALID_VALUE;
+  if (d->dtype != NSA_DTYPE_BF16) return NSA_ERROR_NOT_SUPPORTED;
+  if (d->head_dim != 64 && d->head_dim != 128) return NSA_ERROR_NOT_SUPPORTED;
+  if (block_size != 32 && block_size != 64 && block_size != 128) return NSA_ERROR_NOT_SUPPORTED;
+  if (d->num_selected > 64) return NSA_ERROR_NOT_SUPPORTED;
+  nsa::DecodePlan p;
+  p.B = d->batch;
+  p.Smax = d->seqlen;
+  p.Hq = d->num_q_heads;
+  p.Hkv = d->num_kv_heads;
+  p.D = d->head_dim;
+  p.S = d->num_selected;
+  p.bs = block_size;
+  p.G = p.Hq / p.Hkv;
+  if (p.G <= 16) {
+    p.gv = p.G;
+    p.gpk = 1;
+  } else if (p.G % 16 == 0 && p.G <= 1024) {
+    p.gv = 16;
+    p.gpk = p.G / 16;
+  } else {
+    return NSA_ERROR_NOT_SUPPORTED;
+  }
+  const int64_t rows = (int64_t)p.B * p.Smax;
+  if (rows * p.Hkv * p.D > INT64_C(1) << 40 || (int64_t)p.B * p.Hkv * p.gpk > INT32_MAX / 2 ||
+      rows > INT32_MAX / 2)
+    return NSA_ERROR_NOT_SUPPORTED;
+  if (!q || !k || !v || !out || !seq_lens || !block_indices || !block_counts) return NSA_ERROR_INVALID_VALUE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return NSA_ERROR_INVALID_VALUE;
+  if (!std::isfinite(scale)) return NSA_ERROR_INVALID_VALUE;
+  if (nsa::launch_decode(p, q, k, v, seq_lens, block_indices, block_counts, scale, out, lse,
+                         reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
+    return NSA_ERROR_LAUNCH_FAILED;
+  return NSA_SUCCESS;
+}
+
 const char* nsa_status_string(nsa_status status) {
   switch (status) {
     case NSA_SUCCESS: return "NSA_SUCCESS";

@@ -72,11 +72,21 @@ struct Plan {
       off_total, off_worklist, off_err, bytes;
 };
 
+// Decode (one query token per sequence against a KV cache): derived sizes.
+struct DecodePlan {
+  int32_t B, Smax, Hq, Hkv, D, S, bs, G;
+  int32_t gv, gpk;           // heads per group (<= 16), groups per kv head
+};
+
 // Launchers (defined in the .hip files).
 hipError_t launch_schedule(const Plan& p, const int32_t* block_indices, const int32_t* block_counts,
                            const int32_t* cu_seqlens, char* ws, hipStream_t stream);
 hipError_t launch_fwd(const Plan& p, const void* q, const void* k, const void* v, float scale,
                       void* out, float* lse, char* ws, hipStream_t stream);
+hipError_t launch_decode(const DecodePlan& p, const void* q, const void* k, const void* v,
+                         const int32_t* seq_lens, const int32_t* block_indices,
+                         const int32_t* block_counts, float scale, void* out, float* lse,
+                         hipStream_t stream);
 int device_cu_count();
 
 }  // namespace nsa

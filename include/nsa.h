@@ -125,6 +125,33 @@ nsa_status nsa_fwd_qblock(const nsa_dims* dims, const void* q, const void* k, co
                           void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Decode step: one query token per sequence against its KV cache, with the
+ * block selection applied (the NSA page's operation restricted to the
+ * newest token, with the ragged per-sequence key range of the
+ * ragged-decode page's `ragged_decode_mqa_xla`: query [B, Hq, D], cache
+ * [B, S, Hkv, D] and a key range per sequence).
+ *  dims->batch   B sequences; dims->seqlen = Smax, cache rows per sequence;
+ *  dims->dtype   NSA_DTYPE_BF16 only; dims->num_selected = S <= 64.
+ *  q        [B, Hq, D]        bf16, the newest token of each sequence
+ *  k, v     [B, Smax, Hkv, D] bf16 cache; row s of sequence b is key s
+ *  seq_lens [B] int32 DEVICE array: len_b, clamped to [0, Smax]; keys
+ *           0 .. len_b - 1 exist and the query sits at t = len_b - 1
+ *  block_indices [B, Hkv, S] int32 and block_counts [B, Hkv] int32: the
+ *           query's row, read with the rules of nsa_fwd (entries past the
+ *           count, negative or past t's own block t / block_size contribute
+ *           nothing, repeats count once, keys after t are masked)
+ *  out      [B, Hq, D] bf16;  lse [B, Hq] float32 or NULL.
+ * len_b = 0 (or no visible key) gives out = 0 and lse = -inf.  No
+ * workspace.  Argument errors return synchronously as for nsa_fwd;
+ * NSA_ERROR_NOT_SUPPORTED for fp32, S > 64 and the head_dim / block_size /
+ * group limits of nsa_fwd.
+ */
+nsa_status nsa_decode(const nsa_dims* dims, const void* q, const void* k, const void* v,
+                      const int32_t* seq_lens, const int32_t* block_indices,
+                      const int32_t* block_counts, int32_t block_size, float scale, void* out,
+                      float* lse, void* stream);
+
+/*
  * The two halves of a forward call.  nsa_fwd(...) is exactly
  * nsa_fwd_schedule(...) followed by nsa_fwd_execute(...) on the same stream.
  *

@@ -52,6 +52,7 @@ __all__ = [
     "Workload", "make_config", "make_workload", "CONFIG_NAMES",
     "uniform", "normal", "hash_u64", "to_bf16_bits", "bf16_bits_to_f32",
     "sha256_arrays", "varlen_lengths", "to_torch", "make_qblock_workload",
+    "DecodeWorkload", "make_decode_workload", "make_decode_config", "DECODE_NAME",
 ]
 
 _GOLDEN = np.uint64(0x9E3779B97F4A7C15)
@@ -250,8 +251,13 @@ def _rows_for(seqlens, Hkv, block_size):
 def _build_rows(pattern, seqlens, Hkv, block_size, S, seed, counts_mode, chunk_rows=16384):
     """Index rows for every (packed token, kv head).  Returns (idx[R,S], counts[R])."""
     row_ids, pos, seq, own = _rows_for(seqlens, Hkv, block_size)
-    R = len(row_ids)
     nb_max = max(1, max((L + block_size - 1) // block_size for L in seqlens)) if seqlens else 1
+    return _rows_from_own(pattern, row_ids, own, nb_max, S, seed, counts_mode, chunk_rows)
+
+
+def _rows_from_own(pattern, row_ids, own, nb_max, S, seed, counts_mode, chunk_rows=16384):
+    """Index rows given each row's id (its random stream) and own block."""
+    R = len(row_ids)
     idx = np.full((R, S), -1, dtype=np.int32)
     valid = np.zeros(R, dtype=np.int64)
     for s in range(0, R, chunk_rows):
@@ -458,3 +464,104 @@ def make_qblock_workload(name, dtype, B, T, Hq, Hkv, D, block_size, S, pattern, 
     w.index_layout = "query_block"
     w.meta.update({"pattern": pattern, "counts_mode": counts_mode, "index_layout": "query_block"})
     return w
+
+
+# ----------------------------------------------------------------------------
+# decode: one query token per sequence against its KV cache
+# ----------------------------------------------------------------------------
+
+STREAM_DEC_LEN = 8
+
+
+@dataclass
+class DecodeWorkload:
+    """The newest token of each of B sequences against a bf16 KV cache of
+    Smax rows per sequence: q ``[B, Hq, D]``, k/v ``[B, Smax, Hkv, D]``,
+    ``seq_lens [B]`` (the query sits at position len - 1), and the query's
+    selected blocks ``block_indices [B, Hkv, S]``, ``block_counts
+    [B, Hkv]``.  float32 arrays hold the exact bf16 values; ``*_bits`` the
+    bf16 bit patterns."""
+    name: str
+    B: int
+    Smax: int
+    Hq: int
+    Hkv: int
+    D: int
+    block_size: int
+    S: int
+    scale: float
+    q: np.ndarray
+    k: np.ndarray
+    v: np.ndarray
+    seq_lens: np.ndarray
+    block_indices: np.ndarray
+    block_counts: np.ndarray
+    q_bits: np.ndarray
+    k_bits: np.ndarray
+    v_bits: np.ndarray
+    meta: dict = field(default_factory=dict)
+    dtype: str = "bf16"
+
+    @property
+    def G(self) -> int:
+        return self.Hq // self.Hkv
+
+    def digest(self) -> str:
+        return sha256_arrays(self.q_bits, self.k_bits, self.v_bits, self.seq_lens, self.block_indices,
+                             self.block_counts)
+
+
+def make_decode_workload(name, B, Smax, len_lo, len_hi, Hq, Hkv, D, block_size, S, pattern, counts_mode,
+                         seed, value_scale=1.0, scale=None) -> DecodeWorkload:
+    """Seeded decode problem: lengths ~ U[len_lo, len_hi] (inclusive, capped at
+    Smax), normal q/k/v rounded to bf16, and index rows drawn with the token
+    patterns for the query position len - 1."""
+    if Hq % Hkv:
+        raise ValueError("Hq must be a multiple of Hkv")
+    u = uniform(seed, STREAM_DEC_LEN, np.arange(B, dtype=np.uint64))
+    lens = np.minimum(len_lo + np.floor(u * (len_hi - len_lo + 1)).astype(np.int64), Smax).astype(np.int32)
+
+    def gen(stream, shape):
+        x = normal(seed, stream, int(np.prod(shape))).reshape(shape)
+        if value_scale != 1.0:
+            x *= np.float32(value_scale)
+        bits = to_bf16_bits(x)
+        return bf16_bits_to_f32(bits).reshape(shape), bits.reshape(shape)
+
+    q, qb = gen(STREAM_Q, (B, Hq, D))
+    k, kb = gen(STREAM_K, (B, Smax, Hkv, D))
+    v, vb = gen(STREAM_V, (B, Smax, Hkv, D))
+    own = np.repeat(np.maximum(lens.astype(np.int64) - 1, 0) // block_size, Hkv)
+    nb_max = max(1, (Smax + block_size - 1) // block_size)
+    idx, cnt = _rows_from_own(pattern, np.arange(B * Hkv, dtype=np.int64), own, nb_max, S, seed, counts_mode)
+    idx = idx.reshape(B, Hkv, S)
+    cnt = cnt.reshape(B, Hkv)
+    if scale is None:
+        scale = float(np.float32(1.0 / math.sqrt(D)))
+    return DecodeWorkload(name=name, B=B, Smax=Smax, Hq=Hq, Hkv=Hkv, D=D, block_size=block_size, S=S,
+                          scale=float(np.float32(scale)), q=q, k=k, v=v, seq_lens=lens, block_indices=idx,
+                          block_counts=cnt, q_bits=qb, k_bits=kb, v_bits=vb,
+                          meta={"pattern": pattern, "counts_mode": counts_mode, "seed": seed,
+                                "lens": [len_lo, len_hi], "value_scale": value_scale})
+
+
+DECODE_NAME = "d0_bf16_decode_B128_S8192"
+
+
+def make_decode_config(seed: int = 6) -> DecodeWorkload:
+    """Decode workload of the long-context shapes: 128 sequences with
+    lengths ~ U[1024, 8192] in a cache of 8192 rows, Hq=64, Hkv=4, D=128,
+    block_size=64, S=16 (sink, local and random blocks), 0.5 N(0, 1) values."""
+    return make_decode_workload(DECODE_NAME, 128, 8192, 1024, 8192, 64, 4, 128, 64, 16, "sink_local_random",
+                                "full", seed, value_scale=0.5)
+
+
+def decode_to_torch(w: DecodeWorkload, device="cuda"):
+    """Device copies (q, k, v, seq_lens, block_indices, block_counts)."""
+    import torch
+
+    def t(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(device)
+    return (t(w.q_bits), t(w.k_bits), t(w.v_bits), torch.from_numpy(w.seq_lens).to(device),
+            torch.from_numpy(np.ascontiguousarray(w.block_indices)).to(device),
+            torch.from_numpy(np.ascontiguousarray(w.block_counts)).to(device))

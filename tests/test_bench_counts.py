@@ -32,3 +32,16 @@ def test_visible_key_count_query_block_rows():
     m = visible_keys_per_row(w)
     exp = np.round(np.exp(lse)).astype(np.int64)
     assert np.array_equal(np.repeat(m, w.G, axis=1), exp)
+
+
+def test_decode_visible_key_count_matches_oracle():
+    from bench import decode_visible_keys
+    from oracle import decode as odec
+    w = ni.make_decode_workload("dc", 6, 90, 0, 90, 4, 2, 8, 16, 6, "sink_local_random", "uniform", seed=2)
+    w.block_indices[..., -1] = w.block_indices[..., 0]
+    w.q[:] = 0
+    _, lse = odec.decode_workload(w)
+    m = decode_visible_keys(w)
+    got = np.repeat(m, w.G, axis=1)
+    exp = np.where(np.isneginf(lse), 0, np.round(np.exp(np.where(np.isneginf(lse), 0, lse)))).astype(np.int64)
+    assert np.array_equal(got, exp)

@@ -311,3 +311,95 @@ def test_query_block_dense_rows_equal_causal_sdpa():
     ref = torch.nn.functional.scaled_dot_product_attention(q, k, v, is_causal=True, scale=w.scale,
                                                            enable_gqa=True)
     np.testing.assert_allclose(out, ref.permute(0, 2, 1, 3).reshape(B * T, Hq, D).numpy(), rtol=0, atol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# decode step (one query token per sequence against its cache)
+# --------------------------------------------------------------------------
+from oracle import decode as odec   # noqa: E402
+
+
+def _tiny_decode(seed=2, B=4, Smax=40, Hq=4, Hkv=2, D=8, bs=8, S=4, pattern="sink_local_random",
+                 counts="uniform", lens=(1, 40)):
+    w = ni.make_decode_workload("td", B, Smax, lens[0], lens[1], Hq, Hkv, D, bs, S, pattern, counts, seed)
+    for a in ("q", "k", "v"):   # fp32 values for the fp64 comparisons
+        setattr(w, a, getattr(w, a).astype(np.float32))
+    return w
+
+
+def test_decode_matches_per_token_oracle_at_the_last_token():
+    """The decode oracle equals the C per-token oracle evaluated at position
+    len - 1 of each sequence (cache rows as the keys, the decode row as that
+    token's row)."""
+    w = _tiny_decode(B=5, lens=(1, 40))
+    w.seq_lens[0] = 1
+    out, lse = odec.decode_workload(w)
+    for b in range(w.B):
+        L = int(w.seq_lens[b])
+        q = np.zeros((1, L, w.Hq, w.D), np.float32)
+        q[0, L - 1] = w.q[b]
+        bi = np.full((1, L, w.Hkv, w.S), -1, np.int32)
+        bc = np.zeros((1, L, w.Hkv), np.int32)
+        bi[0, L - 1] = w.block_indices[b]
+        bc[0, L - 1] = w.block_counts[b]
+        ro, rl = oracle.fwd(q, w.k[b:b + 1, :L], w.v[b:b + 1, :L], bi, bc, w.block_size, w.scale,
+                            tokens=np.array([L - 1]))
+        np.testing.assert_allclose(out[b], ro[0], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(lse[b], rl[0], rtol=0, atol=1e-12)
+
+
+def test_decode_brute_force_with_hostile_entries():
+    """Python sets and math.fsum; negative, repeated and out-of-range entries,
+    counts outside [0, S], a zero-length sequence."""
+    w = _tiny_decode(seed=4, B=4, Smax=30, Hq=2, Hkv=1, D=4, bs=4, S=6)
+    rng = np.random.default_rng(3)
+    w.block_indices = rng.integers(-2, 9, size=w.block_indices.shape).astype(np.int32)
+    w.block_counts = rng.integers(-1, 8, size=w.block_counts.shape).astype(np.int32)
+    w.seq_lens[1] = 0
+    out, lse = odec.decode_workload(w)
+    for b in range(w.B):
+        L = int(w.seq_lens[b])
+        keys = brute.visible_keys(list(w.block_indices[b, 0]), w.block_counts[b, 0], w.S, w.block_size,
+                                  L - 1, L) if L > 0 else set()
+        for hq in range(w.Hq):
+            if not keys:
+                assert lse[b, hq] == -math.inf and np.all(out[b, hq] == 0)
+                continue
+            z = {s: w.scale * math.fsum(float(w.q[b, hq, d]) * float(w.k[b, s, 0, d]) for d in range(w.D))
+                 for s in keys}
+            m = max(z.values())
+            l = m + math.log(math.fsum(math.exp(x - m) for x in z.values()))
+            assert abs(lse[b, hq] - l) < 1e-12
+            for d in range(w.D):
+                o = math.fsum(math.exp(z[s] - l) * float(w.v[b, s, 0, d]) for s in keys)
+                assert abs(out[b, hq, d] - o) < 1e-12
+    assert np.isneginf(lse).any() and np.isfinite(lse).any()
+
+
+def test_decode_dense_selection_equals_sdpa():
+    """All blocks up to the query's own: plain attention of the query over
+    keys 0 .. len - 1 (library routine)."""
+    w = _tiny_decode(seed=6, B=3, Smax=45, Hq=4, Hkv=2, D=16, bs=8, S=6, pattern="dense", counts="full",
+                     lens=(20, 45))
+    out, _ = odec.decode_workload(w)
+    for b in range(w.B):
+        L = int(w.seq_lens[b])
+        q = torch.from_numpy(w.q[b]).double()[:, None, None, :]                    # [Hq, 1, 1, D]
+        k = torch.from_numpy(w.k[b, :L]).double().permute(1, 0, 2).repeat_interleave(w.G, 0)[:, None]
+        v = torch.from_numpy(w.v[b, :L]).double().permute(1, 0, 2).repeat_interleave(w.G, 0)[:, None]
+        ref = torch.nn.functional.scaled_dot_product_attention(q, k, v, scale=w.scale)[:, 0, 0]
+        np.testing.assert_allclose(out[b], ref.numpy(), rtol=0, atol=1e-12)
+
+
+def test_decode_zero_query_counts_and_mean():
+    w = _tiny_decode(seed=8, B=4, Smax=50, lens=(5, 50))
+    w.q[:] = 0
+    out, lse = odec.decode_workload(w)
+    for b in range(w.B):
+        L = int(w.seq_lens[b])
+        for h in range(w.Hkv):
+            m = odec.key_mask(w.block_indices[b, h], w.block_counts[b, h], w.S, w.block_size, L)
+            n = int(m.sum())
+            for hq in range(h * w.G, (h + 1) * w.G):
+                assert abs(lse[b, hq] - math.log(n)) < 1e-12
+                np.testing.assert_allclose(out[b, hq], w.v[b, :L, h][m].astype(np.float64).mean(0), atol=1e-12)

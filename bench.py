@@ -307,8 +307,11 @@ def main():
     args = ap.parse_args()
     if args.traffic_summary:
         import nsa_inputs as ni
-        name = ni.workload_name(args.config)
-        kern = "fwd_f32_kernel" if args.config == 0 else "fwd_bf16_ring_kernel"
+        if args.decode:
+            name, kern = ni.DECODE_NAME, "decode_bf16_kernel"
+        else:
+            name = ni.workload_name(args.config)
+            kern = "fwd_f32_kernel" if args.config == 0 else "fwd_bf16_ring_kernel"
         traffic_summary(name, *args.traffic_summary, kernel=kern)
         return
     if args.gpus != 1:

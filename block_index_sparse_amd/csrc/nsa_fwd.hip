@@ -912,8 +912,10 @@ __global__ void __launch_bounds__(256, 2) fwd_f32_kernel(FwdArgs a) {
 // past the count, negative or beyond t's own block contribute nothing, a
 // repeated block counts once, keys after t inside the own block are masked).
 // One workgroup of kDecWaves waves per (sequence, kv head, group of <= 16
-// query heads).  The kept blocks' units (KB keys each) are dealt round robin
-// to the waves, and every wave works alone on its units:
+// query heads); two workgroups share a CU, so one's index loads overlap the
+// other's K/V traffic.  The kept blocks' units (KB = 32 keys, so that a
+// unit's K and V registers and the next unit's fit two waves per SIMD) are
+// dealt round robin to the waves, and every wave works alone on its units:
 //  * K rows are loaded straight into registers in the MFMA A-operand layout
 //    (lane (c, g): key row c of a 16-key tile, 16 bytes at d = 32 kk + 8 g);
 //  * V rows are loaded into registers row by row, written to the wave's own
@@ -927,7 +929,7 @@ __global__ void __launch_bounds__(256, 2) fwd_f32_kernel(FwdArgs a) {
 // are merged through LDS at the end, as the flash-attention carry is merged
 // on the ragged-decode page.
 // ---------------------------------------------------------------------------
-constexpr int kDecWaves = 8;
+constexpr int kDecWaves = 4;   // two workgroups per CU (two waves per SIMD), all resident at once
 
 struct DecArgs {
   const void* q;          // [B, Hq, D]
@@ -943,7 +945,8 @@ struct DecArgs {
 };
 
 template <int D, int KB>
-__global__ void __launch_bounds__(64 * kDecWaves) decode_bf16_kernel(DecArgs a) {
+__global__ void __launch_bounds__(64 * kDecWaves) __attribute__((amdgpu_waves_per_eu(2)))
+decode_bf16_kernel(DecArgs a) {
   constexpr int KT = D / 32;   // k-steps of S^T = K Q^T
   constexpr int MT = KB / 16;  // 16-key row tiles
   constexpr int KQ = KB / 32;  // 32-key k-steps of O^T += V^T P^T
@@ -977,10 +980,12 @@ __global__ void __launch_bounds__(64 * kDecWaves) decode_bf16_kernel(DecArgs a) 
   // kept entries of the row: lane i holds entry i (S <= 64); an entry is
   // dropped if an earlier valid entry lists the same block
   const int64_t row = (int64_t)b * a.Hkv + h;
+  // the count and the row are loaded independently (the row lies inside the
+  // tensor whatever the count), so the two loads overlap
   int n = a.bc[row];
+  const int idx = lane < a.S ? a.bi[row * a.S + lane] : -1;
   n = n < 0 ? 0 : (n > a.S ? a.S : n);
   n = __builtin_amdgcn_readfirstlane(n);
-  const int idx = lane < n ? a.bi[row * a.S + lane] : -1;
   bool keep = lane < n && idx >= 0 && idx <= own;
   const uint64_t valid = __ballot(keep);
   for (int j = 0; j < n; j++) {
@@ -1072,7 +1077,7 @@ __global__ void __launch_bounds__(64 * kDecWaves) decode_bf16_kernel(DecArgs a) 
   // issued inside the step.  The last unit is peeled off the loop so that
   // every pass of the loop issues the same loads in the same order (V, then
   // K), which lets the compiler wait for exactly the loads each use needs.
-  auto step = [&]<bool kMore>(int i) {
+  auto step = [&]<bool kMore>(int i) __attribute__((always_inline)) {
     const int ks = __builtin_amdgcn_readlane(my_ks, i);
     const int64_t rb_n = kMore ? unit_base(__builtin_amdgcn_readlane(my_ks, i + 1)) : 0;
     // V rows into the wave's slot (its previous contents were read by the
@@ -1211,8 +1216,9 @@ __global__ void __launch_bounds__(64 * kDecWaves) decode_bf16_kernel(DecArgs a) 
 typedef void (*DecFn)(DecArgs);
 
 DecFn pick_decode(int D, int KB) {
-  if (D == 64) return KB == 32 ? decode_bf16_kernel<64, 32> : decode_bf16_kernel<64, 64>;
-  if (D == 128) return KB == 32 ? decode_bf16_kernel<128, 32> : decode_bf16_kernel<128, 64>;
+  if (KB != 32) return nullptr;
+  if (D == 64) return decode_bf16_kernel<64, 32>;
+  if (D == 128) return decode_bf16_kernel<128, 32>;
   return nullptr;
 }
 
@@ -1315,7 +1321,9 @@ hipError_t launch_decode(const DecodePlan& p, const void* q, const void* k, cons
   a.gv = p.gv;
   a.gpk = p.gpk;
   a.scale_log2 = scale * 1.4426950408889634f;
-  DecFn fn = pick_decode(p.D, p.bs < 64 ? p.bs : 64);
+  // 32-key units: a 64-key unit's K and V registers plus the next unit's
+  // would not fit the 256 VGPRs of two waves per SIMD
+  DecFn fn = pick_decode(p.D, 32);
   if (!fn) return hipErrorInvalidValue;
   hipLaunchKernelGGL(fn, dim3(p.B * p.Hkv * p.gpk), dim3(64 * kDecWaves), 0, stream, a);
   return hipGetLastError();

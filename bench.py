@@ -54,23 +54,34 @@ CSRC = os.path.join(ROOT, "block_index_sparse_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
 
 
-def kernel_source_digest() -> str:
-    """sha256 over the sources that decide what the attention kernel does: the
-    kernel, its shared header and the host code that sizes its tiles."""
+KERNEL_SOURCES = {
+    # the forward kernel, the helpers it includes and the host code that sizes its tiles
+    "fwd": ("nsa_fwd.hip", "nsa_device.h", "nsa_internal.h", "nsa_api.hip"),
+    "decode": ("nsa_decode.hip", "nsa_device.h", "nsa_internal.h"),
+}
+
+
+def kernel_source_digest(kind: str = "fwd") -> str:
+    """sha256 over the sources that decide what a kernel does (comments and
+    layout stripped: they do not change the kernel)."""
     h = hashlib.sha256()
-    for f in ("nsa_fwd.hip", "nsa_internal.h", "nsa_api.hip"):
+    for f in KERNEL_SOURCES[kind]:
         h.update(f.encode())
         with open(os.path.join(CSRC, f)) as fh:
             text = fh.read()
-        # comments and layout do not change the kernel
         text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
         text = re.sub(r"//[^\n]*", "", text)
         h.update(" ".join(text.split()).encode())
     return h.hexdigest()
 
 
+def _kind(workload: str) -> str:
+    return "decode" if workload.startswith("d") else "fwd"
+
+
 def traffic_path(workload: str) -> str:
-    return os.path.join(PROFILES, f"nsa_fwd_traffic_{workload}.json")
+    prefix = "nsa_decode_traffic" if _kind(workload) == "decode" else "nsa_fwd_traffic"
+    return os.path.join(PROFILES, f"{prefix}_{workload}.json")
 
 
 def read_traffic(workload: str):
@@ -81,7 +92,7 @@ def read_traffic(workload: str):
         return None
     with open(p) as fh:
         t = json.load(fh)
-    if t.get("kernel_source_sha256") != kernel_source_digest():
+    if t.get("kernel_source_sha256") != kernel_source_digest(_kind(workload)):
         return None
     return t["traffic_bytes_per_launch"]
 
@@ -108,7 +119,8 @@ def _mean_for(rows, needle: str, skip: str = "\0") -> tuple:
 
 def traffic_summary(workload: str, fetch_dir: str, write_dir: str, copy_fetch_dir: str,
                     copy_write_dir: str, kernel: str):
-    """Write profiles/nsa_fwd_traffic_<workload>.json from four --pmc runs."""
+    """Write the traffic summary of a workload (profiles/nsa_fwd_traffic_<workload>.json,
+    or nsa_decode_traffic_<workload>.json for the decode step) from four --pmc runs."""
     copy_kib = COPY_BYTES / 1024.0
     cf, _ = _mean_for(_pmc_rows(copy_fetch_dir, "FETCH_SIZE"), "elementwise", skip="Fill")
     cw, _ = _mean_for(_pmc_rows(copy_write_dir, "WRITE_SIZE"), "elementwise", skip="Fill")
@@ -117,7 +129,7 @@ def traffic_summary(workload: str, fetch_dir: str, write_dir: str, copy_fetch_di
     ff, fw = copy_kib / cf, copy_kib / cw
     res = {
         "workload": workload, "kernel": kernel,
-        "kernel_source_sha256": kernel_source_digest(),
+        "kernel_source_sha256": kernel_source_digest(_kind(workload)),
         "fetch_kib_per_launch_raw": kf, "write_kib_per_launch_raw": kw, "launches": [nf, nw],
         "copy_bytes": COPY_BYTES, "copy_fetch_kib_raw": cf, "copy_write_kib_raw": cw,
         "fetch_scale": ff, "write_scale": fw,

@@ -142,6 +142,58 @@ def traffic_summary(workload: str, fetch_dir: str, write_dir: str, copy_fetch_di
     print(json.dumps(res))
 
 
+def counters_path(workload: str) -> str:
+    prefix = "nsa_decode_counters" if _kind(workload) == "decode" else "nsa_fwd_counters"
+    return os.path.join(PROFILES, f"{prefix}_{workload}.json")
+
+
+def counters_summary(workload: str, sq_dir: str, ta_dir: str, kernel: str, n_cus: int = 256,
+                     n_xcds: int = 8, simds_per_cu: int = 4):
+    """Unit utilisations of a kernel from two rocprofv3 --pmc runs (SQ block:
+    SQ_VALU_MFMA_BUSY_CYCLES, SQ_LDS_IDX_ACTIVE, GRBM_GUI_ACTIVE, ...; TA
+    block: TA_TA_BUSY, GRBM_GUI_ACTIVE), written next to the traffic record.
+    GRBM_GUI_ACTIVE sums the cycles of the 8 XCDs; busy counters sum over
+    CUs (SIMDs for the MFMA pipe)."""
+    def means(d):
+        f = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+        if not f:
+            raise SystemExit(f"no counter_collection.csv under {d}")
+        acc = {}
+        for r in csv.DictReader(open(f[0])):
+            if kernel in r["Kernel_Name"]:
+                acc.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+        return {k: float(np.mean(v)) for k, v in acc.items()}
+    sq, ta = means(sq_dir), means(ta_dir)
+    cyc_sq = sq["GRBM_GUI_ACTIVE"] / n_xcds
+    cyc_ta = ta["GRBM_GUI_ACTIVE"] / n_xcds
+    res = {
+        "workload": workload, "kernel": kernel, "kernel_source_sha256": kernel_source_digest(_kind(workload)),
+        "gpu_cycles": cyc_sq,
+        "mfma_busy_frac": sq["SQ_VALU_MFMA_BUSY_CYCLES"] / (n_cus * simds_per_cu) / cyc_sq,
+        "lds_active_frac": sq["SQ_LDS_IDX_ACTIVE"] / n_cus / cyc_sq,
+        "lds_bank_conflicts": sq.get("SQ_LDS_BANK_CONFLICT"),
+        "vmem_path_busy_frac": ta["TA_TA_BUSY"] / n_cus / cyc_ta,
+        "raw": {"sq": sq, "ta": ta},
+    }
+    with open(counters_path(workload), "w") as fh:
+        json.dump(res, fh, indent=1)
+        fh.write("\n")
+    print(json.dumps(res))
+
+
+def read_counters(workload: str):
+    """Unit utilisations from the committed counter record, or None when
+    there is none or the kernel sources changed since it was taken."""
+    p = counters_path(workload)
+    if not os.path.exists(p):
+        return None
+    with open(p) as fh:
+        t = json.load(fh)
+    if t.get("kernel_source_sha256") != kernel_source_digest(_kind(workload)):
+        return None
+    return {k: round(t[k], 4) for k in ("mfma_busy_frac", "lds_active_frac", "vmem_path_busy_frac")}
+
+
 def calibrate_copy():
     """A plain elementwise copy of COPY_BYTES (x * 1 into a second buffer)."""
     import torch
@@ -288,7 +340,8 @@ def decode_bench(args):
                    "useful_tflops": round(flop / (avg * 1e-3) / 1e12, 3), "input_sha256": w.digest()[:16]},
         "roofline": {"bound": "hbm", "kernel": "decode_bf16_kernel", "achieved": round(gbs, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
-                     "traffic": read_traffic(w.name), "kernel_ms_avg": round(avg, 4),
+                     "traffic": read_traffic(w.name), "counters": read_counters(w.name),
+                     "kernel_ms_avg": round(avg, 4),
                      "kernel_ms_min": round(float(np.min(ms)), 4), "algorithmic_bytes_per_launch": nbytes},
     }
     if not args.no_cpu_baseline:
@@ -316,7 +369,18 @@ def main():
     ap.add_argument("--traffic-summary", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR",
                                                            "COPY_WRITE_DIR"),
                     help="write the traffic summary of --config from four rocprofv3 --pmc runs")
+    ap.add_argument("--counters-summary", nargs=2, metavar=("SQ_DIR", "TA_DIR"),
+                    help="write the unit-utilisation summary of --config (or --decode) from two --pmc runs")
     args = ap.parse_args()
+    if args.counters_summary:
+        import nsa_inputs as ni
+        if args.decode:
+            name, kern = ni.DECODE_NAME, "decode_bf16_kernel"
+        else:
+            name = ni.workload_name(args.config)
+            kern = "fwd_f32_kernel" if args.config == 0 else "fwd_bf16_ring_kernel"
+        counters_summary(name, *args.counters_summary, kernel=kern)
+        return
     if args.traffic_summary:
         import nsa_inputs as ni
         if args.decode:
@@ -412,6 +476,7 @@ def main():
             "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4),
             "traffic": read_traffic(w.name),
+            "counters": read_counters(w.name),
             "kernel_ms_avg": round(kern_avg, 4),
             "kernel_ms_min": round(float(np.min(kern_ms)), 4),
             "algorithmic_flop_per_launch": flop,

@@ -99,3 +99,26 @@ def test_named_workload_full_size(cfg):
     assert bool(o.isfinite().all())
     vmax = float(np.abs(w.v).max())
     assert float(o.abs().max()) <= vmax * (1 + 1e-2) + 1e-2
+
+
+def test_maximum_row_length_dense_rows():
+    """The longest rows the header allows: S = 1024 entries per row, every
+    causal block listed (bs = 32, T = 32763, not a multiple of the block),
+    so items plan 12 x 1024 index entries on a workgroup each and merge
+    1024-entry lists.  Sampled rows against the oracle; the q = 0 count
+    probe gives exp(lse) = t + 1 exactly on every row."""
+    import torch
+    _say("[parity] maximum row length: generating")
+    w = ni.make_workload("max_rows", "bf16", [32763], 16, 1, 64, 32, 1024, "dense", "full", seed=41)
+    assert int(w.block_counts.max()) == 1024
+    out, lse = run_gpu(w)
+    rows = sample_rows(w, 48, seed=41)
+    ref_o, ref_l = oracle.fwd_workload(w, tokens=rows)
+    stats = compare(w, out, lse, ref_o, ref_l, rows=rows, what="max_rows")
+    _say(f"[parity] maximum row length: {stats}")
+    w.q[:] = 0
+    w.q_bits[:] = 0
+    _, lse0 = run_gpu(w)
+    cnt = torch.exp(lse0.double().reshape(-1, w.Hq)).cpu().numpy()
+    want = np.arange(1, w.T + 1, dtype=np.float64)[:, None]
+    assert np.array_equal(np.round(cnt), np.broadcast_to(want, cnt.shape))

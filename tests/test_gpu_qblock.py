@@ -93,3 +93,17 @@ def test_qblock_long_context_sampled_rows():
     assert np.all(np.abs(cnt - np.round(cnt)) < 1e-3 * np.maximum(cnt, 1))
     _, ref_l0 = oracle.fwd_workload(w, tokens=rows)
     assert np.array_equal(np.round(cnt[rows]).astype(np.int64), np.round(np.exp(ref_l0)).astype(np.int64))
+
+
+def test_qblock_hostile_entries():
+    """Negative entries, blocks past the query block or the sequence, repeats
+    and counts outside [0, S], in query-block rows."""
+    _say("[qblock] hostile entries")
+    w = ni.make_qblock_workload("qb_hostile", "bf16", 2, 330, 32, 2, 128, 64, 7, "local_random", "full", seed=3)
+    rng = np.random.default_rng(4)
+    w.block_indices = rng.integers(-3, 9, size=w.block_indices.shape).astype(np.int32)
+    w.block_counts = rng.integers(-2, 10, size=w.block_counts.shape).astype(np.int32)
+    out, lse = run_gpu(w)
+    ref_o, ref_l = oracle.fwd_workload(w)
+    compare(w, out, lse, ref_o, ref_l, what="qb_hostile")
+    assert np.isneginf(ref_l).any()

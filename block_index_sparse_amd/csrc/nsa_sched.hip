@@ -197,6 +197,13 @@ __global__ void __launch_bounds__(256) plan_kernel(PlanArgs a) {
   // Entry e = tau * S + i of the item (token tau, list position i) is kept
   // iff i < clamp(count, 0, S) and 0 <= idx <= tau's own block; the loads of
   // kPlanBatch entries per lane are issued before any of them is used.
+  // When the item's entries fit one batch per thread (every item of up to
+  // 8 x nthr entries), the first batch stays in registers for the token-set
+  // pass below instead of being loaded again.
+  const bool one_batch = nent <= nthr * kPlanBatch;
+  int32_t keep0[kPlanBatch];
+#pragma unroll
+  for (int u = 0; u < kPlanBatch; u++) keep0[u] = -1;
   for (int32_t e0 = tid; e0 < nent; e0 += nthr * kPlanBatch) {
     int32_t keep[kPlanBatch];
 #pragma unroll
@@ -204,6 +211,10 @@ __global__ void __launch_bounds__(256) plan_kernel(PlanArgs a) {
 #pragma unroll
     for (int u = 0; u < kPlanBatch; u++)
       if (keep[u] >= 0) atomicOr(&bitmap[keep[u] >> 5], 1u << (keep[u] & 31));
+    if (e0 == tid) {
+#pragma unroll
+      for (int u = 0; u < kPlanBatch; u++) keep0[u] = keep[u];
+    }
   }
   item_sync();
   // merged-list position of the first block of every bitmap word: each lane
@@ -233,7 +244,8 @@ __global__ void __launch_bounds__(256) plan_kernel(PlanArgs a) {
   for (int32_t e0 = tid; e0 < nent; e0 += nthr * kPlanBatch) {
     int32_t keep[kPlanBatch];
 #pragma unroll
-    for (int u = 0; u < kPlanBatch; u++) keep[u] = entry_block(a, e0 + nthr * u, nent, tok0, pos0, h);
+    for (int u = 0; u < kPlanBatch; u++)
+      keep[u] = one_batch ? keep0[u] : entry_block(a, e0 + nthr * u, nent, tok0, pos0, h);
 #pragma unroll
     for (int u = 0; u < kPlanBatch; u++) {
       if (keep[u] >= 0) {

@@ -1,0 +1,66 @@
+"""CPU fp64 oracle of the gradients of the native sparse attention forward.
+
+TEST INFRASTRUCTURE ONLY (not imported by the product path; no GPU
+counterpart exists yet).  The pages define the forward only (ejKernel
+``native_sparse_attention`` API page, module description and
+"Parameters"); its gradients are those of that function.  With the token
+mask of row (t, h) materialised from the indices exactly as the forward
+oracle does, and for each query head hq of the group:
+
+    P_s   = exp(scale * q.k_s - lse)              over the visible keys s
+    O     = sum_s P_s v_s
+    dV_s += P_s dO                                 (every (t, hq) that sees s)
+    dP_s  = dO . v_s
+    Delta = sum_s P_s dP_s  (= dO . O)
+    dS_s  = P_s (dP_s - Delta)
+    dQ    = scale * sum_s dS_s k_s
+    dK_s += scale * dS_s q
+
+(the chain rule through softmax; rows with no visible key contribute
+nothing).  Plain numpy, one row at a time: for small inputs.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def _visible(row, count, S, block_size, t):
+    n = max(0, min(int(count), S))
+    listed = {int(e) for e in np.asarray(row)[:n] if 0 <= int(e) <= t // block_size}
+    return np.array([s for s in range(t + 1) if s // block_size in listed], dtype=np.int64)
+
+
+def bwd(q, k, v, dout, block_indices, block_counts, block_size, scale):
+    """Fixed-length sequences.  q, dout [B, T, Hq, D]; k, v [B, T, Hkv, D];
+    block_indices [B, T, Hkv, S]; block_counts [B, T, Hkv].  Returns
+    (dq, dk, dv) in float64 with the shapes of q, k, v."""
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    dout = np.asarray(dout, np.float64)
+    B, T, Hq, D = q.shape
+    Hkv = k.shape[2]
+    S = block_indices.shape[-1]
+    G = Hq // Hkv
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for b in range(B):
+        for t in range(T):
+            for h in range(Hkv):
+                keys = _visible(block_indices[b, t, h], block_counts[b, t, h], S, block_size, t)
+                if len(keys) == 0:
+                    continue
+                K = k[b, keys, h]            # [n, D]
+                V = v[b, keys, h]
+                for hq in range(h * G, (h + 1) * G):
+                    z = scale * (K @ q[b, t, hq])
+                    p = np.exp(z - z.max())
+                    p /= p.sum()
+                    do = dout[b, t, hq]
+                    dv[b, keys, h] += p[:, None] * do[None, :]
+                    dp = V @ do
+                    ds = p * (dp - p @ dp)
+                    dq[b, t, hq] += scale * (ds @ K)
+                    dk[b, keys, h] += scale * ds[:, None] * q[b, t, hq][None, :]
+    return dq, dk, dv

@@ -403,3 +403,68 @@ def test_decode_zero_query_counts_and_mean():
             for hq in range(h * w.G, (h + 1) * w.G):
                 assert abs(lse[b, hq] - math.log(n)) < 1e-12
                 np.testing.assert_allclose(out[b, hq], w.v[b, :L, h][m].astype(np.float64).mean(0), atol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# gradients (groundwork of the backward pass; CPU only)
+# --------------------------------------------------------------------------
+from oracle import backward as obwd   # noqa: E402
+
+
+def _loss(w, q, k, v, dout):
+    out, _ = oracle.fwd(q, k, v, w.block_indices, w.block_counts, w.block_size, w.scale)
+    return float(np.sum(out.reshape(dout.shape) * dout))
+
+
+def test_gradients_match_central_differences_of_the_forward():
+    """Directional derivatives of L = <dO, out> through the (pinned) forward
+    oracle, along random directions in q, k and v, against the gradients."""
+    w = ni.make_workload("g", "f32", [24, 24], 4, 2, 8, 4, 4, "sink_local_random", "uniform", seed=12)
+    rng = np.random.default_rng(0)
+    dout = rng.standard_normal(w.q.shape)
+    dq, dk, dv = obwd.bwd(w.q, w.k, w.v, dout, w.block_indices, w.block_counts, w.block_size, w.scale)
+    eps = 1e-3
+    for name, grad in (("q", dq), ("k", dk), ("v", dv)):
+        for trial in range(2):
+            u = rng.standard_normal(grad.shape)
+            x = getattr(w, name).astype(np.float64)
+            args = {"q": w.q.astype(np.float64), "k": w.k.astype(np.float64), "v": w.v.astype(np.float64)}
+            args[name] = x + eps * u
+            lp = _loss(w, args["q"].astype(np.float32), args["k"].astype(np.float32), args["v"].astype(np.float32), dout)
+            args[name] = x - eps * u
+            lm = _loss(w, args["q"].astype(np.float32), args["k"].astype(np.float32), args["v"].astype(np.float32), dout)
+            fd = (lp - lm) / (2 * eps)
+            an = float(np.sum(grad * u))
+            # the forward takes float32 inputs: the step's rounding sets the tolerance
+            assert abs(fd - an) <= 2e-3 * max(1.0, abs(an)), (name, fd, an)
+
+
+def test_gradients_dense_rows_equal_autograd_sdpa():
+    """Dense causal rows: the library's autograd through SDPA in fp64."""
+    T, Hq, Hkv, D, bs = 20, 4, 2, 8, 4
+    nb = (T + bs - 1) // bs
+    w = ni.make_workload("gd", "f32", [T], Hq, Hkv, D, bs, nb, "dense", "full", seed=13)
+    rng = np.random.default_rng(1)
+    dout = rng.standard_normal(w.q.shape)
+    dq, dk, dv = obwd.bwd(w.q, w.k, w.v, dout, w.block_indices, w.block_counts, w.block_size, w.scale)
+    q = torch.from_numpy(w.q).double().permute(0, 2, 1, 3).requires_grad_()
+    k = torch.from_numpy(w.k).double().permute(0, 2, 1, 3).requires_grad_()
+    v = torch.from_numpy(w.v).double().permute(0, 2, 1, 3).requires_grad_()
+    o = torch.nn.functional.scaled_dot_product_attention(q, k, v, is_causal=True, scale=w.scale, enable_gqa=True)
+    o.backward(torch.from_numpy(dout).permute(0, 2, 1, 3))
+    np.testing.assert_allclose(dq, q.grad.permute(0, 2, 1, 3).numpy(), rtol=0, atol=1e-11)
+    np.testing.assert_allclose(dk, k.grad.permute(0, 2, 1, 3).numpy(), rtol=0, atol=1e-11)
+    np.testing.assert_allclose(dv, v.grad.permute(0, 2, 1, 3).numpy(), rtol=0, atol=1e-11)
+
+
+def test_gradients_of_empty_rows_and_unlisted_keys_vanish():
+    w = ni.make_workload("ge", "f32", [16], 2, 1, 4, 4, 3, "local_random", "full", seed=14)
+    w.block_counts[0, :8] = 0                      # tokens 0..7 see nothing
+    w.block_indices[0, 8:, 0, :] = [1, 3, -1]      # tokens 8.. see blocks 1 and 3 only
+    w.block_counts[0, 8:] = 3
+    dout = np.ones(w.q.shape)
+    dq, dk, dv = obwd.bwd(w.q, w.k, w.v, dout, w.block_indices, w.block_counts, w.block_size, w.scale)
+    assert np.all(dq[0, :8] == 0)
+    assert np.all(dk[0, 0:4] == 0) and np.all(dv[0, 0:4] == 0)     # block 0 never listed
+    assert np.all(dk[0, 8:12] == 0) and np.all(dv[0, 8:12] == 0)   # block 2 never listed
+    assert np.any(dv[0, 4:8] != 0) and np.any(dv[0, 12:16] != 0)

@@ -281,12 +281,11 @@ decode_bf16_kernel(DecArgs a) {
 
   // merge the waves' partial results through LDS (the V slots hold O)
   __syncthreads();
-  float* ow = reinterpret_cast<float*>(&vslot[wave][0]);   // [16 columns][D]
+  // [d tile][lane group][column] float4s: lane (c, g) writes and reads 16
+  // consecutive bytes, lanes side by side (no bank conflicts)
+  float* ow = reinterpret_cast<float*>(&vslot[wave][0]);
 #pragma unroll
-  for (int dt = 0; dt < DT; dt++) {
-#pragma unroll
-    for (int jj = 0; jj < 4; jj++) ow[c * D + dt * 16 + g * 4 + jj] = o[dt][jj];
-  }
+  for (int dt = 0; dt < DT; dt++) *reinterpret_cast<f32x4*>(ow + ((dt * 4 + g) * 16 + c) * 4) = o[dt];
   if (g == 0) {
     mw_lds[wave][c] = mrun;
     lw_lds[wave][c] = lrun;
@@ -307,15 +306,14 @@ decode_bf16_kernel(DecArgs a) {
   __bf16* __restrict__ Out = reinterpret_cast<__bf16*>(a.out);
   // wave w writes the d tiles dt = w (mod kDecWaves) of every column
   for (int dt = wave; dt < DT; dt += kDecWaves) {
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w = 0; w < kDecWaves; w++)
+      acc += *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(&vslot[w][0]) +
+                                             ((dt * 4 + g) * 16 + c) * 4) * wgt[w];
     bf16x4 ov;
 #pragma unroll
-    for (int jj = 0; jj < 4; jj++) {
-      float acc = 0.f;
-#pragma unroll
-      for (int w = 0; w < kDecWaves; w++)
-        acc += reinterpret_cast<const float*>(&vslot[w][0])[c * D + dt * 16 + g * 4 + jj] * wgt[w];
-      ov[jj] = (__bf16)(acc * inv);
-    }
+    for (int jj = 0; jj < 4; jj++) ov[jj] = (__bf16)(acc[jj] * inv);
     if (cvalid) *reinterpret_cast<bf16x4*>(Out + ((int64_t)b * a.Hq + hq) * D + dt * 16 + g * 4) = ov;
   }
   if (a.lse && wave == 0 && g == 0 && cvalid)

@@ -9,12 +9,12 @@
 // bf16 kernel: persistent workgroups of 16 waves, one per CU.
 //  * 4 loader waves stream the K and V rows of each item's merged block list
 //    (ascending block order, `kb` keys per unit) into a ring of R LDS slots.
-//    Loader p owns the units v = p (mod 4).  Once every attention wave that
-//    reads the slot's occupant has released its K rows, it sends the new K
-//    rows straight to LDS with 16-byte buffer loads and the V rows into its
-//    registers behind them, publishes the K rows when they have landed, and
-//    once the occupant's V rows are released too it stores the new V rows
-//    and publishes them.
+//    Loader p owns the units v = p (mod 4).  It fetches the V rows of its
+//    next unit into registers a unit ahead; once every attention wave that
+//    reads the slot's occupant has released its K rows it sends the new K
+//    rows straight to LDS with 16-byte buffer loads and publishes them when
+//    they have landed, and once the V rows are released too it stores the
+//    staged V rows and publishes them.
 //  * 12 attention waves each own a fixed set of the item's tokens and walk
 //    the same unit sequence without any barrier: a wave waits only for the
 //    unit's data, computes its own tokens that selected the block, releases
@@ -288,12 +288,11 @@ __global__ void __launch_bounds__(64 * (kConsumers + kProducers), 1) fwd_bf16_ri
     int tgt[kOwn];                          // participant releases owed to each own slot
 #pragma unroll
     for (int j = 0; j < kOwn; j++) tgt[j] = 0;
-    // The K rows go straight from memory to LDS as soon as the slot's K half
-    // is free (its readers have formed S^T), and the V rows into registers
-    // (16 bytes per lane per 1 KB load) behind them, so both latencies
-    // overlap the earlier occupant's softmax and PV, and the V half, freed
-    // last, only waits for the stores.  (Staging V a unit ahead instead put
-    // those loads in front of the next K loads in the vector-memory queue.)
+    // The V rows of the next own unit wait in registers (16 bytes per lane
+    // per 1 KB load), fetched a whole unit ahead; the K rows go straight
+    // from memory to LDS as soon as the slot's K half is free (its readers
+    // have formed S^T), so their latency overlaps the earlier occupant's
+    // softmax and PV, and the V half, freed last, only waits for the stores.
     u32x4 vst[C::kLoadsKV];
     // the item holding the next unit to locate: its first stream index, units, kv head
     int it_v0 = 0;
@@ -347,13 +346,14 @@ __global__ void __launch_bounds__(64 * (kConsumers + kProducers), 1) fwd_bf16_ri
       __atomic_signal_fence(__ATOMIC_SEQ_CST);
       return true;
     };
-    // Each pass places own unit v_cur: K loads into the slot and V loads into
-    // registers, the next unit's word, K landed -> publish K, V half free ->
-    // store V -> publish V.
+    // Each pass places own unit v_cur (its V rows already in registers):
+    // K loads into the slot, the next unit's word, K landed -> publish K,
+    // V half free -> store V -> publish V, then stage the next unit's V rows.
     int v_cur = p;
     int np = 0;               // participants of v_cur
     int64_t rb = 0;           // byte offset of v_cur's first row
     bool have = locate(v_cur, np, rb);
+    if (have && np > 0) issue_v(rb);
     bool stuck = false;
     while (have) {
       const int slot = v_cur % R;
@@ -371,13 +371,12 @@ __global__ void __launch_bounds__(64 * (kConsumers + kProducers), 1) fwd_bf16_ri
           break;
         }
         issue_k(rb, kdst);
-        issue_v(rb);   // behind the K loads: V only has to land before its store
       }
       int np_n = 0;
       int64_t rb_n = 0;
       const bool have_n = locate(v_cur + kProducers, np_n, rb_n);
       if (np > 0) {
-        wait_vmcnt<C::kLoadsKV>();   // the K rows have landed (the V loads behind them may not have)
+        wait_vmcnt<0>();   // the K rows (and this unit's staged V rows) have landed
         loader_bump(&ready_k[slot]);
         if (a.split_release && !wait_free(&done[slot], t)) {
           stuck = true;
@@ -395,6 +394,7 @@ __global__ void __launch_bounds__(64 * (kConsumers + kProducers), 1) fwd_bf16_ri
         loader_bump(&ready_k[slot]);   // no attention wave reads this unit: nothing to load
         loader_bump(&ready[slot]);
       }
+      if (have_n && np_n > 0) issue_v(rb_n);
       v_cur += kProducers;
       np = np_n;
       rb = rb_n;

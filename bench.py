@@ -16,7 +16,8 @@ workload on the host's cores.
 
 --config 0..4 selects the other named workloads (parity cases, not the
 headline); --config 5 is the same long-context shape with one index row per
-query block (nsa_fwd_qblock).  --decode measures the decode step
+query block (nsa_fwd_qblock); --config 6 and 7 repeat it at block sizes
+128 (D = 64) and 32.  --decode measures the decode step
 (nsa_decode: 128 sequences' newest tokens against a bf16 cache of 8192 rows,
 Hq=64, Hkv=4, D=128, bs=64, S=16) against the HBM roofline.
 

@@ -435,12 +435,21 @@ def make_config(i: int, seed: int | None = None) -> Workload:
     if i == 5:
         return make_qblock_workload(EXTRA_NAMES[5], "bf16", 1, 32768, 64, 4, 128, 64, 16, "sink_local_random",
                                     "full", s, value_scale=0.5)
+    if i == 6:
+        return make_qblock_workload(EXTRA_NAMES[6], "bf16", 1, 32768, 64, 4, 64, 128, 8, "sink_local_random",
+                                    "full", s, value_scale=0.5)
+    if i == 7:
+        return make_qblock_workload(EXTRA_NAMES[7], "bf16", 1, 32768, 64, 4, 128, 32, 32, "sink_local_random",
+                                    "full", s, value_scale=0.5)
     raise ValueError(f"no config {i}")
 
 
 # Workloads beyond the five named ones, by number: the long-context shapes
-# with one index row per query block.
-EXTRA_NAMES = {5: "c3q_bf16_qblock_T32768"}
+# with one index row per query block, at block size 64 (D = 128, S = 16),
+# 128 (D = 64, S = 8) and 32 (D = 128, S = 32): the same 1024 selected keys
+# per row at each block size.
+EXTRA_NAMES = {5: "c3q_bf16_qblock_T32768", 6: "c3q_bf16_qblock_bs128_d64_T32768",
+               7: "c3q_bf16_qblock_bs32_T32768"}
 
 
 def workload_name(i: int) -> str:

@@ -25,7 +25,7 @@ import ctypes
 import math
 import os
 
-__all__ = ["fwd", "Forward", "decode", "Decode", "workspace_size", "schedule", "load_library", "library_path", "NsaError",
+__all__ = ["fwd", "Forward", "decode", "Decode", "bwd", "workspace_size", "schedule", "load_library", "library_path", "NsaError",
            "DTYPE_F32", "DTYPE_BF16"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -74,6 +74,10 @@ def load_library():
     lib.nsa_fwd_qblock.argtypes = [dp, p, p, p, p, p, i32, f32, p, p, p, sz, p]
     lib.nsa_fwd_schedule_qblock.restype = ctypes.c_int
     lib.nsa_fwd_schedule_qblock.argtypes = [dp, p, p, i32, p, sz, p, ctypes.POINTER(sz), ctypes.POINTER(i32)]
+    lib.nsa_bwd_workspace_size.restype = sz
+    lib.nsa_bwd_workspace_size.argtypes = [dp]
+    lib.nsa_bwd.restype = ctypes.c_int
+    lib.nsa_bwd.argtypes = [dp, p, p, p, p, p, p, p, p, i32, f32, p, p, p, p, sz, p]
     lib.nsa_decode.restype = ctypes.c_int
     lib.nsa_decode.argtypes = [dp, p, p, p, p, p, p, i32, f32, p, p, p]
     lib.nsa_fwd_schedule.restype = ctypes.c_int
@@ -344,3 +348,34 @@ def decode(q, k_cache, v_cache, seq_lens, block_indices, block_counts, block_siz
     """Decode step on the GPU (see ``Decode``).  Returns (out, lse)."""
     return Decode(q, k_cache, v_cache, seq_lens, block_indices, block_counts, block_size, scale, out, lse,
                   return_lse).run()
+
+
+def bwd(q, k, v, out, lse, dout, block_indices, block_counts, block_size: int = 64,
+        scale: float | None = None, workspace=None):
+    """Gradients of ``fwd`` (``nsa_bwd``; fixed-length, bf16): returns
+    (dq, dk, dv) as float32 tensors shaped like q, k, v.  ``out`` and ``lse``
+    are the forward's results for the same inputs and indices."""
+    import torch
+    lib = load_library()
+    (q, k, v, bi, bc, _, B, T, Hq, Hkv, D, S, code) = _prepare(q, k, v, block_indices, block_counts, None,
+                                                                int(block_size), "token")
+    if code != DTYPE_BF16:
+        raise ValueError("the backward takes bf16 inputs")
+    out, dout = out.contiguous(), dout.contiguous()
+    if out.shape != q.shape or dout.shape != q.shape or out.dtype != q.dtype or dout.dtype != q.dtype:
+        raise ValueError("out and dout must match q")
+    lse = lse.to(torch.float32).contiguous()
+    if tuple(lse.shape) != (B, T, Hq):
+        raise ValueError("lse must be [B, T, Hq]")
+    dims = _dims(B, T, Hq, Hkv, D, S, code)
+    need = max(int(lib.nsa_bwd_workspace_size(ctypes.byref(dims))), 256)
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    dq = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    dk = torch.empty(k.shape, dtype=torch.float32, device=q.device)
+    dv = torch.empty(v.shape, dtype=torch.float32, device=q.device)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    _check(lib.nsa_bwd(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dout), _ptr(bi),
+                       _ptr(bc), int(block_size), scale, _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
+                       workspace.numel() * workspace.element_size(), _stream(torch, q.device)))
+    return dq, dk, dv

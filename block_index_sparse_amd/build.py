@@ -15,7 +15,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(BUILD, "libnsa.so")
-SOURCES = ["nsa_api.hip", "nsa_sched.hip", "nsa_fwd.hip", "nsa_decode.hip"]
+SOURCES = ["nsa_api.hip", "nsa_sched.hip", "nsa_fwd.hip", "nsa_decode.hip", "nsa_bwd.hip"]
 ARCH = "gfx950"
 
 

@@ -315,6 +315,70 @@ nsa_status nsa_decode(const nsa_dims* d, const void* q, const void* k, const voi
   return NSA_SUCCESS;
 }
 
+namespace {
+
+nsa_status make_bwd_plan(const nsa_dims* d, int32_t block_size, nsa::BwdPlan* p) {
+  if (!d) return NSA_ERROR_INVALID_VALUE;
+  if (d->batch <= 0 || d->seqlen <= 0 || d->num_q_heads <= 0 || d->num_kv_heads <= 0 ||
+      d->head_dim <= 0 || d->num_selected <= 0 || block_size <= 0)
+    return NSA_ERROR_INVALID_VALUE;
+  if (d->num_q_heads % d->num_kv_heads) return NSA_ERROR_INVALID_VALUE;
+  if (d->dtype != NSA_DTYPE_BF16) return NSA_ERROR_NOT_SUPPORTED;
+  if (d->head_dim != 64 && d->head_dim != 128) return NSA_ERROR_NOT_SUPPORTED;
+  if (block_size != 32 && block_size != 64 && block_size != 128) return NSA_ERROR_NOT_SUPPORTED;
+  if (d->num_selected > 64) return NSA_ERROR_NOT_SUPPORTED;
+  p->B = d->batch;
+  p->T = d->seqlen;
+  p->Hq = d->num_q_heads;
+  p->Hkv = d->num_kv_heads;
+  p->D = d->head_dim;
+  p->S = d->num_selected;
+  p->bs = block_size;
+  p->G = p->Hq / p->Hkv;
+  if (p->G <= 16) {
+    p->gv = p->G;
+    p->gpk = 1;
+  } else if (p->G % 16 == 0 && p->G <= 1024) {
+    p->gv = 16;
+    p->gpk = p->G / 16;
+  } else {
+    return NSA_ERROR_NOT_SUPPORTED;
+  }
+  const int64_t rows = (int64_t)p->B * p->T;
+  if (rows * p->Hq * p->D > INT64_C(1) << 40 || rows * p->Hkv * p->gpk > INT32_MAX / 2)
+    return NSA_ERROR_NOT_SUPPORTED;
+  return NSA_SUCCESS;
+}
+
+}  // namespace
+
+size_t nsa_bwd_workspace_size(const nsa_dims* dims) {
+  nsa::BwdPlan p;
+  if (make_bwd_plan(dims, 64, &p) != NSA_SUCCESS) return 0;
+  return align_up(sizeof(float) * (size_t)p.B * p.T * p.Hq, 256);
+}
+
+nsa_status nsa_bwd(const nsa_dims* d, const void* q, const void* k, const void* v, const void* out,
+                   const float* lse, const void* dout, const int32_t* block_indices,
+                   const int32_t* block_counts, int32_t block_size, float scale, float* dq, float* dk,
+                   float* dv, void* workspace, size_t workspace_bytes, void* stream) {
+  nsa::BwdPlan p;
+  nsa_status st = make_bwd_plan(d, block_size, &p);
+  if (st != NSA_SUCCESS) return st;
+  if (!q || !k || !v || !out || !lse || !dout || !block_indices || !block_counts || !dq || !dk || !dv ||
+      !workspace)
+    return NSA_ERROR_INVALID_VALUE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(dout) ||
+      !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || (reinterpret_cast<uintptr_t>(workspace) & 255u))
+    return NSA_ERROR_INVALID_VALUE;
+  if (!std::isfinite(scale)) return NSA_ERROR_INVALID_VALUE;
+  if (workspace_bytes < sizeof(float) * (size_t)p.B * p.T * p.Hq) return NSA_ERROR_WORKSPACE_TOO_SMALL;
+  if (nsa::launch_bwd(p, q, k, v, out, lse, dout, block_indices, block_counts, scale, dq, dk, dv,
+                      reinterpret_cast<float*>(workspace), reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
+    return NSA_ERROR_LAUNCH_FAILED;
+  return NSA_SUCCESS;
+}
+
 const char* nsa_status_string(nsa_status status) {
   switch (status) {
     case NSA_SUCCESS: return "NSA_SUCCESS";

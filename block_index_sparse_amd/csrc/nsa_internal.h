@@ -78,6 +78,12 @@ struct DecodePlan {
   int32_t gv, gpk;           // heads per group (<= 16), groups per kv head
 };
 
+// Backward: sizes of a call (fixed-length sequences, bf16).
+struct BwdPlan {
+  int32_t B, T, Hq, Hkv, D, S, bs, G;
+  int32_t gv, gpk;
+};
+
 // Launchers (defined in the .hip files).
 hipError_t launch_schedule(const Plan& p, const int32_t* block_indices, const int32_t* block_counts,
                            const int32_t* cu_seqlens, char* ws, hipStream_t stream);
@@ -87,6 +93,10 @@ hipError_t launch_decode(const DecodePlan& p, const void* q, const void* k, cons
                          const int32_t* seq_lens, const int32_t* block_indices,
                          const int32_t* block_counts, float scale, void* out, float* lse,
                          hipStream_t stream);
+hipError_t launch_bwd(const BwdPlan& p, const void* q, const void* k, const void* v, const void* out,
+                      const float* lse, const void* dout, const int32_t* block_indices,
+                      const int32_t* block_counts, float scale, float* dq, float* dk, float* dv,
+                      float* delta, hipStream_t stream);
 int device_cu_count();
 
 }  // namespace nsa

@@ -152,6 +152,30 @@ nsa_status nsa_decode(const nsa_dims* dims, const void* q, const void* k, const 
                       float* lse, void* stream);
 
 /*
+ * Backward of nsa_fwd (fixed-length sequences, bf16): the gradients of the
+ * forward's out with respect to q, k and v, given dout.  With P the
+ * forward's probabilities over each token's visible keys (recomputed from
+ * q, k and the forward's lse):
+ *   Delta = dout . out,  dS = P (dout . v - Delta),
+ *   dq = scale sum dS k,  dk = scale sum dS q,  dv = sum P dout
+ * (the chain rule through the masked softmax of the NSA page's operation).
+ *  q, k, v, out, dout bf16 in the layouts of nsa_fwd; lse [B, T, Hq]
+ *  float32 from the same forward; dq [B, T, Hq, D], dk, dv [B, T, Hkv, D]
+ *  float32, fully written (rows of keys no token reads get zeros).
+ *  The index rows and their rules are those of nsa_fwd; S <= 64.
+ *  Workspace: nsa_bwd_workspace_size() bytes (Delta), 256-byte aligned.
+ * The summation order of dk and dv is fixed per key tile (token order), so
+ * results are deterministic.  NSA_ERROR_NOT_SUPPORTED for fp32, S > 64 and
+ * the head_dim / block_size / group limits of nsa_fwd.
+ */
+size_t nsa_bwd_workspace_size(const nsa_dims* dims);
+nsa_status nsa_bwd(const nsa_dims* dims, const void* q, const void* k, const void* v,
+                   const void* out, const float* lse, const void* dout,
+                   const int32_t* block_indices, const int32_t* block_counts,
+                   int32_t block_size, float scale, float* dq, float* dk, float* dv,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * The two halves of a forward call.  nsa_fwd(...) is exactly
  * nsa_fwd_schedule(...) followed by nsa_fwd_execute(...) on the same stream.
  *

@@ -1,0 +1,89 @@
+"""GPU parity of the backward pass (nsa_bwd: dq, dk, dv) against the CPU
+fp64 gradient oracle (oracle/backward.py, pinned by central differences of
+the forward oracle and by autograd through SDPA).
+
+Tolerance, derived from the arithmetic: the kernels round P and dS to bf16
+(relative error <= 2^-9 each) before the MFMAs that accumulate dq, dk and
+dv in fp32, so a gradient entry's error is bounded by a few 2^-9 times the
+sum of its terms' magnitudes; the bar is |gpu - ref| <= 1e-2 max|ref| +
+1e-2 |ref| per gradient tensor."""
+import sys
+
+import numpy as np
+import pytest
+
+import nsa_inputs as ni
+from oracle import backward as obwd
+from tests._util import to_device
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _dout(w, seed):
+    x = ni.normal(seed, 9, w.B * w.T * w.Hq * w.D).reshape(w.B, w.T, w.Hq, w.D)
+    bits = ni.to_bf16_bits(x)
+    return ni.bf16_bits_to_f32(bits).reshape(x.shape), bits.reshape(x.shape)
+
+
+def run_bwd(w, dout_bits):
+    import torch
+    import block_index_sparse_amd as nsa
+    q, k, v, bi, bc, _ = to_device(w)
+    f = nsa.Forward(q, k, v, bi, bc, w.block_size, w.scale)
+    out, lse = f.run()
+    assert f.device_status() == 0
+    dout = torch.from_numpy(np.ascontiguousarray(dout_bits).view(np.int16)).view(torch.bfloat16).cuda()
+    return nsa.bwd(q, k, v, out, lse, dout, bi, bc, w.block_size, w.scale)
+
+
+def check(name, got, ref):
+    g = got.cpu().numpy().astype(np.float64)
+    err = np.abs(g - ref)
+    scale = float(np.abs(ref).max(initial=0))
+    ok = np.all(err <= 1e-2 * scale + 1e-2 * np.abs(ref))
+    _say(f"[bwd] {name}: max|err| {err.max(initial=0):.3e}, max|ref| {scale:.3e}")
+    assert ok, f"{name}: max|err| {err.max()} vs max|ref| {scale}"
+
+
+CASES = [
+    # name, B, T, Hq, Hkv, D, bs, S, pattern, counts
+    ("bwd_g16_d128_bs64", 2, 300, 32, 2, 128, 64, 6, "sink_local_random", "uniform"),
+    ("bwd_g4_d64_bs32", 1, 200, 8, 2, 64, 32, 5, "shuffled", "uniform"),
+    ("bwd_g1_d128_bs128", 1, 300, 2, 2, 128, 128, 3, "local_random", "full"),
+    ("bwd_g32_d64_bs64", 1, 150, 32, 1, 64, 64, 3, "sink_local_random", "full"),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_bwd_small_cases_all_gradients(case):
+    name, B, T, Hq, Hkv, D, bs, S, pattern, counts = case
+    _say(f"[bwd] {name}")
+    w = ni.make_workload(name, "bf16", [T] * B, Hq, Hkv, D, bs, S, pattern, counts, seed=19)
+    dout, dbits = _dout(w, 19)
+    dq, dk, dv = run_bwd(w, dbits)
+    rq, rk, rv = obwd.bwd(w.q, w.k, w.v, dout, w.block_indices, w.block_counts, bs, w.scale)
+    check(f"{name} dq", dq, rq)
+    check(f"{name} dk", dk, rk)
+    check(f"{name} dv", dv, rv)
+
+
+def test_bwd_hostile_entries():
+    """Negative, repeated and out-of-range entries, counts outside [0, S],
+    rows with no visible key (zero dq) and blocks no token reads (zero dk, dv)."""
+    _say("[bwd] hostile entries")
+    w = ni.make_workload("bwd_hostile", "bf16", [260, 260], 16, 1, 128, 64, 6, "local_random", "full", seed=7)
+    rng = np.random.default_rng(3)
+    w.block_indices = rng.integers(-3, 6, size=w.block_indices.shape).astype(np.int32)
+    w.block_counts = rng.integers(-2, 8, size=w.block_counts.shape).astype(np.int32)
+    dout, dbits = _dout(w, 7)
+    dq, dk, dv = run_bwd(w, dbits)
+    rq, rk, rv = obwd.bwd(w.q, w.k, w.v, dout, w.block_indices, w.block_counts, 64, w.scale)
+    check("hostile dq", dq, rq)
+    check("hostile dk", dk, rk)
+    check("hostile dv", dv, rv)
+    assert np.any(np.all(rq == 0, axis=(-1, -2)))   # some token sees nothing

@@ -19,7 +19,9 @@ headline); --config 5 is the same long-context shape with one index row per
 query block (nsa_fwd_qblock); --config 6 and 7 repeat it at block sizes
 128 (D = 64) and 32.  --decode measures the decode step
 (nsa_decode: 128 sequences' newest tokens against a bf16 cache of 8192 rows,
-Hq=64, Hkv=4, D=128, bs=64, S=16) against the HBM roofline.
+Hq=64, Hkv=4, D=128, bs=64, S=16) against the HBM roofline.  --backward
+measures nsa_bwd (dq, dk, dv) on --config's workload: useful FLOP = 10 D per
+visible (token, query head, key) triple (S, dP, dQ, dK, dV).
 
 HBM traffic of the attention kernel comes from two rocprofv3 counter runs
 (FETCH_SIZE, then WRITE_SIZE) of this script, each scaled by what the same
@@ -356,6 +358,58 @@ def decode_bench(args):
     print(json.dumps(line), flush=True)
 
 
+METRIC_BWD = "sparse-attn bwd useful TFLOP/s + % of bf16 MFMA peak, 1 GPU"
+
+
+def backward_bench(args):
+    import torch
+    import block_index_sparse_amd as nsa
+    import nsa_inputs as ni
+    dev = torch.device("cuda:0")
+    w = ni.make_config(args.config)
+    if w.dtype != "bf16" or w.cu_seqlens is not None or w.index_layout != "token":
+        sys.exit("bench --backward: the backward takes fixed-length bf16 workloads with per-token rows")
+    q, k, v, bi, bc, _ = ni.to_torch(w, dev)
+    f = nsa.Forward(q, k, v, bi, bc, w.block_size, w.scale)
+    out, lse = f.run()
+    x = ni.normal(200 + args.config, 9, w.B * w.T * w.Hq * w.D).reshape(w.B, w.T, w.Hq, w.D)
+    dout = torch.from_numpy(ni.to_bf16_bits(x).view(np.int16)).view(torch.bfloat16).to(dev)
+    need = nsa.load_library().nsa_bwd_workspace_size(__import__("ctypes").byref(nsa._dims(
+        w.B, w.T, w.Hq, w.Hkv, w.D, w.S, nsa.DTYPE_BF16)), w.block_size)
+    ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    flop = int(10 * w.D * w.G * int(visible_keys_per_row(w).sum()))
+
+    def call():
+        return nsa.bwd(q, k, v, out, lse, dout, bi, bc, w.block_size, w.scale, workspace=ws)
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    K = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    for i in range(K):
+        ev[i][0].record()
+        call()
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(b) for a, b in ev]
+    avg = float(np.mean(ms))
+    tf = flop / (avg * 1e-3) / 1e12
+    line = {
+        "metric": METRIC_BWD, "value": round(tf, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(avg, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "T": w.T, "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D,
+                   "block_size": w.block_size, "S": w.S, "useful_flop_per_step": flop,
+                   "input_sha256": w.digest()[:16]},
+        "roofline": {"bound": "mfma", "kernel": "bwd_dq_kernel + bwd_dkdv_kernel", "achieved": round(tf, 3),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None, "kernel_ms_avg": round(avg, 4), "kernel_ms_min": round(float(np.min(ms)), 4),
+                     "algorithmic_flop_per_launch": flop},
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -364,6 +418,7 @@ def main():
     ap.add_argument("--config", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decode", action="store_true", help="measure the decode step instead")
+    ap.add_argument("--backward", action="store_true", help="measure the backward pass on --config")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run the copy kernel used to scale the traffic counters")
@@ -401,6 +456,9 @@ def main():
         return
     if args.decode:
         decode_bench(args)
+        return
+    if args.backward:
+        backward_bench(args)
         return
 
     import torch

@@ -75,7 +75,7 @@ def load_library():
     lib.nsa_fwd_schedule_qblock.restype = ctypes.c_int
     lib.nsa_fwd_schedule_qblock.argtypes = [dp, p, p, i32, p, sz, p, ctypes.POINTER(sz), ctypes.POINTER(i32)]
     lib.nsa_bwd_workspace_size.restype = sz
-    lib.nsa_bwd_workspace_size.argtypes = [dp]
+    lib.nsa_bwd_workspace_size.argtypes = [dp, i32]
     lib.nsa_bwd.restype = ctypes.c_int
     lib.nsa_bwd.argtypes = [dp, p, p, p, p, p, p, p, p, i32, f32, p, p, p, p, sz, p]
     lib.nsa_decode.restype = ctypes.c_int
@@ -368,7 +368,7 @@ def bwd(q, k, v, out, lse, dout, block_indices, block_counts, block_size: int = 
     if tuple(lse.shape) != (B, T, Hq):
         raise ValueError("lse must be [B, T, Hq]")
     dims = _dims(B, T, Hq, Hkv, D, S, code)
-    need = max(int(lib.nsa_bwd_workspace_size(ctypes.byref(dims))), 256)
+    need = max(int(lib.nsa_bwd_workspace_size(ctypes.byref(dims), int(block_size))), 256)
     if workspace is None or workspace.numel() * workspace.element_size() < need:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     dq = torch.empty(q.shape, dtype=torch.float32, device=q.device)

@@ -352,10 +352,10 @@ nsa_status make_bwd_plan(const nsa_dims* d, int32_t block_size, nsa::BwdPlan* p)
 
 }  // namespace
 
-size_t nsa_bwd_workspace_size(const nsa_dims* dims) {
+size_t nsa_bwd_workspace_size(const nsa_dims* dims, int32_t block_size) {
   nsa::BwdPlan p;
-  if (make_bwd_plan(dims, 64, &p) != NSA_SUCCESS) return 0;
-  return align_up(sizeof(float) * (size_t)p.B * p.T * p.Hq, 256);
+  if (make_bwd_plan(dims, block_size, &p) != NSA_SUCCESS) return 0;
+  return nsa::bwd_workspace_bytes(p);
 }
 
 nsa_status nsa_bwd(const nsa_dims* d, const void* q, const void* k, const void* v, const void* out,
@@ -372,7 +372,7 @@ nsa_status nsa_bwd(const nsa_dims* d, const void* q, const void* k, const void* 
       !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || (reinterpret_cast<uintptr_t>(workspace) & 255u))
     return NSA_ERROR_INVALID_VALUE;
   if (!std::isfinite(scale)) return NSA_ERROR_INVALID_VALUE;
-  if (workspace_bytes < sizeof(float) * (size_t)p.B * p.T * p.Hq) return NSA_ERROR_WORKSPACE_TOO_SMALL;
+  if (workspace_bytes < nsa::bwd_workspace_bytes(p)) return NSA_ERROR_WORKSPACE_TOO_SMALL;
   if (nsa::launch_bwd(p, q, k, v, out, lse, dout, block_indices, block_counts, scale, dq, dk, dv,
                       reinterpret_cast<float*>(workspace), reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
     return NSA_ERROR_LAUNCH_FAILED;

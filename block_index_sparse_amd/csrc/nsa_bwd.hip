@@ -15,11 +15,14 @@
 // as the A operand of dQ^T += K^T dS^T.  The waves' partial dQ are summed
 // through LDS.  The kernel also writes Delta for the dk/dv kernel.
 //
-// dkdv kernel: one workgroup per (sequence, kv head, key block), one wave per
-// 16-key tile of the block.  The block's readers are found by scanning the
-// rows of the tokens at or after the block (a token reads the block iff it
-// is among its first clamp(count, 0, S) entries; repeats do not matter for
-// membership); for each reader token and head group the wave forms
+// readers kernel: a bitmap over tokens per (sequence, kv head, key block)
+// marking the tokens that read the block (set from every row's first
+// clamp(count, 0, S) entries 0 <= j <= own, repeats idempotent).
+//
+// dkdv kernel: one workgroup per (sequence, kv head, 64-key chunk), one wave
+// per 16-key tile.  The wave walks the bits of its block's reader bitmap from
+// its first key on, in token order (so the sums are deterministic); for each
+// reader token and head group it forms
 // S = Q K^T and dP = dO V^T for its 16 keys (K and V rows in registers as
 // B operands), P and dS, and accumulates dV += P^T dO and dK += dS^T Q with
 // 16x16x16 MFMAs whose B operands (dO and Q, heads x d) are read transposed
@@ -38,6 +41,9 @@ namespace {
 using namespace dev;
 
 constexpr int kBwdWaves = 4;
+constexpr int kKvTiles = 4;    // 16-key tiles per dk/dv workgroup (a 64-key chunk)
+constexpr int kKvPhases = 2;   // waves per tile, taking alternate readers
+constexpr int kSegTokens = 1024;   // readers of a chunk are split into segments of this many tokens
 
 struct BwdArgs {
   const void* q;          // [B, T, Hq, D] bf16
@@ -52,7 +58,9 @@ struct BwdArgs {
   float* dk;              // [B, T, Hkv, D]
   float* dv;
   float* delta;           // [B, T, Hq] workspace
-  int32_t B, T, Hq, Hkv, S, bs, G, gv, gpk, nb;
+  uint32_t* readers;      // [B, Hkv, nb, nw] workspace: bit t of block j = token t reads j
+  float* part;            // [ns][2][B, T, Hkv, D] workspace: per token segment, dK (unscaled) and dV
+  int32_t B, T, Hq, Hkv, S, bs, G, gv, gpk, nb, nw, ns;
   float scale;
   float scale_log2;
 };
@@ -268,30 +276,75 @@ bwd_dq_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// readers of every key block: a bitmap over tokens per (sequence, kv head,
+// block), set by one thread per (token, kv head) row for each of its first
+// clamp(count, 0, S) entries 0 <= j <= own (OR is idempotent, so repeats and
+// the order of the atomics do not matter)
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) bwd_clear_kernel(uint32_t* __restrict__ p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0u;
+}
+
+__global__ void __launch_bounds__(256) bwd_readers_kernel(BwdArgs a) {
+  const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;   // (b * T + t) * Hkv + h
+  if (r >= (int64_t)a.B * a.T * a.Hkv) return;
+  const int h = (int)(r % a.Hkv);
+  const int64_t bt = r / a.Hkv;
+  const int t = (int)(bt % a.T);
+  const int b = (int)(bt / a.T);
+  int n = a.bc[r];
+  n = n < 0 ? 0 : (n > a.S ? a.S : n);
+  const int own = t / a.bs;
+  uint32_t* base = a.readers + ((int64_t)b * a.Hkv + h) * a.nb * a.nw + t / 32;
+  const uint32_t bit = 1u << (t & 31);
+  for (int i = 0; i < n; i++) {
+    const int j = a.bi[r * a.S + i];
+    if (j >= 0 && j <= own) atomicOr(base + (int64_t)j * a.nw, bit);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // dk, dv
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ void __launch_bounds__(64 * kBwdWaves) bwd_dkdv_kernel(BwdArgs a) {
+__global__ void __launch_bounds__(64 * kKvTiles * kKvPhases) bwd_dkdv_kernel(BwdArgs a) {
   constexpr int KT = D / 32;   // k-steps of S = Q K^T over d
   constexpr int DT = D / 16;   // 16-column d tiles of dK, dV
   constexpr int kRow = D * 2;  // bytes of one head's row in the slot
-  __shared__ __attribute__((aligned(1024))) char slot[kBwdWaves][2][16 * kRow];   // Q_t, dO_t
+  __shared__ __attribute__((aligned(1024))) char slot[kKvTiles * kKvPhases][2][16 * kRow];   // Q_t, dO_t
+  // the second phase's accumulators, lane-contiguous: [tile][dk, dv][dt * 4 + jj][lane]
+  __shared__ float red[kKvTiles][2][DT * 4 * 64];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c = lane & 15;
   const int g = lane >> 4;
   const int nchunk = (a.T + 63) / 64;
-  const int wg = blockIdx.x;
+  const int seg = blockIdx.x % a.ns;           // token segment [seg * kSegTokens, + kSegTokens)
+  const int wg = blockIdx.x / a.ns;
   const int chunk = wg % nchunk;
   const int bh = wg / nchunk;
+  const int seg_lo = seg * kSegTokens;
+  const int seg_hi = min(seg_lo + kSegTokens, a.T);
+  // a segment that ends at or before the chunk's first key has no reader:
+  // the whole workgroup leaves (and the reduction skips it by the same rule)
+  if (seg_hi <= chunk * 64) return;
   const int h = bh % a.Hkv;
   const int b = bh / a.Hkv;
-  const int key0 = chunk * 64 + wave * 16;     // this wave's 16-key tile (position in the sequence)
-  if (key0 >= a.T) return;                     // no barrier follows: a wave past the end just leaves
-  const int blk = key0 / a.bs;                 // the block holding the tile
+  const int tile = wave % kKvTiles;            // 16-key tile of the chunk
+  const int phase = wave / kKvTiles;           // which of every kKvPhases readers this wave takes
+  const int key0 = chunk * 64 + tile * 16;     // the tile's first key (position in the sequence)
+  const bool active = key0 < a.T;              // every wave reaches the barriers below
+  const int blk = active ? key0 / a.bs : 0;    // the block holding the tile
 
   // K and V rows of the tile as B operands (lane (c, g): key row c, d = 32 kk + 8 g)
+  f32x4 dk[DT], dv[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; dt++) {
+    dk[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    dv[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  if (active) {
   const __bf16* __restrict__ Kp = reinterpret_cast<const __bf16*>(a.k);
   const __bf16* __restrict__ Vp = reinterpret_cast<const __bf16*>(a.v);
   const int key = key0 + c;
@@ -303,95 +356,112 @@ __global__ void __launch_bounds__(64 * kBwdWaves) bwd_dkdv_kernel(BwdArgs a) {
     kf[kk] = *reinterpret_cast<const bf16x8*>(Kp + krow + kk * 32 + g * 8);
     vf[kk] = *reinterpret_cast<const bf16x8*>(Vp + krow + kk * 32 + g * 8);
   }
-  f32x4 dk[DT], dv[DT];
-#pragma unroll
-  for (int dt = 0; dt < DT; dt++) {
-    dk[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    dv[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
   const __bf16* __restrict__ Q = reinterpret_cast<const __bf16*>(a.q);
   const __bf16* __restrict__ dO = reinterpret_cast<const __bf16*>(a.dout);
   NSA_LDS char* qs = (NSA_LDS char*)&slot[wave][0][0];
   NSA_LDS char* ds = (NSA_LDS char*)&slot[wave][1][0];
   const float sl = a.scale_log2;
 
-  // the tile's readers: tokens t >= key0 of this sequence whose first
-  // clamp(count, 0, S) entries list blk (blk <= t's own block follows)
-  for (int t0 = key0; t0 < a.T; t0 += 64) {
-    const int tt = t0 + lane;
-    bool reads = false;
-    if (tt < a.T) {
-      const int64_t row = ((int64_t)b * a.T + tt) * a.Hkv + h;
-      int n = a.bc[row];
-      n = n < 0 ? 0 : (n > a.S ? a.S : n);
-      const int32_t* r = a.bi + row * a.S;
-      for (int i = 0; i < n; i++) reads = reads || (r[i] == blk);
-    }
-    uint64_t todo = __ballot(reads);
-    while (todo != 0ull) {
-      const int bit = __builtin_ctzll(todo);
-      todo &= todo - 1ull;
-      const int t = t0 + bit;
-      const int64_t tok = (int64_t)b * a.T + t;
-      for (int grp = 0; grp < a.gpk; grp++) {
-        // Q_t, dO_t of the group's heads: A operands (lane (c, g): head c,
-        // d = 32 kk + 8 g), also written row-major to the slot for the
-        // transposed B reads; lse and Delta of heads 4 g .. 4 g + 3
-        const int hq = (h * a.gpk + grp) * a.gv + c;
-        const bool cvalid = c < a.gv;
-        const int64_t qrow = (tok * a.Hq + (cvalid ? hq : 0)) * D;
-        bf16x8 qa[KT], da[KT];
+  // the tile's readers, in token order: bits t >= key0 of the block's
+  // reader bitmap inside this segment (64 words of 32 tokens per pass, lane
+  // i holding word i); every kKvPhases-th reader belongs to this wave
+  const uint32_t* rbits = a.readers + (((int64_t)b * a.Hkv + h) * a.nb + blk) * a.nw;
+  int seen = 0;                                // readers met so far (the same in every lane)
+  const int t_lo = max(key0, seg_lo);          // this wave's tokens: [t_lo, seg_hi)
+  const int w_hi = (seg_hi + 31) / 32;
+  for (int w0 = t_lo / 32; w0 < w_hi; w0 += 64) {
+    const int wi = w0 + lane;
+    uint32_t word = wi < w_hi ? rbits[wi] : 0u;
+    if (wi == t_lo / 32) word &= 0xFFFFFFFFu << (t_lo & 31);
+    if (wi == (seg_hi - 1) / 32 && (seg_hi & 31) != 0) word &= 0xFFFFFFFFu >> (32 - (seg_hi & 31));
+    uint64_t lanes = __ballot(word != 0u);
+    while (lanes != 0ull) {
+      const int l = __builtin_ctzll(lanes);
+      lanes &= lanes - 1ull;
+      uint32_t wl = (uint32_t)__builtin_amdgcn_readlane((int)word, l);
+      while (wl != 0u) {
+        const int t = (w0 + l) * 32 + __builtin_ctz(wl);
+        wl &= wl - 1u;
+        if ((seen++ % kKvPhases) != phase) continue;
+        const int64_t tok = (int64_t)b * a.T + t;
+        for (int grp = 0; grp < a.gpk; grp++) {
+          // Q_t, dO_t of the group's heads: A operands (lane (c, g): head c,
+          // d = 32 kk + 8 g), also written row-major to the slot for the
+          // transposed B reads; lse and Delta of heads 4 g .. 4 g + 3
+          const int hq = (h * a.gpk + grp) * a.gv + c;
+          const bool cvalid = c < a.gv;
+          const int64_t qrow = (tok * a.Hq + (cvalid ? hq : 0)) * D;
+          bf16x8 qa[KT], da[KT];
 #pragma unroll
-        for (int kk = 0; kk < KT; kk++) {
-          if (cvalid) {
-            qa[kk] = *reinterpret_cast<const bf16x8*>(Q + qrow + kk * 32 + g * 8);
-            da[kk] = *reinterpret_cast<const bf16x8*>(dO + qrow + kk * 32 + g * 8);
-          } else {
-            qa[kk] = bf16x8{0, 0, 0, 0, 0, 0, 0, 0};
-            da[kk] = bf16x8{0, 0, 0, 0, 0, 0, 0, 0};
+          for (int kk = 0; kk < KT; kk++) {
+            if (cvalid) {
+              qa[kk] = *reinterpret_cast<const bf16x8*>(Q + qrow + kk * 32 + g * 8);
+              da[kk] = *reinterpret_cast<const bf16x8*>(dO + qrow + kk * 32 + g * 8);
+            } else {
+              qa[kk] = bf16x8{0, 0, 0, 0, 0, 0, 0, 0};
+              da[kk] = bf16x8{0, 0, 0, 0, 0, 0, 0, 0};
+            }
+            *(NSA_LDS bf16x8*)(qs + c * kRow + (kk * 32 + g * 8) * 2) = qa[kk];
+            *(NSA_LDS bf16x8*)(ds + c * kRow + (kk * 32 + g * 8) * 2) = da[kk];
           }
-          *(NSA_LDS bf16x8*)(qs + c * kRow + (kk * 32 + g * 8) * 2) = qa[kk];
-          *(NSA_LDS bf16x8*)(ds + c * kRow + (kk * 32 + g * 8) * 2) = da[kk];
-        }
-        float lse2[4], dl[4];
+          float lse2[4], dl[4];
 #pragma unroll
-        for (int jj = 0; jj < 4; jj++) {
-          const int hh = g * 4 + jj;
-          const bool hv = hh < a.gv;
-          const int64_t li = tok * a.Hq + (h * a.gpk + grp) * a.gv + (hv ? hh : 0);
-          lse2[jj] = hv ? a.lse[li] * 1.4426950408889634f : INFINITY;
-          dl[jj] = hv ? a.delta[li] : 0.f;
-        }
-        // S = Q K^T and dP = dO V^T: lane (c, g) holds heads 4 g + jj of key c
-        f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f}, pacc = f32x4{0.f, 0.f, 0.f, 0.f};
+          for (int jj = 0; jj < 4; jj++) {
+            const int hh = g * 4 + jj;
+            const bool hv = hh < a.gv;
+            const int64_t li = tok * a.Hq + (h * a.gpk + grp) * a.gv + (hv ? hh : 0);
+            lse2[jj] = hv ? a.lse[li] * 1.4426950408889634f : INFINITY;
+            dl[jj] = hv ? a.delta[li] : 0.f;
+          }
+          // S = Q K^T and dP = dO V^T: lane (c, g) holds heads 4 g + jj of key c
+          f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f}, pacc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kk = 0; kk < KT; kk++) {
-          sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[kk], kf[kk], sacc, 0, 0, 0);
-          pacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(da[kk], vf[kk], pacc, 0, 0, 0);
-        }
-        bf16x4 pa, sa;
+          for (int kk = 0; kk < KT; kk++) {
+            sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[kk], kf[kk], sacc, 0, 0, 0);
+            pacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(da[kk], vf[kk], pacc, 0, 0, 0);
+          }
+          bf16x4 pa, sa;
 #pragma unroll
-        for (int jj = 0; jj < 4; jj++) {
-          const float p = (key > t) ? 0.f : fast_exp2(__builtin_fmaf(sacc[jj], sl, -lse2[jj]));
-          pa[jj] = (__bf16)p;
-          sa[jj] = (__bf16)(p * (pacc[jj] - dl[jj]));
-        }
-        // dV += P^T dO, dK += dS^T Q; B operands (heads 4 g .. + 3 at d =
-        // 16 dt + c) read transposed from the slot
-        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the slot rows are written
+          for (int jj = 0; jj < 4; jj++) {
+            const float p = (key > t) ? 0.f : fast_exp2(__builtin_fmaf(sacc[jj], sl, -lse2[jj]));
+            pa[jj] = (__bf16)p;
+            sa[jj] = (__bf16)(p * (pacc[jj] - dl[jj]));
+          }
+          // dV += P^T dO, dK += dS^T Q; B operands (heads 4 g .. + 3 at d =
+          // 16 dt + c) read transposed from the slot
+          __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the slot rows are written
 #pragma unroll
-        for (int dt = 0; dt < DT; dt++) {
-          const int off = (g * 4 + (c >> 2)) * kRow + (dt * 16 + (c & 3) * 4) * 2;
-          const bf16x4 qb = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((NSA_LDS s16x4*)(qs + off)));
-          const bf16x4 db = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((NSA_LDS s16x4*)(ds + off)));
-          dv[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, db, dv[dt], 0, 0, 0);
-          dk[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(sa, qb, dk[dt], 0, 0, 0);
+          for (int dt = 0; dt < DT; dt++) {
+            const int off = (g * 4 + (c >> 2)) * kRow + (dt * 16 + (c & 3) * 4) * 2;
+            const bf16x4 qb = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((NSA_LDS s16x4*)(qs + off)));
+            const bf16x4 db = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((NSA_LDS s16x4*)(ds + off)));
+            dv[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, db, dv[dt], 0, 0, 0);
+            dk[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(sa, qb, dk[dt], 0, 0, 0);
+          }
+          __builtin_amdgcn_s_waitcnt(0xC07F);   // the slot reads have returned before it is rewritten
         }
-        __builtin_amdgcn_s_waitcnt(0xC07F);   // the slot reads have returned before it is rewritten
       }
     }
   }
-  // dK = scale * sum dS^T Q, dV = sum P^T dO; lane (c, g) holds keys 4 g + jj at d = 16 dt + c
+  }  // active
+  // the phases' sums meet in LDS in a fixed order (deterministic)
+  __syncthreads();
+  if (phase == 1 && active) {
+#pragma unroll
+    for (int dt = 0; dt < DT; dt++) {
+#pragma unroll
+      for (int jj = 0; jj < 4; jj++) {
+        red[tile][0][(dt * 4 + jj) * 64 + lane] = dk[dt][jj];
+        red[tile][1][(dt * 4 + jj) * 64 + lane] = dv[dt][jj];
+      }
+    }
+  }
+  __syncthreads();
+  if (phase != 0 || !active) return;
+  // the segment's partial sum dS^T Q and P^T dO; lane (c, g) holds keys 4 g + jj at d = 16 dt + c
+  const int64_t plane = (int64_t)a.B * a.T * a.Hkv * D;
+  float* pk = a.part + (int64_t)seg * 2 * plane;
+  float* pv = pk + plane;
 #pragma unroll
   for (int jj = 0; jj < 4; jj++) {
     const int kr = key0 + g * 4 + jj;
@@ -399,13 +469,48 @@ __global__ void __launch_bounds__(64 * kBwdWaves) bwd_dkdv_kernel(BwdArgs a) {
     const int64_t o = (((int64_t)b * a.T + kr) * a.Hkv + h) * D;
 #pragma unroll
     for (int dt = 0; dt < DT; dt++) {
-      a.dk[o + dt * 16 + c] = dk[dt][jj] * a.scale;
-      a.dv[o + dt * 16 + c] = dv[dt][jj];
+      pk[o + dt * 16 + c] = dk[dt][jj] + red[tile][0][(dt * 4 + jj) * 64 + lane];
+      pv[o + dt * 16 + c] = dv[dt][jj] + red[tile][1][(dt * 4 + jj) * 64 + lane];
     }
   }
 }
 
+// dK = scale * sum over the key's segments, dV = sum over them, in segment
+// order; segments that end at or before the key's 64-key chunk hold nothing
+// (their workgroups left without writing)
+template <int D>
+__global__ void __launch_bounds__(256) bwd_reduce_kernel(BwdArgs a) {
+  const int64_t plane = (int64_t)a.B * a.T * a.Hkv * D;
+  const int64_t i4 = (int64_t)blockIdx.x * 256 + threadIdx.x;   // float4 index into a plane
+  if (i4 * 4 >= plane) return;
+  const int64_t rowi = i4 * 4 / D;                               // (b * T + key) * Hkv + h
+  const int key = (int)((rowi / a.Hkv) % a.T);
+  const int seg0 = (key / 64) * 64 / kSegTokens;                 // first segment ending after the chunk start
+  f32x4 sk = f32x4{0.f, 0.f, 0.f, 0.f}, sv = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int sgi = seg0; sgi < a.ns; sgi++) {
+    const float* pk = a.part + (int64_t)sgi * 2 * plane;
+    sk += *reinterpret_cast<const f32x4*>(pk + i4 * 4);
+    sv += *reinterpret_cast<const f32x4*>(pk + plane + i4 * 4);
+  }
+  *reinterpret_cast<f32x4*>(a.dk + i4 * 4) = sk * a.scale;
+  *reinterpret_cast<f32x4*>(a.dv + i4 * 4) = sv;
+}
+
 }  // namespace
+
+size_t bwd_delta_bytes(const BwdPlan& p) {
+  return ((size_t)p.B * p.T * p.Hq * sizeof(float) + 255) / 256 * 256;
+}
+
+size_t bwd_readers_bytes(const BwdPlan& p) {
+  const size_t nb = (size_t)(p.T + p.bs - 1) / p.bs, nw = (size_t)(p.T + 31) / 32;
+  return ((size_t)p.B * p.Hkv * nb * nw * sizeof(uint32_t) + 255) / 256 * 256;
+}
+
+size_t bwd_workspace_bytes(const BwdPlan& p) {
+  const size_t ns = (size_t)(p.T + kSegTokens - 1) / kSegTokens;
+  return bwd_delta_bytes(p) + bwd_readers_bytes(p) + ns * 2 * (size_t)p.B * p.T * p.Hkv * p.D * sizeof(float);
+}
 
 hipError_t launch_bwd(const BwdPlan& p, const void* q, const void* k, const void* v, const void* out,
                       const float* lse, const void* dout, const int32_t* block_indices,
@@ -434,16 +539,28 @@ hipError_t launch_bwd(const BwdPlan& p, const void* q, const void* k, const void
   a.gv = p.gv;
   a.gpk = p.gpk;
   a.nb = (p.T + p.bs - 1) / p.bs;
+  a.nw = (p.T + 31) / 32;
+  a.readers = reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(delta) + bwd_delta_bytes(p));
+  a.part = reinterpret_cast<float*>(reinterpret_cast<char*>(a.readers) + bwd_readers_bytes(p));
+  a.ns = (p.T + kSegTokens - 1) / kSegTokens;
   a.scale = scale;
   a.scale_log2 = scale * 1.4426950408889634f;
   const int64_t n_dq = (int64_t)p.B * p.T * p.Hkv * p.gpk;
-  const int64_t n_kv = (int64_t)p.B * p.Hkv * ((p.T + 63) / 64);
+  const int64_t n_kv = (int64_t)p.B * p.Hkv * ((p.T + 63) / 64) * a.ns;
+  const int64_t n_red = ((int64_t)p.B * p.T * p.Hkv * p.D / 4 + 255) / 256;
+  const int64_t n_bits = (int64_t)p.B * p.Hkv * a.nb * a.nw;
+  const int64_t n_rows = (int64_t)p.B * p.T * p.Hkv;
+  hipLaunchKernelGGL(bwd_clear_kernel, dim3((unsigned)std::min<int64_t>((n_bits + 255) / 256, 4096)), dim3(256), 0,
+                     stream, a.readers, n_bits);
+  hipLaunchKernelGGL(bwd_readers_kernel, dim3((unsigned)((n_rows + 255) / 256)), dim3(256), 0, stream, a);
   if (p.D == 64) {
     hipLaunchKernelGGL(bwd_dq_kernel<64>, dim3((unsigned)n_dq), dim3(64 * kBwdWaves), 0, stream, a);
-    hipLaunchKernelGGL(bwd_dkdv_kernel<64>, dim3((unsigned)n_kv), dim3(64 * kBwdWaves), 0, stream, a);
+    hipLaunchKernelGGL(bwd_dkdv_kernel<64>, dim3((unsigned)n_kv), dim3(64 * kKvTiles * kKvPhases), 0, stream, a);
+    hipLaunchKernelGGL(bwd_reduce_kernel<64>, dim3((unsigned)n_red), dim3(256), 0, stream, a);
   } else if (p.D == 128) {
     hipLaunchKernelGGL(bwd_dq_kernel<128>, dim3((unsigned)n_dq), dim3(64 * kBwdWaves), 0, stream, a);
-    hipLaunchKernelGGL(bwd_dkdv_kernel<128>, dim3((unsigned)n_kv), dim3(64 * kBwdWaves), 0, stream, a);
+    hipLaunchKernelGGL(bwd_dkdv_kernel<128>, dim3((unsigned)n_kv), dim3(64 * kKvTiles * kKvPhases), 0, stream, a);
+    hipLaunchKernelGGL(bwd_reduce_kernel<128>, dim3((unsigned)n_red), dim3(256), 0, stream, a);
   } else {
     return hipErrorInvalidValue;
   }

@@ -93,6 +93,7 @@ hipError_t launch_decode(const DecodePlan& p, const void* q, const void* k, cons
                          const int32_t* seq_lens, const int32_t* block_indices,
                          const int32_t* block_counts, float scale, void* out, float* lse,
                          hipStream_t stream);
+size_t bwd_workspace_bytes(const BwdPlan& p);   // Delta, then the reader bitmaps
 hipError_t launch_bwd(const BwdPlan& p, const void* q, const void* k, const void* v, const void* out,
                       const float* lse, const void* dout, const int32_t* block_indices,
                       const int32_t* block_counts, float scale, float* dq, float* dk, float* dv,

@@ -163,12 +163,14 @@ nsa_status nsa_decode(const nsa_dims* dims, const void* q, const void* k, const 
  *  float32 from the same forward; dq [B, T, Hq, D], dk, dv [B, T, Hkv, D]
  *  float32, fully written (rows of keys no token reads get zeros).
  *  The index rows and their rules are those of nsa_fwd; S <= 64.
- *  Workspace: nsa_bwd_workspace_size() bytes (Delta), 256-byte aligned.
- * The summation order of dk and dv is fixed per key tile (token order), so
- * results are deterministic.  NSA_ERROR_NOT_SUPPORTED for fp32, S > 64 and
+ *  Workspace: nsa_bwd_workspace_size() bytes (Delta and a reader bitmap
+ *  per key block: B * Hkv * ceil(T / block_size) * ceil(T / 32) words),
+ *  256-byte aligned, no initialisation needed.
+ * dk and dv sum over a block's readers in token order, so results are
+ * deterministic.  NSA_ERROR_NOT_SUPPORTED for fp32, S > 64 and
  * the head_dim / block_size / group limits of nsa_fwd.
  */
-size_t nsa_bwd_workspace_size(const nsa_dims* dims);
+size_t nsa_bwd_workspace_size(const nsa_dims* dims, int32_t block_size);
 nsa_status nsa_bwd(const nsa_dims* dims, const void* q, const void* k, const void* v,
                    const void* out, const float* lse, const void* dout,
                    const int32_t* block_indices, const int32_t* block_counts,

@@ -64,3 +64,30 @@ def bwd(q, k, v, dout, block_indices, block_counts, block_size, scale):
                     dq[b, t, hq] += scale * (ds @ K)
                     dk[b, keys, h] += scale * ds[:, None] * q[b, t, hq][None, :]
     return dq, dk, dv
+
+
+def dq_rows(q, k, v, dout, block_indices, block_counts, block_size, scale, tokens):
+    """dq of the listed packed tokens (b * T + t) only, float64 [n, Hq, D]:
+    a token's dq depends on its own row alone."""
+    q = np.asarray(q, np.float64)
+    B, T, Hq, D = q.shape
+    Hkv = k.shape[2]
+    S = block_indices.shape[-1]
+    G = Hq // Hkv
+    out = np.zeros((len(tokens), Hq, D))
+    for r, x in enumerate(tokens):
+        b, t = int(x) // T, int(x) % T
+        for h in range(Hkv):
+            keys = _visible(block_indices[b, t, h], block_counts[b, t, h], S, block_size, t)
+            if len(keys) == 0:
+                continue
+            K = np.asarray(k[b, keys, h], np.float64)
+            V = np.asarray(v[b, keys, h], np.float64)
+            for hq in range(h * G, (h + 1) * G):
+                z = scale * (K @ q[b, t, hq])
+                p = np.exp(z - z.max())
+                p /= p.sum()
+                dp = V @ np.asarray(dout[b, t, hq], np.float64)
+                ds = p * (dp - p @ dp)
+                out[r, hq] = scale * (ds @ K)
+    return out

@@ -87,3 +87,30 @@ def test_bwd_hostile_entries():
     check("hostile dk", dk, rk)
     check("hostile dv", dv, rv)
     assert np.any(np.all(rq == 0, axis=(-1, -2)))   # some token sees nothing
+
+
+@pytest.mark.parametrize("cfg", [1, 3])
+def test_bwd_named_workload_full_size(cfg):
+    """Full-size workloads: dq on sampled tokens against the oracle; at every
+    (sequence, kv head, d) the invariants sum_s dV_s = sum over the group's
+    (token, head) of dO (rows of P sum to one) and sum_s dK_s = 0 (each row's
+    dS sums to zero)."""
+    from tests._util import sample_rows
+    _say(f"[bwd] config {cfg}: generating")
+    w = ni.make_config(cfg)
+    dout, dbits = _dout(w, 100 + cfg)
+    dq, dk, dv = run_bwd(w, dbits)
+    rows = sample_rows(w, 24, seed=cfg)
+    rq = obwd.dq_rows(w.q, w.k, w.v, dout, w.block_indices, w.block_counts, w.block_size, w.scale, rows)
+    check(f"config {cfg} dq rows", dq.reshape(-1, w.Hq, w.D)[rows], rq)
+    dvs = dv.double().sum(dim=1).cpu().numpy()                      # [B, Hkv, D]
+    dks = dk.double().sum(dim=1).cpu().numpy()
+    dos = dout.astype(np.float64).sum(axis=1).reshape(w.B, w.Hkv, w.G, w.D).sum(axis=2)
+    dv_abs = dv.double().abs().sum(dim=1).cpu().numpy()
+    dk_abs = dk.double().abs().sum(dim=1).cpu().numpy()
+    err_v = np.abs(dvs - dos)
+    _say(f"[bwd] config {cfg}: max|sum dV - sum dO| {err_v.max():.3e} (sum|dV| up to {dv_abs.max():.3e}), "
+         f"max|sum dK| {np.abs(dks).max():.3e} (sum|dK| up to {dk_abs.max():.3e})")
+    assert np.all(err_v <= 1e-2 * dv_abs + 1e-3)
+    assert np.all(np.abs(dks) <= 1e-2 * dk_abs + 1e-3)
+    assert bool(dq.isfinite().all() and dk.isfinite().all() and dv.isfinite().all())

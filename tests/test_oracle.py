@@ -468,3 +468,12 @@ def test_gradients_of_empty_rows_and_unlisted_keys_vanish():
     assert np.all(dk[0, 0:4] == 0) and np.all(dv[0, 0:4] == 0)     # block 0 never listed
     assert np.all(dk[0, 8:12] == 0) and np.all(dv[0, 8:12] == 0)   # block 2 never listed
     assert np.any(dv[0, 4:8] != 0) and np.any(dv[0, 12:16] != 0)
+
+
+def test_gradient_rows_match_full_gradients():
+    w = ni.make_workload("gr", "f32", [30, 30], 4, 2, 8, 4, 4, "sink_local_random", "uniform", seed=15)
+    dout = np.random.default_rng(2).standard_normal(w.q.shape)
+    dq, _, _ = obwd.bwd(w.q, w.k, w.v, dout, w.block_indices, w.block_counts, w.block_size, w.scale)
+    rows = np.array([0, 7, 29, 30, 45, 59])
+    got = obwd.dq_rows(w.q, w.k, w.v, dout, w.block_indices, w.block_counts, w.block_size, w.scale, rows)
+    np.testing.assert_allclose(got, dq.reshape(-1, w.Hq, w.D)[rows], rtol=0, atol=1e-13)

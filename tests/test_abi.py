@@ -139,3 +139,28 @@ def test_qblock_schedule_rejects_bad_arguments():
     assert args(D(), wsb=16) == 3
     assert args(D(Dh=96)) == 2
     assert n.value == -1
+
+
+def test_bwd_rejects_bad_arguments():
+    """nsa_bwd checks its arguments on the host before anything is enqueued."""
+    lib = nsa.load_library()
+    p = ctypes.c_void_p(256)
+
+    def call(dims, bs=64, scale=1.0, ptr=p, ws_bytes=1 << 40, null_at=None):
+        args = [ptr] * 12
+        if null_at is not None:
+            args[null_at] = None
+        return lib.nsa_bwd(ctypes.byref(dims), args[0], args[1], args[2], args[3], args[4], args[5], args[6],
+                           args[7], bs, scale, args[8], args[9], args[10], args[11], ws_bytes, None)
+    assert call(D(Hkv=3)) == 1
+    assert call(D(dt=0)) == 2            # fp32: the backward is bf16 only
+    assert call(D(Dh=96)) == 2
+    assert call(D(S=65)) == 2
+    assert call(D(), bs=48) == 2
+    assert call(D(), scale=float("nan")) == 1
+    assert call(D(), null_at=5) == 1     # dout
+    assert call(D(), null_at=11) == 1    # workspace
+    assert call(D(), ptr=ctypes.c_void_p(264)) == 1
+    assert call(D(), ws_bytes=16) == 3
+    assert lib.nsa_bwd_workspace_size(ctypes.byref(D()), 64) > 0
+    assert lib.nsa_bwd_workspace_size(ctypes.byref(D(dt=0)), 64) == 0

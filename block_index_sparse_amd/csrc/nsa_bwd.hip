@@ -405,13 +405,27 @@ __global__ void __launch_bounds__(64 * kKvTiles * kKvPhases) bwd_dkdv_kernel(Bwd
             *(NSA_LDS bf16x8*)(ds + c * kRow + (kk * 32 + g * 8) * 2) = da[kk];
           }
           float lse2[4], dl[4];
+          if (a.gv % 4 == 0) {
+            // heads 4 g .. 4 g + 3 are contiguous: one 16-byte load each
+            // (an index past the group's heads is clamped and masked below)
+            const bool gvalid = g * 4 < a.gv;
+            const int64_t li = tok * a.Hq + (h * a.gpk + grp) * a.gv + (gvalid ? g * 4 : 0);
+            const f32x4 l4 = *reinterpret_cast<const f32x4*>(a.lse + li);
+            const f32x4 d4 = *reinterpret_cast<const f32x4*>(a.delta + li);
 #pragma unroll
-          for (int jj = 0; jj < 4; jj++) {
-            const int hh = g * 4 + jj;
-            const bool hv = hh < a.gv;
-            const int64_t li = tok * a.Hq + (h * a.gpk + grp) * a.gv + (hv ? hh : 0);
-            lse2[jj] = hv ? a.lse[li] * 1.4426950408889634f : INFINITY;
-            dl[jj] = hv ? a.delta[li] : 0.f;
+            for (int jj = 0; jj < 4; jj++) {
+              lse2[jj] = gvalid ? l4[jj] * 1.4426950408889634f : INFINITY;
+              dl[jj] = gvalid ? d4[jj] : 0.f;
+            }
+          } else {
+#pragma unroll
+            for (int jj = 0; jj < 4; jj++) {
+              const int hh = g * 4 + jj;
+              const bool hv = hh < a.gv;
+              const int64_t li = tok * a.Hq + (h * a.gpk + grp) * a.gv + (hv ? hh : 0);
+              lse2[jj] = hv ? a.lse[li] * 1.4426950408889634f : INFINITY;
+              dl[jj] = hv ? a.delta[li] : 0.f;
+            }
           }
           // S = Q K^T and dP = dO V^T: lane (c, g) holds heads 4 g + jj of key c
           f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f}, pacc = f32x4{0.f, 0.f, 0.f, 0.f};

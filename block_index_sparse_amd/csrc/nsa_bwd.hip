@@ -401,8 +401,12 @@ __global__ void __launch_bounds__(64 * kKvTiles * kKvPhases) bwd_dkdv_kernel(Bwd
               qa[kk] = bf16x8{0, 0, 0, 0, 0, 0, 0, 0};
               da[kk] = bf16x8{0, 0, 0, 0, 0, 0, 0, 0};
             }
-            *(NSA_LDS bf16x8*)(qs + c * kRow + (kk * 32 + g * 8) * 2) = qa[kk];
-            *(NSA_LDS bf16x8*)(ds + c * kRow + (kk * 32 + g * 8) * 2) = da[kk];
+            // 16-byte chunk 4 kk + g of head row c, XOR-swizzled by row (the
+            // forward's V-slot layout) so the writes and the transposed
+            // reads below are free of bank conflicts
+            const int ch = (kk * 4 + g) ^ v_swizzle<D>(c);
+            *(NSA_LDS bf16x8*)(qs + c * kRow + ch * 16) = qa[kk];
+            *(NSA_LDS bf16x8*)(ds + c * kRow + ch * 16) = da[kk];
           }
           float lse2[4], dl[4];
           if (a.gv % 4 == 0) {
@@ -446,7 +450,9 @@ __global__ void __launch_bounds__(64 * kKvTiles * kKvPhases) bwd_dkdv_kernel(Bwd
           __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the slot rows are written
 #pragma unroll
           for (int dt = 0; dt < DT; dt++) {
-            const int off = (g * 4 + (c >> 2)) * kRow + (dt * 16 + (c & 3) * 4) * 2;
+            const int row = g * 4 + (c >> 2);
+            const int d0 = dt * 16 + (c & 3) * 4;
+            const int off = row * kRow + ((d0 >> 3) ^ v_swizzle<D>(row)) * 16 + (d0 & 7) * 2;
             const bf16x4 qb = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((NSA_LDS s16x4*)(qs + off)));
             const bf16x4 db = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((NSA_LDS s16x4*)(ds + off)));
             dv[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, db, dv[dt], 0, 0, 0);

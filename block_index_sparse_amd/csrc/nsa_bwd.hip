@@ -19,15 +19,19 @@
 // marking the tokens that read the block (set from every row's first
 // clamp(count, 0, S) entries 0 <= j <= own, repeats idempotent).
 //
-// dkdv kernel: one workgroup per (sequence, kv head, 64-key chunk), one wave
-// per 16-key tile.  The wave walks the bits of its block's reader bitmap from
-// its first key on, in token order (so the sums are deterministic); for each
-// reader token and head group it forms
-// S = Q K^T and dP = dO V^T for its 16 keys (K and V rows in registers as
-// B operands), P and dS, and accumulates dV += P^T dO and dK += dS^T Q with
+// dkdv kernel: one workgroup per (sequence, kv head, 64-key chunk, token
+// segment), one wave per (16-key tile, phase).  Wave 0 turns the chunk's
+// reader bitmaps into a list of the segment's reader tokens, in token order
+// (so the sums are deterministic).  The workgroup then walks the list two
+// (reader, head group) units per step: all its lanes load the two units' Q_t,
+// dO_t, lse and Delta once into registers two steps ahead and store them into
+// one of two LDS buffers, and each wave takes the unit of its phase: it forms
+// S = Q K^T and dP = dO V^T for its 16 keys (K and V rows in registers as B
+// operands), P and dS, and accumulates dV += P^T dO and dK += dS^T Q with
 // 16x16x16 MFMAs whose B operands (dO and Q, heads x d) are read transposed
-// from LDS.  Every key row of every block gets written (zeros where no token
-// reads the block).
+// from the buffer.  The two phases' sums meet in LDS, and the segments'
+// partial sums are added in segment order by the reduce kernel.  Every key
+// row gets written (zeros where no token reads the block).
 #include <utility>
 
 #include "nsa.h"
@@ -306,24 +310,131 @@ __global__ void __launch_bounds__(256) bwd_readers_kernel(BwdArgs a) {
 // ---------------------------------------------------------------------------
 // dk, dv
 // ---------------------------------------------------------------------------
+// one Q_t / dO_t / lse / Delta unit of 16 query heads as staged in LDS
+template <int D>
+struct KvUnit {
+  static constexpr int kRow = D * 2;                  // bytes of one head's row
+  static constexpr int kRows = 16 * kRow;             // Q (or dO) rows of 16 heads
+  static constexpr int kBytes = 2 * kRows + 2 * 64;   // Q, dO, lse[16], Delta[16]
+  static constexpr int kChunks = kRows / 16;          // 16-byte chunks of Q (or dO)
+  static constexpr int kStepChunks = kKvPhases * 2 * kChunks;
+  static constexpr int kThreads = 64 * kKvTiles * kKvPhases;
+  static constexpr int kLoads = kStepChunks / kThreads;   // 16-byte loads per lane per step
+  static_assert(kStepChunks % kThreads == 0, "a step's chunks spread evenly over the workgroup");
+};
+
+// the next step's Q_t / dO_t chunks and one lse or Delta value, in flight
+// in registers while the current step computes
+template <int D>
+struct KvStage {
+  u32x4 v[KvUnit<D>::kLoads];
+  float f;
+};
+
+template <int D>
+__device__ __forceinline__ void kv_stage_load(const BwdArgs& a, const uint16_t* rlist, int nunits, int seg_lo,
+                                              int64_t tok_base, int h, int tid, int step, KvStage<D>& st) {
+  using U = KvUnit<D>;
+  const __bf16* __restrict__ Q = reinterpret_cast<const __bf16*>(a.q);
+  const __bf16* __restrict__ dO = reinterpret_cast<const __bf16*>(a.dout);
+#pragma unroll
+  for (int l = 0; l < U::kLoads; l++) {
+    const int gi = l * U::kThreads + tid;
+    const int unit = gi / (2 * U::kChunks);
+    const int rem = gi % (2 * U::kChunks);
+    const int row = (rem % U::kChunks) / (D / 8);
+    const int ck = rem % (D / 8);
+    // past the last unit or the group's heads: a clamped in-bounds address
+    // (the value is replaced by zeros or never read)
+    const int u = min(kKvPhases * step + unit, nunits - 1);
+    const int t = seg_lo + (rlist[u / a.gpk] & 1023);
+    const int hq = (h * a.gpk + u % a.gpk) * a.gv + min(row, a.gv - 1);
+    const __bf16* src = rem < U::kChunks ? Q : dO;
+    st.v[l] = *reinterpret_cast<const u32x4*>(src + ((tok_base + t) * a.Hq + hq) * D + ck * 8);
+  }
+  // lanes 0..63: unit (tid / 32) % 2, lse or Delta ((tid / 16) % 2), head tid % 16
+  const int unit = (tid >> 5) & 1;
+  const int u = min(kKvPhases * step + unit, nunits - 1);
+  const int t = seg_lo + (rlist[u / a.gpk] & 1023);
+  const int hq = (h * a.gpk + u % a.gpk) * a.gv + min(tid & 15, a.gv - 1);
+  st.f = ((tid >> 4) & 1 ? a.delta : a.lse)[(tok_base + t) * a.Hq + hq];
+}
+
+template <int D>
+__device__ __forceinline__ void kv_stage_store(const BwdArgs& a, NSA_LDS char* buf, int tid, const KvStage<D>& st) {
+  using U = KvUnit<D>;
+#pragma unroll
+  for (int l = 0; l < U::kLoads; l++) {
+    const int gi = l * U::kThreads + tid;
+    const int unit = gi / (2 * U::kChunks);
+    const int rem = gi % (2 * U::kChunks);
+    const int row = (rem % U::kChunks) / (D / 8);
+    const int ck = rem % (D / 8);
+    // rows of heads past the group are zero (their P and dS are zero too,
+    // and 0 times a stale value could be NaN)
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    // row-major 16-byte chunks XOR-swizzled by row, as in the forward's V
+    // slot: the A-operand reads and the transposed reads are conflict-free
+    *(NSA_LDS u32x4*)(buf + unit * U::kBytes + (rem < U::kChunks ? 0 : U::kRows) + row * U::kRow +
+                      ((ck ^ v_swizzle<D>(row)) * 16)) = row < a.gv ? st.v[l] : z;
+  }
+  if (tid < 64) {
+    const int unit = (tid >> 5) & 1;
+    const int which = (tid >> 4) & 1;
+    const int j = tid & 15;
+    // a head past the group: lse = +inf makes its P zero, Delta = 0
+    const float val = j < a.gv ? st.f : (which ? 0.f : INFINITY);
+    *(NSA_LDS float*)(buf + unit * U::kBytes + 2 * U::kRows + which * 64 + j * 4) = val;
+  }
+}
+
+// LDS writes of every wave done and visible before any wave goes on; global
+// loads in flight stay in flight (no vector-memory wait)
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 template <int D>
 __global__ void __launch_bounds__(64 * kKvTiles * kKvPhases) bwd_dkdv_kernel(BwdArgs a) {
+  using U = KvUnit<D>;
   constexpr int KT = D / 32;   // k-steps of S = Q K^T over d
   constexpr int DT = D / 16;   // 16-column d tiles of dK, dV
-  constexpr int kRow = D * 2;  // bytes of one head's row in the slot
-  __shared__ __attribute__((aligned(1024))) char slot[kKvTiles * kKvPhases][2][16 * kRow];   // Q_t, dO_t
+  constexpr int kRow = U::kRow;
+  // two step buffers of kKvPhases units each
+  __shared__ __attribute__((aligned(1024))) char slot[2][kKvPhases * U::kBytes];
   // the second phase's accumulators, lane-contiguous: [tile][dk, dv][dt * 4 + jj][lane]
   __shared__ float red[kKvTiles][2][DT * 4 * 64];
+  // the chunk's readers in the segment: token - segment start (bits 0..9),
+  // and which of the chunk's key blocks the token reads (bits 10, 11)
+  __shared__ uint16_t rlist[kSegTokens];
+  __shared__ int nread_s;
 
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c = lane & 15;
   const int g = lane >> 4;
   const int nchunk = (a.T + 63) / 64;
-  const int seg = blockIdx.x % a.ns;           // token segment [seg * kSegTokens, + kSegTokens)
-  const int wg = blockIdx.x / a.ns;
-  const int chunk = wg % nchunk;
-  const int bh = wg / nchunk;
+  // workgroup order: first chunk 0 of every (sequence, kv head, segment):
+  // block 0 is read by most tokens under attention-sink selections, so the
+  // longest workgroups start first; then segment-major, the chunks of one
+  // token segment in a row, so the Q_t and dO_t rows those workgroups
+  // gather come from HBM about once and then from the last-level cache
+  const int nbhs = a.B * a.Hkv * a.ns;
+  int chunk, r;
+  if ((int)blockIdx.x < nbhs) {
+    chunk = 0;
+    r = blockIdx.x;
+  } else {
+    const int rest = max(nchunk - 1, 1);
+    const int i = blockIdx.x - nbhs;
+    chunk = 1 + i % rest;
+    r = i / rest;
+  }
+  const int seg = r % a.ns;                    // token segment [seg * kSegTokens, + kSegTokens)
+  const int bh = r / a.ns;
   const int seg_lo = seg * kSegTokens;
   const int seg_hi = min(seg_lo + kSegTokens, a.T);
   // a segment that ends at or before the chunk's first key has no reader:
@@ -332,138 +443,144 @@ __global__ void __launch_bounds__(64 * kKvTiles * kKvPhases) bwd_dkdv_kernel(Bwd
   const int h = bh % a.Hkv;
   const int b = bh / a.Hkv;
   const int tile = wave % kKvTiles;            // 16-key tile of the chunk
-  const int phase = wave / kKvTiles;           // which of every kKvPhases readers this wave takes
+  const int phase = wave / kKvTiles;           // which unit of every step this wave takes
   const int key0 = chunk * 64 + tile * 16;     // the tile's first key (position in the sequence)
   const bool active = key0 < a.T;              // every wave reaches the barriers below
-  const int blk = active ? key0 / a.bs : 0;    // the block holding the tile
+  const int blk0 = chunk * 64 / a.bs;          // the chunk's first key block
+  const int nblk = a.bs >= 64 ? 1 : 64 / a.bs; // key blocks in the chunk (bs = 32: two)
+  const int tblk = a.bs >= 64 ? 0 : tile * 16 / a.bs;   // the tile's block among them
+  const int64_t tok_base = (int64_t)b * a.T;
 
-  // K and V rows of the tile as B operands (lane (c, g): key row c, d = 32 kk + 8 g)
+  // the reader list: tokens t >= the chunk's first key in the segment that
+  // read any of the chunk's blocks, in token order (wave 0; <= 32 words)
+  if (wave == 0) {
+    const int t_lo = max(chunk * 64, seg_lo);  // a multiple of 32
+    const int w_lo = t_lo / 32;
+    const int nwd = (seg_hi + 31) / 32 - w_lo;
+    const int wi = w_lo + lane;
+    uint32_t per0 = 0u, per1 = 0u;             // the words of the chunk's first and second block
+    if (lane < nwd) {
+      const uint32_t* rb = a.readers + (((int64_t)b * a.Hkv + h) * a.nb + blk0) * a.nw + wi;
+      per0 = rb[0];
+      if (nblk > 1 && blk0 + 1 < a.nb) per1 = rb[a.nw];
+      if (wi == (seg_hi - 1) / 32 && (seg_hi & 31) != 0) {
+        const uint32_t m = 0xFFFFFFFFu >> (32 - (seg_hi & 31));
+        per0 &= m;
+        per1 &= m;
+      }
+    }
+    uint32_t any = per0 | per1;
+    const int cnt = __builtin_popcount(any);
+    int incl = cnt;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += y;
+    }
+    int pos = incl - cnt;
+    while (any != 0u) {
+      const int bit = __builtin_ctz(any);
+      any &= any - 1u;
+      const int t = wi * 32 + bit;
+      rlist[pos++] = (uint16_t)((t - seg_lo) | (((per0 >> bit) & 1u) << 10) | (((per1 >> bit) & 1u) << 11));
+    }
+    if (lane == 63) nread_s = incl;
+  }
+  __syncthreads();
+  const int nunits = nread_s * a.gpk;          // (reader, head group) pairs, reader-major
+  const int nsteps = (nunits + kKvPhases - 1) / kKvPhases;
+
   f32x4 dk[DT], dv[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; dt++) {
     dk[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     dv[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  if (active) {
-  const __bf16* __restrict__ Kp = reinterpret_cast<const __bf16*>(a.k);
-  const __bf16* __restrict__ Vp = reinterpret_cast<const __bf16*>(a.v);
-  const int key = key0 + c;
-  const bool kvalid = key < a.T;
-  const int64_t krow = (((int64_t)b * a.T + (kvalid ? key : key0)) * a.Hkv + h) * D;
-  bf16x8 kf[KT], vf[KT];
+  if (nsteps > 0) {
+    // K and V rows of the tile as B operands (lane (c, g): key row c, d = 32 kk + 8 g)
+    const __bf16* __restrict__ Kp = reinterpret_cast<const __bf16*>(a.k);
+    const __bf16* __restrict__ Vp = reinterpret_cast<const __bf16*>(a.v);
+    const int key = key0 + c;
+    const bool kvalid = active && key < a.T;
+    const int64_t krow = ((tok_base + (kvalid ? key : 0)) * a.Hkv + h) * D;
+    bf16x8 kf[KT], vf[KT];
 #pragma unroll
-  for (int kk = 0; kk < KT; kk++) {
-    kf[kk] = *reinterpret_cast<const bf16x8*>(Kp + krow + kk * 32 + g * 8);
-    vf[kk] = *reinterpret_cast<const bf16x8*>(Vp + krow + kk * 32 + g * 8);
-  }
-  const __bf16* __restrict__ Q = reinterpret_cast<const __bf16*>(a.q);
-  const __bf16* __restrict__ dO = reinterpret_cast<const __bf16*>(a.dout);
-  NSA_LDS char* qs = (NSA_LDS char*)&slot[wave][0][0];
-  NSA_LDS char* ds = (NSA_LDS char*)&slot[wave][1][0];
-  const float sl = a.scale_log2;
+    for (int kk = 0; kk < KT; kk++) {
+      kf[kk] = *reinterpret_cast<const bf16x8*>(Kp + krow + kk * 32 + g * 8);
+      vf[kk] = *reinterpret_cast<const bf16x8*>(Vp + krow + kk * 32 + g * 8);
+    }
+    const float sl = a.scale_log2;
 
-  // the tile's readers, in token order: bits t >= key0 of the block's
-  // reader bitmap inside this segment (64 words of 32 tokens per pass, lane
-  // i holding word i); every kKvPhases-th reader belongs to this wave
-  const uint32_t* rbits = a.readers + (((int64_t)b * a.Hkv + h) * a.nb + blk) * a.nw;
-  int seen = 0;                                // readers met so far (the same in every lane)
-  const int t_lo = max(key0, seg_lo);          // this wave's tokens: [t_lo, seg_hi)
-  const int w_hi = (seg_hi + 31) / 32;
-  for (int w0 = t_lo / 32; w0 < w_hi; w0 += 64) {
-    const int wi = w0 + lane;
-    uint32_t word = wi < w_hi ? rbits[wi] : 0u;
-    if (wi == t_lo / 32) word &= 0xFFFFFFFFu << (t_lo & 31);
-    if (wi == (seg_hi - 1) / 32 && (seg_hi & 31) != 0) word &= 0xFFFFFFFFu >> (32 - (seg_hi & 31));
-    uint64_t lanes = __ballot(word != 0u);
-    while (lanes != 0ull) {
-      const int l = __builtin_ctzll(lanes);
-      lanes &= lanes - 1ull;
-      uint32_t wl = (uint32_t)__builtin_amdgcn_readlane((int)word, l);
-      while (wl != 0u) {
-        const int t = (w0 + l) * 32 + __builtin_ctz(wl);
-        wl &= wl - 1u;
-        if ((seen++ % kKvPhases) != phase) continue;
-        const int64_t tok = (int64_t)b * a.T + t;
-        for (int grp = 0; grp < a.gpk; grp++) {
-          // Q_t, dO_t of the group's heads: A operands (lane (c, g): head c,
-          // d = 32 kk + 8 g), also written row-major to the slot for the
-          // transposed B reads; lse and Delta of heads 4 g .. 4 g + 3
-          const int hq = (h * a.gpk + grp) * a.gv + c;
-          const bool cvalid = c < a.gv;
-          const int64_t qrow = (tok * a.Hq + (cvalid ? hq : 0)) * D;
-          bf16x8 qa[KT], da[KT];
+    // one step's work for this wave: unit kKvPhases * step + phase, if it
+    // exists, reads the tile's block and reaches the tile's first key
+    auto compute = [&](NSA_LDS const char* buf, int step) __attribute__((always_inline)) {
+      const int u = kKvPhases * step + phase;
+      if (u >= nunits) return;
+      const int e = rlist[u / a.gpk];
+      const int t = seg_lo + (e & 1023);
+      if (!active || !((e >> (10 + tblk)) & 1) || key0 > t) return;
+      NSA_LDS const char* qs = buf + phase * U::kBytes;
+      NSA_LDS const char* ds = qs + U::kRows;
+      // Q_t, dO_t of the group's heads as A operands (lane (c, g): head c,
+      // d = 32 kk + 8 g); lse and Delta of heads 4 g .. 4 g + 3
+      bf16x8 qa[KT], da[KT];
 #pragma unroll
-          for (int kk = 0; kk < KT; kk++) {
-            if (cvalid) {
-              qa[kk] = *reinterpret_cast<const bf16x8*>(Q + qrow + kk * 32 + g * 8);
-              da[kk] = *reinterpret_cast<const bf16x8*>(dO + qrow + kk * 32 + g * 8);
-            } else {
-              qa[kk] = bf16x8{0, 0, 0, 0, 0, 0, 0, 0};
-              da[kk] = bf16x8{0, 0, 0, 0, 0, 0, 0, 0};
-            }
-            // 16-byte chunk 4 kk + g of head row c, XOR-swizzled by row (the
-            // forward's V-slot layout) so the writes and the transposed
-            // reads below are free of bank conflicts
-            const int ch = (kk * 4 + g) ^ v_swizzle<D>(c);
-            *(NSA_LDS bf16x8*)(qs + c * kRow + ch * 16) = qa[kk];
-            *(NSA_LDS bf16x8*)(ds + c * kRow + ch * 16) = da[kk];
-          }
-          float lse2[4], dl[4];
-          if (a.gv % 4 == 0) {
-            // heads 4 g .. 4 g + 3 are contiguous: one 16-byte load each
-            // (an index past the group's heads is clamped and masked below)
-            const bool gvalid = g * 4 < a.gv;
-            const int64_t li = tok * a.Hq + (h * a.gpk + grp) * a.gv + (gvalid ? g * 4 : 0);
-            const f32x4 l4 = *reinterpret_cast<const f32x4*>(a.lse + li);
-            const f32x4 d4 = *reinterpret_cast<const f32x4*>(a.delta + li);
-#pragma unroll
-            for (int jj = 0; jj < 4; jj++) {
-              lse2[jj] = gvalid ? l4[jj] * 1.4426950408889634f : INFINITY;
-              dl[jj] = gvalid ? d4[jj] : 0.f;
-            }
-          } else {
-#pragma unroll
-            for (int jj = 0; jj < 4; jj++) {
-              const int hh = g * 4 + jj;
-              const bool hv = hh < a.gv;
-              const int64_t li = tok * a.Hq + (h * a.gpk + grp) * a.gv + (hv ? hh : 0);
-              lse2[jj] = hv ? a.lse[li] * 1.4426950408889634f : INFINITY;
-              dl[jj] = hv ? a.delta[li] : 0.f;
-            }
-          }
-          // S = Q K^T and dP = dO V^T: lane (c, g) holds heads 4 g + jj of key c
-          f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f}, pacc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int kk = 0; kk < KT; kk++) {
-            sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[kk], kf[kk], sacc, 0, 0, 0);
-            pacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(da[kk], vf[kk], pacc, 0, 0, 0);
-          }
-          bf16x4 pa, sa;
-#pragma unroll
-          for (int jj = 0; jj < 4; jj++) {
-            const float p = (key > t) ? 0.f : fast_exp2(__builtin_fmaf(sacc[jj], sl, -lse2[jj]));
-            pa[jj] = (__bf16)p;
-            sa[jj] = (__bf16)(p * (pacc[jj] - dl[jj]));
-          }
-          // dV += P^T dO, dK += dS^T Q; B operands (heads 4 g .. + 3 at d =
-          // 16 dt + c) read transposed from the slot
-          __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the slot rows are written
-#pragma unroll
-          for (int dt = 0; dt < DT; dt++) {
-            const int row = g * 4 + (c >> 2);
-            const int d0 = dt * 16 + (c & 3) * 4;
-            const int off = row * kRow + ((d0 >> 3) ^ v_swizzle<D>(row)) * 16 + (d0 & 7) * 2;
-            const bf16x4 qb = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((NSA_LDS s16x4*)(qs + off)));
-            const bf16x4 db = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((NSA_LDS s16x4*)(ds + off)));
-            dv[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, db, dv[dt], 0, 0, 0);
-            dk[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(sa, qb, dk[dt], 0, 0, 0);
-          }
-          __builtin_amdgcn_s_waitcnt(0xC07F);   // the slot reads have returned before it is rewritten
-        }
+      for (int kk = 0; kk < KT; kk++) {
+        const int ch = (kk * 4 + g) ^ v_swizzle<D>(c);
+        qa[kk] = *(NSA_LDS const bf16x8*)(qs + c * kRow + ch * 16);
+        da[kk] = *(NSA_LDS const bf16x8*)(ds + c * kRow + ch * 16);
       }
+      const f32x4 l4 = *(NSA_LDS const f32x4*)(qs + 2 * U::kRows + g * 16);
+      const f32x4 d4 = *(NSA_LDS const f32x4*)(qs + 2 * U::kRows + 64 + g * 16);
+      // S = Q K^T and dP = dO V^T: lane (c, g) holds heads 4 g + jj of key c
+      f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f}, pacc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < KT; kk++) {
+        sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[kk], kf[kk], sacc, 0, 0, 0);
+        pacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(da[kk], vf[kk], pacc, 0, 0, 0);
+      }
+      bf16x4 pa, sa;
+#pragma unroll
+      for (int jj = 0; jj < 4; jj++) {
+        const float p = (key > t) ? 0.f : fast_exp2(__builtin_fmaf(sacc[jj], sl, -l4[jj] * 1.4426950408889634f));
+        pa[jj] = (__bf16)p;
+        sa[jj] = (__bf16)(p * (pacc[jj] - d4[jj]));
+      }
+      // dV += P^T dO, dK += dS^T Q; B operands (heads 4 g .. + 3 at d =
+      // 16 dt + c) read transposed from the slot
+#pragma unroll
+      for (int dt = 0; dt < DT; dt++) {
+        const int row = g * 4 + (c >> 2);
+        const int d0 = dt * 16 + (c & 3) * 4;
+        const int off = row * kRow + ((d0 >> 3) ^ v_swizzle<D>(row)) * 16 + (d0 & 7) * 2;
+        const bf16x4 qb = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((NSA_LDS s16x4*)(qs + off)));
+        const bf16x4 db = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((NSA_LDS s16x4*)(ds + off)));
+        dv[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, db, dv[dt], 0, 0, 0);
+        dk[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(sa, qb, dk[dt], 0, 0, 0);
+      }
+    };
+
+    // software pipeline over steps: the workgroup loads step s + 2 into
+    // registers while it computes step s from one LDS buffer, then stores
+    // step s + 1 into the other; one barrier per step
+    NSA_LDS char* buf0 = (NSA_LDS char*)&slot[0][0];
+    NSA_LDS char* buf1 = (NSA_LDS char*)&slot[1][0];
+    KvStage<D> s0, s1;
+    kv_stage_load<D>(a, rlist, nunits, seg_lo, tok_base, h, tid, 0, s0);
+    kv_stage_load<D>(a, rlist, nunits, seg_lo, tok_base, h, tid, 1, s1);
+    kv_stage_store<D>(a, buf0, tid, s0);
+    lds_barrier();
+    for (int step = 0; step < nsteps; step += 2) {
+      kv_stage_load<D>(a, rlist, nunits, seg_lo, tok_base, h, tid, step + 2, s0);
+      compute(buf0, step);
+      kv_stage_store<D>(a, buf1, tid, s1);
+      lds_barrier();
+      kv_stage_load<D>(a, rlist, nunits, seg_lo, tok_base, h, tid, step + 3, s1);
+      compute(buf1, step + 1);
+      kv_stage_store<D>(a, buf0, tid, s0);
+      lds_barrier();
     }
   }
-  }  // active
   // the phases' sums meet in LDS in a fixed order (deterministic)
   __syncthreads();
   if (phase == 1 && active) {
@@ -486,7 +603,7 @@ __global__ void __launch_bounds__(64 * kKvTiles * kKvPhases) bwd_dkdv_kernel(Bwd
   for (int jj = 0; jj < 4; jj++) {
     const int kr = key0 + g * 4 + jj;
     if (kr >= a.T) continue;
-    const int64_t o = (((int64_t)b * a.T + kr) * a.Hkv + h) * D;
+    const int64_t o = ((tok_base + kr) * a.Hkv + h) * D;
 #pragma unroll
     for (int dt = 0; dt < DT; dt++) {
       pk[o + dt * 16 + c] = dk[dt][jj] + red[tile][0][(dt * 4 + jj) * 64 + lane];

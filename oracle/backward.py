@@ -91,3 +91,41 @@ def dq_rows(q, k, v, dout, block_indices, block_counts, block_size, scale, token
                 ds = p * (dp - p @ dp)
                 out[r, hq] = scale * (ds @ K)
     return out
+
+
+def dkdv_blocks(q, k, v, dout, block_indices, block_counts, block_size, scale, blocks):
+    """dK and dV of the keys of the listed key blocks only, float64
+    [n, block_size, D] each, for ``blocks`` = [(b, kv head, block), ...]
+    (rows of keys past the sequence end stay zero).  A key's gradients
+    gather the (token, query head) rows that see it: the rows whose kept
+    entries (the first clamp(count, 0, S), 0 <= entry <= own block) hold its
+    block; each such row contributes exactly its terms in ``bwd``."""
+    B, T, Hq, D = np.shape(q)
+    Hkv = np.shape(k)[2]
+    S = block_indices.shape[-1]
+    G = Hq // Hkv
+    bs = block_size
+    dk = np.zeros((len(blocks), bs, D))
+    dv = np.zeros((len(blocks), bs, D))
+    for r, (b, h, j) in enumerate(blocks):
+        lo = j * bs
+        for t in range(lo, T):
+            n = max(0, min(int(block_counts[b, t, h]), S))
+            listed = sorted({int(e) for e in block_indices[b, t, h, :n] if 0 <= int(e) <= t // bs})
+            if j not in listed:
+                continue
+            keys = np.concatenate([np.arange(e * bs, min((e + 1) * bs, t + 1)) for e in listed])
+            K = np.asarray(k[b, keys, h], np.float64)
+            V = np.asarray(v[b, keys, h], np.float64)
+            Qg = np.asarray(q[b, t, h * G:(h + 1) * G], np.float64)        # [G, D]
+            dO = np.asarray(dout[b, t, h * G:(h + 1) * G], np.float64)
+            z = scale * (Qg @ K.T)                                         # [G, n]
+            p = np.exp(z - z.max(axis=1, keepdims=True))
+            p /= p.sum(axis=1, keepdims=True)
+            dp = dO @ V.T
+            ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+            sel = (keys // bs) == j
+            at = keys[sel] - lo
+            dv[r, at] += p[:, sel].T @ dO
+            dk[r, at] += scale * (ds[:, sel].T @ Qg)
+    return dk, dv

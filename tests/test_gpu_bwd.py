@@ -42,7 +42,7 @@ def run_bwd(w, dout_bits):
 
 
 def check(name, got, ref):
-    g = got.cpu().numpy().astype(np.float64)
+    g = (got.cpu().numpy() if hasattr(got, "cpu") else got).astype(np.float64)
     err = np.abs(g - ref)
     scale = float(np.abs(ref).max(initial=0))
     ok = np.all(err <= 1e-2 * scale + 1e-2 * np.abs(ref))
@@ -114,3 +114,41 @@ def test_bwd_named_workload_full_size(cfg):
     assert np.all(err_v <= 1e-2 * dv_abs + 1e-3)
     assert np.all(np.abs(dks) <= 1e-2 * dk_abs + 1e-3)
     assert bool(dq.isfinite().all() and dk.isfinite().all() and dv.isfinite().all())
+    # dK, dV of sampled key blocks against the oracle: block 0 (read by
+    # every token: every token segment contributes), the last block and a
+    # few in between
+    nb = (w.T + w.block_size - 1) // w.block_size
+    rng = np.random.default_rng(cfg)
+    blocks = [(0, 0, 0), (w.B - 1, w.Hkv - 1, nb - 1)]
+    blocks += [(int(rng.integers(w.B)), int(rng.integers(w.Hkv)), int(rng.integers(1, nb))) for _ in range(3)]
+    _check_blocks(w, dout, dk, dv, blocks, f"config {cfg}")
+
+
+def _check_blocks(w, dout, dk, dv, blocks, what):
+    _say(f"[bwd] {what}: oracle dK, dV of key blocks {blocks}")
+    rk, rv = obwd.dkdv_blocks(w.q, w.k, w.v, dout, w.block_indices, w.block_counts, w.block_size, w.scale, blocks)
+    bs = w.block_size
+    gk = np.zeros_like(rk)
+    gv = np.zeros_like(rv)
+    dk_ = dk.cpu().numpy()
+    dv_ = dv.cpu().numpy()
+    for r, (b, h, j) in enumerate(blocks):
+        n = min(bs, w.T - j * bs)
+        gk[r, :n] = dk_[b, j * bs:j * bs + n, h]
+        gv[r, :n] = dv_[b, j * bs:j * bs + n, h]
+    check(f"{what} dk blocks", gk, rk)
+    check(f"{what} dv blocks", gv, rv)
+
+
+def test_bwd_segments_deterministic():
+    """T = 2500 with an attention-sink block: block 0 is read by tokens in
+    three token segments, whose partial sums the reduction adds in order.
+    Two calls give bitwise-equal gradients; sampled blocks match the oracle."""
+    import torch
+    _say("[bwd] segments and determinism")
+    w = ni.make_workload("bwd_seg", "bf16", [2500], 16, 1, 128, 64, 8, "sink_local_random", "uniform", seed=29)
+    dout, dbits = _dout(w, 29)
+    dq, dk, dv = run_bwd(w, dbits)
+    dq2, dk2, dv2 = run_bwd(w, dbits)
+    assert torch.equal(dq, dq2) and torch.equal(dk, dk2) and torch.equal(dv, dv2)
+    _check_blocks(w, dout, dk, dv, [(0, 0, 0), (0, 0, 1), (0, 0, 15), (0, 0, 20), (0, 0, 39)], "bwd_seg")

@@ -477,3 +477,23 @@ def test_gradient_rows_match_full_gradients():
     rows = np.array([0, 7, 29, 30, 45, 59])
     got = obwd.dq_rows(w.q, w.k, w.v, dout, w.block_indices, w.block_counts, w.block_size, w.scale, rows)
     np.testing.assert_allclose(got, dq.reshape(-1, w.Hq, w.D)[rows], rtol=0, atol=1e-13)
+
+
+def test_block_gradients_match_full_gradients():
+    """The per-block dK/dV against the full gradients, with repeated,
+    negative and out-of-range entries, counts outside [0, S] and a ragged
+    last block (T = 30, block size 4)."""
+    w = ni.make_workload("gb", "f32", [30, 30], 4, 2, 8, 4, 5, "sink_local_random", "uniform", seed=16)
+    rng = np.random.default_rng(4)
+    w.block_indices = rng.integers(-2, 9, size=w.block_indices.shape).astype(np.int32)
+    w.block_counts = rng.integers(-1, 7, size=w.block_counts.shape).astype(np.int32)
+    dout = rng.standard_normal(w.q.shape)
+    _, dk, dv = obwd.bwd(w.q, w.k, w.v, dout, w.block_indices, w.block_counts, w.block_size, w.scale)
+    blocks = [(0, 0, 0), (0, 1, 3), (1, 0, 5), (1, 1, 7), (0, 1, 7)]
+    gk, gv = obwd.dkdv_blocks(w.q, w.k, w.v, dout, w.block_indices, w.block_counts, w.block_size, w.scale, blocks)
+    for r, (b, h, j) in enumerate(blocks):
+        n = min(4, 30 - 4 * j)
+        np.testing.assert_allclose(gk[r, :n], dk[b, 4 * j:4 * j + n, h], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(gv[r, :n], dv[b, 4 * j:4 * j + n, h], rtol=0, atol=1e-12)
+        assert np.all(gk[r, n:] == 0) and np.all(gv[r, n:] == 0)
+    assert sum(bool(np.any(gv[r] != 0)) for r in range(len(blocks))) >= 3

@@ -9,10 +9,11 @@
 //
 // dq kernel: one workgroup of kBwdWaves waves per (token, kv head, group of
 // <= 16 query heads), the token's kept blocks dealt in 32-key units to the
-// waves like the decode kernel: K and V rows go straight into registers as
-// the A operands of S^T = K Q^T and dP^T = V dO^T, the K rows are also
-// written to the wave's LDS slot and read back transposed (ds_read_b64_tr_b16)
-// as the A operand of dQ^T += K^T dS^T.  The waves' partial dQ are summed
+// waves like the decode kernel: each wave loads a unit's K and V rows whole
+// (every load instruction reads complete rows) into registers one unit
+// ahead, stores them into its LDS slot and reads back the A operands of
+// S^T = K Q^T and dP^T = V dO^T, and K transposed (ds_read_b64_tr_b16) as
+// the A operand of dQ^T += K^T dS^T.  The waves' partial dQ are summed
 // through LDS.  The kernel also writes Delta for the dk/dv kernel.
 //
 // readers kernel: a bitmap over tokens per (sequence, kv head, key block)
@@ -82,7 +83,8 @@ bwd_dq_kernel(BwdArgs a) {
   constexpr int DT = D / 16;
   constexpr int kHalf = KB * D * 2;
   static_assert(16 * D * 4 <= kHalf, "the merge buffer fits a slot");
-  __shared__ __attribute__((aligned(1024))) char kslot[kBwdWaves][kHalf];
+  // per wave: the unit's K rows, then its V rows (row-major, swizzled)
+  __shared__ __attribute__((aligned(1024))) char kslot[kBwdWaves][2 * kHalf];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -164,19 +166,25 @@ bwd_dq_kernel(BwdArgs a) {
   const int row_bytes = a.Hkv * D * 2;
   const int64_t kv_bytes = (int64_t)a.B * a.T * row_bytes;
   const int b = bt / a.T;
-  const uint32_t koff = (uint32_t)(c * row_bytes + g * 16);
+  // a unit's rows are loaded whole: load l of a lane covers row l * kRpi +
+  // lane / (D / 8), 16-byte chunk lane % (D / 8), so each load instruction
+  // reads kRpi complete rows (full cache lines)
+  constexpr int kRpi = 64 / (D / 8);
+  constexpr int kNl = KB / kRpi;
+  static_assert(kNl == MT * KT, "one register per A fragment");
+  const int lrow = lane / (D / 8);
+  const int lch = lane % (D / 8);
+  const uint32_t loff = (uint32_t)(lrow * row_bytes + lch * 16);
   auto unit_base = [&](int ks) -> int64_t { return (((int64_t)b * a.T + ks) * a.Hkv + h) * (D * 2); };
-  u32x4 kreg[MT * KT], vreg[MT * KT];
-  auto load_rows = [&](const char* base, int64_t rb, u32x4 (&r)[MT * KT]) {
+  u32x4 kreg[kNl], vreg[kNl];
+  auto load_rows = [&](const char* base, int64_t rb, u32x4 (&r)[kNl]) {
+    const __amdgpu_buffer_rsrc_t rs = group_rsrc(base, rb, kv_bytes);
 #pragma unroll
-    for (int mt = 0; mt < MT; mt++) {
-      const __amdgpu_buffer_rsrc_t rs = group_rsrc(base, rb + (int64_t)mt * 16 * row_bytes, kv_bytes);
-#pragma unroll
-      for (int kk = 0; kk < KT; kk++)
-        r[mt * KT + kk] = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(koff + kk * 64), 0, 0);
-    }
+    for (int l = 0; l < kNl; l++)
+      r[l] = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(loff + l * kRpi * row_bytes), 0, 0);
   };
   NSA_LDS char* kl = (NSA_LDS char*)&kslot[wave][0];
+  NSA_LDS char* vl = kl + kHalf;
 
   f32x4 o[DT];
 #pragma unroll
@@ -186,33 +194,41 @@ bwd_dq_kernel(BwdArgs a) {
   auto step = [&]<bool kMore>(int i) __attribute__((always_inline)) {
     const int ks = __builtin_amdgcn_readlane(my_ks, i);
     const int64_t rb_n = kMore ? unit_base(__builtin_amdgcn_readlane(my_ks, i + 1)) : 0;
-    // K rows into the slot for the transposed reads (lane (c, g): key row
-    // 16 mt + c, 16-byte chunk 4 kk + g)
+    // the unit's K and V rows into the slot, row-major with 16-byte chunks
+    // XOR-swizzled by row (conflict-free writes, A-operand reads and
+    // transposed reads)
 #pragma unroll
-    for (int mt = 0; mt < MT; mt++) {
-      const int key = mt * 16 + c;
-#pragma unroll
-      for (int kk = 0; kk < KT; kk++) {
-        const int ch = (kk * 4 + g) ^ v_swizzle<D>(key);
-        *(NSA_LDS u32x4*)(kl + key * (D * 2) + ch * 16) = kreg[mt * KT + kk];
-      }
+    for (int l = 0; l < kNl; l++) {
+      const int key = l * kRpi + lrow;
+      const int off = key * (D * 2) + ((lch ^ v_swizzle<D>(key)) * 16);
+      *(NSA_LDS u32x4*)(kl + off) = kreg[l];
+      *(NSA_LDS u32x4*)(vl + off) = vreg[l];
     }
+    // the next unit's loads go out as soon as the registers are free (not
+    // before the stores: the two register sets would not fit)
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (kMore) {
+      load_rows(Kc, rb_n, kreg);
+      load_rows(Vc, rb_n, vreg);
+    }
+    // S^T = K Q^T and dP^T = V dO^T; A fragments (lane (c, g): key row
+    // 16 mt + c, 16-byte chunk 4 kk + g) read back from the slot
     f32x4 s[MT], dp[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; mt++) {
       s[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
       dp[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const int key = mt * 16 + c;
 #pragma unroll
       for (int kk = 0; kk < KT; kk++) {
-        s[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kreg[mt * KT + kk]), qf[kk],
-                                                        s[mt], 0, 0, 0);
-        dp[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vreg[mt * KT + kk]), df[kk],
-                                                         dp[mt], 0, 0, 0);
+        const int off = key * (D * 2) + (((kk * 4 + g) ^ v_swizzle<D>(key)) * 16);
+        const bf16x8 ka = *(NSA_LDS const bf16x8*)(kl + off);
+        const bf16x8 va = *(NSA_LDS const bf16x8*)(vl + off);
+        s[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[kk], s[mt], 0, 0, 0);
+        dp[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, df[kk], dp[mt], 0, 0, 0);
       }
-    }
-    if constexpr (kMore) {
-      load_rows(Kc, rb_n, kreg);
-      load_rows(Vc, rb_n, vreg);
+      // one 16-key tile's fragments live at a time (register budget)
+      __builtin_amdgcn_sched_barrier(0);
     }
     // P^T = exp2(S^T sl - lse2) (zero where masked), dS^T = P^T (dP^T - Delta)
 #pragma unroll

@@ -537,8 +537,11 @@ __global__ void __launch_bounds__(64 * kKvTiles * kKvPhases) bwd_dkdv_kernel(Bwd
       if (!active || !((e >> (10 + tblk)) & 1) || key0 > t) return;
       NSA_LDS const char* qs = buf + phase * U::kBytes;
       NSA_LDS const char* ds = qs + U::kRows;
-      // Q_t, dO_t of the group's heads as A operands (lane (c, g): head c,
-      // d = 32 kk + 8 g); lse and Delta of heads 4 g .. 4 g + 3
+      // every LDS read of the step goes out first, so their latencies
+      // overlap: Q_t, dO_t of the group's heads as A operands (lane (c, g):
+      // head c, d = 32 kk + 8 g), lse and Delta of heads 4 g .. 4 g + 3, and
+      // the B operands of dV and dK (heads 4 g .. + 3 at d = 16 dt + c)
+      // read transposed
       bf16x8 qa[KT], da[KT];
 #pragma unroll
       for (int kk = 0; kk < KT; kk++) {
@@ -548,6 +551,16 @@ __global__ void __launch_bounds__(64 * kKvTiles * kKvPhases) bwd_dkdv_kernel(Bwd
       }
       const f32x4 l4 = *(NSA_LDS const f32x4*)(qs + 2 * U::kRows + g * 16);
       const f32x4 d4 = *(NSA_LDS const f32x4*)(qs + 2 * U::kRows + 64 + g * 16);
+      bf16x4 qb[DT], db[DT];
+#pragma unroll
+      for (int dt = 0; dt < DT; dt++) {
+        const int row = g * 4 + (c >> 2);
+        const int d0 = dt * 16 + (c & 3) * 4;
+        const int off = row * kRow + ((d0 >> 3) ^ v_swizzle<D>(row)) * 16 + (d0 & 7) * 2;
+        qb[dt] = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((NSA_LDS s16x4*)(qs + off)));
+        db[dt] = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((NSA_LDS s16x4*)(ds + off)));
+      }
+      __builtin_amdgcn_sched_barrier(0);
       // S = Q K^T and dP = dO V^T: lane (c, g) holds heads 4 g + jj of key c
       f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f}, pacc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -562,17 +575,11 @@ __global__ void __launch_bounds__(64 * kKvTiles * kKvPhases) bwd_dkdv_kernel(Bwd
         pa[jj] = (__bf16)p;
         sa[jj] = (__bf16)(p * (pacc[jj] - d4[jj]));
       }
-      // dV += P^T dO, dK += dS^T Q; B operands (heads 4 g .. + 3 at d =
-      // 16 dt + c) read transposed from the slot
+      // dV += P^T dO, dK += dS^T Q
 #pragma unroll
       for (int dt = 0; dt < DT; dt++) {
-        const int row = g * 4 + (c >> 2);
-        const int d0 = dt * 16 + (c & 3) * 4;
-        const int off = row * kRow + ((d0 >> 3) ^ v_swizzle<D>(row)) * 16 + (d0 & 7) * 2;
-        const bf16x4 qb = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((NSA_LDS s16x4*)(qs + off)));
-        const bf16x4 db = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((NSA_LDS s16x4*)(ds + off)));
-        dv[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, db, dv[dt], 0, 0, 0);
-        dk[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(sa, qb, dk[dt], 0, 0, 0);
+        dv[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, db[dt], dv[dt], 0, 0, 0);
+        dk[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(sa, qb[dt], dk[dt], 0, 0, 0);
       }
     };
 

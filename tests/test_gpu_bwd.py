@@ -56,6 +56,9 @@ CASES = [
     ("bwd_g4_d64_bs32", 1, 200, 8, 2, 64, 32, 5, "shuffled", "uniform"),
     ("bwd_g1_d128_bs128", 1, 300, 2, 2, 128, 128, 3, "local_random", "full"),
     ("bwd_g32_d64_bs64", 1, 150, 32, 1, 64, 64, 3, "sink_local_random", "full"),
+    # two token segments, two key blocks per 64-key chunk, two head groups,
+    # a ragged last chunk
+    ("bwd_g32_d128_bs32_T1100", 1, 1100, 64, 2, 128, 32, 8, "sink_local_random", "uniform"),
 ]
 
 

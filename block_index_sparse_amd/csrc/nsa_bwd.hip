@@ -48,7 +48,11 @@ using namespace dev;
 constexpr int kBwdWaves = 4;
 constexpr int kKvTiles = 4;    // 16-key tiles per dk/dv workgroup (a 64-key chunk)
 constexpr int kKvPhases = 2;   // waves per tile, taking alternate readers
-constexpr int kSegTokens = 1024;   // readers of a chunk are split into segments of this many tokens
+constexpr int kSegMax = 2048;   // readers of a chunk are split into token segments of at most this many tokens
+
+// the segment length: 1024 tokens, 2048 past 8192 (fewer workgroups and partial sums where
+// every segment still has many workgroups)
+inline int seg_tokens(int T) { return T > 8192 ? 2048 : 1024; }
 
 struct BwdArgs {
   const void* q;          // [B, T, Hq, D] bf16
@@ -65,7 +69,7 @@ struct BwdArgs {
   float* delta;           // [B, T, Hq] workspace
   uint32_t* readers;      // [B, Hkv, nb, nw] workspace: bit t of block j = token t reads j
   float* part;            // [ns][2][B, T, Hkv, D] workspace: per token segment, dK (unscaled) and dV
-  int32_t B, T, Hq, Hkv, S, bs, G, gv, gpk, nb, nw, ns;
+  int32_t B, T, Hq, Hkv, S, bs, G, gv, gpk, nb, nw, ns, seg;   // seg: tokens per segment
   float scale;
   float scale_log2;
 };
@@ -363,7 +367,7 @@ __device__ __forceinline__ void kv_stage_load(const BwdArgs& a, const uint16_t* 
     // past the last unit or the group's heads: a clamped in-bounds address
     // (the value is replaced by zeros or never read)
     const int u = min(kKvPhases * step + unit, nunits - 1);
-    const int t = seg_lo + (rlist[u / a.gpk] & 1023);
+    const int t = seg_lo + (rlist[u / a.gpk] & 2047);
     const int hq = (h * a.gpk + u % a.gpk) * a.gv + min(row, a.gv - 1);
     const __bf16* src = rem < U::kChunks ? Q : dO;
     st.v[l] = *reinterpret_cast<const u32x4*>(src + ((tok_base + t) * a.Hq + hq) * D + ck * 8);
@@ -371,7 +375,7 @@ __device__ __forceinline__ void kv_stage_load(const BwdArgs& a, const uint16_t* 
   // lanes 0..63: unit (tid / 32) % 2, lse or Delta ((tid / 16) % 2), head tid % 16
   const int unit = (tid >> 5) & 1;
   const int u = min(kKvPhases * step + unit, nunits - 1);
-  const int t = seg_lo + (rlist[u / a.gpk] & 1023);
+  const int t = seg_lo + (rlist[u / a.gpk] & 2047);
   const int hq = (h * a.gpk + u % a.gpk) * a.gv + min(tid & 15, a.gv - 1);
   st.f = ((tid >> 4) & 1 ? a.delta : a.lse)[(tok_base + t) * a.Hq + hq];
 }
@@ -422,9 +426,9 @@ __global__ void __launch_bounds__(64 * kKvTiles * kKvPhases) bwd_dkdv_kernel(Bwd
   __shared__ __attribute__((aligned(1024))) char slot[2][kKvPhases * U::kBytes];
   // the second phase's accumulators, lane-contiguous: [tile][dk, dv][dt * 4 + jj][lane]
   __shared__ float red[kKvTiles][2][DT * 4 * 64];
-  // the chunk's readers in the segment: token - segment start (bits 0..9),
-  // and which of the chunk's key blocks the token reads (bits 10, 11)
-  __shared__ uint16_t rlist[kSegTokens];
+  // the chunk's readers in the segment: token - segment start (bits 0..10),
+  // and which of the chunk's key blocks the token reads (bits 11, 12)
+  __shared__ uint16_t rlist[kSegMax];
   __shared__ int nread_s;
 
   const int tid = threadIdx.x;
@@ -449,10 +453,10 @@ __global__ void __launch_bounds__(64 * kKvTiles * kKvPhases) bwd_dkdv_kernel(Bwd
     chunk = 1 + i % rest;
     r = i / rest;
   }
-  const int seg = r % a.ns;                    // token segment [seg * kSegTokens, + kSegTokens)
+  const int seg = r % a.ns;                    // token segment [seg * a.seg, + a.seg)
   const int bh = r / a.ns;
-  const int seg_lo = seg * kSegTokens;
-  const int seg_hi = min(seg_lo + kSegTokens, a.T);
+  const int seg_lo = seg * a.seg;
+  const int seg_hi = min(seg_lo + a.seg, a.T);
   // a segment that ends at or before the chunk's first key has no reader:
   // the whole workgroup leaves (and the reduction skips it by the same rule)
   if (seg_hi <= chunk * 64) return;
@@ -468,7 +472,7 @@ __global__ void __launch_bounds__(64 * kKvTiles * kKvPhases) bwd_dkdv_kernel(Bwd
   const int64_t tok_base = (int64_t)b * a.T;
 
   // the reader list: tokens t >= the chunk's first key in the segment that
-  // read any of the chunk's blocks, in token order (wave 0; <= 32 words)
+  // read any of the chunk's blocks, in token order (wave 0; <= 64 words)
   if (wave == 0) {
     const int t_lo = max(chunk * 64, seg_lo);  // a multiple of 32
     const int w_lo = t_lo / 32;
@@ -498,7 +502,7 @@ __global__ void __launch_bounds__(64 * kKvTiles * kKvPhases) bwd_dkdv_kernel(Bwd
       const int bit = __builtin_ctz(any);
       any &= any - 1u;
       const int t = wi * 32 + bit;
-      rlist[pos++] = (uint16_t)((t - seg_lo) | (((per0 >> bit) & 1u) << 10) | (((per1 >> bit) & 1u) << 11));
+      rlist[pos++] = (uint16_t)((t - seg_lo) | (((per0 >> bit) & 1u) << 11) | (((per1 >> bit) & 1u) << 12));
     }
     if (lane == 63) nread_s = incl;
   }
@@ -533,8 +537,8 @@ __global__ void __launch_bounds__(64 * kKvTiles * kKvPhases) bwd_dkdv_kernel(Bwd
       const int u = kKvPhases * step + phase;
       if (u >= nunits) return;
       const int e = rlist[u / a.gpk];
-      const int t = seg_lo + (e & 1023);
-      if (!active || !((e >> (10 + tblk)) & 1) || key0 > t) return;
+      const int t = seg_lo + (e & 2047);
+      if (!active || !((e >> (11 + tblk)) & 1) || key0 > t) return;
       NSA_LDS const char* qs = buf + phase * U::kBytes;
       NSA_LDS const char* ds = qs + U::kRows;
       // every LDS read of the step goes out first, so their latencies
@@ -645,7 +649,7 @@ __global__ void __launch_bounds__(256) bwd_reduce_kernel(BwdArgs a) {
   if (i4 * 4 >= plane) return;
   const int64_t rowi = i4 * 4 / D;                               // (b * T + key) * Hkv + h
   const int key = (int)((rowi / a.Hkv) % a.T);
-  const int seg0 = (key / 64) * 64 / kSegTokens;                 // first segment ending after the chunk start
+  const int seg0 = (key / 64) * 64 / a.seg;                 // first segment ending after the chunk start
   f32x4 sk = f32x4{0.f, 0.f, 0.f, 0.f}, sv = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int sgi = seg0; sgi < a.ns; sgi++) {
     const float* pk = a.part + (int64_t)sgi * 2 * plane;
@@ -668,7 +672,7 @@ size_t bwd_readers_bytes(const BwdPlan& p) {
 }
 
 size_t bwd_workspace_bytes(const BwdPlan& p) {
-  const size_t ns = (size_t)(p.T + kSegTokens - 1) / kSegTokens;
+  const size_t ns = (size_t)(p.T + seg_tokens(p.T) - 1) / seg_tokens(p.T);
   return bwd_delta_bytes(p) + bwd_readers_bytes(p) + ns * 2 * (size_t)p.B * p.T * p.Hkv * p.D * sizeof(float);
 }
 
@@ -702,7 +706,8 @@ hipError_t launch_bwd(const BwdPlan& p, const void* q, const void* k, const void
   a.nw = (p.T + 31) / 32;
   a.readers = reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(delta) + bwd_delta_bytes(p));
   a.part = reinterpret_cast<float*>(reinterpret_cast<char*>(a.readers) + bwd_readers_bytes(p));
-  a.ns = (p.T + kSegTokens - 1) / kSegTokens;
+  a.seg = seg_tokens(p.T);
+  a.ns = (p.T + a.seg - 1) / a.seg;
   a.scale = scale;
   a.scale_log2 = scale * 1.4426950408889634f;
   const int64_t n_dq = (int64_t)p.B * p.T * p.Hkv * p.gpk;

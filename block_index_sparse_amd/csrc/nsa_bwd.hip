@@ -23,10 +23,11 @@
 // dkdv kernel: one workgroup per (sequence, kv head, 64-key chunk, token
 // segment), one wave per (16-key tile, phase).  Wave 0 turns the chunk's
 // reader bitmaps into a list of the segment's reader tokens, in token order
-// (so the sums are deterministic).  The workgroup then walks the list two
-// (reader, head group) units per step: all its lanes load the two units' Q_t,
-// dO_t, lse and Delta once into registers two steps ahead and store them into
-// one of two LDS buffers, and each wave takes the unit of its phase: it forms
+// (so the sums are deterministic).  The workgroup then walks the list four
+// (reader, head group) units per step: all its lanes load the four units'
+// Q_t, dO_t, lse and Delta once into registers two steps ahead and store them
+// into one of two LDS buffers, and each wave takes the two units of its
+// phase, one after the other: it forms
 // S = Q K^T and dP = dO V^T for its 16 keys (K and V rows in registers as B
 // operands), P and dS, and accumulates dV += P^T dO and dK += dS^T Q with
 // 16x16x16 MFMAs whose B operands (dO and Q, heads x d) are read transposed
@@ -48,6 +49,8 @@ using namespace dev;
 constexpr int kBwdWaves = 4;
 constexpr int kKvTiles = 4;    // 16-key tiles per dk/dv workgroup (a 64-key chunk)
 constexpr int kKvPhases = 2;   // waves per tile, taking alternate readers
+constexpr int kUnitsPerWave = 2;                       // units a wave takes per dk/dv step
+constexpr int kStepUnits = kKvPhases * kUnitsPerWave;  // (reader, head group) units per step
 constexpr int kSegMax = 2048;   // readers of a chunk are split into token segments of at most this many tokens
 
 // the segment length: 1024 tokens, 2048 past 8192 (fewer workgroups and partial sums where
@@ -337,7 +340,7 @@ struct KvUnit {
   static constexpr int kRows = 16 * kRow;             // Q (or dO) rows of 16 heads
   static constexpr int kBytes = 2 * kRows + 2 * 64;   // Q, dO, lse[16], Delta[16]
   static constexpr int kChunks = kRows / 16;          // 16-byte chunks of Q (or dO)
-  static constexpr int kStepChunks = kKvPhases * 2 * kChunks;
+  static constexpr int kStepChunks = kStepUnits * 2 * kChunks;
   static constexpr int kThreads = 64 * kKvTiles * kKvPhases;
   static constexpr int kLoads = kStepChunks / kThreads;   // 16-byte loads per lane per step
   static_assert(kStepChunks % kThreads == 0, "a step's chunks spread evenly over the workgroup");
@@ -366,15 +369,15 @@ __device__ __forceinline__ void kv_stage_load(const BwdArgs& a, const uint16_t* 
     const int ck = rem % (D / 8);
     // past the last unit or the group's heads: a clamped in-bounds address
     // (the value is replaced by zeros or never read)
-    const int u = min(kKvPhases * step + unit, nunits - 1);
+    const int u = min(kStepUnits * step + unit, nunits - 1);
     const int t = seg_lo + (rlist[u / a.gpk] & 2047);
     const int hq = (h * a.gpk + u % a.gpk) * a.gv + min(row, a.gv - 1);
     const __bf16* src = rem < U::kChunks ? Q : dO;
     st.v[l] = *reinterpret_cast<const u32x4*>(src + ((tok_base + t) * a.Hq + hq) * D + ck * 8);
   }
-  // lanes 0..63: unit (tid / 32) % 2, lse or Delta ((tid / 16) % 2), head tid % 16
-  const int unit = (tid >> 5) & 1;
-  const int u = min(kKvPhases * step + unit, nunits - 1);
+  // lanes 0 .. 32 kStepUnits - 1: unit tid / 32, lse or Delta ((tid / 16) % 2), head tid % 16
+  const int unit = (tid >> 5) % kStepUnits;
+  const int u = min(kStepUnits * step + unit, nunits - 1);
   const int t = seg_lo + (rlist[u / a.gpk] & 2047);
   const int hq = (h * a.gpk + u % a.gpk) * a.gv + min(tid & 15, a.gv - 1);
   st.f = ((tid >> 4) & 1 ? a.delta : a.lse)[(tok_base + t) * a.Hq + hq];
@@ -398,8 +401,8 @@ __device__ __forceinline__ void kv_stage_store(const BwdArgs& a, NSA_LDS char* b
     *(NSA_LDS u32x4*)(buf + unit * U::kBytes + (rem < U::kChunks ? 0 : U::kRows) + row * U::kRow +
                       ((ck ^ v_swizzle<D>(row)) * 16)) = row < a.gv ? st.v[l] : z;
   }
-  if (tid < 64) {
-    const int unit = (tid >> 5) & 1;
+  if (tid < 32 * kStepUnits) {
+    const int unit = tid >> 5;
     const int which = (tid >> 4) & 1;
     const int j = tid & 15;
     // a head past the group: lse = +inf makes its P zero, Delta = 0
@@ -422,8 +425,8 @@ __global__ void __launch_bounds__(64 * kKvTiles * kKvPhases) bwd_dkdv_kernel(Bwd
   constexpr int KT = D / 32;   // k-steps of S = Q K^T over d
   constexpr int DT = D / 16;   // 16-column d tiles of dK, dV
   constexpr int kRow = U::kRow;
-  // two step buffers of kKvPhases units each
-  __shared__ __attribute__((aligned(1024))) char slot[2][kKvPhases * U::kBytes];
+  // two step buffers of kStepUnits units each
+  __shared__ __attribute__((aligned(1024))) char slot[2][kStepUnits * U::kBytes];
   // the second phase's accumulators, lane-contiguous: [tile][dk, dv][dt * 4 + jj][lane]
   __shared__ float red[kKvTiles][2][DT * 4 * 64];
   // the chunk's readers in the segment: token - segment start (bits 0..10),
@@ -508,7 +511,7 @@ __global__ void __launch_bounds__(64 * kKvTiles * kKvPhases) bwd_dkdv_kernel(Bwd
   }
   __syncthreads();
   const int nunits = nread_s * a.gpk;          // (reader, head group) pairs, reader-major
-  const int nsteps = (nunits + kKvPhases - 1) / kKvPhases;
+  const int nsteps = (nunits + kStepUnits - 1) / kStepUnits;
 
   f32x4 dk[DT], dv[DT];
 #pragma unroll
@@ -531,15 +534,17 @@ __global__ void __launch_bounds__(64 * kKvTiles * kKvPhases) bwd_dkdv_kernel(Bwd
     }
     const float sl = a.scale_log2;
 
-    // one step's work for this wave: unit kKvPhases * step + phase, if it
-    // exists, reads the tile's block and reaches the tile's first key
-    auto compute = [&](NSA_LDS const char* buf, int step) __attribute__((always_inline)) {
-      const int u = kKvPhases * step + phase;
+    // the wave's j-th unit of a step: unit kStepUnits * step + j * kKvPhases
+    // + phase, if it exists, reads the tile's block and reaches the tile's
+    // first key
+    auto compute = [&](NSA_LDS const char* buf, int step, int j) __attribute__((always_inline)) {
+      const int slot_unit = j * kKvPhases + phase;
+      const int u = kStepUnits * step + slot_unit;
       if (u >= nunits) return;
       const int e = rlist[u / a.gpk];
       const int t = seg_lo + (e & 2047);
       if (!active || !((e >> (11 + tblk)) & 1) || key0 > t) return;
-      NSA_LDS const char* qs = buf + phase * U::kBytes;
+      NSA_LDS const char* qs = buf + slot_unit * U::kBytes;
       NSA_LDS const char* ds = qs + U::kRows;
       // every LDS read of the step goes out first, so their latencies
       // overlap: Q_t, dO_t of the group's heads as A operands (lane (c, g):
@@ -589,7 +594,7 @@ __global__ void __launch_bounds__(64 * kKvTiles * kKvPhases) bwd_dkdv_kernel(Bwd
 
     // software pipeline over steps: the workgroup loads step s + 2 into
     // registers while it computes step s from one LDS buffer, then stores
-    // step s + 1 into the other; one barrier per step
+    // step s + 1 into the other; one barrier per step of kStepUnits units
     NSA_LDS char* buf0 = (NSA_LDS char*)&slot[0][0];
     NSA_LDS char* buf1 = (NSA_LDS char*)&slot[1][0];
     KvStage<D> s0, s1;
@@ -599,11 +604,13 @@ __global__ void __launch_bounds__(64 * kKvTiles * kKvPhases) bwd_dkdv_kernel(Bwd
     lds_barrier();
     for (int step = 0; step < nsteps; step += 2) {
       kv_stage_load<D>(a, rlist, nunits, seg_lo, tok_base, h, tid, step + 2, s0);
-      compute(buf0, step);
+#pragma unroll
+      for (int j = 0; j < kUnitsPerWave; j++) compute(buf0, step, j);
       kv_stage_store<D>(a, buf1, tid, s1);
       lds_barrier();
       kv_stage_load<D>(a, rlist, nunits, seg_lo, tok_base, h, tid, step + 3, s1);
-      compute(buf1, step + 1);
+#pragma unroll
+      for (int j = 0; j < kUnitsPerWave; j++) compute(buf1, step + 1, j);
       kv_stage_store<D>(a, buf0, tid, s0);
       lds_barrier();
     }

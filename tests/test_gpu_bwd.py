@@ -59,6 +59,10 @@ CASES = [
     # two token segments, two key blocks per 64-key chunk, two head groups,
     # a ragged last chunk
     ("bwd_g32_d128_bs32_T1100", 1, 1100, 64, 2, 128, 32, 8, "sink_local_random", "uniform"),
+    # three heads per group, T not a multiple of 32
+    ("bwd_g3_d64_bs32_T33", 2, 33, 6, 2, 64, 32, 4, "local_random", "uniform"),
+    # three head groups of 16, block size 128
+    ("bwd_g48_d128_bs128_T260", 1, 260, 48, 1, 128, 128, 3, "sink_local_random", "uniform"),
 ]
 
 
@@ -73,6 +77,23 @@ def test_bwd_small_cases_all_gradients(case):
     check(f"{name} dq", dq, rq)
     check(f"{name} dk", dk, rk)
     check(f"{name} dv", dv, rv)
+
+
+def test_bwd_single_token_sequences():
+    """T = 1: each row sees one key, so P = 1 and dS = P (dP - Delta) = 0:
+    dq = dk = 0 exactly in the mathematics, dv = the group's sum of dO.  The
+    kernels reach zero up to fp32 rounding of dP against Delta (a few ulp of
+    |dO . v|), far below 1e-3 here."""
+    _say("[bwd] single-token sequences")
+    w = ni.make_workload("bwd_t1", "bf16", [1, 1, 1], 4, 2, 128, 64, 2, "sink_local_random", "full", seed=19)
+    dout, dbits = _dout(w, 19)
+    dq, dk, dv = run_bwd(w, dbits)
+    rq, rk, rv = obwd.bwd(w.q, w.k, w.v, dout, w.block_indices, w.block_counts, 64, w.scale)
+    assert np.all(rq == 0) and np.all(rk == 0)
+    assert float(dq.abs().max()) <= 1e-3 and float(dk.abs().max()) <= 1e-3
+    check("T=1 dv", dv, rv)
+    want = dout.astype(np.float64).reshape(3, 1, 2, 2, 128).sum(axis=3)        # [B, T, Hkv, D]
+    np.testing.assert_allclose(rv, want, rtol=0, atol=1e-12)
 
 
 def test_bwd_hostile_entries():

@@ -51,11 +51,11 @@ constexpr int kKvTiles = 4;    // 16-key tiles per dk/dv workgroup (a 64-key chu
 constexpr int kKvPhases = 2;   // waves per tile, taking alternate readers
 constexpr int kUnitsPerWave = 2;                       // units a wave takes per dk/dv step
 constexpr int kStepUnits = kKvPhases * kUnitsPerWave;  // (reader, head group) units per step
-constexpr int kSegMax = 2048;   // readers of a chunk are split into token segments of at most this many tokens
+constexpr int kSegMax = 4096;   // readers of a chunk are split into token segments of at most this many tokens
 
-// the segment length: 1024 tokens, 2048 past 8192 (fewer workgroups and partial sums where
-// every segment still has many workgroups)
-inline int seg_tokens(int T) { return T > 8192 ? 2048 : 1024; }
+// the segment length: 1024 tokens, 2048 past 8192 and 4096 past 16384 tokens (fewer
+// workgroups and partial sums where every segment still has many workgroups)
+inline int seg_tokens(int T) { return T > 16384 ? 4096 : (T > 8192 ? 2048 : 1024); }
 
 struct BwdArgs {
   const void* q;          // [B, T, Hq, D] bf16
@@ -370,7 +370,7 @@ __device__ __forceinline__ void kv_stage_load(const BwdArgs& a, const uint16_t* 
     // past the last unit or the group's heads: a clamped in-bounds address
     // (the value is replaced by zeros or never read)
     const int u = min(kStepUnits * step + unit, nunits - 1);
-    const int t = seg_lo + (rlist[u / a.gpk] & 2047);
+    const int t = seg_lo + (rlist[u / a.gpk] & 4095);
     const int hq = (h * a.gpk + u % a.gpk) * a.gv + min(row, a.gv - 1);
     const __bf16* src = rem < U::kChunks ? Q : dO;
     st.v[l] = *reinterpret_cast<const u32x4*>(src + ((tok_base + t) * a.Hq + hq) * D + ck * 8);
@@ -378,7 +378,7 @@ __device__ __forceinline__ void kv_stage_load(const BwdArgs& a, const uint16_t* 
   // lanes 0 .. 32 kStepUnits - 1: unit tid / 32, lse or Delta ((tid / 16) % 2), head tid % 16
   const int unit = (tid >> 5) % kStepUnits;
   const int u = min(kStepUnits * step + unit, nunits - 1);
-  const int t = seg_lo + (rlist[u / a.gpk] & 2047);
+  const int t = seg_lo + (rlist[u / a.gpk] & 4095);
   const int hq = (h * a.gpk + u % a.gpk) * a.gv + min(tid & 15, a.gv - 1);
   st.f = ((tid >> 4) & 1 ? a.delta : a.lse)[(tok_base + t) * a.Hq + hq];
 }
@@ -429,8 +429,8 @@ __global__ void __launch_bounds__(64 * kKvTiles * kKvPhases) bwd_dkdv_kernel(Bwd
   __shared__ __attribute__((aligned(1024))) char slot[2][kStepUnits * U::kBytes];
   // the second phase's accumulators, lane-contiguous: [tile][dk, dv][dt * 4 + jj][lane]
   __shared__ float red[kKvTiles][2][DT * 4 * 64];
-  // the chunk's readers in the segment: token - segment start (bits 0..10),
-  // and which of the chunk's key blocks the token reads (bits 11, 12)
+  // the chunk's readers in the segment: token - segment start (bits 0..11),
+  // and which of the chunk's key blocks the token reads (bits 12, 13)
   __shared__ uint16_t rlist[kSegMax];
   __shared__ int nread_s;
 
@@ -475,39 +475,43 @@ __global__ void __launch_bounds__(64 * kKvTiles * kKvPhases) bwd_dkdv_kernel(Bwd
   const int64_t tok_base = (int64_t)b * a.T;
 
   // the reader list: tokens t >= the chunk's first key in the segment that
-  // read any of the chunk's blocks, in token order (wave 0; <= 64 words)
+  // read any of the chunk's blocks, in token order (wave 0; <= 128 words)
   if (wave == 0) {
     const int t_lo = max(chunk * 64, seg_lo);  // a multiple of 32
     const int w_lo = t_lo / 32;
     const int nwd = (seg_hi + 31) / 32 - w_lo;
-    const int wi = w_lo + lane;
-    uint32_t per0 = 0u, per1 = 0u;             // the words of the chunk's first and second block
-    if (lane < nwd) {
-      const uint32_t* rb = a.readers + (((int64_t)b * a.Hkv + h) * a.nb + blk0) * a.nw + wi;
-      per0 = rb[0];
-      if (nblk > 1 && blk0 + 1 < a.nb) per1 = rb[a.nw];
-      if (wi == (seg_hi - 1) / 32 && (seg_hi & 31) != 0) {
-        const uint32_t m = 0xFFFFFFFFu >> (32 - (seg_hi & 31));
-        per0 &= m;
-        per1 &= m;
+    const uint32_t* rb = a.readers + (((int64_t)b * a.Hkv + h) * a.nb + blk0) * a.nw;
+    int base = 0;                              // readers listed by earlier passes
+    for (int w0 = 0; w0 < nwd; w0 += 64) {     // 64 words (2048 tokens) per pass
+      const int wi = w_lo + w0 + lane;
+      uint32_t per0 = 0u, per1 = 0u;           // the words of the chunk's first and second block
+      if (w0 + lane < nwd) {
+        per0 = rb[wi];
+        if (nblk > 1 && blk0 + 1 < a.nb) per1 = rb[a.nw + wi];
+        if (wi == (seg_hi - 1) / 32 && (seg_hi & 31) != 0) {
+          const uint32_t m = 0xFFFFFFFFu >> (32 - (seg_hi & 31));
+          per0 &= m;
+          per1 &= m;
+        }
       }
-    }
-    uint32_t any = per0 | per1;
-    const int cnt = __builtin_popcount(any);
-    int incl = cnt;
+      uint32_t any = per0 | per1;
+      const int cnt = __builtin_popcount(any);
+      int incl = cnt;
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int y = __shfl_up(incl, o, 64);
-      if (lane >= o) incl += y;
+      for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += y;
+      }
+      int pos = base + incl - cnt;
+      while (any != 0u) {
+        const int bit = __builtin_ctz(any);
+        any &= any - 1u;
+        const int t = wi * 32 + bit;
+        rlist[pos++] = (uint16_t)((t - seg_lo) | (((per0 >> bit) & 1u) << 12) | (((per1 >> bit) & 1u) << 13));
+      }
+      base += __shfl(incl, 63, 64);
     }
-    int pos = incl - cnt;
-    while (any != 0u) {
-      const int bit = __builtin_ctz(any);
-      any &= any - 1u;
-      const int t = wi * 32 + bit;
-      rlist[pos++] = (uint16_t)((t - seg_lo) | (((per0 >> bit) & 1u) << 11) | (((per1 >> bit) & 1u) << 12));
-    }
-    if (lane == 63) nread_s = incl;
+    if (lane == 0) nread_s = base;
   }
   __syncthreads();
   const int nunits = nread_s * a.gpk;          // (reader, head group) pairs, reader-major
@@ -542,8 +546,8 @@ __global__ void __launch_bounds__(64 * kKvTiles * kKvPhases) bwd_dkdv_kernel(Bwd
       const int u = kStepUnits * step + slot_unit;
       if (u >= nunits) return;
       const int e = rlist[u / a.gpk];
-      const int t = seg_lo + (e & 2047);
-      if (!active || !((e >> (11 + tblk)) & 1) || key0 > t) return;
+      const int t = seg_lo + (e & 4095);
+      if (!active || !((e >> (12 + tblk)) & 1) || key0 > t) return;
       NSA_LDS const char* qs = buf + slot_unit * U::kBytes;
       NSA_LDS const char* ds = qs + U::kRows;
       // every LDS read of the step goes out first, so their latencies

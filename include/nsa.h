@@ -163,9 +163,12 @@ nsa_status nsa_decode(const nsa_dims* dims, const void* q, const void* k, const 
  *  float32 from the same forward; dq [B, T, Hq, D], dk, dv [B, T, Hkv, D]
  *  float32, fully written (rows of keys no token reads get zeros).
  *  The index rows and their rules are those of nsa_fwd; S <= 64.
- *  Workspace: nsa_bwd_workspace_size() bytes (Delta and a reader bitmap
- *  per key block: B * Hkv * ceil(T / block_size) * ceil(T / 32) words),
- *  256-byte aligned, no initialisation needed.
+ *  Workspace: nsa_bwd_workspace_size() bytes (Delta [B, T, Hq] float32, a
+ *  reader bitmap per key block: B * Hkv * ceil(T / block_size) *
+ *  ceil(T / 32) words, and each token segment's partial dK and dV sums:
+ *  2 * ceil(T / L) * B * T * Hkv * D float32 with segments of L = 1024
+ *  tokens, 2048 when T > 8192, 4096 when T > 16384), 256-byte aligned, no
+ *  initialisation needed.
  * dk and dv sum over a block's readers in token order, so results are
  * deterministic.  NSA_ERROR_NOT_SUPPORTED for fp32, S > 64 and
  * the head_dim / block_size / group limits of nsa_fwd.

@@ -21,19 +21,20 @@
 // clamp(count, 0, S) entries 0 <= j <= own, repeats idempotent).
 //
 // dkdv kernel: one workgroup per (sequence, kv head, 64-key chunk, token
-// segment), one wave per (16-key tile, phase).  Wave 0 turns the chunk's
-// reader bitmaps into a list of the segment's reader tokens, in token order
-// (so the sums are deterministic).  The workgroup then walks the list four
-// (reader, head group) units per step: all its lanes load the four units'
-// Q_t, dO_t, lse and Delta once into registers two steps ahead and store them
-// into one of two LDS buffers, and each wave takes the two units of its
-// phase, one after the other: it forms
-// S = Q K^T and dP = dO V^T for its 16 keys (K and V rows in registers as B
-// operands), P and dS, and accumulates dV += P^T dO and dK += dS^T Q with
-// 16x16x16 MFMAs whose B operands (dO and Q, heads x d) are read transposed
-// from the buffer.  The two phases' sums meet in LDS, and the segments'
-// partial sums are added in segment order by the reduce kernel.  Every key
-// row gets written (zeros where no token reads the block).
+// segment), one wave per (16-key tile, phase) (kKvPhases = 1: one wave per
+// tile, two workgroups per CU).  Wave 0 turns the chunk's reader bitmaps
+// into a list of the segment's reader tokens, in token order (so the sums
+// are deterministic).  The workgroup then walks the list kStepUnits (reader,
+// head group) units per step: all its lanes load the step's Q_t, dO_t, lse
+// and Delta once into registers two steps ahead and store them into one of
+// two LDS buffers, and each wave takes its phase's units, one after the
+// other: it forms S = Q K^T and dP = dO V^T for its 16 keys (K and V rows in
+// registers as B operands), P and dS, and accumulates dV += P^T dO and
+// dK += dS^T Q with 16x16x16 MFMAs whose B operands (dO and Q, heads x d)
+// are read transposed from the buffer.  With two phases their sums meet in
+// LDS in a fixed order; the segments' partial sums are added in segment
+// order by the reduce kernel.  Every key row gets written (zeros where no
+// token reads the block).
 #include <utility>
 
 #include "nsa.h"
@@ -48,14 +49,15 @@ using namespace dev;
 
 constexpr int kBwdWaves = 4;
 constexpr int kKvTiles = 4;    // 16-key tiles per dk/dv workgroup (a 64-key chunk)
-constexpr int kKvPhases = 2;   // waves per tile, taking alternate readers
+constexpr int kKvPhases = 1;   // waves per tile, taking alternate readers
 constexpr int kUnitsPerWave = 2;                       // units a wave takes per dk/dv step
 constexpr int kStepUnits = kKvPhases * kUnitsPerWave;  // (reader, head group) units per step
 constexpr int kSegMax = 4096;   // readers of a chunk are split into token segments of at most this many tokens
 
-// the segment length: 1024 tokens, 2048 past 8192 and 4096 past 16384 tokens (fewer
-// workgroups and partial sums where every segment still has many workgroups)
-inline int seg_tokens(int T) { return T > 16384 ? 4096 : (T > 8192 ? 2048 : 1024); }
+// the segment length: 512 tokens up to T = 4096, then 1024, 2048 past 8192 and 4096 past
+// 16384 tokens (fewer workgroups and partial sums where every segment still has many
+// workgroups; short segments bound the longest workgroup, that of a block every token reads)
+inline int seg_tokens(int T) { return T > 16384 ? 4096 : (T > 8192 ? 2048 : (T > 4096 ? 1024 : 512)); }
 
 struct BwdArgs {
   const void* q;          // [B, T, Hq, D] bf16
@@ -420,7 +422,8 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 template <int D>
-__global__ void __launch_bounds__(64 * kKvTiles * kKvPhases) bwd_dkdv_kernel(BwdArgs a) {
+__global__ void __launch_bounds__(64 * kKvTiles * kKvPhases) __attribute__((amdgpu_waves_per_eu(2)))
+bwd_dkdv_kernel(BwdArgs a) {
   using U = KvUnit<D>;
   constexpr int KT = D / 32;   // k-steps of S = Q K^T over d
   constexpr int DT = D / 16;   // 16-column d tiles of dK, dV
@@ -428,7 +431,10 @@ __global__ void __launch_bounds__(64 * kKvTiles * kKvPhases) bwd_dkdv_kernel(Bwd
   // two step buffers of kStepUnits units each
   __shared__ __attribute__((aligned(1024))) char slot[2][kStepUnits * U::kBytes];
   // the second phase's accumulators, lane-contiguous: [tile][dk, dv][dt * 4 + jj][lane]
-  __shared__ float red[kKvTiles][2][DT * 4 * 64];
+  // (a placeholder with one phase)
+  constexpr int kRedTiles = kKvPhases > 1 ? kKvTiles : 1;
+  constexpr int kRedLen = kKvPhases > 1 ? DT * 4 * 64 : 1;
+  __shared__ float red[kRedTiles][2][kRedLen];
   // the chunk's readers in the segment: token - segment start (bits 0..11),
   // and which of the chunk's key blocks the token reads (bits 12, 13)
   __shared__ uint16_t rlist[kSegMax];
@@ -620,18 +626,28 @@ __global__ void __launch_bounds__(64 * kKvTiles * kKvPhases) bwd_dkdv_kernel(Bwd
     }
   }
   // the phases' sums meet in LDS in a fixed order (deterministic)
-  __syncthreads();
-  if (phase == 1 && active) {
+  if constexpr (kKvPhases > 1) {
+    __syncthreads();
+    if (phase == 1 && active) {
+#pragma unroll
+      for (int dt = 0; dt < DT; dt++) {
+#pragma unroll
+        for (int jj = 0; jj < 4; jj++) {
+          red[tile][0][(dt * 4 + jj) * 64 + lane] = dk[dt][jj];
+          red[tile][1][(dt * 4 + jj) * 64 + lane] = dv[dt][jj];
+        }
+      }
+    }
+    __syncthreads();
 #pragma unroll
     for (int dt = 0; dt < DT; dt++) {
 #pragma unroll
       for (int jj = 0; jj < 4; jj++) {
-        red[tile][0][(dt * 4 + jj) * 64 + lane] = dk[dt][jj];
-        red[tile][1][(dt * 4 + jj) * 64 + lane] = dv[dt][jj];
+        dk[dt][jj] += red[tile][0][(dt * 4 + jj) * 64 + lane];
+        dv[dt][jj] += red[tile][1][(dt * 4 + jj) * 64 + lane];
       }
     }
   }
-  __syncthreads();
   if (phase != 0 || !active) return;
   // the segment's partial sum dS^T Q and P^T dO; lane (c, g) holds keys 4 g + jj at d = 16 dt + c
   const int64_t plane = (int64_t)a.B * a.T * a.Hkv * D;
@@ -644,8 +660,8 @@ __global__ void __launch_bounds__(64 * kKvTiles * kKvPhases) bwd_dkdv_kernel(Bwd
     const int64_t o = ((tok_base + kr) * a.Hkv + h) * D;
 #pragma unroll
     for (int dt = 0; dt < DT; dt++) {
-      pk[o + dt * 16 + c] = dk[dt][jj] + red[tile][0][(dt * 4 + jj) * 64 + lane];
-      pv[o + dt * 16 + c] = dv[dt][jj] + red[tile][1][(dt * 4 + jj) * 64 + lane];
+      pk[o + dt * 16 + c] = dk[dt][jj];
+      pv[o + dt * 16 + c] = dv[dt][jj];
     }
   }
 }

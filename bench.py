@@ -276,6 +276,34 @@ def cpu_baseline(w, seconds_target=12.0, seed=0):
             "seconds": used, "tokens": int(len(rows))}
 
 
+def bwd_cpu_baseline(w, dout, seconds_target=12.0, seed=0):
+    """Time the gradient oracle's per-token dq (oracle.backward.dq_rows, fp64
+    numpy, BLAS held to one thread) on a seeded token sample sized to
+    ~seconds_target.  Only the dq share of the backward is timed: 6 D FLOP
+    per visible (token, query head, key) triple of the 10 D the metric
+    counts."""
+    from threadpoolctl import threadpool_limits
+    from oracle import backward as obwd
+    rng = np.random.default_rng(seed)
+    total = w.B * w.T
+    m = visible_keys_per_row(w)                                     # [B * T, Hkv]
+    n = 16
+    with threadpool_limits(limits=1):
+        while True:
+            rows = np.sort(rng.choice(total, size=min(n, total), replace=False))
+            t0 = time.perf_counter()
+            obwd.dq_rows(w.q, w.k, w.v, dout, w.block_indices, w.block_counts, w.block_size, w.scale, rows)
+            used = time.perf_counter() - t0
+            if used >= seconds_target * 0.6 or n >= total:
+                break
+            n = min(total, int(n * min(8.0, max(1.2, seconds_target / max(used, 1e-3)))))
+    fl = 6 * w.D * w.G * int(m[rows].sum())
+    return {"value": fl / used / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+            "sample": f"dq of {len(rows)} of {total} tokens (seeded uniform sample, all {w.Hq} query heads; "
+                      f"6 D FLOP per visible triple, dq's share of the 10 D), {used:.2f} s fp64 numpy on one thread",
+            "seconds": used, "tokens": int(len(rows))}
+
+
 METRIC_DECODE = "sparse-attn decode step: useful HBM GB/s + % of HBM peak, 1 GPU"
 
 
@@ -407,6 +435,9 @@ def backward_bench(args):
                      "traffic": None, "kernel_ms_avg": round(avg, 4), "kernel_ms_min": round(float(np.min(ms)), 4),
                      "algorithmic_flop_per_launch": flop},
     }
+    if not args.no_cpu_baseline:
+        dout_f = ni.bf16_bits_to_f32(ni.to_bf16_bits(x)).reshape(x.shape)
+        line["cpu_baseline"] = bwd_cpu_baseline(w, dout_f, seconds_target=args.cpu_seconds)
     print(json.dumps(line), flush=True)
 
 

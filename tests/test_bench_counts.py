@@ -5,6 +5,7 @@ import pytest
 
 import nsa_inputs as ni
 import oracle
+import bench
 from bench import visible_keys_per_row, useful_flops
 
 
@@ -45,3 +46,16 @@ def test_decode_visible_key_count_matches_oracle():
     got = np.repeat(m, w.G, axis=1)
     exp = np.where(np.isneginf(lse), 0, np.round(np.exp(np.where(np.isneginf(lse), 0, lse)))).astype(np.int64)
     assert np.array_equal(got, exp)
+
+
+def test_backward_cpu_baseline_counts_dq_flop():
+    """The backward line's CPU baseline times the oracle's dq on a token
+    sample and counts 6 D FLOP per visible triple of the sampled rows."""
+    w = ni.make_workload("bcb", "bf16", [96], 8, 2, 64, 32, 4, "sink_local_random", "uniform", seed=3)
+    dout = np.random.default_rng(0).standard_normal(w.q.shape).astype(np.float32)
+    r = bench.bwd_cpu_baseline(w, dout, seconds_target=0.0)    # stops after the first 16-token sample
+    m = bench.visible_keys_per_row(w)
+    rows = np.sort(np.random.default_rng(0).choice(96, size=16, replace=False))
+    assert r["kind"] == "oracle" and r["cores"] == 1 and r["tokens"] == 16
+    want = 6 * w.D * w.G * int(m[rows].sum())
+    assert abs(r["value"] * r["seconds"] * 1e12 - want) <= 1e-6 * want

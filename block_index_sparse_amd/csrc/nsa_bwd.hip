@@ -21,20 +21,18 @@
 // clamp(count, 0, S) entries 0 <= j <= own, repeats idempotent).
 //
 // dkdv kernel: one workgroup per (sequence, kv head, 64-key chunk, token
-// segment), one wave per (16-key tile, phase) (kKvPhases = 1: one wave per
-// tile, two workgroups per CU).  Wave 0 turns the chunk's reader bitmaps
-// into a list of the segment's reader tokens, in token order (so the sums
-// are deterministic).  The workgroup then walks the list kStepUnits (reader,
-// head group) units per step: all its lanes load the step's Q_t, dO_t, lse
-// and Delta once into registers two steps ahead and store them into one of
-// two LDS buffers, and each wave takes its phase's units, one after the
-// other: it forms S = Q K^T and dP = dO V^T for its 16 keys (K and V rows in
-// registers as B operands), P and dS, and accumulates dV += P^T dO and
-// dK += dS^T Q with 16x16x16 MFMAs whose B operands (dO and Q, heads x d)
-// are read transposed from the buffer.  With two phases their sums meet in
-// LDS in a fixed order; the segments' partial sums are added in segment
-// order by the reduce kernel.  Every key row gets written (zeros where no
-// token reads the block).
+// segment), one wave per 16-key tile, two workgroups per CU.  Wave 0 turns
+// the chunk's reader bitmaps into a list of the segment's reader tokens, in
+// token order (so the sums are deterministic).  The workgroup then walks the
+// list kStepUnits (reader, head group) units per step: all its lanes load the
+// step's Q_t, dO_t, lse and Delta once into registers two steps ahead and
+// store them into one of two LDS buffers, and each wave takes every unit of
+// the step, one after the other: it forms S = Q K^T and dP = dO V^T for its
+// 16 keys (K and V rows in registers as B operands), P and dS, and
+// accumulates dV += P^T dO and dK += dS^T Q with 16x16x16 MFMAs whose B
+// operands (dO and Q, heads x d) are read transposed from the buffer.  The
+// segments' partial sums are added in segment order by the reduce kernel.
+// Every key row gets written (zeros where no token reads the block).
 #include <utility>
 
 #include "nsa.h"
@@ -49,9 +47,7 @@ using namespace dev;
 
 constexpr int kBwdWaves = 4;
 constexpr int kKvTiles = 4;    // 16-key tiles per dk/dv workgroup (a 64-key chunk)
-constexpr int kKvPhases = 1;   // waves per tile, taking alternate readers
-constexpr int kUnitsPerWave = 2;                       // units a wave takes per dk/dv step
-constexpr int kStepUnits = kKvPhases * kUnitsPerWave;  // (reader, head group) units per step
+constexpr int kStepUnits = 2;  // (reader, head group) units per dk/dv step, taken by every tile wave
 constexpr int kSegMax = 4096;   // readers of a chunk are split into token segments of at most this many tokens
 
 // the segment length: 512 tokens up to T = 4096, then 1024, 2048 past 8192 and 4096 past
@@ -343,7 +339,7 @@ struct KvUnit {
   static constexpr int kBytes = 2 * kRows + 2 * 64;   // Q, dO, lse[16], Delta[16]
   static constexpr int kChunks = kRows / 16;          // 16-byte chunks of Q (or dO)
   static constexpr int kStepChunks = kStepUnits * 2 * kChunks;
-  static constexpr int kThreads = 64 * kKvTiles * kKvPhases;
+  static constexpr int kThreads = 64 * kKvTiles;
   static constexpr int kLoads = kStepChunks / kThreads;   // 16-byte loads per lane per step
   static_assert(kStepChunks % kThreads == 0, "a step's chunks spread evenly over the workgroup");
 };
@@ -422,7 +418,7 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 template <int D>
-__global__ void __launch_bounds__(64 * kKvTiles * kKvPhases) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ void __launch_bounds__(64 * kKvTiles) __attribute__((amdgpu_waves_per_eu(2)))
 bwd_dkdv_kernel(BwdArgs a) {
   using U = KvUnit<D>;
   constexpr int KT = D / 32;   // k-steps of S = Q K^T over d
@@ -430,11 +426,6 @@ bwd_dkdv_kernel(BwdArgs a) {
   constexpr int kRow = U::kRow;
   // two step buffers of kStepUnits units each
   __shared__ __attribute__((aligned(1024))) char slot[2][kStepUnits * U::kBytes];
-  // the second phase's accumulators, lane-contiguous: [tile][dk, dv][dt * 4 + jj][lane]
-  // (a placeholder with one phase)
-  constexpr int kRedTiles = kKvPhases > 1 ? kKvTiles : 1;
-  constexpr int kRedLen = kKvPhases > 1 ? DT * 4 * 64 : 1;
-  __shared__ float red[kRedTiles][2][kRedLen];
   // the chunk's readers in the segment: token - segment start (bits 0..11),
   // and which of the chunk's key blocks the token reads (bits 12, 13)
   __shared__ uint16_t rlist[kSegMax];
@@ -471,8 +462,7 @@ bwd_dkdv_kernel(BwdArgs a) {
   if (seg_hi <= chunk * 64) return;
   const int h = bh % a.Hkv;
   const int b = bh / a.Hkv;
-  const int tile = wave % kKvTiles;            // 16-key tile of the chunk
-  const int phase = wave / kKvTiles;           // which unit of every step this wave takes
+  const int tile = wave;                       // 16-key tile of the chunk
   const int key0 = chunk * 64 + tile * 16;     // the tile's first key (position in the sequence)
   const bool active = key0 < a.T;              // every wave reaches the barriers below
   const int blk0 = chunk * 64 / a.bs;          // the chunk's first key block
@@ -544,11 +534,10 @@ bwd_dkdv_kernel(BwdArgs a) {
     }
     const float sl = a.scale_log2;
 
-    // the wave's j-th unit of a step: unit kStepUnits * step + j * kKvPhases
-    // + phase, if it exists, reads the tile's block and reaches the tile's
-    // first key
+    // unit j of a step: unit kStepUnits * step + j, if it exists, reads the
+    // tile's block and reaches the tile's first key
     auto compute = [&](NSA_LDS const char* buf, int step, int j) __attribute__((always_inline)) {
-      const int slot_unit = j * kKvPhases + phase;
+      const int slot_unit = j;
       const int u = kStepUnits * step + slot_unit;
       if (u >= nunits) return;
       const int e = rlist[u / a.gpk];
@@ -615,40 +604,18 @@ bwd_dkdv_kernel(BwdArgs a) {
     for (int step = 0; step < nsteps; step += 2) {
       kv_stage_load<D>(a, rlist, nunits, seg_lo, tok_base, h, tid, step + 2, s0);
 #pragma unroll
-      for (int j = 0; j < kUnitsPerWave; j++) compute(buf0, step, j);
+      for (int j = 0; j < kStepUnits; j++) compute(buf0, step, j);
       kv_stage_store<D>(a, buf1, tid, s1);
       lds_barrier();
       kv_stage_load<D>(a, rlist, nunits, seg_lo, tok_base, h, tid, step + 3, s1);
 #pragma unroll
-      for (int j = 0; j < kUnitsPerWave; j++) compute(buf1, step + 1, j);
+      for (int j = 0; j < kStepUnits; j++) compute(buf1, step + 1, j);
       kv_stage_store<D>(a, buf0, tid, s0);
       lds_barrier();
     }
   }
-  // the phases' sums meet in LDS in a fixed order (deterministic)
-  if constexpr (kKvPhases > 1) {
-    __syncthreads();
-    if (phase == 1 && active) {
-#pragma unroll
-      for (int dt = 0; dt < DT; dt++) {
-#pragma unroll
-        for (int jj = 0; jj < 4; jj++) {
-          red[tile][0][(dt * 4 + jj) * 64 + lane] = dk[dt][jj];
-          red[tile][1][(dt * 4 + jj) * 64 + lane] = dv[dt][jj];
-        }
-      }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int dt = 0; dt < DT; dt++) {
-#pragma unroll
-      for (int jj = 0; jj < 4; jj++) {
-        dk[dt][jj] += red[tile][0][(dt * 4 + jj) * 64 + lane];
-        dv[dt][jj] += red[tile][1][(dt * 4 + jj) * 64 + lane];
-      }
-    }
-  }
-  if (phase != 0 || !active) return;
+  if (!active) return;
+
   // the segment's partial sum dS^T Q and P^T dO; lane (c, g) holds keys 4 g + jj at d = 16 dt + c
   const int64_t plane = (int64_t)a.B * a.T * a.Hkv * D;
   float* pk = a.part + (int64_t)seg * 2 * plane;
@@ -747,11 +714,11 @@ hipError_t launch_bwd(const BwdPlan& p, const void* q, const void* k, const void
   hipLaunchKernelGGL(bwd_readers_kernel, dim3((unsigned)((n_rows + 255) / 256)), dim3(256), 0, stream, a);
   if (p.D == 64) {
     hipLaunchKernelGGL(bwd_dq_kernel<64>, dim3((unsigned)n_dq), dim3(64 * kBwdWaves), 0, stream, a);
-    hipLaunchKernelGGL(bwd_dkdv_kernel<64>, dim3((unsigned)n_kv), dim3(64 * kKvTiles * kKvPhases), 0, stream, a);
+    hipLaunchKernelGGL(bwd_dkdv_kernel<64>, dim3((unsigned)n_kv), dim3(64 * kKvTiles), 0, stream, a);
     hipLaunchKernelGGL(bwd_reduce_kernel<64>, dim3((unsigned)n_red), dim3(256), 0, stream, a);
   } else if (p.D == 128) {
     hipLaunchKernelGGL(bwd_dq_kernel<128>, dim3((unsigned)n_dq), dim3(64 * kBwdWaves), 0, stream, a);
-    hipLaunchKernelGGL(bwd_dkdv_kernel<128>, dim3((unsigned)n_kv), dim3(64 * kKvTiles * kKvPhases), 0, stream, a);
+    hipLaunchKernelGGL(bwd_dkdv_kernel<128>, dim3((unsigned)n_kv), dim3(64 * kKvTiles), 0, stream, a);
     hipLaunchKernelGGL(bwd_reduce_kernel<128>, dim3((unsigned)n_red), dim3(256), 0, stream, a);
   } else {
     return hipErrorInvalidValue;

@@ -14,11 +14,10 @@
 // ahead, stores them into its LDS slot and reads back the A operands of
 // S^T = K Q^T and dP^T = V dO^T, and K transposed (ds_read_b64_tr_b16) as
 // the A operand of dQ^T += K^T dS^T.  The waves' partial dQ are summed
-// through LDS.  The kernel also writes Delta for the dk/dv kernel.
-//
-// readers kernel: a bitmap over tokens per (sequence, kv head, key block)
-// marking the tokens that read the block (set from every row's first
-// clamp(count, 0, S) entries 0 <= j <= own, repeats idempotent).
+// through LDS.  The kernel also writes Delta and the reader bitmaps for the
+// dk/dv kernel: per (sequence, kv head, key block) a bit per token that
+// keeps the block (from the row's first clamp(count, 0, S) entries
+// 0 <= j <= own; atomic OR, so repeats and order do not matter).
 //
 // dkdv kernel: one workgroup per (sequence, kv head, 64-key chunk, token
 // segment), one wave per 16-key tile, two workgroups per CU.  Wave 0 turns
@@ -119,6 +118,11 @@ bwd_dq_kernel(BwdArgs a) {
     if (lane > j && idx == vj) keep = false;
   }
   const uint64_t kept = __ballot(keep);
+  // the token's bit in the reader bitmap of each block it keeps, for the
+  // dk/dv kernel (atomic OR: order and repeats do not matter); set by the
+  // first head group's workgroup of the (token, kv head)
+  if (grp == 0 && keep)
+    atomicOr(a.readers + (((int64_t)(bt / a.T) * a.Hkv + h) * a.nb + idx) * a.nw + t / 32, 1u << (t & 31));
   int my_ks = 0;
   int my_n = 0;
   {
@@ -301,32 +305,12 @@ bwd_dq_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// readers of every key block: a bitmap over tokens per (sequence, kv head,
-// block), set by one thread per (token, kv head) row for each of its first
-// clamp(count, 0, S) entries 0 <= j <= own (OR is idempotent, so repeats and
-// the order of the atomics do not matter)
+// the reader bitmaps start cleared (the dq kernel sets their bits)
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(256) bwd_clear_kernel(uint32_t* __restrict__ p, int64_t n) {
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0u;
 }
 
-__global__ void __launch_bounds__(256) bwd_readers_kernel(BwdArgs a) {
-  const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;   // (b * T + t) * Hkv + h
-  if (r >= (int64_t)a.B * a.T * a.Hkv) return;
-  const int h = (int)(r % a.Hkv);
-  const int64_t bt = r / a.Hkv;
-  const int t = (int)(bt % a.T);
-  const int b = (int)(bt / a.T);
-  int n = a.bc[r];
-  n = n < 0 ? 0 : (n > a.S ? a.S : n);
-  const int own = t / a.bs;
-  uint32_t* base = a.readers + ((int64_t)b * a.Hkv + h) * a.nb * a.nw + t / 32;
-  const uint32_t bit = 1u << (t & 31);
-  for (int i = 0; i < n; i++) {
-    const int j = a.bi[r * a.S + i];
-    if (j >= 0 && j <= own) atomicOr(base + (int64_t)j * a.nw, bit);
-  }
-}
 
 // ---------------------------------------------------------------------------
 // dk, dv
@@ -708,10 +692,8 @@ hipError_t launch_bwd(const BwdPlan& p, const void* q, const void* k, const void
   const int64_t n_kv = (int64_t)p.B * p.Hkv * ((p.T + 63) / 64) * a.ns;
   const int64_t n_red = ((int64_t)p.B * p.T * p.Hkv * p.D / 4 + 255) / 256;
   const int64_t n_bits = (int64_t)p.B * p.Hkv * a.nb * a.nw;
-  const int64_t n_rows = (int64_t)p.B * p.T * p.Hkv;
   hipLaunchKernelGGL(bwd_clear_kernel, dim3((unsigned)std::min<int64_t>((n_bits + 255) / 256, 4096)), dim3(256), 0,
                      stream, a.readers, n_bits);
-  hipLaunchKernelGGL(bwd_readers_kernel, dim3((unsigned)((n_rows + 255) / 256)), dim3(256), 0, stream, a);
   if (p.D == 64) {
     hipLaunchKernelGGL(bwd_dq_kernel<64>, dim3((unsigned)n_dq), dim3(64 * kBwdWaves), 0, stream, a);
     hipLaunchKernelGGL(bwd_dkdv_kernel<64>, dim3((unsigned)n_kv), dim3(64 * kKvTiles), 0, stream, a);

@@ -57,6 +57,8 @@ CSRC = os.path.join(ROOT, "block_index_sparse_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
 
 
+FWD_KERNEL = "fwd_bf16_ring_kernel"   # the attention kernel of the bf16 forward
+
 KERNEL_SOURCES = {
     # the forward kernel, the helpers it includes and the host code that sizes its tiles
     "fwd": ("nsa_fwd.hip", "nsa_device.h", "nsa_internal.h", "nsa_api.hip"),
@@ -451,6 +453,8 @@ def main():
     ap.add_argument("--decode", action="store_true", help="measure the decode step instead")
     ap.add_argument("--backward", action="store_true", help="measure the backward pass on --config")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--headline-only", dest="all_configs", action="store_false",
+                    help="skip the per-workload lines of the other named workloads")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run the copy kernel used to scale the traffic counters")
     ap.add_argument("--traffic-summary", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR",
@@ -465,7 +469,7 @@ def main():
             name, kern = ni.DECODE_NAME, "decode_bf16_kernel"
         else:
             name = ni.workload_name(args.config)
-            kern = "fwd_f32_kernel" if args.config == 0 else "fwd_bf16_ring_kernel"
+            kern = "fwd_f32_kernel" if args.config == 0 else FWD_KERNEL
         counters_summary(name, *args.counters_summary, kernel=kern)
         return
     if args.traffic_summary:
@@ -474,7 +478,7 @@ def main():
             name, kern = ni.DECODE_NAME, "decode_bf16_kernel"
         else:
             name = ni.workload_name(args.config)
-            kern = "fwd_f32_kernel" if args.config == 0 else "fwd_bf16_ring_kernel"
+            kern = "fwd_f32_kernel" if args.config == 0 else FWD_KERNEL
         traffic_summary(name, *args.traffic_summary, kernel=kern)
         return
     if args.gpus != 1:
@@ -493,7 +497,6 @@ def main():
         return
 
     import torch
-    import block_index_sparse_amd as nsa
     import nsa_inputs as ni
 
     dev = torch.device("cuda:0")
@@ -501,37 +504,10 @@ def main():
     w = ni.make_config(args.config)
     gen_s = time.perf_counter() - t0
     print(f"[bench] {w.name}: generated in {gen_s:.1f} s", file=sys.stderr, flush=True)
-    q, k, v, bi, bc, cu = ni.to_torch(w, dev)
     flop = useful_flops(w)
-    f = nsa.Forward(q, k, v, bi, bc, w.block_size, w.scale, cu_seqlens=cu, index_layout=w.index_layout)
-    torch.cuda.synchronize()
-
-    for _ in range(args.warmup):
-        f.schedule()
-        f.execute()
-    torch.cuda.synchronize()
-
-    K = args.steps
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
-    e_start, e_stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    e_start.record()
-    for i in range(K):
-        f.schedule()
-        ev[i][0].record()
-        f.execute()
-        ev[i][1].record()
-    e_stop.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    # outside the timed region: every timed launch must have completed its
-    # bounded waits, or the numbers describe a broken run
-    if f.device_status() != 0:
-        sys.exit("bench: a bounded wait in the forward kernel expired; no result reported")
-    step_ms = e_start.elapsed_time(e_stop) / K
-    kern_ms = [a.elapsed_time(b) for a, b in ev]
-    kern_avg = float(np.mean(kern_ms))
+    tm = time_forward(w, dev, args.warmup, args.steps)
+    step_ms = tm["window_ms"] / args.steps
+    kern_avg = tm["kernel_ms"]["mean"]
 
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
     value = flop / (step_ms * 1e-3) / 1e12
@@ -542,7 +518,7 @@ def main():
         "value": round(value, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
-        "steps": K,
+        "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(step_ms, 4),
         "higher_is_better": True,
@@ -556,11 +532,12 @@ def main():
             "index_layout": w.index_layout,
             "useful_flop_per_step": flop, "pct_of_bf16_mfma_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
             "input_sha256": w.digest()[:16], "device": (getattr(props, "gcnArchName", "") or props.name or "gfx950").split(":")[0], "cus": props.multi_processor_count,
-            "wall_s_timed": round(wall, 4),
+            "wall_s_timed": round(tm["wall_s"], 4),
         },
+        "timing": {"step_ms": tm["step_ms"], "kernel_ms": tm["kernel_ms"]},
         "roofline": {
             "bound": "mfma",
-            "kernel": "fwd_bf16_ring_kernel" if w.dtype == "bf16" else "fwd_f32_kernel",
+            "kernel": FWD_KERNEL if w.dtype == "bf16" else "fwd_f32_kernel",
             "achieved": round(achieved, 3),
             "peak": peak,
             "unit": "TFLOP/s",
@@ -568,7 +545,9 @@ def main():
             "traffic": read_traffic(w.name),
             "counters": read_counters(w.name),
             "kernel_ms_avg": round(kern_avg, 4),
-            "kernel_ms_min": round(float(np.min(kern_ms)), 4),
+            "kernel_ms_min": tm["kernel_ms"]["min"],
+            "kernel_ms_median": tm["kernel_ms"]["median"],
+            "kernel_ms_p90": tm["kernel_ms"]["p90"],
             "algorithmic_flop_per_launch": flop,
             "algorithmic_bytes_per_launch": algorithmic_bytes(w),
         },
@@ -576,7 +555,113 @@ def main():
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a token sample", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(w, seconds_target=args.cpu_seconds)
+    if args.all_configs:
+        # every named workload, in the same run: one JSON line each on stderr,
+        # a compact copy in the headline line
+        summary = {}
+        for cfg in range(5):
+            if cfg == args.config:
+                cl = {"workload": w.name, "step_ms": tm["step_ms"], "kernel_ms": tm["kernel_ms"],
+                      "useful_flop": flop, "steps": args.steps, "warmup": args.warmup}
+                cl.update(_rates(flop, tm, w))
+                if "cpu_baseline" in line:
+                    cl["oracle"] = line["cpu_baseline"]
+            else:
+                cl = config_line(cfg, dev, warmup=10, steps=50, cpu_seconds=0 if args.no_cpu_baseline else 2.5)
+            print(json.dumps({"config_line": cl}), file=sys.stderr, flush=True)
+            summary[cl["workload"]] = {k: cl[k] for k in ("kernel_tflops_median", "kernel_pct_peak_median",
+                                                            "step_ms_median", "kernel_ms_median")}
+            if "oracle" in cl:
+                summary[cl["workload"]]["oracle_tflops"] = round(cl["oracle"]["value"], 5)
+        line["all_configs"] = summary
     print(json.dumps(line), flush=True)
+
+
+def _stats(xs) -> dict:
+    a = np.asarray(xs, dtype=np.float64)
+    return {"median": round(float(np.median(a)), 4), "min": round(float(a.min()), 4),
+            "p90": round(float(np.percentile(a, 90)), 4), "mean": round(float(a.mean()), 4)}
+
+
+def time_forward(w, dev, warmup, steps):
+    """`warmup` untimed steps, then `steps` timed ones; a step is the whole
+    call (scheduler, then the attention kernel).  HIP events on the launch
+    stream bracket every step, every kernel and the whole timed window."""
+    import torch
+    import block_index_sparse_amd as nsa
+    import nsa_inputs as ni
+    q, k, v, bi, bc, cu = ni.to_torch(w, dev)
+    f = nsa.Forward(q, k, v, bi, bc, w.block_size, w.scale, cu_seqlens=cu, index_layout=w.index_layout)
+    torch.cuda.synchronize()
+    for _ in range(warmup):
+        f.schedule()
+        f.execute(check=False)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    e_start, e_stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    e_start.record()
+    for i in range(steps):
+        ev[i][0].record()
+        f.schedule()
+        ev[i][1].record()
+        f.execute(check=False)
+        ev[i][2].record()
+    e_stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    # outside the timed region: every timed launch must have completed its
+    # bounded waits, or the numbers describe a broken run
+    if f.device_status() != 0:
+        sys.exit(f"bench: a bounded wait in the forward kernel expired on {w.name}; no result reported")
+    out = {"window_ms": e_start.elapsed_time(e_stop), "wall_s": wall,
+           "step_ms": _stats([a.elapsed_time(c) for a, _, c in ev]),
+           "kernel_ms": _stats([b.elapsed_time(c) for _, b, c in ev])}
+    del f, q, k, v, bi, bc, cu
+    torch.cuda.empty_cache()
+    return out
+
+
+def _rates(flop, tm, w):
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+    kt = flop / (tm["kernel_ms"]["median"] * 1e-3) / 1e12
+    return {"kernel_tflops_median": round(kt, 3), "kernel_pct_peak_median": round(100 * kt / peak, 2),
+            "peak_tflops": peak, "step_ms_median": tm["step_ms"]["median"],
+            "kernel_ms_median": tm["kernel_ms"]["median"],
+            "step_tflops_median": round(flop / (tm["step_ms"]["median"] * 1e-3) / 1e12, 3)}
+
+
+def config_line(cfg, dev, warmup=10, steps=50, cpu_seconds=2.5):
+    """Median / min / p90 of `steps` timed steps of named workload `cfg`, and
+    the oracle's time on a bounded sample (the whole workload, median of
+    three, plus one single-thread run, when it is the tiny fp32 one)."""
+    import nsa_inputs as ni
+    import oracle
+    w = ni.make_config(cfg)
+    flop = useful_flops(w)
+    tm = time_forward(w, dev, warmup, steps)
+    cl = {"workload": w.name, "step_ms": tm["step_ms"], "kernel_ms": tm["kernel_ms"], "useful_flop": flop,
+          "steps": steps, "warmup": warmup}
+    cl.update(_rates(flop, tm, w))
+    if cpu_seconds > 0:
+        if w.B * w.T <= 4096:
+            runs = []
+            for _ in range(3):
+                t0 = time.perf_counter()
+                oracle.fwd_workload(w)
+                runs.append(time.perf_counter() - t0)
+            t0 = time.perf_counter()
+            oracle.fwd_workload(w, threads=1)
+            one = time.perf_counter() - t0
+            used = float(np.median(runs))
+            cl["oracle"] = {"value": flop / used / 1e12, "unit": "TFLOP/s", "cores": oracle.max_threads(),
+                            "kind": "oracle", "seconds": used,
+                            "sample": f"whole workload, median of 3 runs on {oracle.max_threads()} OpenMP threads",
+                            "single_thread_seconds": one}
+        else:
+            cl["oracle"] = cpu_baseline(w, seconds_target=cpu_seconds, seed=cfg)
+    return cl
 
 
 if __name__ == "__main__":

@@ -26,7 +26,7 @@ import math
 import os
 
 __all__ = ["fwd", "Forward", "decode", "Decode", "bwd", "workspace_size", "schedule", "load_library", "library_path", "NsaError",
-           "DTYPE_F32", "DTYPE_BF16"]
+           "NsaDeviceError", "DTYPE_F32", "DTYPE_BF16"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "_build", "libnsa.so")
@@ -40,6 +40,13 @@ class NsaError(RuntimeError):
     def __init__(self, status: int, message: str):
         super().__init__(message)
         self.status = status
+
+
+class NsaDeviceError(NsaError):
+    """The launch was accepted (the C call returned NSA_SUCCESS) but the
+    device status word of the run is not zero: a bounded wait inside the
+    forward kernel expired and out / lse are incomplete.  ``status`` holds
+    the word (bit 0 = NSA_DEVICE_WAIT_EXPIRED)."""
 
 
 class NsaDims(ctypes.Structure):
@@ -176,6 +183,14 @@ class Forward:
     ``schedule()`` and ``execute()`` are its two halves (``nsa_fwd_schedule``
     or ``nsa_fwd_schedule_qblock``, then ``nsa_fwd_execute``).  All launch on
     torch's current stream of q's device.
+
+    ``run()`` and ``execute()`` check the device status word after the
+    launch by default (``check=True``): that waits for the stream, and an
+    expired bounded wait inside the kernel raises ``NsaDeviceError`` instead
+    of returning incomplete rows.  ``check=False`` returns right after the
+    launch (asynchronous); the caller then reads ``device_status()`` itself
+    before trusting the results, as the benchmark does once after its timed
+    launches.
     """
 
     def __init__(self, q, k, v, block_indices, block_counts, block_size: int = 64,
@@ -203,7 +218,13 @@ class Forward:
         self._p = {n: _ptr(getattr(self, n)) for n in ("q", "k", "v", "bi", "bc", "cu", "out", "lse",
                                                         "workspace")}
 
-    def run(self):
+    def _check_device(self):
+        word = self.device_status()
+        if word != 0:
+            raise NsaDeviceError(word, f"forward device status {word:#x}: a bounded wait inside the kernel "
+                                       "expired (NSA_DEVICE_WAIT_EXPIRED); out and lse are incomplete")
+
+    def run(self, check: bool = True):
         P, L = self._p, self.lib
         if self.qblock:
             st = L.nsa_fwd_qblock(ctypes.byref(self.dims), P["q"], P["k"], P["v"], P["bi"], P["bc"],
@@ -218,6 +239,8 @@ class Forward:
                                   P["cu"], self.nseq, self.block_size, self.scale, P["out"], P["lse"],
                                   P["workspace"], self.ws_bytes, self.stream)
         _check(st)
+        if check:
+            self._check_device()
         return self.out, self.lse
 
     def schedule(self):
@@ -235,11 +258,13 @@ class Forward:
                                          ctypes.byref(off), ctypes.byref(n)))
         return off.value, n.value
 
-    def execute(self):
+    def execute(self, check: bool = True):
         P = self._p
         _check(self.lib.nsa_fwd_execute(ctypes.byref(self.dims), P["q"], P["k"], P["v"], self.nseq,
                                         self.block_size, self.scale, P["out"], P["lse"], P["workspace"],
                                         self.ws_bytes, self.stream))
+        if check:
+            self._check_device()
         return self.out, self.lse
 
     def device_status(self) -> int:
@@ -261,10 +286,12 @@ class Forward:
 
 def fwd(q, k, v, block_indices, block_counts, block_size: int = 64, scale: float | None = None,
         cu_seqlens=None, out=None, lse=None, workspace=None, return_lse: bool = True,
-        index_layout: str = "token"):
-    """Native sparse attention forward on the GPU.  Returns (out, lse)."""
+        index_layout: str = "token", check: bool = True):
+    """Native sparse attention forward on the GPU.  Returns (out, lse).
+    With ``check`` (the default) the device status is read after the launch
+    and an expired wait raises ``NsaDeviceError`` (see ``Forward``)."""
     return Forward(q, k, v, block_indices, block_counts, block_size, scale, cu_seqlens, out, lse,
-                   workspace, return_lse, index_layout).run()
+                   workspace, return_lse, index_layout).run(check=check)
 
 
 def schedule(block_indices, block_counts, Hq, D, block_size, dtype="bf16", cu_seqlens=None):

@@ -11,115 +11,16 @@ namespace {
 
 using nsa::Plan;
 
-size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
-
-bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
-
-// Derive tiling and workspace layout.  Returns NSA_SUCCESS or an error.
+// The plan of a forward call on the current device (its CU count sets the
+// number of persistent workgroups).
 nsa_status make_plan(const nsa_dims* d, int32_t block_size, int32_t num_seqs, bool varlen, Plan* p,
                      bool qblock = false) {
-  if (!d) return NSA_ERROR_INVALID_VALUE;
-  if (d->batch <= 0 || d->seqlen <= 0 || d->num_q_heads <= 0 || d->num_kv_heads <= 0 ||
-      d->head_dim <= 0 || d->num_selected <= 0 || block_size <= 0)
-    return NSA_ERROR_INVALID_VALUE;
-  if (d->num_q_heads % d->num_kv_heads) return NSA_ERROR_INVALID_VALUE;
-  if (varlen && (d->batch != 1 || num_seqs <= 0)) return NSA_ERROR_INVALID_VALUE;
-  if (varlen && qblock) return NSA_ERROR_NOT_SUPPORTED;
-  if (d->dtype != NSA_DTYPE_F32 && d->dtype != NSA_DTYPE_BF16) return NSA_ERROR_NOT_SUPPORTED;
-  if (d->head_dim != 64 && d->head_dim != 128) return NSA_ERROR_NOT_SUPPORTED;
-  if (block_size != 32 && block_size != 64 && block_size != 128) return NSA_ERROR_NOT_SUPPORTED;
-  const int64_t rows = (int64_t)d->batch * d->seqlen;
-  if (rows * d->num_q_heads * d->head_dim > INT64_C(1) << 40 || rows > INT32_MAX / 2)
-    return NSA_ERROR_NOT_SUPPORTED;
-
-  Plan& P = *p;
-  P = Plan{};
-  P.B = d->batch;
-  P.T = d->seqlen;
-  P.Hq = d->num_q_heads;
-  P.Hkv = d->num_kv_heads;
-  P.D = d->head_dim;
-  P.S = d->num_selected;
-  P.bs = block_size;
-  P.G = P.Hq / P.Hkv;
-  P.varlen = varlen;
-  P.qblock = qblock;
-  P.nqb = (P.T + P.bs - 1) / P.bs;
-  P.num_seqs = varlen ? num_seqs : P.B;
-  P.bf16 = d->dtype == NSA_DTYPE_BF16;
-  // head groups of at most 16 heads (one MFMA column tile)
-  if (P.G <= 16) {
-    P.gv = P.G;
-    P.gpk = 1;
-  } else if (P.G % 16 == 0 && P.G <= 1024) {
-    P.gv = 16;
-    P.gpk = P.G / 16;
-  } else {
-    return NSA_ERROR_NOT_SUPPORTED;
-  }
-  P.hv = P.Hkv * P.gpk;
-  // tokens per 16-column tile: the largest power of two with tpt * gv <= 16
-  P.tpt = 1;
-  while (P.tpt * 2 * P.gv <= 16) P.tpt *= 2;
-  P.ntpw = P.bf16 ? 1 : ((P.tpt * 2 * nsa::kConsumers <= nsa::kMaxTileTokensF32) ? 2 : 1);
-  P.tpw = P.tpt * P.ntpw;
-  P.kb = P.bs < 64 ? P.bs : 64;
-  P.nsb = P.bs / P.kb;
-  const int64_t nb_max = (P.T + P.bs - 1) / P.bs;  // a sequence is at most T long
-  if (nb_max > (int64_t)nsa::kMaxBitmapWords * 32) return NSA_ERROR_NOT_SUPPORTED;
-  // Tokens per item: one tile per attention wave (bf16 up to 256 tokens,
-  // fp32 up to 128).  An item wider than 128 tokens is used only where its
-  // merged list and token masks fit the scheduler's 64 KB of LDS per wave;
-  // otherwise the item falls back to 128 tokens.
-  const int64_t nbw = (nb_max + 31) / 32;
-  int64_t umax = 1;
-  auto size_for = [&](int32_t tq) {
-    P.tq = tq;
-    P.mw = (tq + 31) / 32;
-    umax = std::max<int64_t>(1, std::min<int64_t>((int64_t)tq * P.S, nb_max));
-  };
-  size_for(std::min(nsa::kConsumers * P.tpw, P.bf16 ? nsa::kMaxTileTokens : nsa::kMaxTileTokensF32) / P.tpw *
-           P.tpw);
-  if (P.tq > 128 &&
-      (umax > nsa::kMaxUnion || (2 * nbw + (int64_t)P.mw * umax) * (int64_t)sizeof(uint32_t) > 64 * 1024))
-    size_for(std::min(nsa::kConsumers * P.tpw, 128) / P.tpw * P.tpw);
-  if (umax > nsa::kMaxUnion) return NSA_ERROR_NOT_SUPPORTED;
-  const int64_t Ttot = rows;
-  const int64_t n_tiles =
-      varlen ? Ttot / P.tq + P.num_seqs : (int64_t)P.B * ((P.T + P.tq - 1) / P.tq);
-  const int64_t n_items = n_tiles * P.hv;
-  if (n_items > INT32_MAX / 2) return NSA_ERROR_NOT_SUPPORTED;
-  P.n_tiles = (int32_t)n_tiles;
-  P.n_items = (int32_t)n_items;
-  P.nb_max = (int32_t)nb_max;
-  P.umax = (int32_t)umax;
-  P.umax_units = (int32_t)((umax * P.nsb + 15) / 16 * 16);
-  P.n_chunks = (int32_t)((n_items + nsa::kChunk - 1) / nsa::kChunk);
-  int cus = nsa::device_cu_count();
-  if (cus <= 0) cus = 256;
-  const int64_t wg = std::min<int64_t>(n_items, cus);
-  P.nwg = (int32_t)((wg + nsa::kXcds - 1) / nsa::kXcds * nsa::kXcds);
-
-  size_t off = 0;
-  auto take = [&](size_t bytes) {
-    const size_t at = off;
-    off = align_up(off + bytes, 256);
-    return at;
-  };
-  P.off_tile_start = take(sizeof(int32_t) * (P.num_seqs + 1));
-  P.off_hdr = take(sizeof(nsa::ItemHeader) * n_items);
-  P.off_bucket = take(sizeof(int32_t) * n_items);
-  P.off_blocks = take(sizeof(int32_t) * n_items * P.umax);
-  P.off_masks = take(sizeof(uint32_t) * P.mw * n_items * P.umax);
-  P.off_units = take(sizeof(uint32_t) * n_items * P.umax_units);
-  P.off_hist = take(sizeof(int32_t) * (size_t)nsa::kNumBuckets * P.n_chunks);
-  P.off_off = take(sizeof(int32_t) * (size_t)nsa::kNumBuckets * P.n_chunks);
-  P.off_total = take(sizeof(int32_t) * nsa::kNumBuckets);
-  P.off_worklist = take(sizeof(int32_t) * n_items);
-  P.off_err = take(sizeof(int32_t) * 4);
-  P.bytes = off;
-  return NSA_SUCCESS;
+  return nsa::make_plan(d, block_size, num_seqs, varlen, p, qblock, nsa::device_cu_count());
 }
+
+using nsa::make_bwd_plan;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 nsa_status check_tensors(const Plan& p, const void* q, const void* k, const void* v, const void* out,
                          const void* workspace, size_t workspace_bytes, float scale) {
@@ -303,8 +204,8 @@ nsa_status nsa_decode(const nsa_dims* d, const void* q, const void* k, const voi
     return NSA_ERROR_NOT_SUPPORTED;
   }
   const int64_t rows = (int64_t)p.B * p.Smax;
-  if (rows * p.Hkv * p.D > INT64_C(1) << 40 || (int64_t)p.B * p.Hkv * p.gpk > INT32_MAX / 2 ||
-      rows > INT32_MAX / 2)
+  if (rows > INT32_MAX / 2 || !nsa::product_le(rows, p.Hkv, p.D, INT64_C(1) << 40) ||
+      !nsa::product_le(p.B, p.Hkv, p.gpk, INT32_MAX / 2))
     return NSA_ERROR_NOT_SUPPORTED;
   if (!q || !k || !v || !out || !seq_lens || !block_indices || !block_counts) return NSA_ERROR_INVALID_VALUE;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return NSA_ERROR_INVALID_VALUE;
@@ -314,43 +215,6 @@ nsa_status nsa_decode(const nsa_dims* d, const void* q, const void* k, const voi
     return NSA_ERROR_LAUNCH_FAILED;
   return NSA_SUCCESS;
 }
-
-namespace {
-
-nsa_status make_bwd_plan(const nsa_dims* d, int32_t block_size, nsa::BwdPlan* p) {
-  if (!d) return NSA_ERROR_INVALID_VALUE;
-  if (d->batch <= 0 || d->seqlen <= 0 || d->num_q_heads <= 0 || d->num_kv_heads <= 0 ||
-      d->head_dim <= 0 || d->num_selected <= 0 || block_size <= 0)
-    return NSA_ERROR_INVALID_VALUE;
-  if (d->num_q_heads % d->num_kv_heads) return NSA_ERROR_INVALID_VALUE;
-  if (d->dtype != NSA_DTYPE_BF16) return NSA_ERROR_NOT_SUPPORTED;
-  if (d->head_dim != 64 && d->head_dim != 128) return NSA_ERROR_NOT_SUPPORTED;
-  if (block_size != 32 && block_size != 64 && block_size != 128) return NSA_ERROR_NOT_SUPPORTED;
-  if (d->num_selected > 64) return NSA_ERROR_NOT_SUPPORTED;
-  p->B = d->batch;
-  p->T = d->seqlen;
-  p->Hq = d->num_q_heads;
-  p->Hkv = d->num_kv_heads;
-  p->D = d->head_dim;
-  p->S = d->num_selected;
-  p->bs = block_size;
-  p->G = p->Hq / p->Hkv;
-  if (p->G <= 16) {
-    p->gv = p->G;
-    p->gpk = 1;
-  } else if (p->G % 16 == 0 && p->G <= 1024) {
-    p->gv = 16;
-    p->gpk = p->G / 16;
-  } else {
-    return NSA_ERROR_NOT_SUPPORTED;
-  }
-  const int64_t rows = (int64_t)p->B * p->T;
-  if (rows * p->Hq * p->D > INT64_C(1) << 40 || rows * p->Hkv * p->gpk > INT32_MAX / 2)
-    return NSA_ERROR_NOT_SUPPORTED;
-  return NSA_SUCCESS;
-}
-
-}  // namespace
 
 size_t nsa_bwd_workspace_size(const nsa_dims* dims, int32_t block_size) {
   nsa::BwdPlan p;

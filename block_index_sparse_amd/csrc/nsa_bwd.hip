@@ -44,15 +44,11 @@ namespace {
 
 using namespace dev;
 
-constexpr int kBwdWaves = 4;
-constexpr int kKvTiles = 4;    // 16-key tiles per dk/dv workgroup (a 64-key chunk)
+constexpr int kBwdWaves = kBwdDqThreads / 64;
+constexpr int kKvTiles = kBwdKvThreads / 64;    // 16-key tiles per dk/dv workgroup (a 64-key chunk)
 constexpr int kStepUnits = 2;  // (reader, head group) units per dk/dv step, taken by every tile wave
 constexpr int kSegMax = 4096;   // readers of a chunk are split into token segments of at most this many tokens
 
-// the segment length: 512 tokens up to T = 4096, then 1024, 2048 past 8192 and 4096 past
-// 16384 tokens (fewer workgroups and partial sums where every segment still has many
-// workgroups; short segments bound the longest workgroup, that of a block every token reads)
-inline int seg_tokens(int T) { return T > 16384 ? 4096 : (T > 8192 ? 2048 : (T > 4096 ? 1024 : 512)); }
 
 struct BwdArgs {
   const void* q;          // [B, T, Hq, D] bf16
@@ -640,20 +636,6 @@ __global__ void __launch_bounds__(256) bwd_reduce_kernel(BwdArgs a) {
 
 }  // namespace
 
-size_t bwd_delta_bytes(const BwdPlan& p) {
-  return ((size_t)p.B * p.T * p.Hq * sizeof(float) + 255) / 256 * 256;
-}
-
-size_t bwd_readers_bytes(const BwdPlan& p) {
-  const size_t nb = (size_t)(p.T + p.bs - 1) / p.bs, nw = (size_t)(p.T + 31) / 32;
-  return ((size_t)p.B * p.Hkv * nb * nw * sizeof(uint32_t) + 255) / 256 * 256;
-}
-
-size_t bwd_workspace_bytes(const BwdPlan& p) {
-  const size_t ns = (size_t)(p.T + seg_tokens(p.T) - 1) / seg_tokens(p.T);
-  return bwd_delta_bytes(p) + bwd_readers_bytes(p) + ns * 2 * (size_t)p.B * p.T * p.Hkv * p.D * sizeof(float);
-}
-
 hipError_t launch_bwd(const BwdPlan& p, const void* q, const void* k, const void* v, const void* out,
                       const float* lse, const void* dout, const int32_t* block_indices,
                       const int32_t* block_counts, float scale, float* dq, float* dk, float* dv,
@@ -688,24 +670,25 @@ hipError_t launch_bwd(const BwdPlan& p, const void* q, const void* k, const void
   a.ns = (p.T + a.seg - 1) / a.seg;
   a.scale = scale;
   a.scale_log2 = scale * 1.4426950408889634f;
-  const int64_t n_dq = (int64_t)p.B * p.T * p.Hkv * p.gpk;
-  const int64_t n_kv = (int64_t)p.B * p.Hkv * ((p.T + 63) / 64) * a.ns;
-  const int64_t n_red = ((int64_t)p.B * p.T * p.Hkv * p.D / 4 + 255) / 256;
-  const int64_t n_bits = (int64_t)p.B * p.Hkv * a.nb * a.nw;
-  hipLaunchKernelGGL(bwd_clear_kernel, dim3((unsigned)std::min<int64_t>((n_bits + 255) / 256, 4096)), dim3(256), 0,
-                     stream, a.readers, n_bits);
-  if (p.D == 64) {
-    hipLaunchKernelGGL(bwd_dq_kernel<64>, dim3((unsigned)n_dq), dim3(64 * kBwdWaves), 0, stream, a);
-    hipLaunchKernelGGL(bwd_dkdv_kernel<64>, dim3((unsigned)n_kv), dim3(64 * kKvTiles), 0, stream, a);
-    hipLaunchKernelGGL(bwd_reduce_kernel<64>, dim3((unsigned)n_red), dim3(256), 0, stream, a);
-  } else if (p.D == 128) {
-    hipLaunchKernelGGL(bwd_dq_kernel<128>, dim3((unsigned)n_dq), dim3(64 * kBwdWaves), 0, stream, a);
-    hipLaunchKernelGGL(bwd_dkdv_kernel<128>, dim3((unsigned)n_kv), dim3(64 * kKvTiles), 0, stream, a);
-    hipLaunchKernelGGL(bwd_reduce_kernel<128>, dim3((unsigned)n_red), dim3(256), 0, stream, a);
-  } else {
-    return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
+  const BwdGrids gr = bwd_grids(p);   // make_bwd_plan kept every grid inside 2^32 work-items
+  hipLaunchKernelGGL(bwd_clear_kernel, dim3((unsigned)std::min<int64_t>((gr.clear_words + 255) / 256, 4096)),
+                     dim3(256), 0, stream, a.readers, gr.clear_words);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // a launch that fails leaves the later ones unlaunched
+  auto three = [&](auto dq_fn, auto kv_fn, auto red_fn) -> hipError_t {
+    hipLaunchKernelGGL(dq_fn, dim3((unsigned)gr.dq), dim3(kBwdDqThreads), 0, stream, a);
+    hipError_t r = hipGetLastError();
+    if (r != hipSuccess) return r;
+    hipLaunchKernelGGL(kv_fn, dim3((unsigned)gr.dkdv), dim3(kBwdKvThreads), 0, stream, a);
+    r = hipGetLastError();
+    if (r != hipSuccess) return r;
+    hipLaunchKernelGGL(red_fn, dim3((unsigned)gr.reduce), dim3(256), 0, stream, a);
+    return hipGetLastError();
+  };
+  if (p.D == 64) return three(bwd_dq_kernel<64>, bwd_dkdv_kernel<64>, bwd_reduce_kernel<64>);
+  if (p.D == 128) return three(bwd_dq_kernel<128>, bwd_dkdv_kernel<128>, bwd_reduce_kernel<128>);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace nsa

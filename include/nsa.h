@@ -34,6 +34,13 @@
  *    lse = -inf.
  *  - Host-detectable argument errors return synchronously before anything is
  *    enqueued; a failed launch returns NSA_ERROR_LAUNCH_FAILED.
+ *  - NSA_SUCCESS from an enqueuing call means the arguments were valid and
+ *    the work was enqueued; it says nothing about how the device run ended.
+ *    The forward kernels' waits are bounded: a wait that expires leaves the
+ *    affected out / lse rows unwritten and is reported ONLY through
+ *    nsa_fwd_device_status (below), which a caller must read before
+ *    trusting the results of nsa_fwd, nsa_fwd_varlen, nsa_fwd_qblock or
+ *    nsa_fwd_execute.
  *  - The workspace is caller-owned device memory of at least
  *    nsa_fwd_workspace_size() bytes, 256-byte aligned; its contents need no
  *    initialisation and are overwritten.  Two calls that share a workspace
@@ -68,7 +75,7 @@ typedef struct {
   int32_t num_kv_heads; /* Hkv                                                */
   int32_t head_dim;     /* D: 64 or 128                                       */
   int32_t num_selected; /* S, last dimension of block_indices (1..1024)       */
-  nsa_dtype dtype;      /* dtype of q, k, v and out                           */
+  int32_t dtype;        /* nsa_dtype of q, k, v and out (other values: NOT_SUPPORTED) */
 } nsa_dims;
 
 /*
@@ -166,9 +173,13 @@ nsa_status nsa_decode(const nsa_dims* dims, const void* q, const void* k, const 
  *  Workspace: nsa_bwd_workspace_size() bytes (Delta [B, T, Hq] float32, a
  *  reader bitmap per key block: B * Hkv * ceil(T / block_size) *
  *  ceil(T / 32) words, and each token segment's partial dK and dV sums:
- *  2 * ceil(T / L) * B * T * Hkv * D float32 with segments of L = 1024
- *  tokens, 2048 when T > 8192, 4096 when T > 16384), 256-byte aligned, no
- *  initialisation needed.
+ *  2 * ceil(T / L) * B * T * Hkv * D float32 with segments of L = 512
+ *  tokens up to T = 4096, 1024 up to 8192, 2048 up to 16384, else 4096),
+ *  256-byte aligned, no initialisation needed.  Past T = 16384 the
+ *  segment length stays 4096, so the partial sums grow as T^2: about
+ *  1.07 GB at B = 1, T = 32768, Hkv = 4, D = 128, 4.3 GB at T = 65536.
+ *  Dims whose kernels would exceed a grid of 2^32 work-items return
+ *  NSA_ERROR_NOT_SUPPORTED.
  * dk and dv sum over a block's readers in token order, so results are
  * deterministic.  NSA_ERROR_NOT_SUPPORTED for fp32, S > 64 and
  * the head_dim / block_size / group limits of nsa_fwd.

@@ -31,6 +31,12 @@ def compare(w, out, lse, ref_out, ref_lse, rows=None, what=""):
     l = lse.reshape(-1, w.Hq).cpu().numpy().astype(np.float64)
     if rows is not None:
         o, l = o[rows], l[rows]
+    return _compare_arrays(w, o, l, ref_out, ref_lse, what)
+
+
+def _compare_arrays(w, o, l, ref_out, ref_lse, what=""):
+    """o/l: GPU results as float64 arrays [n, Hq, D]/[n, Hq] matching the
+    oracle's rows ref_out/ref_lse."""
     ninf_ref = np.isneginf(ref_lse)
     assert np.array_equal(np.isneginf(l), ninf_ref), f"{what}: -inf lse pattern differs"
     fin = ~ninf_ref
@@ -47,6 +53,28 @@ def compare(w, out, lse, ref_out, ref_lse, rows=None, what=""):
     assert ok_o and ok_l, f"{what}: parity failed {stats}"
     assert np.all(o[np.repeat(ninf_ref[..., None], w.D, axis=-1)] == 0.0), f"{what}: empty rows must be 0"
     return stats
+
+
+def compare_every_row(w, out, lse, chunk=4096, threads=0, what=""):
+    """Every output row against the oracle, element by element, in chunks of
+    `chunk` packed tokens (the oracle runs each chunk on all host threads),
+    so host memory stays bounded at any workload size.  Returns the worst
+    max-abs errors over all chunks."""
+    import oracle
+    total = w.B * w.T
+    o_all = out.float().reshape(total, w.Hq, w.D).cpu().numpy()
+    l_all = lse.reshape(total, w.Hq).cpu().numpy()
+    worst = dict(max_abs_out=0.0, max_abs_lse=0.0, max_rel_out=0.0, rows=0)
+    for a in range(0, total, chunk):
+        rows = np.arange(a, min(total, a + chunk), dtype=np.int64)
+        ref_o, ref_l = oracle.fwd_workload(w, tokens=rows, threads=threads)
+        st = _compare_arrays(w, o_all[rows].astype(np.float64), l_all[rows].astype(np.float64), ref_o, ref_l,
+                             what=f"{what} rows {a}..{rows[-1]}")
+        for k in ("max_abs_out", "max_abs_lse", "max_rel_out"):
+            worst[k] = max(worst[k], st[k])
+        worst["rows"] += len(rows)
+    assert worst["rows"] == total
+    return worst
 
 
 def sample_rows(w, n, seed=0):

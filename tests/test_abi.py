@@ -164,3 +164,55 @@ def test_bwd_rejects_bad_arguments():
     assert call(D(), ws_bytes=16) == 3
     assert lib.nsa_bwd_workspace_size(ctypes.byref(D()), 64) > 0
     assert lib.nsa_bwd_workspace_size(ctypes.byref(D(dt=0)), 64) == 0
+
+
+class _StatusLib:
+    """Stands in for libnsa.so with the same call signatures: every launch
+    returns NSA_SUCCESS and nsa_fwd_device_status reports `word`."""
+
+    def __init__(self, word):
+        self.word = word
+        self.status_reads = 0
+
+    def nsa_fwd(self, *args):
+        return 0
+
+    nsa_fwd_varlen = nsa_fwd_qblock = nsa_fwd_execute = nsa_fwd
+
+    def nsa_fwd_device_status(self, dims, bs, nseq, ws, wsb, stream, status_ref):
+        self.status_reads += 1
+        status_ref._obj.value = self.word
+        return 0
+
+
+def _forward_with(lib):
+    f = nsa.Forward.__new__(nsa.Forward)
+    f.lib, f.qblock, f.cu, f.nseq, f.block_size, f.scale = lib, False, None, 0, 64, 0.125
+    f.dims, f.ws_bytes, f.stream = D(), 1 << 20, None
+    f.out, f.lse = "out", "lse"
+    f._p = {n: None for n in ("q", "k", "v", "bi", "bc", "cu", "out", "lse", "workspace")}
+    return f
+
+
+@pytest.mark.parametrize("word", [1, 3])
+def test_expired_wait_raises_through_the_binding(word):
+    """A launch the C call accepted but whose device status word is non-zero
+    (a bounded wait expired) raises NsaDeviceError from run() and execute()
+    by default; check=False returns without reading the word."""
+    lib = _StatusLib(word)
+    f = _forward_with(lib)
+    for call in (f.run, f.execute):
+        with pytest.raises(nsa.NsaDeviceError) as e:
+            call()
+        assert e.value.status == word
+    assert lib.status_reads == 2
+    assert f.run(check=False) == ("out", "lse") and f.execute(check=False) == ("out", "lse")
+    assert lib.status_reads == 2
+    assert f.device_status() == word
+
+
+def test_clean_status_returns_results():
+    lib = _StatusLib(0)
+    f = _forward_with(lib)
+    assert f.run() == ("out", "lse") and f.execute() == ("out", "lse")
+    assert lib.status_reads == 2

@@ -1,8 +1,7 @@
 """GPU parity: the HIP library (through the C ABI) against the CPU fp64
-oracle on the same seeded inputs.  Small cases are compared element by
-element over every output; the five named workloads at full size are
-compared on every output where the oracle finishes in seconds (c0) and on
-sampled token rows otherwise."""
+oracle on the same seeded inputs.  Small cases and the five named workloads
+at full size are compared element by element over every output row (the
+full-size workloads in chunks of tokens, each chunk on all host threads)."""
 import sys
 
 import numpy as np
@@ -10,7 +9,7 @@ import pytest
 
 import nsa_inputs as ni
 import oracle
-from tests._util import compare, run_gpu, sample_rows
+from tests._util import compare, compare_every_row, run_gpu, sample_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -86,13 +85,8 @@ def test_named_workload_full_size(cfg):
     w = ni.make_config(cfg)
     _say(f"[parity] config {cfg} {w.name}: gpu run")
     out, lse = run_gpu(w)
-    if cfg == 0:
-        ref_o, ref_l = oracle.fwd_workload(w)
-        rows = None
-    else:
-        rows = sample_rows(w, 192, seed=cfg)
-        ref_o, ref_l = oracle.fwd_workload(w, tokens=rows)
-    stats = compare(w, out, lse, ref_o, ref_l, rows=rows, what=w.name)
+    _say(f"[parity] config {cfg} {w.name}: oracle on every row")
+    stats = compare_every_row(w, out, lse, what=w.name)
     _say(f"[parity] config {cfg}: {stats}")
     # properties that hold on every row: finite, and |out| bounded by max |v|
     o = out.float()

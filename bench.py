@@ -254,19 +254,31 @@ def algorithmic_bytes(w) -> int:
                + w.block_indices.nbytes + w.block_counts.nbytes)
 
 
+_THREADS = []
+
+
+def _oracle_threads() -> int:
+    """The host threads the oracle runs on, read once before any call that
+    sets a different count (OpenMP keeps the last count it was given)."""
+    import oracle
+    if not _THREADS:
+        _THREADS.append(oracle.max_threads())
+    return _THREADS[0]
+
+
 def cpu_baseline(w, seconds_target=12.0, seed=0):
     """Time the fp64 oracle on a seeded token sample sized to ~seconds_target."""
     import oracle
     rng = np.random.default_rng(seed)
     total = w.B * w.T
-    threads = oracle.max_threads()
+    threads = _oracle_threads()
     n = 32
     used = 0.0
     rows = None
     while True:
         rows = np.sort(rng.choice(total, size=min(n, total), replace=False))
         t0 = time.perf_counter()
-        oracle.fwd_workload(w, tokens=rows)
+        oracle.fwd_workload(w, tokens=rows, threads=threads)
         used = time.perf_counter() - t0
         if used >= seconds_target * 0.6 or n >= total:
             break
@@ -646,18 +658,19 @@ def config_line(cfg, dev, warmup=10, steps=50, cpu_seconds=2.5):
     cl.update(_rates(flop, tm, w))
     if cpu_seconds > 0:
         if w.B * w.T <= 4096:
+            threads = _oracle_threads()
             runs = []
             for _ in range(3):
                 t0 = time.perf_counter()
-                oracle.fwd_workload(w)
+                oracle.fwd_workload(w, threads=threads)
                 runs.append(time.perf_counter() - t0)
             t0 = time.perf_counter()
             oracle.fwd_workload(w, threads=1)
             one = time.perf_counter() - t0
             used = float(np.median(runs))
-            cl["oracle"] = {"value": flop / used / 1e12, "unit": "TFLOP/s", "cores": oracle.max_threads(),
+            cl["oracle"] = {"value": flop / used / 1e12, "unit": "TFLOP/s", "cores": threads,
                             "kind": "oracle", "seconds": used,
-                            "sample": f"whole workload, median of 3 runs on {oracle.max_threads()} OpenMP threads",
+                            "sample": f"whole workload, median of 3 runs on {threads} OpenMP threads",
                             "single_thread_seconds": one}
         else:
             cl["oracle"] = cpu_baseline(w, seconds_target=cpu_seconds, seed=cfg)

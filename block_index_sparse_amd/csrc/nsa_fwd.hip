@@ -688,421 +688,6 @@ __global__ void __launch_bounds__(64 * (kConsumers + kProducers), 1) fwd_bf16_ri
 }
 
 // ---------------------------------------------------------------------------
-// bf16 kernel for head groups of 16 query heads: every wave computes and
-// the ring is refilled by its readers
-//
-// One persistent workgroup of kMtWaves waves per CU; every wave owns NTPW
-// tokens of an item (one 16-column tile each: the token's 16 heads), so an
-// item is kMtWaves * NTPW tokens and each gathered unit serves more of them
-// than one-token waves could (the accumulators of all an item's tokens
-// stay in registers).  There are no loader waves: the units stream through
-// the ring in the same order as in the ring kernel, and the wave that
-// releases the last read of a slot's occupant refills the slot with the
-// next occupant (K and V rows straight from memory to LDS), then publishes
-// it after its next unit of work, or before it next waits, once the loads
-// have landed.  Units that no wave reads are published at once, so every
-// slot sees one publication per unit in stream order:
-//   ready[s] = publications into slot s (unit v readable once
-//              ready[v % R] >= v / R + 1);
-//   done[s]  = releases of the slot's current occupant; the wave whose
-//              release completes the occupant's reader count resets it.
-// A wave waits only for units it reads.  Any unit is published in bounded
-// time: the smallest unpublished one has its slot's previous occupant
-// published, so that occupant's readers (each walking its own units in
-// stream order) all release it, the last one issues the loads and
-// publishes them before its own next wait.  The refill loads are inline
-// asm without outputs, so the compiler's wait insertion never sees them:
-// each wave retires its own refill loads (s_waitcnt vmcnt(0)) before it
-// publishes them, and never needs any other wave's.
-// ---------------------------------------------------------------------------
-template <int D, int KB>
-struct MtCfg {
-  static constexpr int kHalf = KB * D * 2;                        // K (or V) rows of a unit
-  static constexpr int kSlot = 2 * kHalf;
-  static constexpr int kR0 = (128 * 1024) / kSlot;
-  static constexpr int R = kR0 > 8 ? 8 : kR0;                      // ring slots
-  static constexpr int kLoads = kHalf / 1024;                      // 1 KB loads per half
-  static constexpr int kRowsPerLoad = 1024 / (D * 2);
-  static_assert(kLoads % 4 == 0, "loads come in groups of four");
-};
-
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-// One 16-byte-per-lane load from a raw buffer straight into LDS at
-// `lds_addr` (+ 16 * lane).  Nothing else in the kernel keeps a value in m0.
-__device__ __forceinline__ void dma_b128(uint32_t lds_addr, uint32_t voff, i32x4 rsrc, uint32_t soff) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-               :
-               : "s"(lds_addr), "v"(voff), "s"(rsrc), "s"(soff)
-               : "memory", "m0");
-}
-#pragma clang diagnostic pop
-
-// Raw buffer resource (scalar) for the bytes from `at` of a tensor of
-// `total` bytes; reads past the end return zero.
-__device__ __forceinline__ i32x4 rsrc_at(const char* base, int64_t at, int64_t total) {
-  int64_t left = total - at;
-  left = left < 0 ? 0 : (left > 0x7FFFFFFF ? 0x7FFFFFFF : left);
-  const uint64_t p = (uint64_t)(uintptr_t)(base + at);
-  i32x4 r;
-  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)p);
-  r[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(p >> 32) & 0xFFFFu));
-  r[2] = __builtin_amdgcn_readfirstlane((int)left);
-  r[3] = kBufferFlags;
-  return r;
-}
-
-__device__ __forceinline__ int lds_add_rtn(int* p) {
-  int old;
-  asm volatile("ds_add_rtn_u32 %0, %1, %2\n\ts_waitcnt lgkmcnt(0)"
-               : "=v"(old)
-               : "v"(lds_offset(p)), "v"(1)
-               : "memory");
-  return old;
-}
-
-template <int D, int KB, int NTPW, bool kPosScale>
-__global__ void __launch_bounds__(64 * kMtWaves, 1) fwd_bf16_mt_kernel(FwdArgs a) {
-  using C = MtCfg<D, KB>;
-  constexpr int R = C::R;
-  constexpr int KT = D / 32;   // k-steps of S^T = K Q^T
-  constexpr int MT = KB / 16;  // 16-key row tiles of S^T
-  constexpr int KQ = KB / 32;  // 32-key k-steps of O^T += V^T P^T
-  constexpr int DT = D / 16;   // 16-row tiles of O^T
-  constexpr int CH = D / 8;    // 16-byte chunks per row
-  static_assert(MT == 2 || MT == 4, "units of 32 or 64 keys");
-  static_assert(R <= kMtWaves, "the initial fill gives every slot to one wave");
-
-  __shared__ __attribute__((aligned(1024))) char ring[R][C::kSlot];
-  __shared__ int ready[R];
-  __shared__ int done[R];
-
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  if (threadIdx.x < R) {
-    ready[threadIdx.x] = 0;
-    done[threadIdx.x] = 0;
-  }
-  __syncthreads();
-  const int nsb = a.bs / KB;  // units per listed block (1 or 2)
-
-  // ------------------------------------------------------------ refills
-  const char* __restrict__ Kp = reinterpret_cast<const char*>(a.k);
-  const char* __restrict__ Vp = reinterpret_cast<const char*>(a.v);
-  const int row_bytes = a.Hkv * D * 2;   // stride between key rows of one kv head
-  const int64_t kv_bytes = (int64_t)a.Ttot * row_bytes;
-  // a cursor over the stream for the refills (ahead of the compute walk)
-  ItemCursor rc;
-  rc.round = 0;
-  next_item(rc, a);
-  int rc_v0 = 0;
-  int rc_n = rc.valid ? rc.hd.nunion * nsb : 0;
-  uint32_t pend = 0u;   // bit s: this wave's loads into slot s are not yet published
-
-  // word of stream unit v and the byte offset of its first K/V row
-  auto locate = [&](int v, uint32_t& word, int64_t& rb) -> bool {
-    while (rc.valid && v - rc_v0 >= rc_n) {
-      rc_v0 += rc_n;
-      next_item(rc, a);
-      rc_n = rc.valid ? rc.hd.nunion * nsb : 0;
-    }
-    if (!rc.valid) return false;
-    const int uu = v - rc_v0;
-    word = ld_const(a.units, (int64_t)rc.item * a.umax_units + uu);
-    const int h = rc.item / a.n_tiles / a.gpk;
-    const int kstart = (int)(word & 0xFFFFFFu) * a.bs + (uu & (nsb - 1)) * KB;   // nsb is 1 or 2
-    const int row0 = rc.hd.tok0 - rc.hd.pos0 + kstart;
-    rb = ((int64_t)row0 * a.Hkv + h) * (D * 2);
-    return true;
-  };
-  // The unit's K rows into the slot's first half, its V rows into the
-  // second, in the chunk-swizzled layouts the fragment reads expect: load
-  // ld of a half covers rows ld * kRowsPerLoad .. + kRowsPerLoad - 1, lane l
-  // writing the 16 bytes at l * 16 of the load's 1 KB.  Rows past the
-  // tensor's end read as zero (they are masked by causality).
-  auto issue = [&](int slot, int64_t rb) {
-    const i32x4 rs_k = rsrc_at(Kp, rb, kv_bytes);
-    const i32x4 rs_v = rsrc_at(Vp, rb, kv_bytes);
-    const uint32_t base = (uint32_t)__builtin_amdgcn_readfirstlane(
-        (int)(uint32_t)(uintptr_t)((NSA_LDS char*)&ring[slot][0]));
-    // The lane's offsets are formed here from an opaque copy of the lane id,
-    // so the compiler does not keep 2 * kLoads of them alive across the loop.
-    int ln = lane;
-    asm volatile("" : "+v"(ln));
-    // the chunk swizzles repeat every four loads: load 4 q + j is load j
-    // shifted by q groups of rows (a scalar offset)
-    const uint32_t grp = (uint32_t)(4 * C::kRowsPerLoad * row_bytes);
-#pragma unroll
-    for (int j = 0; j < 4; j++) {
-      const int r = j * C::kRowsPerLoad + ln / CH;
-      const uint32_t ko = (uint32_t)(r * row_bytes + ((ln % CH) ^ k_swizzle<D>(r)) * 16);
-#pragma unroll
-      for (int q4 = 0; q4 < C::kLoads / 4; q4++) dma_b128(base + (4 * q4 + j) * 1024, ko, rs_k, q4 * grp);
-    }
-#pragma unroll
-    for (int j = 0; j < 4; j++) {
-      const int r = j * C::kRowsPerLoad + ln / CH;
-      const uint32_t vo = (uint32_t)(r * row_bytes + ((ln % CH) ^ v_swizzle<D>(r)) * 16);
-#pragma unroll
-      for (int q4 = 0; q4 < C::kLoads / 4; q4++)
-        dma_b128(base + C::kHalf + (4 * q4 + j) * 1024, vo, rs_v, q4 * grp);
-    }
-  };
-  // Place stream unit v into its slot (whose previous occupant every reader
-  // has released).  A unit nobody reads is published at once and the next
-  // occupant of the slot placed in its stead.
-  auto refill = [&](int v) {
-    while (true) {
-      uint32_t word;
-      int64_t rb;
-      if (!locate(v, word, rb)) return;
-      const int np = (word >> 31) != 0u ? (int)((word >> 24) & 15u) : 0;
-      const int slot = v % R;
-      if (np > 0) {
-        issue(slot, rb);
-        pend |= 1u << slot;
-        return;
-      }
-      loader_bump(&ready[slot]);
-      v += R;
-    }
-  };
-  // publish this wave's landed refills
-  auto service = [&]() {
-    if (pend != 0u) {
-      wait_vmcnt<0>();
-#pragma unroll
-      for (int s = 0; s < R; s++)
-        if ((pend >> s) & 1u) loader_bump(&ready[s]);
-      pend = 0u;
-    }
-  };
-  if (wave < R) refill(wave);   // initial fill: stream unit w by wave w
-
-  // ------------------------------------------------------------ attention
-  // Column c of every tile is query head c of the group; tile n is token
-  // tok_first + n of the item (wave-uniform).
-  const int c = lane & 15;
-  const int g = lane >> 4;
-  const int tok_first = wave * NTPW;   // this wave's first token inside an item
-  const __bf16* __restrict__ Q = reinterpret_cast<const __bf16*>(a.q);
-  __bf16* __restrict__ Out = reinterpret_cast<__bf16*>(a.out);
-  ItemCursor cs;
-  cs.round = 0;
-  next_item(cs, a);
-  int v_base = 0;
-  bool stuck = false;
-  while (cs.valid && !stuck) {
-    const int item = cs.item;
-    const ItemHeader hd = cs.hd;
-    const int hq = (item / a.n_tiles) * 16 + c;   // this lane's query head
-    const int my_ntok = min(max(hd.ntok - tok_first, 0), NTPW);
-    const int my_tmin = hd.pos0 + tok_first;
-    const int my_tmax = my_tmin + my_ntok - 1;
-    const int nunits = hd.nunion * nsb;
-
-    bf16x8 qf[NTPW][KT];
-    f32x4 o[NTPW][DT];
-    float mrun[NTPW], lrun[NTPW];
-#pragma unroll
-    for (int n = 0; n < NTPW; n++) {
-      // a wave with fewer tokens loads a real row in their place (never read)
-      const int tq_row = my_ntok > 0 ? tok_first + min(n, my_ntok - 1) : 0;
-      const int64_t qrow = ((int64_t)(hd.tok0 + tq_row) * a.Hq + hq) * D;
-#pragma unroll
-      for (int kk = 0; kk < KT; kk++) qf[n][kk] = *reinterpret_cast<const bf16x8*>(Q + qrow + kk * 32 + g * 8);
-#pragma unroll
-      for (int dt = 0; dt < DT; dt++) o[n][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      mrun[n] = -INFINITY;
-      lrun[n] = 0.f;
-    }
-
-    // Token n of the wave against the unit in the slot: S^T = K Q^T, causal
-    // mask on the token's own block, online softmax in the log2 domain,
-    // O^T += V^T P^T.  Only called for tokens that listed the unit's block.
-    auto tile = [&](auto nc, NSA_LDS const char* kl, NSA_LDS const char* vl, int kstart, bool diag) {
-      constexpr int n = decltype(nc)::value;
-      // the unit in 32-key halves: S^T of 32 keys, its softmax step, then its
-      // PV (a smaller working set next to the tokens' accumulators)
-#pragma unroll
-      for (int hk = 0; hk < KQ; hk++) {
-        f32x4 s[2];
-#pragma unroll
-        for (int m2 = 0; m2 < 2; m2++) {
-          s[m2] = f32x4{0.f, 0.f, 0.f, 0.f};
-          const int row = (2 * hk + m2) * 16 + c;
-#pragma unroll
-          for (int kk = 0; kk < KT; kk++) {
-            const int pc = (kk * 4 + g) ^ k_swizzle<D>(row);
-            const bf16x8 kf = *(NSA_LDS const bf16x8*)(kl + row * (D * 2) + pc * 16);
-            s[m2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[n][kk], s[m2], 0, 0, 0);
-          }
-        }
-        const int k0 = kstart + hk * 32;
-        if (diag && k0 + 31 > my_tmin + n) {
-          const int tpos = my_tmin + n;   // the token's position
-#pragma unroll
-          for (int m2 = 0; m2 < 2; m2++) {
-#pragma unroll
-            for (int jj = 0; jj < 4; jj++) {
-              const int kp = k0 + m2 * 16 + g * 4 + jj;
-              if (kp > tpos) s[m2][jj] = -INFINITY;
-            }
-          }
-        }
-        float mx;
-        const float sc = a.scale_log2;
-        if constexpr (kPosScale) {
-          mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
-                     fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
-          mx = max_over_groups(mx) * sc;
-        } else {
-          mx = -INFINITY;
-#pragma unroll
-          for (int m2 = 0; m2 < 2; m2++) {
-#pragma unroll
-            for (int jj = 0; jj < 4; jj++) {
-              s[m2][jj] = s[m2][jj] == -INFINITY ? -INFINITY : s[m2][jj] * sc;
-              mx = fmaxf(mx, s[m2][jj]);
-            }
-          }
-          mx = max_over_groups(mx);
-        }
-        // the running max moves only when a score exceeds it by more than 2^8
-        const bool raise = mx > mrun[n] + 8.f;
-        const float mnew = raise ? mx : mrun[n];
-        const float muse = (mnew == -INFINITY) ? 0.f : mnew;
-        float rsum[2] = {0.f, 0.f};
-        bf16x8 pf;
-#pragma unroll
-        for (int m2 = 0; m2 < 2; m2++) {
-#pragma unroll
-          for (int jj = 0; jj < 4; jj++) {
-            const float pv = kPosScale ? fast_exp2(__builtin_fmaf(s[m2][jj], sc, -muse)) : fast_exp2(s[m2][jj] - muse);
-            pf[m2 * 4 + jj] = (__bf16)pv;
-            rsum[jj & 1] += pv;
-          }
-        }
-        float rs = rsum[0] + rsum[1];
-        rs = sum_over_groups(rs);
-        if (__ballot(raise) != 0ull) {
-          const float alpha = raise ? fast_exp2(mrun[n] - muse) : 1.f;
-          lrun[n] *= alpha;
-#pragma unroll
-          for (int dt = 0; dt < DT; dt++) o[n][dt] *= alpha;
-        }
-        lrun[n] += rs;
-        mrun[n] = mnew;
-        // V^T fragments one 16-row tile at a time (lane (c, g) reads keys
-        // 4g + c/4 of each 16-key quarter of the half, columns 4 (c % 4) .. + 3)
-#pragma unroll
-        for (int dt = 0; dt < DT; dt++) {
-          bf16x8 vf;
-#pragma unroll
-          for (int q2 = 0; q2 < 2; q2++) {
-            const int key = hk * 32 + q2 * 16 + g * 4 + (c >> 2);
-            const int d0 = dt * 16 + (c & 3) * 4;
-            const int pc = (d0 >> 3) ^ v_swizzle<D>(key);
-            const s16x4 t = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (NSA_LDS s16x4*)(vl + key * (D * 2) + pc * 16 + (d0 & 7) * 2));
-            const bf16x4 tb = __builtin_bit_cast(bf16x4, t);
-#pragma unroll
-            for (int e = 0; e < 4; e++) vf[q2 * 4 + e] = tb[e];
-          }
-          o[n][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf, o[n][dt], 0, 0, 0);
-        }
-      }
-    };
-
-    // find this wave's units 64 at a time: lane i examines unit cbase + i
-    for (int cbase = 0; cbase < nunits && my_ntok > 0 && !stuck; cbase += 64) {
-      const int uu = cbase + lane;
-      uint32_t lword = 0u;
-      uint32_t lbits = 0u;
-      if (uu < nunits) {
-        lword = a.units[(int64_t)item * a.umax_units + uu];
-        const int ks = (int)(lword & 0xFFFFFFu) * a.bs + (uu & (nsb - 1)) * KB;   // nsb is 1 or 2
-        if ((lword >> 31) != 0u && ks <= my_tmax) {
-          const uint32_t mk = a.masks[((int64_t)item * a.umax + (uu >> (nsb - 1))) * a.mw + (tok_first >> 5)];
-          lbits = mask_field(mk, tok_first, NTPW);
-        }
-      }
-      uint64_t todo = __ballot(lbits != 0u);
-      while (todo != 0ull && !stuck) {
-        const int b = __builtin_ctzll(todo);
-        todo &= todo - 1ull;
-        const int uu_b = cbase + b;
-        const uint32_t word = (uint32_t)__builtin_amdgcn_readlane((int)lword, b);
-        const uint32_t mine = (uint32_t)__builtin_amdgcn_readlane((int)lbits, b);
-        const int np = (int)((word >> 24) & 15u);
-        const int kstart = (int)(word & 0xFFFFFFu) * a.bs + (uu_b & (nsb - 1)) * KB;
-        const int v = v_base + uu_b;
-        const int slot = v % R;
-        const int need = v / R + 1;
-        if (lds_poll(&ready[slot]) < need) {
-          service();   // whatever this wave owes is published before it waits
-          int spins = 0;
-          while (lds_poll(&ready[slot]) < need) {
-            __builtin_amdgcn_s_sleep(1);
-            if (++spins > kMaxSpin) {
-              stuck = true;
-              break;
-            }
-          }
-          if (stuck) break;
-        }
-        __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        const bool diag = (kstart + KB - 1) > my_tmin;
-        NSA_LDS const char* kl = (NSA_LDS const char*)&ring[slot][0];
-        NSA_LDS const char* vl = kl + C::kHalf;
-        [&]<int... NI>(std::integer_sequence<int, NI...>) {
-          ((((mine >> NI) & 1u) != 0u ? tile(std::integral_constant<int, NI>{}, kl, vl, kstart, diag) : void()),
-           ...);
-        }(std::make_integer_sequence<int, NTPW>{});
-        service();   // refills issued at the previous release have had a unit of work to land
-        // release: this wave's reads of the slot have returned
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        int old = 0;
-        if (lane == 0) old = lds_add_rtn(&done[slot]);
-        old = __builtin_amdgcn_readfirstlane(old);
-        if (old + 1 == np) {
-          // the last reader: reset the count, place the slot's next occupant
-          if (lane == 0) __hip_atomic_store(&done[slot], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-          refill(v + R);
-        }
-      }
-    }
-    if (stuck) break;
-
-    // epilogue: out = O / l (bf16, round to nearest even), lse = ln 2 * (m + log2 l)
-#pragma unroll
-    for (int n = 0; n < NTPW; n++) {
-      if (n >= my_ntok) continue;
-      const float l = lrun[n];
-      const float inv = l > 0.f ? 1.f / l : 0.f;
-      const int64_t orow = ((int64_t)(hd.tok0 + tok_first + n) * a.Hq + hq) * D;
-#pragma unroll
-      for (int dt = 0; dt < DT; dt++) {
-        bf16x4 ov;
-#pragma unroll
-        for (int jj = 0; jj < 4; jj++) ov[jj] = (__bf16)(o[n][dt][jj] * inv);
-        *reinterpret_cast<bf16x4*>(Out + orow + dt * 16 + g * 4) = ov;
-      }
-      if (a.lse && g == 0) {
-        const float lv = l > 0.f ? (mrun[n] + __log2f(l)) * 0.69314718055994530942f : -INFINITY;
-        a.lse[(int64_t)(hd.tok0 + tok_first + n) * a.Hq + hq] = lv;
-      }
-    }
-    v_base += nunits;
-    next_item(cs, a);
-  }
-  service();   // every refill this wave issued is published before it leaves
-  if (stuck) atomicOr(a.err, kErrStuck);
-}
-
-// ---------------------------------------------------------------------------
 // fp32: one wave per (item, token group of `tpw` tokens), no LDS
 // ---------------------------------------------------------------------------
 template <int D, int KB, int NTPW>
@@ -1249,11 +834,8 @@ __global__ void __launch_bounds__(256, 2) fwd_f32_kernel(FwdArgs a) {
 typedef void (*KernelFn)(FwdArgs);
 
 template <int D, int KB>
-KernelFn pick_ntpw(bool bf16, bool mt, int ntpw, bool pos_scale) {
-  if (mt) {
-    if (ntpw == kMtTiles)
-      return pos_scale ? fwd_bf16_mt_kernel<D, KB, kMtTiles, true> : fwd_bf16_mt_kernel<D, KB, kMtTiles, false>;
-  } else if (bf16) {
+KernelFn pick_ntpw(bool bf16, int ntpw, bool pos_scale) {
+  if (bf16) {
     if (ntpw == 1) return pos_scale ? fwd_bf16_ring_kernel<D, KB, 1, true> : fwd_bf16_ring_kernel<D, KB, 1, false>;
   } else {
     switch (ntpw) {
@@ -1264,11 +846,10 @@ KernelFn pick_ntpw(bool bf16, bool mt, int ntpw, bool pos_scale) {
   return nullptr;
 }
 
-KernelFn pick(bool bf16, bool mt, int D, int KB, int ntpw, bool pos_scale) {
-  if (D == 64)
-    return KB == 32 ? pick_ntpw<64, 32>(bf16, mt, ntpw, pos_scale) : pick_ntpw<64, 64>(bf16, mt, ntpw, pos_scale);
+KernelFn pick(bool bf16, int D, int KB, int ntpw, bool pos_scale) {
+  if (D == 64) return KB == 32 ? pick_ntpw<64, 32>(bf16, ntpw, pos_scale) : pick_ntpw<64, 64>(bf16, ntpw, pos_scale);
   if (D == 128)
-    return KB == 32 ? pick_ntpw<128, 32>(bf16, mt, ntpw, pos_scale) : pick_ntpw<128, 64>(bf16, mt, ntpw, pos_scale);
+    return KB == 32 ? pick_ntpw<128, 32>(bf16, ntpw, pos_scale) : pick_ntpw<128, 64>(bf16, ntpw, pos_scale);
   return nullptr;
 }
 
@@ -1315,11 +896,9 @@ hipError_t launch_fwd(const Plan& p, const void* q, const void* k, const void* v
   // Split releases pay where a unit has few readers (one token per wave);
   // with many readers per unit the second release atomic costs more.
   a.split_release = p.tpw == 1 ? 1 : 0;
-  KernelFn fn = pick(p.bf16, p.mt, p.D, p.kb, p.ntpw, a.scale_log2 > 0.f);
+  KernelFn fn = pick(p.bf16, p.D, p.kb, p.ntpw, a.scale_log2 > 0.f);
   if (!fn) return hipErrorInvalidValue;
-  if (p.mt) {
-    hipLaunchKernelGGL(fn, dim3(p.nwg), dim3(64 * kMtWaves), 0, stream, a);
-  } else if (p.bf16) {
+  if (p.bf16) {
     hipLaunchKernelGGL(fn, dim3(p.nwg), dim3(64 * (kConsumers + kProducers)), 0, stream, a);
   } else {
     const int waves = p.n_items * kConsumers;

@@ -32,10 +32,8 @@ constexpr int kMaxTileTokens = 32 * kMaxMaskWords;
 constexpr int kMaxTileTokensF32 = 128;   // tokens per item of the fp32 path
 constexpr int kMaxBitmapWords = 2048;   // blocks per sequence the planner can merge: 65536
 constexpr int kMaxUnion = 2048;         // entries of one item's merged list
-constexpr int kConsumers = 12;      // attention waves per workgroup of the loader-ring kernel
-constexpr int kProducers = 4;       // loader waves per workgroup of the loader-ring kernel
-constexpr int kMtWaves = 8;         // waves per workgroup of the kernel for 16-head groups
-constexpr int kMtTiles = 4;         // tokens per wave there (a power of two)
+constexpr int kConsumers = 12;      // attention waves per forward workgroup
+constexpr int kProducers = 4;       // loader waves per forward workgroup
 constexpr int kXcds = 8;            // XCDs of an MI355X
 
 // Everything the host derives from the call arguments.
@@ -56,9 +54,7 @@ struct Plan {
   int32_t tpt;               // tokens per 16-column MFMA tile
   int32_t ntpw;              // column tiles per attention wave
   int32_t tpw;               // tokens per attention wave
-  bool mt;                   // bf16 with 16-head groups: every wave computes, readers refill the ring
-  int32_t waves;             // attention waves per item
-  int32_t tq;                // tokens per item (at most waves * tpw)
+  int32_t tq;                // tokens per item (at most kConsumers * tpw)
   int32_t mw;                // token-mask words per merged-list entry (ceil(tq / 32))
   int32_t kb;                // keys per streamed unit (min(bs, 64))
   int32_t nsb;               // streamed units per listed block (bs / kb)
@@ -179,9 +175,7 @@ inline nsa_status make_plan(const nsa_dims* d, int32_t block_size, int32_t num_s
   // tokens per 16-column tile: the largest power of two with tpt * gv <= 16
   P.tpt = 1;
   while (P.tpt * 2 * P.gv <= 16) P.tpt *= 2;
-  P.mt = P.bf16 && P.gv == 16;
-  P.waves = P.mt ? kMtWaves : kConsumers;
-  P.ntpw = P.mt ? kMtTiles : (P.bf16 ? 1 : ((P.tpt * 2 * kConsumers <= kMaxTileTokensF32) ? 2 : 1));
+  P.ntpw = P.bf16 ? 1 : ((P.tpt * 2 * kConsumers <= kMaxTileTokensF32) ? 2 : 1);
   P.tpw = P.tpt * P.ntpw;
   P.kb = P.bs < 64 ? P.bs : 64;
   P.nsb = P.bs / P.kb;
@@ -198,10 +192,11 @@ inline nsa_status make_plan(const nsa_dims* d, int32_t block_size, int32_t num_s
     P.mw = (tq + 31) / 32;
     umax = std::max<int64_t>(1, std::min<int64_t>((int64_t)tq * P.S, nb_max));
   };
-  size_for(std::min(P.waves * P.tpw, P.bf16 ? kMaxTileTokens : kMaxTileTokensF32) / P.tpw * P.tpw);
+  size_for(std::min(kConsumers * P.tpw, P.bf16 ? kMaxTileTokens : kMaxTileTokensF32) / P.tpw *
+           P.tpw);
   if (P.tq > 128 &&
       (umax > kMaxUnion || (2 * nbw + (int64_t)P.mw * umax) * (int64_t)sizeof(uint32_t) > 64 * 1024))
-    size_for(std::min(P.waves * P.tpw, 128) / P.tpw * P.tpw);
+    size_for(std::min(kConsumers * P.tpw, 128) / P.tpw * P.tpw);
   if (umax > kMaxUnion) return NSA_ERROR_NOT_SUPPORTED;
   const int64_t Ttot = rows;
   const int64_t n_tiles =

@@ -25,7 +25,7 @@ import ctypes
 import math
 import os
 
-__all__ = ["fwd", "Forward", "decode", "Decode", "bwd", "workspace_size", "schedule", "load_library", "library_path", "NsaError",
+__all__ = ["fwd", "fwd_noalloc", "Forward", "decode", "Decode", "bwd", "workspace_size", "schedule", "load_library", "library_path", "NsaError",
            "NsaDeviceError", "DTYPE_F32", "DTYPE_BF16"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -75,6 +75,8 @@ def load_library():
     lib.nsa_fwd_workspace_size.argtypes = [dp, i32, i32]
     lib.nsa_fwd.restype = ctypes.c_int
     lib.nsa_fwd.argtypes = [dp, p, p, p, p, p, i32, f32, p, p, p, sz, p]
+    lib.nsa_fwd_noalloc.restype = ctypes.c_int
+    lib.nsa_fwd_noalloc.argtypes = [dp, p, p, p, p, p, i32, f32, p, p, p, p]
     lib.nsa_fwd_varlen.restype = ctypes.c_int
     lib.nsa_fwd_varlen.argtypes = [dp, p, p, p, p, p, p, i32, i32, f32, p, p, p, sz, p]
     lib.nsa_fwd_qblock.restype = ctypes.c_int
@@ -292,6 +294,39 @@ def fwd(q, k, v, block_indices, block_counts, block_size: int = 64, scale: float
     and an expired wait raises ``NsaDeviceError`` (see ``Forward``)."""
     return Forward(q, k, v, block_indices, block_counts, block_size, scale, cu_seqlens, out, lse,
                    workspace, return_lse, index_layout).run(check=check)
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def fwd_noalloc(q, k, v, block_indices, block_counts, block_size: int = 64, scale: float | None = None,
+                out=None, lse=None, return_lse: bool = True, device_status=None, check: bool = True):
+    """``nsa_fwd_noalloc``: the fixed-length forward with its workspace in
+    the library's static device array (NOALLOC_SCRATCH_BYTES per GPU), so
+    the C call allocates nothing.  Calls on one GPU must be ordered on one
+    stream (they share the array).  ``device_status``: an int32 GPU tensor of
+    one element that receives the run's status word, or None; with ``check``
+    one is made here, read after the call and an expired wait raises
+    ``NsaDeviceError``.  Returns (out, lse)."""
+    import torch
+    lib = load_library()
+    (q, k, v, bi, bc, _, B, T, Hq, Hkv, D, S, code) = _prepare(q, k, v, block_indices, block_counts, None,
+                                                                int(block_size), "token")
+    dims = _dims(B, T, Hq, Hkv, D, S, code)
+    out = torch.empty_like(q) if out is None else out
+    if lse is None and return_lse:
+        lse = torch.empty((B, T, Hq), dtype=torch.float32, device=q.device)
+    if device_status is None and check:
+        device_status = torch.zeros(1, dtype=torch.int32, device=q.device)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    _check(lib.nsa_fwd_noalloc(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(bi), _ptr(bc), int(block_size),
+                               scale, _ptr(out), _ptr(lse), _ptr(device_status), _stream(torch, q.device)))
+    if check:
+        word = int(device_status.item())
+        if word != 0:
+            raise NsaDeviceError(word, f"forward device status {word:#x}: a bounded wait inside the kernel "
+                                       "expired (NSA_DEVICE_WAIT_EXPIRED); out and lse are incomplete")
+    return out, lse
 
 
 def schedule(block_indices, block_counts, Hq, D, block_size, dtype="bf16", cu_seqlens=None):

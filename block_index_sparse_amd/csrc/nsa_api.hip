@@ -3,6 +3,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstdlib>
+#include <mutex>
 
 #include "nsa.h"
 #include "nsa_internal.h"
@@ -66,6 +67,37 @@ nsa_status run(const nsa_dims* d, const void* q, const void* k, const void* v,
   return NSA_SUCCESS;
 }
 
+// ---------------------------------------------------------------------------
+// Scratch of nsa_fwd_noalloc: the schedule workspace of a fixed-length call,
+// a static device array every GPU the library runs on holds until the
+// process ends.  Host code never uses the array's name as an address: the
+// device address of each GPU's copy is looked up once, with that GPU
+// current, and kept per device.
+constexpr size_t kScratchBytes = NSA_NOALLOC_SCRATCH_BYTES;
+__device__ __attribute__((aligned(256))) char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_ptr[kMaxDevices];
+
+nsa_status scratch_of_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return NSA_ERROR_LAUNCH_FAILED;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return NSA_ERROR_LAUNCH_FAILED;
+    scratch_ptr[dev] = p;
+  }
+  *out = scratch_ptr[dev];
+  return NSA_SUCCESS;
+}
+
+// The run's device status word, copied where the caller asked for it.
+__global__ void copy_status_kernel(const int32_t* __restrict__ err, int32_t* __restrict__ out) {
+  if (threadIdx.x == 0) *out = *err;
+}
+
 }  // namespace
 
 extern "C" {
@@ -82,6 +114,29 @@ nsa_status nsa_fwd(const nsa_dims* dims, const void* q, const void* k, const voi
                    void* stream) {
   return run(dims, q, k, v, block_indices, block_counts, nullptr, 0, false, block_size, scale, out,
              lse, workspace, workspace_bytes, stream);
+}
+
+nsa_status nsa_fwd_noalloc(const nsa_dims* dims, const void* q, const void* k, const void* v,
+                           const int32_t* block_indices, const int32_t* block_counts,
+                           int32_t block_size, float scale, void* out, float* lse,
+                           int32_t* device_status, void* stream) {
+  Plan p;
+  nsa_status st = make_plan(dims, block_size, 0, false, &p);
+  if (st != NSA_SUCCESS) return st;
+  // argument errors first: they need no device
+  if (!block_indices || !block_counts || !q || !k || !v || !out) return NSA_ERROR_INVALID_VALUE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return NSA_ERROR_INVALID_VALUE;
+  if (!std::isfinite(scale)) return NSA_ERROR_INVALID_VALUE;
+  if (p.bytes > kScratchBytes) return NSA_ERROR_WORKSPACE_TOO_SMALL;
+  void* ws = nullptr;
+  st = scratch_of_current_device(&ws);
+  if (st != NSA_SUCCESS) return st;
+  st = run(dims, q, k, v, block_indices, block_counts, nullptr, 0, false, block_size, scale, out, lse, ws,
+           kScratchBytes, stream);
+  if (st != NSA_SUCCESS || !device_status) return st;
+  hipLaunchKernelGGL(copy_status_kernel, dim3(1), dim3(64), 0, reinterpret_cast<hipStream_t>(stream),
+                     reinterpret_cast<const int32_t*>(reinterpret_cast<const char*>(ws) + p.off_err), device_status);
+  return hipGetLastError() == hipSuccess ? NSA_SUCCESS : NSA_ERROR_LAUNCH_FAILED;
 }
 
 nsa_status nsa_fwd_varlen(const nsa_dims* dims, const void* q, const void* k, const void* v,

@@ -97,6 +97,31 @@ nsa_status nsa_fwd(const nsa_dims* dims, const void* q, const void* k, const voi
                    void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * nsa_fwd for callers that cannot allocate (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation): the same
+ * computation, kernels and results as nsa_fwd, with the workspace taken
+ * from a static device array of 32 MiB (NSA_NOALLOC_SCRATCH_BYTES) that every
+ * GPU the library runs on holds until the process ends.  It calls no
+ * allocating routine.  The current device's array is used, so `stream` must
+ * belong to the current device.
+ *  - Dims whose nsa_fwd_workspace_size exceeds the array return
+ *    NSA_ERROR_WORKSPACE_TOO_SMALL before anything is enqueued (the five
+ *    named workloads of the design notes need at most 24.4 MiB).
+ *  - Every call on a GPU uses that GPU's one array: calls that overlap on one
+ *    GPU (different streams, or host threads without ordering) race and give
+ *    undefined results.  Order them on one stream.
+ *  - device_status: NULL, or a DEVICE int32 that receives the run's status
+ *    word (0 = every bounded wait completed; NSA_DEVICE_WAIT_EXPIRED
+ *    otherwise) once the work on `stream` has completed.
+ *  - Other arguments, layouts and errors as nsa_fwd.
+ */
+#define NSA_NOALLOC_SCRATCH_BYTES (32u << 20)
+nsa_status nsa_fwd_noalloc(const nsa_dims* dims, const void* q, const void* k, const void* v,
+                           const int32_t* block_indices, const int32_t* block_counts,
+                           int32_t block_size, float scale, void* out, float* lse,
+                           int32_t* device_status, void* stream);
+
+/*
  * Variable-length forward (the `cu_seqlens` argument of the same page):
  * dims->batch == 1, dims->seqlen = total packed tokens, and the sequences
  * are packed back to back.  cu_seqlens [num_seqs + 1] int32 DEVICE array,

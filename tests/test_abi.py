@@ -216,3 +216,30 @@ def test_clean_status_returns_results():
     f = _forward_with(lib)
     assert f.run() == ("out", "lse") and f.execute() == ("out", "lse")
     assert lib.status_reads == 2
+
+
+def test_noalloc_rejects_before_touching_a_device():
+    """nsa_fwd_noalloc checks its arguments and the scratch limit on the host
+    (no device needed): workspaces above NSA_NOALLOC_SCRATCH_BYTES are refused
+    with NSA_ERROR_WORKSPACE_TOO_SMALL."""
+    lib = nsa.load_library()
+    p = ctypes.c_void_p(256)
+
+    def call(dims, bs=64, scale=1.0, ptr=p, null_at=None):
+        args = [ptr] * 6
+        if null_at is not None:
+            args[null_at] = None
+        return lib.nsa_fwd_noalloc(ctypes.byref(dims), args[0], args[1], args[2], args[3], args[4], bs, scale,
+                                   args[5], None, None, None)
+    big = D(T=65536, Hq=64, Hkv=4, S=16)
+    assert nsa.workspace_size(1, 65536, 64, 4, 128, 16, 64) > nsa.NOALLOC_SCRATCH_BYTES
+    assert call(big) == 3
+    assert call(D(Hkv=3)) == 1
+    assert call(D(Dh=96)) == 2
+    assert call(D(), null_at=0) == 1
+    assert call(D(), null_at=3) == 1
+    assert call(D(), ptr=ctypes.c_void_p(264)) == 1
+    assert call(D(), scale=float("nan")) == 1
+    src = open(os.path.join(ROOT, "include", "nsa.h")).read()
+    assert re.search(r"#define NSA_NOALLOC_SCRATCH_BYTES \(32u << 20\)", src)
+    assert nsa.NOALLOC_SCRATCH_BYTES == 32 << 20

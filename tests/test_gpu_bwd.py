@@ -3,10 +3,13 @@ fp64 gradient oracle (oracle/backward.py, pinned by central differences of
 the forward oracle and by autograd through SDPA).
 
 Tolerance, derived from the arithmetic: the kernels round P and dS to bf16
-(relative error <= 2^-9 each) before the MFMAs that accumulate dq, dk and
-dv in fp32, so a gradient entry's error is bounded by a few 2^-9 times the
-sum of its terms' magnitudes; the bar is |gpu - ref| <= 1e-2 max|ref| +
-1e-2 |ref| per gradient tensor."""
+(relative error <= 2^-9 each) and form Delta from the forward's bf16 out
+before the MFMAs that accumulate dq, dk and dv in fp32, so each gradient
+entry's error is at most 2^-9 times the sum of its terms' magnitudes to
+first order (oracle/backward.py returns that sum per entry; a CPU test
+recomputes the gradients with those roundings and finds every error within
+2^-8 of it).  The bar, per element: |gpu - ref| <= 2^-7 sum|terms| +
+1e-6 max(sum|terms|) (the last for fp32 accumulation order)."""
 import sys
 
 import numpy as np
@@ -41,13 +44,17 @@ def run_bwd(w, dout_bits):
     return nsa.bwd(q, k, v, out, lse, dout, bi, bc, w.block_size, w.scale)
 
 
-def check(name, got, ref):
+def check(name, got, ref, mag):
+    """Per-element bar: |gpu - ref| <= 2^-7 mag + 1e-6 max(mag), mag = the
+    entry's sum of |terms|."""
     g = (got.cpu().numpy() if hasattr(got, "cpu") else got).astype(np.float64)
     err = np.abs(g - ref)
-    scale = float(np.abs(ref).max(initial=0))
-    ok = np.all(err <= 1e-2 * scale + 1e-2 * np.abs(ref))
-    _say(f"[bwd] {name}: max|err| {err.max(initial=0):.3e}, max|ref| {scale:.3e}")
-    assert ok, f"{name}: max|err| {err.max()} vs max|ref| {scale}"
+    bar = 2.0 ** -7 * mag + 1e-6 * float(mag.max(initial=0))
+    ratio = float((err / np.maximum(mag, 1e-30)).max(initial=0))
+    _say(f"[bwd] {name}: max|err| {err.max(initial=0):.3e}, max|ref| {np.abs(ref).max(initial=0):.3e}, "
+         f"max err/sum|terms| {ratio:.2e} (bar {2.0 ** -7:.2e})")
+    bad = np.argwhere(err > bar)
+    assert bad.size == 0, f"{name}: {len(bad)} entries past the bar, first {bad[:3].tolist()}"
 
 
 CASES = [
@@ -73,10 +80,11 @@ def test_bwd_small_cases_all_gradients(case):
     w = ni.make_workload(name, "bf16", [T] * B, Hq, Hkv, D, bs, S, pattern, counts, seed=19)
     dout, dbits = _dout(w, 19)
     dq, dk, dv = run_bwd(w, dbits)
-    rq, rk, rv = obwd.bwd(w.q, w.k, w.v, dout, w.block_indices, w.block_counts, bs, w.scale)
-    check(f"{name} dq", dq, rq)
-    check(f"{name} dk", dk, rk)
-    check(f"{name} dv", dv, rv)
+    rq, rk, rv, mq, mk, mv = obwd.bwd(w.q, w.k, w.v, dout, w.block_indices, w.block_counts, bs, w.scale,
+                                      terms=True)
+    check(f"{name} dq", dq, rq, mq)
+    check(f"{name} dk", dk, rk, mk)
+    check(f"{name} dv", dv, rv, mv)
 
 
 def test_bwd_single_token_sequences():
@@ -88,10 +96,11 @@ def test_bwd_single_token_sequences():
     w = ni.make_workload("bwd_t1", "bf16", [1, 1, 1], 4, 2, 128, 64, 2, "sink_local_random", "full", seed=19)
     dout, dbits = _dout(w, 19)
     dq, dk, dv = run_bwd(w, dbits)
-    rq, rk, rv = obwd.bwd(w.q, w.k, w.v, dout, w.block_indices, w.block_counts, 64, w.scale)
+    rq, rk, rv, mq, mk, mv = obwd.bwd(w.q, w.k, w.v, dout, w.block_indices, w.block_counts, 64, w.scale,
+                                      terms=True)
     assert np.all(rq == 0) and np.all(rk == 0)
     assert float(dq.abs().max()) <= 1e-3 and float(dk.abs().max()) <= 1e-3
-    check("T=1 dv", dv, rv)
+    check("T=1 dv", dv, rv, mv)
     want = dout.astype(np.float64).reshape(3, 1, 2, 2, 128).sum(axis=3)        # [B, T, Hkv, D]
     np.testing.assert_allclose(rv, want, rtol=0, atol=1e-12)
 
@@ -106,10 +115,11 @@ def test_bwd_hostile_entries():
     w.block_counts = rng.integers(-2, 8, size=w.block_counts.shape).astype(np.int32)
     dout, dbits = _dout(w, 7)
     dq, dk, dv = run_bwd(w, dbits)
-    rq, rk, rv = obwd.bwd(w.q, w.k, w.v, dout, w.block_indices, w.block_counts, 64, w.scale)
-    check("hostile dq", dq, rq)
-    check("hostile dk", dk, rk)
-    check("hostile dv", dv, rv)
+    rq, rk, rv, mq, mk, mv = obwd.bwd(w.q, w.k, w.v, dout, w.block_indices, w.block_counts, 64, w.scale,
+                                      terms=True)
+    check("hostile dq", dq, rq, mq)
+    check("hostile dk", dk, rk, mk)
+    check("hostile dv", dv, rv, mv)
     assert np.any(np.all(rq == 0, axis=(-1, -2)))   # some token sees nothing
 
 
@@ -125,8 +135,9 @@ def test_bwd_named_workload_full_size(cfg):
     dout, dbits = _dout(w, 100 + cfg)
     dq, dk, dv = run_bwd(w, dbits)
     rows = sample_rows(w, 24, seed=cfg)
-    rq = obwd.dq_rows(w.q, w.k, w.v, dout, w.block_indices, w.block_counts, w.block_size, w.scale, rows)
-    check(f"config {cfg} dq rows", dq.reshape(-1, w.Hq, w.D)[rows], rq)
+    rq, mq = obwd.dq_rows(w.q, w.k, w.v, dout, w.block_indices, w.block_counts, w.block_size, w.scale, rows,
+                          terms=True)
+    check(f"config {cfg} dq rows", dq.reshape(-1, w.Hq, w.D)[rows], rq, mq)
     dvs = dv.double().sum(dim=1).cpu().numpy()                      # [B, Hkv, D]
     dks = dk.double().sum(dim=1).cpu().numpy()
     dos = dout.astype(np.float64).sum(axis=1).reshape(w.B, w.Hkv, w.G, w.D).sum(axis=2)
@@ -146,11 +157,19 @@ def test_bwd_named_workload_full_size(cfg):
     blocks = [(0, 0, 0), (w.B - 1, w.Hkv - 1, nb - 1)]
     blocks += [(int(rng.integers(w.B)), int(rng.integers(w.Hkv)), int(rng.integers(1, nb))) for _ in range(3)]
     _check_blocks(w, dout, dk, dv, blocks, f"config {cfg}")
+    if cfg == 1:
+        # every key of one kv head of one sequence
+        _say(f"[bwd] config {cfg}: oracle dK, dV of every key of sequence 0, kv head 0")
+        hk, hv, hmk, hmv = obwd.dkdv_head(w.q, w.k, w.v, dout, w.block_indices, w.block_counts, w.block_size,
+                                          w.scale, 0, 0)
+        check(f"config {cfg} dk head", dk[0, :, 0], hk, hmk)
+        check(f"config {cfg} dv head", dv[0, :, 0], hv, hmv)
 
 
 def _check_blocks(w, dout, dk, dv, blocks, what):
     _say(f"[bwd] {what}: oracle dK, dV of key blocks {blocks}")
-    rk, rv = obwd.dkdv_blocks(w.q, w.k, w.v, dout, w.block_indices, w.block_counts, w.block_size, w.scale, blocks)
+    rk, rv, mk, mv = obwd.dkdv_blocks(w.q, w.k, w.v, dout, w.block_indices, w.block_counts, w.block_size, w.scale,
+                                      blocks, terms=True)
     bs = w.block_size
     gk = np.zeros_like(rk)
     gv = np.zeros_like(rv)
@@ -160,8 +179,8 @@ def _check_blocks(w, dout, dk, dv, blocks, what):
         n = min(bs, w.T - j * bs)
         gk[r, :n] = dk_[b, j * bs:j * bs + n, h]
         gv[r, :n] = dv_[b, j * bs:j * bs + n, h]
-    check(f"{what} dk blocks", gk, rk)
-    check(f"{what} dv blocks", gv, rv)
+    check(f"{what} dk blocks", gk, rk, mk)
+    check(f"{what} dv blocks", gv, rv, mv)
 
 
 def test_bwd_segments_deterministic():

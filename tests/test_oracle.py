@@ -497,3 +497,80 @@ def test_block_gradients_match_full_gradients():
         np.testing.assert_allclose(gv[r, :n], dv[b, 4 * j:4 * j + n, h], rtol=0, atol=1e-12)
         assert np.all(gk[r, n:] == 0) and np.all(gv[r, n:] == 0)
     assert sum(bool(np.any(gv[r] != 0)) for r in range(len(blocks))) >= 3
+
+
+# ---------------------------------------------------------------------------
+# term magnitudes of the gradients (the per-entry tolerance scale of the GPU
+# backward test)
+
+
+def _grad_case(seed=3, G=4, D=64, bs=32, T=130):
+    w = ni.make_workload("tm", "bf16", [T], 2 * G, 2, D, bs, 5, "sink_local_random", "uniform", seed=seed)
+    x = ni.normal(seed + 50, 9, w.q.size).reshape(w.q.shape)
+    dout = ni.bf16_bits_to_f32(ni.to_bf16_bits(x)).reshape(x.shape)
+    return w, dout
+
+
+def test_term_magnitudes_bound_the_gradients():
+    """sum |terms| >= |sum terms| entry by entry (zero magnitude only with a
+    zero gradient); asking for the magnitudes leaves the gradients unchanged."""
+    w, dout = _grad_case()
+    g = obwd.bwd(w.q, w.k, w.v, dout, w.block_indices, w.block_counts, w.block_size, w.scale)
+    r = obwd.bwd(w.q, w.k, w.v, dout, w.block_indices, w.block_counts, w.block_size, w.scale, terms=True)
+    for a, b in zip(g, r[:3]):
+        assert np.array_equal(a, b)
+    for grad, mag in zip(r[:3], r[3:]):
+        assert np.all(mag >= np.abs(grad) * (1 - 1e-12))
+        assert np.all(grad[mag == 0] == 0)
+        assert np.any(mag > 0)
+
+
+def test_per_head_dkdv_matches_full_backward():
+    w, dout = _grad_case(seed=8, G=3, D=64, bs=32, T=97)
+    _, dk, dv, _, mk, mv = obwd.bwd(w.q, w.k, w.v, dout, w.block_indices, w.block_counts, w.block_size, w.scale,
+                                    terms=True)
+    for h in range(w.Hkv):
+        hk, hv, hmk, hmv = obwd.dkdv_head(w.q, w.k, w.v, dout, w.block_indices, w.block_counts, w.block_size,
+                                          w.scale, 0, h)
+        np.testing.assert_allclose(hk, dk[0, :, h], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(hv, dv[0, :, h], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(hmk, mk[0, :, h], rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(hmv, mv[0, :, h], rtol=1e-12, atol=1e-12)
+
+
+def _bf16(x):
+    return ni.bf16_bits_to_f32(ni.to_bf16_bits(np.asarray(x, np.float32))).astype(np.float64).reshape(np.shape(x))
+
+
+def test_bf16_rounding_of_p_ds_and_o_stays_inside_the_term_bound():
+    """The backward kernels round P (for dV), dS (for dQ, dK) and read O as
+    bf16; recomputing the gradients that way here, each entry's error stays
+    within 2^-8 of its term magnitude (the GPU test allows 2^-7)."""
+    w, dout = _grad_case(seed=12, G=4, D=64, bs=32, T=160)
+    q, k, v = (np.asarray(a, np.float64) for a in (w.q, w.k, w.v))
+    B, T, Hq, D = q.shape
+    G = Hq // w.Hkv
+    rq, rk, rv, mq, mk, mv = obwd.bwd(w.q, w.k, w.v, dout, w.block_indices, w.block_counts, w.block_size,
+                                      w.scale, terms=True)
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    for t in range(T):
+        for h in range(w.Hkv):
+            n = max(0, min(int(w.block_counts[0, t, h]), w.S))
+            listed = {int(e) for e in w.block_indices[0, t, h, :n] if 0 <= int(e) <= t // w.block_size}
+            keys = np.array([s for s in range(t + 1) if s // w.block_size in listed], dtype=np.int64)
+            if len(keys) == 0:
+                continue
+            K, V = k[0, keys, h], v[0, keys, h]
+            for hq in range(h * G, (h + 1) * G):
+                z = w.scale * (K @ q[0, t, hq])
+                p = np.exp(z - z.max())
+                p /= p.sum()
+                do = np.asarray(dout[0, t, hq], np.float64)
+                o_b = _bf16(p @ V)                       # the forward's rounded output
+                dp = V @ do
+                ds = _bf16(p * (dp - do @ o_b))          # Delta from rounded O, dS rounded
+                dv[0, keys, h] += _bf16(p)[:, None] * do[None, :]
+                dq[0, t, hq] += w.scale * (ds @ K)
+                dk[0, keys, h] += w.scale * ds[:, None] * q[0, t, hq][None, :]
+    for got, ref, mag in ((dq, rq, mq), (dk, rk, mk), (dv, rv, mv)):
+        assert np.all(np.abs(got - ref) <= 2.0 ** -8 * mag + 1e-12)

@@ -61,8 +61,8 @@ FWD_KERNEL = "fwd_bf16_ring_kernel"   # the attention kernel of the bf16 forward
 
 KERNEL_SOURCES = {
     # the forward kernel, the helpers it includes and the host code that sizes its tiles
-    "fwd": ("nsa_fwd.hip", "nsa_device.h", "nsa_internal.h", "nsa_api.hip"),
-    "decode": ("nsa_decode.hip", "nsa_device.h", "nsa_internal.h"),
+    "fwd": ("nsa_fwd.hip", "nsa_device.h", "nsa_internal.h", "nsa_plan.h", "nsa_api.hip"),
+    "decode": ("nsa_decode.hip", "nsa_device.h", "nsa_internal.h", "nsa_plan.h"),
 }
 
 

@@ -71,6 +71,7 @@ struct PlanArgs {
   int32_t wave_words;   // LDS words per wave: 2 * nbw + mw * umax
   int32_t qblock;       // rows per query block: [B, Hkv, nqb, S] / [B, Hkv, nqb]
   int32_t nqb;
+  int32_t vec4;         // rows are read 16 bytes at a time (S % 4 == 0, indices 16-byte aligned)
 };
 
 // Attention waves that read a sub-block of an entry: wave wc owns the
@@ -295,6 +296,158 @@ __global__ void __launch_bounds__(256) plan_kernel(PlanArgs a) {
   }
 }
 
+// Lane-per-token planner for sequences of at most 32 * NW blocks (NW <= 16):
+// one workgroup of ceil(tq / 64) waves per item, thread tau owning token tau
+// of the item.  Each thread reads its token's row (the first clamp(count, 0,
+// S) entries) into a register bitmap of the listed blocks it keeps (0 <= idx
+// <= its own block); the item's merged list is the OR of those bitmaps, and
+// the token set of every merged entry is one wave ballot per 64 tokens.  No
+// entry touches shared memory with an atomic, so rows that list the same
+// blocks (dense or causal selections) do not serialise.  It writes exactly
+// what plan_kernel writes.
+__device__ __forceinline__ uint32_t wave_or(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v |= (uint32_t)__shfl_xor((int)v, o, 64);
+  return v;
+}
+
+template <int NW>
+__global__ void __launch_bounds__(256) plan_tokens_kernel(PlanArgs a) {
+  __shared__ uint32_t s_ibm[NW];                        // the item's listed blocks
+  __shared__ int32_t s_blk[32 * NW];                    // merged list
+  __shared__ uint32_t s_tm[32 * NW * kMaxMaskWords];    // token set of every entry, [entry][mw]
+  __shared__ int32_t s_pairs;
+  const int32_t tid = threadIdx.x;
+  const int32_t lane = tid & 63;
+  const int32_t wv = tid >> 6;
+  const int32_t nthr = blockDim.x;
+  const int32_t item = blockIdx.x;
+  if (item >= a.n_items) return;
+  const int32_t vg = item / a.n_tiles;
+  const int32_t tile = item - vg * a.n_tiles;
+  const int32_t h = vg / a.gpk;
+  const int32_t total_tiles = a.tile_start[a.num_seqs];
+  const int32_t chunk = item / kChunk;
+  if (tile >= total_tiles) {
+    if (tid == 0) {
+      a.hdr[item] = ItemHeader{0, 0, 0, 0};
+      a.bucket[item] = 0;
+      atomicAdd(&a.hist[chunk], 1);  // bucket 0 row
+    }
+    return;
+  }
+  int32_t lo = 0, hi = a.num_seqs - 1;
+  while (lo < hi) {
+    const int32_t mid = (lo + hi + 1) >> 1;
+    if (a.tile_start[mid] <= tile) lo = mid; else hi = mid - 1;
+  }
+  const int32_t s = lo;
+  const int32_t bos = a.cu ? a.cu[s] : s * a.T;
+  const int32_t len = a.cu ? (a.cu[s + 1] - a.cu[s]) : a.T;
+  const int32_t pos0 = (tile - a.tile_start[s]) * a.tq;
+  const int32_t ntok = min(a.tq, len - pos0);
+  const int32_t tok0 = bos + pos0;
+
+  if (tid < NW) s_ibm[tid] = 0u;
+  if (tid == 0) s_pairs = 0;
+  // this thread's token: its kept entries as a bitmap of block ids
+  uint32_t bm[NW];
+#pragma unroll
+  for (int w = 0; w < NW; w++) bm[w] = 0u;
+  if (tid < ntok) {
+    const int32_t t = pos0 + tid;
+    const int64_t row = a.qblock ? ((int64_t)((tok0 - pos0) / a.T) * a.Hkv + h) * a.nqb + t / a.bs
+                                 : (int64_t)(tok0 + tid) * a.Hkv + h;
+    int32_t n = a.bc[row];
+    n = n < 0 ? 0 : (n > a.S ? a.S : n);
+    const int32_t own = t / a.bs;
+    const int32_t* r = a.bi + row * a.S;
+    auto keep = [&](int32_t idx) {
+      if (idx >= 0 && idx <= own) {
+        const uint32_t bit = 1u << (idx & 31);
+        const int32_t w = idx >> 5;
+#pragma unroll
+        for (int ww = 0; ww < NW; ww++) bm[ww] |= (ww == w) ? bit : 0u;
+      }
+    };
+    if (a.vec4) {
+      for (int32_t i = 0; i < n; i += 4) {
+        const int4 e = *reinterpret_cast<const int4*>(r + i);   // the row is inside the tensor
+        keep(e.x);
+        if (i + 1 < n) keep(e.y);
+        if (i + 2 < n) keep(e.z);
+        if (i + 3 < n) keep(e.w);
+      }
+    } else {
+      for (int32_t i = 0; i < n; i++) keep(r[i]);
+    }
+  }
+  __syncthreads();   // s_ibm cleared
+#pragma unroll
+  for (int w = 0; w < NW; w++) {
+    const uint32_t x = wave_or(bm[w]);
+    if (lane == 0 && x != 0u) atomicOr(&s_ibm[w], x);
+  }
+  __syncthreads();
+  // merged-list position of each word's first block
+  uint32_t ibm[NW];
+  int32_t wbase[NW];
+  int32_t U = 0;
+#pragma unroll
+  for (int w = 0; w < NW; w++) {
+    ibm[w] = s_ibm[w];
+    wbase[w] = U;
+    U += __popc(ibm[w]);
+  }
+  // token sets: one ballot per (entry, 64 tokens); wave wv owns token words
+  // 2 wv and 2 wv + 1
+  const int32_t mw = a.mw;
+#pragma unroll
+  for (int w = 0; w < NW; w++) {
+    uint32_t bits = ibm[w];
+    while (bits != 0u) {
+      const int32_t b = __builtin_ctz(bits);
+      bits &= bits - 1u;
+      const int32_t cid = wbase[w] + __popc(ibm[w] & ((1u << b) - 1u));
+      const uint64_t m = __ballot((bm[w] >> b) & 1u);
+      if (lane == 0) {
+        if (2 * wv < mw) s_tm[cid * mw + 2 * wv] = (uint32_t)m;
+        if (2 * wv + 1 < mw) s_tm[cid * mw + 2 * wv + 1] = (uint32_t)(m >> 32);
+        if (wv == 0) s_blk[cid] = w * 32 + b;
+      }
+    }
+  }
+  __syncthreads();
+  // emit the list, the token sets and the unit words
+  int32_t pairs = 0;
+  const int64_t lbase = (int64_t)item * a.umax;
+  for (int32_t cid = tid; cid < U; cid += nthr) {
+    const int32_t blk = s_blk[cid];
+    const uint32_t* tm = s_tm + cid * mw;
+    a.blocks[lbase + cid] = blk;
+    for (int32_t w2 = 0; w2 < mw; w2++) {
+      a.masks[(lbase + cid) * mw + w2] = tm[w2];
+      pairs += __popc(tm[w2]);
+    }
+    for (int32_t sb = 0; sb < a.nsb; sb++) {
+      const int32_t kstart = blk * a.bs + sb * a.kb;
+      uint32_t word = 0u;
+      if (kstart <= pos0 + ntok - 1) word = unit_word(blk, readers(tm, mw, a.tpw, kstart - pos0));
+      a.units[(int64_t)item * a.umax_units + cid * a.nsb + sb] = word;
+    }
+  }
+  pairs = wave_sum(pairs);
+  if (lane == 0 && pairs != 0) atomicAdd(&s_pairs, pairs);
+  __syncthreads();
+  if (tid == 0) {
+    a.hdr[item] = ItemHeader{tok0, pos0, ntok, U};
+    const int64_t wgt = ((int64_t)s_pairs * (kNumBuckets - 1) + a.max_pairs - 1) / a.max_pairs;
+    const int32_t b = wgt < kNumBuckets ? (int32_t)wgt : kNumBuckets - 1;
+    a.bucket[item] = b;
+    atomicAdd(&a.hist[(int64_t)b * a.n_chunks + chunk], 1);
+  }
+}
+
 // One workgroup per bucket: exclusive scan over chunks.
 __global__ void __launch_bounds__(256) scan_kernel(const int32_t* __restrict__ hist,
                                                    int32_t* __restrict__ off,
@@ -392,8 +545,21 @@ hipError_t launch_schedule(const Plan& p, const int32_t* block_indices, const in
   a.wave_words = 2 * a.nbw + p.mw * p.umax;
   a.qblock = p.qblock ? 1 : 0;
   a.nqb = p.nqb;
+  a.vec4 = (p.S % 4 == 0) && ((reinterpret_cast<uintptr_t>(block_indices) & 15u) == 0) ? 1 : 0;
   const size_t wave_bytes = sizeof(uint32_t) * (size_t)a.wave_words;
-  if ((int64_t)p.tq * p.S > 64 * 2 * kPlanBatch) {
+  const int nw = (p.nb_max + 31) / 32;   // bitmap words a token's row needs
+  const bool many = (int64_t)p.tq * p.S > 64 * 2 * kPlanBatch;   // index entries per item
+  if (many && nw <= 16) {
+    // wide items (many tokens listing the same blocks: the entry passes of
+    // plan_kernel would serialise on a few LDS words): one lane per token,
+    // a workgroup of ceil(tq / 64) waves per item
+    const dim3 blk(64 * ((p.tq + 63) / 64));
+    if (nw <= 1) plan_tokens_kernel<1><<<p.n_items, blk, 0, stream>>>(a);
+    else if (nw <= 2) plan_tokens_kernel<2><<<p.n_items, blk, 0, stream>>>(a);
+    else if (nw <= 4) plan_tokens_kernel<4><<<p.n_items, blk, 0, stream>>>(a);
+    else if (nw <= 8) plan_tokens_kernel<8><<<p.n_items, blk, 0, stream>>>(a);
+    else plan_tokens_kernel<16><<<p.n_items, blk, 0, stream>>>(a);
+  } else if (many) {
     // many index entries per item: a workgroup per item
     plan_kernel<true><<<p.n_items, 256, wave_bytes, stream>>>(a);
   } else {

@@ -51,13 +51,17 @@ def test_small_cases_all_outputs(case):
     compare(w, out, lse, ref_o, ref_l, what=name)
 
 
-def test_hostile_entries_and_duplicates():
+@pytest.mark.parametrize("G,S", [(16, 6), (1, 8), (1, 7)])
+def test_hostile_entries_and_duplicates(G, S):
     """Negative entries, blocks past own and past the end, counts outside
-    [0, S], repeated blocks: all handled as the oracle's set semantics."""
-    w = ni.make_workload("hostile", "bf16", [250, 250], 32, 2, 128, 64, 6, "local_random", "full", seed=5)
+    [0, S], repeated blocks: all handled as the oracle's set semantics.  With
+    one query head per kv head the items are 192 tokens wide and planned one
+    lane per token (rows read 16 bytes at a time when S is a multiple of 4)."""
+    _say(f"[parity] hostile entries G={G} S={S}")
+    w = ni.make_workload("hostile", "bf16", [250, 250], 2 * G, 2, 128, 64, S, "local_random", "full", seed=5)
     rng = np.random.default_rng(1)
     w.block_indices = rng.integers(-3, 8, size=w.block_indices.shape).astype(np.int32)
-    w.block_counts = rng.integers(-2, 9, size=w.block_counts.shape).astype(np.int32)
+    w.block_counts = rng.integers(-2, S + 3, size=w.block_counts.shape).astype(np.int32)
     out, lse = run_gpu(w)
     ref_o, ref_l = oracle.fwd_workload(w)
     compare(w, out, lse, ref_o, ref_l, what="hostile")

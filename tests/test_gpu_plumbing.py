@@ -123,3 +123,23 @@ def test_empty_rows_give_zero_and_neg_inf():
     for t in list(range(10, 20)) + list(range(30, 40)):
         assert np.all(o[0, t] == 0) and np.all(np.isneginf(l[0, t]))
     assert np.all(np.isfinite(l[0, :10]))
+
+
+def test_misaligned_index_rows_read_one_entry_at_a_time():
+    """block_indices that start 4 bytes past a 16-byte boundary (the C ABI
+    asks no alignment of them) are read entry by entry instead of 16 bytes
+    at a time by the planner of wide items (192-token items of the dense
+    causal workload); the results are bitwise those of an aligned copy."""
+    import torch
+    import block_index_sparse_amd as nsa
+    _say("[plumbing] misaligned index rows")
+    w = ni.make_config(2)
+    q, k, v, bi, bc, _ = to_device(w)
+    out0, lse0 = nsa.fwd(q, k, v, bi, bc, w.block_size, w.scale)
+    buf = torch.empty(bi.numel() + 4, dtype=torch.int32, device=bi.device)
+    bi_off = buf[1:1 + bi.numel()].view(bi.shape)
+    bi_off.copy_(bi)
+    assert bi_off.data_ptr() % 16 == 4
+    out1, lse1 = nsa.fwd(q, k, v, bi_off, bc, w.block_size, w.scale)
+    assert torch.equal(out0.view(torch.int16), out1.view(torch.int16))
+    assert torch.equal(lse0, lse1)

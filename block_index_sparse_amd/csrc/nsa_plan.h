@@ -66,8 +66,8 @@ struct Plan {
   int32_t nb_max;            // upper bound on blocks per sequence
   int32_t nwg;               // persistent forward workgroups
   // workspace layout (byte offsets)
-  size_t off_tile_start, off_hdr, off_bucket, off_blocks, off_masks, off_units, off_hist, off_off,
-      off_total, off_worklist, off_err, bytes;
+  size_t off_tile_start, off_hdr, off_bucket, off_blocks, off_masks, off_units, off_off, off_total,
+      off_worklist, off_err, bytes;
 };
 
 // Decode (one query token per sequence against a KV cache): derived sizes.
@@ -225,7 +225,6 @@ inline nsa_status make_plan(const nsa_dims* d, int32_t block_size, int32_t num_s
   P.off_blocks = take(sizeof(int32_t) * n_items * P.umax);
   P.off_masks = take(sizeof(uint32_t) * P.mw * n_items * P.umax);
   P.off_units = take(sizeof(uint32_t) * n_items * P.umax_units);
-  P.off_hist = take(sizeof(int32_t) * (size_t)kNumBuckets * P.n_chunks);
   P.off_off = take(sizeof(int32_t) * (size_t)kNumBuckets * P.n_chunks);
   P.off_total = take(sizeof(int32_t) * kNumBuckets);
   P.off_worklist = take(sizeof(int32_t) * n_items);

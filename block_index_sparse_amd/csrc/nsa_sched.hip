@@ -20,22 +20,19 @@ namespace nsa {
 
 namespace {
 
-// tile_start[s] = first token tile of sequence s; tile_start[num_seqs] = total
-// tiles.  Also clears the weight histogram and the error word.
+// Packed sequences: tile_start[s] = first token tile of sequence s;
+// tile_start[num_seqs] = total tiles.  (Fixed-length calls need no table:
+// every sequence has ceil(T / tq) tiles.)
 __global__ void __launch_bounds__(256) init_kernel(const int32_t* __restrict__ cu_seqlens,
-                                                   int32_t num_seqs, int32_t T, int32_t tq,
-                                                   int32_t* __restrict__ tile_start,
-                                                   int32_t* __restrict__ hist, int32_t hist_n,
-                                                   int32_t* __restrict__ err) {
-  for (int32_t i = threadIdx.x; i < hist_n; i += blockDim.x) hist[i] = 0;
-  if (threadIdx.x == 0) *err = 0;
+                                                   int32_t num_seqs, int32_t tq,
+                                                   int32_t* __restrict__ tile_start) {
   __shared__ int32_t part[256];
   int32_t carry = 0;
   for (int32_t base = 0; base <= num_seqs; base += 256) {
     const int32_t s = base + (int32_t)threadIdx.x;
     int32_t tiles = 0;
     if (s < num_seqs) {
-      const int32_t len = cu_seqlens ? (cu_seqlens[s + 1] - cu_seqlens[s]) : T;
+      const int32_t len = cu_seqlens[s + 1] - cu_seqlens[s];
       tiles = len > 0 ? (len + tq - 1) / tq : 0;
     }
     part[threadIdx.x] = tiles;
@@ -62,7 +59,6 @@ struct PlanArgs {
   int32_t* blocks;      // [n_items * umax]
   uint32_t* masks;      // [n_items * umax][mw]
   uint32_t* units;      // [n_items * umax_units]
-  int32_t* hist;        // [kNumBuckets][n_chunks]
   int32_t T, Hkv, S, bs, gpk, tq, num_seqs, n_tiles, n_items, umax, n_chunks;
   int32_t max_pairs;    // tq * min(S, blocks per sequence): the heaviest possible item
   int32_t kb, nsb, umax_units, tpw;
@@ -73,6 +69,28 @@ struct PlanArgs {
   int32_t nqb;
   int32_t vec4;         // rows are read 16 bytes at a time (S % 4 == 0, indices 16-byte aligned)
 };
+
+// Sequence s and first position pos0 of token tile `tile` (false past the
+// last tile): closed form for fixed-length sequences, the tile table of
+// init_kernel for packed ones.
+__device__ __forceinline__ bool locate_tile(const PlanArgs& a, int32_t tile, int32_t& s, int32_t& pos0) {
+  if (!a.cu) {
+    const int32_t tps = (a.T + a.tq - 1) / a.tq;
+    if (tile >= a.num_seqs * tps) return false;
+    s = tile / tps;
+    pos0 = (tile - s * tps) * a.tq;
+    return true;
+  }
+  if (tile >= a.tile_start[a.num_seqs]) return false;
+  int32_t lo = 0, hi = a.num_seqs - 1;   // last s with tile_start[s] <= tile
+  while (lo < hi) {
+    const int32_t mid = (lo + hi + 1) >> 1;
+    if (a.tile_start[mid] <= tile) lo = mid; else hi = mid - 1;
+  }
+  s = lo;
+  pos0 = (tile - a.tile_start[s]) * a.tq;
+  return true;
+}
 
 // Attention waves that read a sub-block of an entry: wave wc owns the
 // item's tokens [wc * tpw, wc * tpw + tpw) and reads the sub-block iff one
@@ -166,27 +184,16 @@ __global__ void __launch_bounds__(256) plan_kernel(PlanArgs a) {
   const int32_t vg = item / a.n_tiles;
   const int32_t tile = item - vg * a.n_tiles;
   const int32_t h = vg / a.gpk;
-  const int32_t total_tiles = a.tile_start[a.num_seqs];
-  const int32_t chunk = item / kChunk;
-
-  if (tile >= total_tiles) {
+  int32_t s = 0, pos0 = 0;
+  if (!locate_tile(a, tile, s, pos0)) {
     if (tid == 0) {
       a.hdr[item] = ItemHeader{0, 0, 0, 0};
       a.bucket[item] = 0;
-      atomicAdd(&a.hist[chunk], 1);  // bucket 0 row
     }
     return;
   }
-  // sequence holding this tile: last s with tile_start[s] <= tile
-  int32_t lo = 0, hi = a.num_seqs - 1;
-  while (lo < hi) {
-    const int32_t mid = (lo + hi + 1) >> 1;
-    if (a.tile_start[mid] <= tile) lo = mid; else hi = mid - 1;
-  }
-  const int32_t s = lo;
   const int32_t bos = a.cu ? a.cu[s] : s * a.T;
   const int32_t len = a.cu ? (a.cu[s + 1] - a.cu[s]) : a.T;
-  const int32_t pos0 = (tile - a.tile_start[s]) * a.tq;
   const int32_t ntok = min(a.tq, len - pos0);
   const int32_t tok0 = bos + pos0;
   const int32_t own_hi = (pos0 + ntok - 1) / a.bs;
@@ -292,7 +299,6 @@ __global__ void __launch_bounds__(256) plan_kernel(PlanArgs a) {
     const int64_t wgt = ((int64_t)pairs * (kNumBuckets - 1) + a.max_pairs - 1) / a.max_pairs;
     const int32_t b = wgt < kNumBuckets ? (int32_t)wgt : kNumBuckets - 1;
     a.bucket[item] = b;
-    atomicAdd(&a.hist[(int64_t)b * a.n_chunks + chunk], 1);
   }
 }
 
@@ -326,25 +332,16 @@ __global__ void __launch_bounds__(256) plan_tokens_kernel(PlanArgs a) {
   const int32_t vg = item / a.n_tiles;
   const int32_t tile = item - vg * a.n_tiles;
   const int32_t h = vg / a.gpk;
-  const int32_t total_tiles = a.tile_start[a.num_seqs];
-  const int32_t chunk = item / kChunk;
-  if (tile >= total_tiles) {
+  int32_t s = 0, pos0 = 0;
+  if (!locate_tile(a, tile, s, pos0)) {
     if (tid == 0) {
       a.hdr[item] = ItemHeader{0, 0, 0, 0};
       a.bucket[item] = 0;
-      atomicAdd(&a.hist[chunk], 1);  // bucket 0 row
     }
     return;
   }
-  int32_t lo = 0, hi = a.num_seqs - 1;
-  while (lo < hi) {
-    const int32_t mid = (lo + hi + 1) >> 1;
-    if (a.tile_start[mid] <= tile) lo = mid; else hi = mid - 1;
-  }
-  const int32_t s = lo;
   const int32_t bos = a.cu ? a.cu[s] : s * a.T;
   const int32_t len = a.cu ? (a.cu[s + 1] - a.cu[s]) : a.T;
-  const int32_t pos0 = (tile - a.tile_start[s]) * a.tq;
   const int32_t ntok = min(a.tq, len - pos0);
   const int32_t tok0 = bos + pos0;
 
@@ -370,16 +367,34 @@ __global__ void __launch_bounds__(256) plan_tokens_kernel(PlanArgs a) {
         for (int ww = 0; ww < NW; ww++) bm[ww] |= (ww == w) ? bit : 0u;
       }
     };
+    // rows are read kRowBatch entries at a time, every load of a batch
+    // issued before any is used
+    constexpr int kRowBatch = 32;
     if (a.vec4) {
-      for (int32_t i = 0; i < n; i += 4) {
-        const int4 e = *reinterpret_cast<const int4*>(r + i);   // the row is inside the tensor
-        keep(e.x);
-        if (i + 1 < n) keep(e.y);
-        if (i + 2 < n) keep(e.z);
-        if (i + 3 < n) keep(e.w);
+      for (int32_t i0 = 0; i0 < n; i0 += kRowBatch) {
+        int4 e[kRowBatch / 4];
+#pragma unroll
+        for (int j = 0; j < kRowBatch / 4; j++)
+          if (i0 + 4 * j < n) e[j] = *reinterpret_cast<const int4*>(r + i0 + 4 * j);   // inside the row
+#pragma unroll
+        for (int j = 0; j < kRowBatch / 4; j++) {
+          const int32_t i = i0 + 4 * j;
+          if (i < n) keep(e[j].x);
+          if (i + 1 < n) keep(e[j].y);
+          if (i + 2 < n) keep(e[j].z);
+          if (i + 3 < n) keep(e[j].w);
+        }
       }
     } else {
-      for (int32_t i = 0; i < n; i++) keep(r[i]);
+      for (int32_t i0 = 0; i0 < n; i0 += kRowBatch) {
+        int32_t e[kRowBatch];
+#pragma unroll
+        for (int j = 0; j < kRowBatch; j++)
+          if (i0 + j < n) e[j] = r[i0 + j];
+#pragma unroll
+        for (int j = 0; j < kRowBatch; j++)
+          if (i0 + j < n) keep(e[j]);
+      }
     }
   }
   __syncthreads();   // s_ibm cleared
@@ -444,22 +459,29 @@ __global__ void __launch_bounds__(256) plan_tokens_kernel(PlanArgs a) {
     const int64_t wgt = ((int64_t)s_pairs * (kNumBuckets - 1) + a.max_pairs - 1) / a.max_pairs;
     const int32_t b = wgt < kNumBuckets ? (int32_t)wgt : kNumBuckets - 1;
     a.bucket[item] = b;
-    atomicAdd(&a.hist[(int64_t)b * a.n_chunks + chunk], 1);
   }
 }
 
-// One workgroup per bucket: exclusive scan over chunks.
-__global__ void __launch_bounds__(256) scan_kernel(const int32_t* __restrict__ hist,
+// One workgroup per bucket b: the items of each chunk that fell into b
+// (counted from the items' buckets), then the exclusive scan over chunks.
+// Workgroup 0 also clears the device status word: the schedule is complete
+// before any forward of it runs.
+__global__ void __launch_bounds__(256) scan_kernel(const int32_t* __restrict__ bucket, int32_t n_items,
                                                    int32_t* __restrict__ off,
-                                                   int32_t* __restrict__ total, int32_t n_chunks) {
+                                                   int32_t* __restrict__ total, int32_t n_chunks,
+                                                   int32_t* __restrict__ err) {
   __shared__ int32_t part[256];
   const int b = blockIdx.x;
-  const int32_t* hrow = hist + (int64_t)b * n_chunks;
+  if (b == 0 && threadIdx.x == 0) *err = 0;
   int32_t* orow = off + (int64_t)b * n_chunks;
   int32_t carry = 0;
   for (int32_t base = 0; base < n_chunks; base += 256) {
     const int32_t c = base + (int32_t)threadIdx.x;
-    const int32_t v = c < n_chunks ? hrow[c] : 0;
+    int32_t v = 0;
+    if (c < n_chunks) {
+      const int32_t i0 = c * kChunk, i1 = min(n_items, i0 + kChunk);
+      for (int32_t i = i0; i < i1; i++) v += bucket[i] == b ? 1 : 0;
+    }
     part[threadIdx.x] = v;
     __syncthreads();
     for (int o = 1; o < 256; o <<= 1) {
@@ -504,15 +526,67 @@ __global__ void __launch_bounds__(64) scatter_kernel(const int32_t* __restrict__
   }
 }
 
+// The scan and the scatter in one workgroup, for at most kOrderMaxChunks
+// chunks: per-chunk bucket counts into LDS, a scan per bucket over the
+// chunks, bucket bases longest-first, then every item placed at the same
+// position scan_kernel + scatter_kernel would give it.  Also clears the
+// device status word.
+constexpr int kOrderMaxChunks = 64;
+
+__global__ void __launch_bounds__(256) order_kernel(const int32_t* __restrict__ bucket, int32_t n_items,
+                                                    int32_t n_chunks, int32_t* __restrict__ worklist,
+                                                    int32_t* __restrict__ err) {
+  __shared__ int32_t cnt[kNumBuckets][kOrderMaxChunks];   // count, then start offset inside its bucket
+  __shared__ int32_t base[kNumBuckets];
+  __shared__ int32_t bk[4][kChunk];
+  const int32_t tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  if (tid == 0) *err = 0;
+  for (int32_t i = tid; i < kNumBuckets * kOrderMaxChunks; i += 256) (&cnt[0][0])[i] = 0;
+  __syncthreads();
+  for (int32_t i = tid; i < n_items; i += 256) atomicAdd(&cnt[bucket[i]][i / kChunk], 1);
+  __syncthreads();
+  if (tid < kNumBuckets) {
+    int32_t run = 0;
+    for (int32_t c = 0; c < n_chunks; c++) {
+      const int32_t v = cnt[tid][c];
+      cnt[tid][c] = run;
+      run += v;
+    }
+    base[tid] = run;   // the bucket's total, for now
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int32_t acc = 0;
+    for (int b = kNumBuckets - 1; b >= 0; b--) {
+      const int32_t t = base[b];
+      base[b] = acc;
+      acc += t;
+    }
+  }
+  __syncthreads();
+  // chunk c is placed by wave c % 4: rank = earlier items of the chunk in the same bucket
+  for (int32_t c = wv; c < n_chunks; c += 4) {
+    const int32_t item = c * kChunk + lane;
+    const int32_t b = item < n_items ? bucket[item] : -1;
+    bk[wv][lane] = b;
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    if (item < n_items) {
+      int32_t rank = 0;
+      for (int j = 0; j < lane; j++) rank += (bk[wv][j] == b) ? 1 : 0;
+      worklist[base[b] + cnt[b][c] + rank] = item;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
 }  // namespace
 
 hipError_t launch_schedule(const Plan& p, const int32_t* block_indices, const int32_t* block_counts,
                            const int32_t* cu_seqlens, char* ws, hipStream_t stream) {
   int32_t* tile_start = reinterpret_cast<int32_t*>(ws + p.off_tile_start);
-  int32_t* hist = reinterpret_cast<int32_t*>(ws + p.off_hist);
-  init_kernel<<<1, 256, 0, stream>>>(p.varlen ? cu_seqlens : nullptr, p.num_seqs, p.T, p.tq,
-                                     tile_start, hist, kNumBuckets * p.n_chunks,
-                                     reinterpret_cast<int32_t*>(ws + p.off_err));
+  if (p.varlen) init_kernel<<<1, 256, 0, stream>>>(cu_seqlens, p.num_seqs, p.tq, tile_start);
   PlanArgs a;
   a.bi = block_indices;
   a.bc = block_counts;
@@ -523,7 +597,6 @@ hipError_t launch_schedule(const Plan& p, const int32_t* block_indices, const in
   a.blocks = reinterpret_cast<int32_t*>(ws + p.off_blocks);
   a.masks = reinterpret_cast<uint32_t*>(ws + p.off_masks);
   a.mw = p.mw;
-  a.hist = hist;
   a.T = p.T;
   a.Hkv = p.Hkv;
   a.S = p.S;
@@ -569,10 +642,14 @@ hipError_t launch_schedule(const Plan& p, const int32_t* block_indices, const in
   }
   int32_t* off = reinterpret_cast<int32_t*>(ws + p.off_off);
   int32_t* total = reinterpret_cast<int32_t*>(ws + p.off_total);
-  scan_kernel<<<kNumBuckets, 256, 0, stream>>>(hist, off, total, p.n_chunks);
-  scatter_kernel<<<p.n_chunks, 64, 0, stream>>>(a.bucket, off, total,
-                                                reinterpret_cast<int32_t*>(ws + p.off_worklist),
-                                                p.n_items, p.n_chunks);
+  int32_t* err = reinterpret_cast<int32_t*>(ws + p.off_err);
+  int32_t* worklist = reinterpret_cast<int32_t*>(ws + p.off_worklist);
+  if (p.n_chunks <= kOrderMaxChunks) {
+    order_kernel<<<1, 256, 0, stream>>>(a.bucket, p.n_items, p.n_chunks, worklist, err);
+  } else {
+    scan_kernel<<<kNumBuckets, 256, 0, stream>>>(a.bucket, p.n_items, off, total, p.n_chunks, err);
+    scatter_kernel<<<p.n_chunks, 64, 0, stream>>>(a.bucket, off, total, worklist, p.n_items, p.n_chunks);
+  }
   return hipGetLastError();
 }
 

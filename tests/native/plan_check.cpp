@@ -36,7 +36,7 @@ void check_fwd(const nsa_dims& d, int bs, int ns, bool qblock) {
   if (st != NSA_SUCCESS) return;
   fwd_ok++;
   const size_t offs[] = {p.off_tile_start, p.off_hdr, p.off_bucket, p.off_blocks, p.off_masks, p.off_units,
-                         p.off_hist, p.off_off, p.off_total, p.off_worklist, p.off_err, p.bytes};
+                         p.off_off, p.off_total, p.off_worklist, p.off_err, p.bytes};
   for (size_t i = 0; i < sizeof(offs) / sizeof(offs[0]); i++) {
     expect(offs[i] % 256 == 0, "fwd section alignment", d, bs, ns);
     if (i) expect(offs[i] > offs[i - 1] || (i + 1 == sizeof(offs) / sizeof(offs[0]) && offs[i] >= offs[i - 1]),

@@ -9,12 +9,14 @@
 // bf16 kernel: persistent workgroups of 16 waves, one per CU.
 //  * 4 loader waves stream the K and V rows of each item's merged block list
 //    (ascending block order, `kb` keys per unit) into a ring of R LDS slots.
-//    Loader p owns the units v = p (mod 4).  It fetches the V rows of its
-//    next unit into registers a unit ahead; once every attention wave that
-//    reads the slot's occupant has released its K rows it sends the new K
+//    Loader p owns the units v = p (mod 4).  Once every attention wave that
+//    reads the slot's occupant has released its K rows, it sends the new K
 //    rows straight to LDS with 16-byte buffer loads and publishes them when
-//    they have landed, and once the V rows are released too it stores the
-//    staged V rows and publishes them.
+//    they have landed; then, once the V rows are released too, it sends the
+//    new V rows the same way and publishes them.  A unit's V loads are
+//    issued only after its K rows have landed: the memory pipeline serves a
+//    CU's loads in order, and V queued ahead of another loader's K would
+//    delay the scores every reader waits for first.
 //  * 12 attention waves each own a fixed set of the item's tokens and walk
 //    the same unit sequence without any barrier: a wave waits only for the
 //    unit's data, computes its own tokens that selected the block, releases
@@ -222,7 +224,7 @@ struct RingCfg {
   static constexpr int kLoadsKV = (KB * D * 2) / 1024;           // 1 KB loads per K (or V) unit
   static constexpr int kRowsPerLoad = 1024 / (D * 2);
   static_assert(R % kProducers == 0, "slots per loader");
-  static_assert(kLoadsKV <= 16, "a unit's K rows must fit the loader's staging registers");
+  static_assert(kLoadsKV <= 16, "at most 16 loads per K (or V) half of a unit");
 };
 
 // kPosScale: the softmax scale is > 0, so max(scale * s) = scale * max(s) and
@@ -288,12 +290,10 @@ __global__ void __launch_bounds__(64 * (kConsumers + kProducers), 1) fwd_bf16_ri
     int tgt[kOwn];                          // participant releases owed to each own slot
 #pragma unroll
     for (int j = 0; j < kOwn; j++) tgt[j] = 0;
-    // The V rows of the next own unit wait in registers (16 bytes per lane
-    // per 1 KB load), fetched a whole unit ahead; the K rows go straight
-    // from memory to LDS as soon as the slot's K half is free (its readers
-    // have formed S^T), so their latency overlaps the earlier occupant's
-    // softmax and PV, and the V half, freed last, only waits for the stores.
-    u32x4 vst[C::kLoadsKV];
+    // The K rows go straight from memory to LDS as soon as the slot's K
+    // half is free (its readers have formed S^T), so their latency overlaps
+    // the earlier occupant's softmax and PV; the V rows follow once the K
+    // rows have landed and the V half is free.
     // the item holding the next unit to locate: its first stream index, units, kv head
     int it_v0 = 0;
     int it_n = cs.valid ? cs.hd.nunion * nsb : 0;
@@ -329,10 +329,10 @@ __global__ void __launch_bounds__(64 * (kConsumers + kProducers), 1) fwd_bf16_ri
          ...);
       }(std::make_integer_sequence<int, C::kLoadsKV>{});
     };
-    auto issue_v = [&](int64_t rb) {
+    auto issue_v = [&](int64_t rb, NSA_LDS char* vdst) {
       [&]<int... LI>(std::integer_sequence<int, LI...>) {
-        ((vst[LI] = __builtin_amdgcn_raw_buffer_load_b128(
-              group_rsrc(V, rb + (int64_t)(LI / 4) * grp_bytes, kv_bytes), (int)voff[LI % 4], 0, 0)),
+        (__builtin_amdgcn_raw_ptr_buffer_load_lds(group_rsrc(V, rb + (int64_t)(LI / 4) * grp_bytes, kv_bytes),
+                                                  (NSA_LDS void*)(vdst + LI * 1024), 16, voff[LI % 4], 0, 0, 0),
          ...);
       }(std::make_integer_sequence<int, C::kLoadsKV>{});
     };
@@ -346,14 +346,13 @@ __global__ void __launch_bounds__(64 * (kConsumers + kProducers), 1) fwd_bf16_ri
       __atomic_signal_fence(__ATOMIC_SEQ_CST);
       return true;
     };
-    // Each pass places own unit v_cur (its V rows already in registers):
-    // K loads into the slot, the next unit's word, K landed -> publish K,
-    // V half free -> store V -> publish V, then stage the next unit's V rows.
+    // Each pass places own unit v_cur: K loads into the slot, the next
+    // unit's word, K landed -> publish K, V half free -> V loads into the
+    // slot, V landed -> publish V.
     int v_cur = p;
     int np = 0;               // participants of v_cur
     int64_t rb = 0;           // byte offset of v_cur's first row
     bool have = locate(v_cur, np, rb);
-    if (have && np > 0) issue_v(rb);
     bool stuck = false;
     while (have) {
       const int slot = v_cur % R;
@@ -376,17 +375,14 @@ __global__ void __launch_bounds__(64 * (kConsumers + kProducers), 1) fwd_bf16_ri
       int64_t rb_n = 0;
       const bool have_n = locate(v_cur + kProducers, np_n, rb_n);
       if (np > 0) {
-        wait_vmcnt<0>();   // the K rows (and this unit's staged V rows) have landed
+        wait_vmcnt<0>();   // the K rows have landed
         loader_bump(&ready_k[slot]);
         if (a.split_release && !wait_free(&done[slot], t)) {
           stuck = true;
           break;
         }
-        NSA_LDS char* dst = kdst + KB * D * 2 + lane * 16;
-        [&]<int... LI>(std::integer_sequence<int, LI...>) {
-          ((*(NSA_LDS u32x4*)(dst + LI * 1024) = vst[LI]), ...);
-        }(std::make_integer_sequence<int, C::kLoadsKV>{});
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");   // the V stores have landed
+        issue_v(rb, kdst + KB * D * 2);
+        wait_vmcnt<0>();   // the V rows have landed
         loader_bump(&ready[slot]);
 #pragma unroll
         for (int j = 0; j < kOwn; j++) tgt[j] += (j == js) ? np : 0;
@@ -394,7 +390,6 @@ __global__ void __launch_bounds__(64 * (kConsumers + kProducers), 1) fwd_bf16_ri
         loader_bump(&ready_k[slot]);   // no attention wave reads this unit: nothing to load
         loader_bump(&ready[slot]);
       }
-      if (have_n && np_n > 0) issue_v(rb_n);
       v_cur += kProducers;
       np = np_n;
       rb = rb_n;

@@ -7,31 +7,40 @@
 //   dK_s  = scale sum_{t, hq} dS_s q,    dV_s = sum_{t, hq} P_s dO
 // (the chain rule through the masked softmax; the forward's lse is reused).
 //
-// dq kernel: one workgroup of kBwdWaves waves per (token, kv head, group of
-// <= 16 query heads), the token's kept blocks dealt in 32-key units to the
-// waves like the decode kernel: each wave loads a unit's K and V rows whole
-// (every load instruction reads complete rows) into registers one unit
-// ahead, stores them into its LDS slot and reads back the A operands of
-// S^T = K Q^T and dP^T = V dO^T, and K transposed (ds_read_b64_tr_b16) as
-// the A operand of dQ^T += K^T dS^T.  The waves' partial dQ are summed
-// through LDS.  The kernel also writes Delta and the reader bitmaps for the
-// dk/dv kernel: per (sequence, kv head, key block) a bit per token that
-// keeps the block (from the row's first clamp(count, 0, S) entries
-// 0 <= j <= own; atomic OR, so repeats and order do not matter).
+// dq kernel: one workgroup of kBwdWaves waves per (tile of tpt tokens, kv
+// head, group of <= 16 query heads).  A tile's 16 MFMA columns are its
+// tokens' query heads (tpt = 16 / gv tokens of gv heads each when a kv head
+// has at most 16 query heads, else one token's group of 16), so a gathered
+// unit serves every column whose token kept its block.  The tokens' kept
+// blocks are merged into one ascending list with a token bit set per block
+// and dealt in 32-key units to the waves like the decode kernel: each wave
+// loads a unit's K and V rows whole (every load instruction reads complete
+// rows) into registers one unit ahead, stores them into its LDS slot and
+// reads back the A operands of S^T = K Q^T and dP^T = V dO^T, and K
+// transposed (ds_read_b64_tr_b16) as the A operand of dQ^T += K^T dS^T; a
+// column sees a unit's key iff its token kept the block and the key is not
+// past the token.  The waves' partial dQ are summed through LDS.  The kernel
+// also writes Delta and the reader bitmaps for the dk/dv kernel: per
+// (sequence, kv head, key block) a bit per token that keeps the block (from
+// the row's first clamp(count, 0, S) entries 0 <= j <= own; atomic OR, so
+// repeats and order do not matter).
 //
 // dkdv kernel: one workgroup per (sequence, kv head, 64-key chunk, token
 // segment), one wave per 16-key tile, two workgroups per CU.  Wave 0 turns
 // the chunk's reader bitmaps into a list of the segment's reader tokens, in
 // token order (so the sums are deterministic).  The workgroup then walks the
-// list kStepUnits (reader, head group) units per step: all its lanes load the
-// step's Q_t, dO_t, lse and Delta once into registers two steps ahead and
-// store them into one of two LDS buffers, and each wave takes every unit of
-// the step, one after the other: it forms S = Q K^T and dP = dO V^T for its
-// 16 keys (K and V rows in registers as B operands), P and dS, and
-// accumulates dV += P^T dO and dK += dS^T Q with 16x16x16 MFMAs whose B
-// operands (dO and Q, heads x d) are read transposed from the buffer.  The
-// segments' partial sums are added in segment order by the reduce kernel.
-// Every key row gets written (zeros where no token reads the block).
+// list kStepUnits units per step, a unit being tpt consecutive readers of
+// the list x one head group (16 rows of (reader, query head)): all its
+// lanes load the step's Q_t, dO_t, lse and Delta rows once into registers
+// two steps ahead and store them into one of two LDS buffers, and each wave
+// takes every unit of the step, one after the other: it forms S = Q K^T and
+// dP = dO V^T for its 16 keys (K and V rows in registers as B operands), P
+// and dS (a row sees a key iff its reader reads the key's block and the key
+// is not past the reader), and accumulates dV += P^T dO and dK += dS^T Q
+// with 16x16x16 MFMAs whose B operands (dO and Q, rows x d) are read
+// transposed from the buffer.  The segments' partial sums are added in
+// segment order by the reduce kernel.  Every key row gets written (zeros
+// where no token reads the block).
 #include <utility>
 
 #include "nsa.h"
@@ -45,8 +54,10 @@ namespace {
 using namespace dev;
 
 constexpr int kBwdWaves = kBwdDqThreads / 64;
+constexpr int kDqWindow = 2048;      // blocks whose token bits a dq workgroup holds at a time (<= 32 stretches of 64)
+constexpr int kPairsPerThread = (16 * 64 + kBwdDqThreads - 1) / kBwdDqThreads;   // (token, entry) pairs of a tile
 constexpr int kKvTiles = kBwdKvThreads / 64;    // 16-key tiles per dk/dv workgroup (a 64-key chunk)
-constexpr int kStepUnits = 2;  // (reader, head group) units per dk/dv step, taken by every tile wave
+constexpr int kStepUnits = 2;  // units of 16 (reader, head) rows per dk/dv step, taken by every tile wave
 constexpr int kSegMax = 4096;   // readers of a chunk are split into token segments of at most this many tokens
 
 
@@ -66,6 +77,8 @@ struct BwdArgs {
   uint32_t* readers;      // [B, Hkv, nb, nw] workspace: bit t of block j = token t reads j
   float* part;            // [ns][2][B, T, Hkv, D] workspace: per token segment, dK (unscaled) and dV
   int32_t B, T, Hq, Hkv, S, bs, G, gv, gpk, nb, nw, ns, seg;   // seg: tokens per segment
+  int32_t tpt;            // tokens per dq tile = readers per dk/dv unit (16 / gv if gpk == 1, else 1)
+  int32_t gv_magic;       // (1 << 16) / gv + 1: r / gv = (r * gv_magic) >> 16 for 0 <= r < 16
   float scale;
   float scale_log2;
 };
@@ -73,6 +86,14 @@ struct BwdArgs {
 // ---------------------------------------------------------------------------
 // dq (and Delta)
 // ---------------------------------------------------------------------------
+// A workgroup takes a tile of tpt consecutive tokens of one sequence (tpt =
+// 16 / gv when a kv head's query heads fit one 16-column MFMA tile, else 1)
+// and one group of <= 16 query heads: column c of every tile is token
+// c / gv, head c % gv.  The blocks the tile's tokens keep are merged into one
+// ascending list with a token bit set per block (an LDS window of
+// kDqWindow blocks at a time), and each 32-key unit of the list is computed
+// once for all columns, a column seeing the unit's keys iff its token kept
+// the block and the key is not past the token.
 template <int D>
 __global__ void __launch_bounds__(64 * kBwdWaves) __attribute__((amdgpu_waves_per_eu(2)))
 bwd_dq_kernel(BwdArgs a) {
@@ -85,68 +106,69 @@ bwd_dq_kernel(BwdArgs a) {
   static_assert(16 * D * 4 <= kHalf, "the merge buffer fits a slot");
   // per wave: the unit's K rows, then its V rows (row-major, swizzled)
   __shared__ __attribute__((aligned(1024))) char kslot[kBwdWaves][2 * kHalf];
+  // token bits of the window's blocks
+  __shared__ uint32_t tmask[kDqWindow];
+  __shared__ uint32_t tnz;   // bit s: some block of the window's stretch s of 64 is kept
+  __shared__ int2 ulist[kBwdWaves][64];   // each wave's units of a stretch (first key, token bits)
 
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c = lane & 15;
   const int g = lane >> 4;
   const int wg = blockIdx.x;
   const int grp = wg % a.gpk;
   const int rest = wg / a.gpk;
   const int h = rest % a.Hkv;
-  const int bt = rest / a.Hkv;           // packed token b * T + t
-  const int t = bt % a.T;
-  const int own = t / a.bs;
+  const int rest2 = rest / a.Hkv;
+  const int ntiles = (a.T + a.tpt - 1) / a.tpt;
+  const int b = rest2 / ntiles;
+  const int t0 = (rest2 % ntiles) * a.tpt;         // the tile's first token
+  const int ntok = min(a.tpt, a.T - t0);
+  const int t_last = t0 + ntok - 1;
+  const int nbl = t_last / a.bs + 1;               // blocks up to the last token's own
   const int nsb = a.bs / KB;
 
-  // kept entries of the token's row (S <= 64): first occurrences of entries
-  // 0 <= idx <= own among the first clamp(count, 0, S)
-  const int64_t row = (int64_t)bt * a.Hkv + h;
-  int n = a.bc[row];
-  const int idx = lane < a.S ? a.bi[row * a.S + lane] : -1;
-  n = n < 0 ? 0 : (n > a.S ? a.S : n);
-  n = __builtin_amdgcn_readfirstlane(n);
-  bool keep = lane < n && idx >= 0 && idx <= own;
-  const uint64_t valid = __ballot(keep);
-  for (int j = 0; j < n; j++) {
-    if (((valid >> j) & 1ull) == 0ull) continue;
-    const int vj = __builtin_amdgcn_readlane(idx, j);
-    if (lane > j && idx == vj) keep = false;
-  }
-  const uint64_t kept = __ballot(keep);
-  // the token's bit in the reader bitmap of each block it keeps, for the
-  // dk/dv kernel (atomic OR: order and repeats do not matter); set by the
-  // first head group's workgroup of the (token, kv head)
-  if (grp == 0 && keep)
-    atomicOr(a.readers + (((int64_t)(bt / a.T) * a.Hkv + h) * a.nb + idx) * a.nw + t / 32, 1u << (t & 31));
-  int my_ks = 0;
-  int my_n = 0;
-  {
-    int u = 0;
-    uint64_t m = kept;
-    while (m != 0ull) {
-      const int j = __builtin_ctzll(m);
-      m &= m - 1ull;
-      const int blk = __builtin_amdgcn_readlane(idx, j);
-      for (int sb = 0; sb < nsb; sb++) {
-        const int ks = blk * a.bs + sb * KB;
-        if (ks > t) continue;
-        if (u % kBwdWaves == wave) {
-          my_ks = (lane == my_n) ? ks : my_ks;
-          my_n++;
-        }
-        u++;
+  // the tile's kept entries: pair p = (token p / S, entry p % S), at most
+  // 16 x 64 pairs, kPairsPerThread per thread.  An entry is kept if it is
+  // among the first clamp(count, 0, S) of the row and 0 <= idx <= own
+  // block; repeats are harmless (their bits are OR-ed).  The first head
+  // group's workgroup also sets the token's bit in the reader bitmap of
+  // each kept block, for the dk/dv kernel.
+  int pidx[kPairsPerThread];
+  uint32_t pbit[kPairsPerThread];
+#pragma unroll
+  for (int k = 0; k < kPairsPerThread; k++) {
+    const int pr = k * kBwdDqThreads + tid;
+    pidx[k] = -1;
+    pbit[k] = 0u;
+    if (pr < ntok * a.S) {
+      const int tau = pr / a.S;
+      const int i = pr - tau * a.S;
+      const int t = t0 + tau;
+      const int64_t row = ((int64_t)b * a.T + t) * a.Hkv + h;
+      const int n = min(max(a.bc[row], 0), a.S);
+      const int idx = i < n ? a.bi[row * a.S + i] : -1;
+      if (idx >= 0 && idx <= t / a.bs) {
+        pidx[k] = idx;
+        pbit[k] = 1u << tau;
+        if (grp == 0)
+          atomicOr(a.readers + (((int64_t)b * a.Hkv + h) * a.nb + idx) * a.nw + t / 32, 1u << (t & 31));
       }
     }
   }
 
-  // Q^T and dO^T fragments (B operands), Delta and lse of column c
+  // column c: token t0 + c / gv, head c % gv of the group; Q^T and dO^T
+  // fragments (B operands), Delta and lse of the column
   const __bf16* __restrict__ Q = reinterpret_cast<const __bf16*>(a.q);
   const __bf16* __restrict__ dO = reinterpret_cast<const __bf16*>(a.dout);
   const __bf16* __restrict__ O = reinterpret_cast<const __bf16*>(a.out);
-  const int hq = (h * a.gpk + grp) * a.gv + c;
-  const bool cvalid = c < a.gv;
-  const int64_t qrow = ((int64_t)bt * a.Hq + (cvalid ? hq : 0)) * D;
+  const int tau = c / a.gv;
+  const bool cvalid = tau < ntok && c < a.tpt * a.gv;
+  const int tcol = t0 + (cvalid ? tau : 0);                     // the column's token
+  const int64_t btc = (int64_t)b * a.T + tcol;
+  const int hq = (h * a.gpk + grp) * a.gv + (c - tau * a.gv);
+  const int64_t qrow = (btc * a.Hq + (cvalid ? hq : 0)) * D;
   bf16x8 qf[KT], df[KT];
   float dpart = 0.f;
 #pragma unroll
@@ -163,14 +185,13 @@ bwd_dq_kernel(BwdArgs a) {
     }
   }
   const float delta = sum_over_groups(dpart);
-  const float lse2 = cvalid ? a.lse[(int64_t)bt * a.Hq + hq] * 1.4426950408889634f : INFINITY;
-  if (wave == 0 && g == 0 && cvalid) a.delta[(int64_t)bt * a.Hq + hq] = delta;
+  const float lse2 = cvalid ? a.lse[btc * a.Hq + hq] * 1.4426950408889634f : INFINITY;
+  if (wave == 0 && g == 0 && cvalid) a.delta[btc * a.Hq + hq] = delta;
 
   const char* __restrict__ Kc = reinterpret_cast<const char*>(a.k);
   const char* __restrict__ Vc = reinterpret_cast<const char*>(a.v);
   const int row_bytes = a.Hkv * D * 2;
   const int64_t kv_bytes = (int64_t)a.B * a.T * row_bytes;
-  const int b = bt / a.T;
   // a unit's rows are loaded whole: load l of a lane covers row l * kRpi +
   // lane / (D / 8), 16-byte chunk lane % (D / 8), so each load instruction
   // reads kRpi complete rows (full cache lines)
@@ -195,9 +216,12 @@ bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
   for (int dt = 0; dt < DT; dt++) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   const float sl = a.scale_log2;
+  int my_ks = 0;        // lane i: first key of the wave's i-th unit of the stretch
+  int my_m = 0;         // lane i: its token bits
 
   auto step = [&]<bool kMore>(int i) __attribute__((always_inline)) {
     const int ks = __builtin_amdgcn_readlane(my_ks, i);
+    const uint32_t m = (uint32_t)__builtin_amdgcn_readlane(my_m, i);
     const int64_t rb_n = kMore ? unit_base(__builtin_amdgcn_readlane(my_ks, i + 1)) : 0;
     // the unit's K and V rows into the slot, row-major with 16-byte chunks
     // XOR-swizzled by row (conflict-free writes, A-operand reads and
@@ -235,13 +259,15 @@ bwd_dq_kernel(BwdArgs a) {
       // one 16-key tile's fragments live at a time (register budget)
       __builtin_amdgcn_sched_barrier(0);
     }
-    // P^T = exp2(S^T sl - lse2) (zero where masked), dS^T = P^T (dP^T - Delta)
+    // P^T = exp2(S^T sl - lse2), zero where the column's token did not keep
+    // the block or the key is past it; dS^T = P^T (dP^T - Delta)
+    const bool sel = ((m >> tau) & 1u) != 0u;
 #pragma unroll
     for (int mt = 0; mt < MT; mt++) {
 #pragma unroll
       for (int jj = 0; jj < 4; jj++) {
         const int key = ks + mt * 16 + g * 4 + jj;
-        const float p = (key > t) ? 0.f : fast_exp2(__builtin_fmaf(s[mt][jj], sl, -lse2));
+        const float p = (!sel || key > tcol) ? 0.f : fast_exp2(__builtin_fmaf(s[mt][jj], sl, -lse2));
         s[mt][jj] = p * (dp[mt][jj] - delta);
       }
     }
@@ -275,17 +301,80 @@ bwd_dq_kernel(BwdArgs a) {
       }
     }
   };
-  if (my_n > 0) {
-    const int64_t rb0 = unit_base(__builtin_amdgcn_readlane(my_ks, 0));
-    load_rows(Kc, rb0, kreg);
-    load_rows(Vc, rb0, vreg);
-    for (int i = 0; i + 1 < my_n; i++) step.template operator()<true>(i);
-    step.template operator()<false>(my_n - 1);
+
+  // The wave's units collect in lanes 0 .. my_n - 1 (my_ks, my_m) across
+  // stretches and windows; 64 of them at most, so a stretch that would
+  // overflow the list first runs the list through the pipelined step loop.
+  int my_n = 0;
+  auto run_list = [&]() {
+    if (my_n > 0) {
+      const int64_t rb0 = unit_base(__builtin_amdgcn_readlane(my_ks, 0));
+      load_rows(Kc, rb0, kreg);
+      load_rows(Vc, rb0, vreg);
+      for (int i = 0; i + 1 < my_n; i++) step.template operator()<true>(i);
+      step.template operator()<false>(my_n - 1);
+      my_n = 0;
+    }
+  };
+  int u_next = 0;   // index of the next unit of the tile (units are dealt round robin to the waves)
+  for (int w0 = 0; w0 < nbl; w0 += kDqWindow) {
+    const int wn = min(kDqWindow, nbl - w0);
+    for (int i = tid; i < wn; i += kBwdDqThreads) tmask[i] = 0u;
+    if (tid == 0) tnz = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < kPairsPerThread; k++) {
+      if (pidx[k] >= w0 && pidx[k] < w0 + wn) {
+        atomicOr(&tmask[pidx[k] - w0], pbit[k]);
+        atomicOr(&tnz, 1u << ((pidx[k] - w0) >> 6));
+      }
+    }
+    __syncthreads();
+    // the kept stretches of 64 blocks: lane e looks at block w0 + e0 + e,
+    // whose sub-blocks up to the tile's last token are units
+    uint32_t todo = (uint32_t)__builtin_amdgcn_readfirstlane((int)tnz);
+    while (todo != 0u) {
+      const int e0 = __builtin_ctz(todo) * 64;
+      todo &= todo - 1u;
+      const int e = e0 + lane;
+      const uint32_t m = e < wn ? tmask[e] : 0u;
+      const int blk = w0 + e;
+      const int nsub = m != 0u ? min(nsb, (t_last - blk * a.bs) / KB + 1) : 0;
+      int incl = nsub;
+#pragma unroll
+      for (int o2 = 1; o2 < 64; o2 <<= 1) {
+        const int y = __shfl_up(incl, o2, 64);
+        if (lane >= o2) incl += y;
+      }
+      const int first = u_next + incl - nsub;        // the tile index of this lane's first unit
+      const int total = __shfl(incl, 63, 64);
+      // this wave's units of the stretch: tile index u with u % waves == wave,
+      // the k-th of them at list position my_n + k
+      const int u_mine = u_next + ((wave - u_next) % kBwdWaves + kBwdWaves) % kBwdWaves;
+      u_next += total;
+      const int cnt = u_mine < u_next ? (u_next - 1 - u_mine) / kBwdWaves + 1 : 0;   // <= 64
+      if (my_n + cnt > 64) run_list();
+      for (int sb = 0; sb < nsub; sb++) {
+        const int u = first + sb;
+        if (u % kBwdWaves == wave) ulist[wave][my_n + (u - u_mine) / kBwdWaves] = int2{blk * a.bs + sb * KB, (int)m};
+      }
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      if (lane >= my_n && lane < my_n + cnt) {
+        const int2 ent = ulist[wave][lane];
+        my_ks = ent.x;
+        my_m = ent.y;
+      }
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      my_n += cnt;
+    }
+    __syncthreads();   // every wave is done with the window's bits
   }
+  run_list();
 
   // sum the waves' partial dQ^T through LDS ([d tile][lane group][column]
   // float4s), scale, store fp32
-  __syncthreads();
   float* ow = reinterpret_cast<float*>(&kslot[wave][0]);
 #pragma unroll
   for (int dt = 0; dt < DT; dt++) *reinterpret_cast<f32x4*>(ow + ((dt * 4 + g) * 16 + c) * 4) = o[dt];
@@ -311,12 +400,18 @@ __global__ void __launch_bounds__(256) bwd_clear_kernel(uint32_t* __restrict__ p
 // ---------------------------------------------------------------------------
 // dk, dv
 // ---------------------------------------------------------------------------
-// one Q_t / dO_t / lse / Delta unit of 16 query heads as staged in LDS
+// one unit of 16 (reader token, query head) rows as staged in LDS: the Q
+// and dO rows, lse and Delta of each row, each row's last visible key of
+// the chunk for each of the chunk's blocks, and the unit's header (the OR
+// of its readers' block bits, its last reader)
 template <int D>
 struct KvUnit {
   static constexpr int kRow = D * 2;                  // bytes of one head's row
   static constexpr int kRows = 16 * kRow;             // Q (or dO) rows of 16 heads
-  static constexpr int kBytes = 2 * kRows + 2 * 64;   // Q, dO, lse[16], Delta[16]
+  static constexpr int kLse = 2 * kRows;              // lse[16], then Delta[16]
+  static constexpr int kLim = kLse + 2 * 64;          // int8 lim[2][16]
+  static constexpr int kHdr = kLim + 64;              // int bits, int last token
+  static constexpr int kBytes = kHdr + 64;
   static constexpr int kChunks = kRows / 16;          // 16-byte chunks of Q (or dO)
   static constexpr int kStepChunks = kStepUnits * 2 * kChunks;
   static constexpr int kThreads = 64 * kKvTiles;
@@ -332,9 +427,28 @@ struct KvStage {
   float f;
 };
 
-template <int D>
-__device__ __forceinline__ void kv_stage_load(const BwdArgs& a, const uint16_t* rlist, int nunits, int seg_lo,
-                                              int64_t tok_base, int h, int tid, int step, KvStage<D>& st) {
+// Row r of unit u.  Packed (tpt > 1 readers per unit, then gpk = 1): reader
+// u tpt + r / gv of the list, query head h gv + r % gv; the row exists if
+// r < tpt gv and its reader is on the list.  Otherwise: reader u / gpk,
+// query head (h gpk + u % gpk) gv + r; the row exists if r < gv.  (r / gv
+// as (r * gv_magic) >> 16, exact for r < 16.)
+template <bool kPacked>
+__device__ __forceinline__ int row_reader(const BwdArgs& a, int u, int r) {
+  return kPacked ? u * a.tpt + ((r * a.gv_magic) >> 16) : u / a.gpk;
+}
+template <bool kPacked>
+__device__ __forceinline__ int row_head(const BwdArgs& a, int h, int u, int r) {
+  return kPacked ? h * a.gv + (r - ((r * a.gv_magic) >> 16) * a.gv) : (h * a.gpk + u % a.gpk) * a.gv + min(r, a.gv - 1);
+}
+template <bool kPacked>
+__device__ __forceinline__ bool row_exists(const BwdArgs& a, int u, int r, int nread) {
+  return kPacked ? (r < a.tpt * a.gv && row_reader<true>(a, u, r) < nread) : r < a.gv;
+}
+
+template <int D, bool kPacked>
+__device__ __forceinline__ void kv_stage_load(const BwdArgs& a, const uint16_t* rlist, int nunits, int nread,
+                                              int seg_lo, int64_t tok_base, int h, int tid, int step,
+                                              KvStage<D>& st) {
   using U = KvUnit<D>;
   const __bf16* __restrict__ Q = reinterpret_cast<const __bf16*>(a.q);
   const __bf16* __restrict__ dO = reinterpret_cast<const __bf16*>(a.dout);
@@ -345,24 +459,26 @@ __device__ __forceinline__ void kv_stage_load(const BwdArgs& a, const uint16_t* 
     const int rem = gi % (2 * U::kChunks);
     const int row = (rem % U::kChunks) / (D / 8);
     const int ck = rem % (D / 8);
-    // past the last unit or the group's heads: a clamped in-bounds address
-    // (the value is replaced by zeros or never read)
+    // past the last unit or reader: a clamped in-bounds address (the value
+    // is replaced by zeros or never read)
     const int u = min(kStepUnits * step + unit, nunits - 1);
-    const int t = seg_lo + (rlist[u / a.gpk] & 4095);
-    const int hq = (h * a.gpk + u % a.gpk) * a.gv + min(row, a.gv - 1);
+    const int t = seg_lo + (rlist[min(row_reader<kPacked>(a, u, row), nread - 1)] & 4095);
+    const int hq = row_head<kPacked>(a, h, u, row);
     const __bf16* src = rem < U::kChunks ? Q : dO;
     st.v[l] = *reinterpret_cast<const u32x4*>(src + ((tok_base + t) * a.Hq + hq) * D + ck * 8);
   }
-  // lanes 0 .. 32 kStepUnits - 1: unit tid / 32, lse or Delta ((tid / 16) % 2), head tid % 16
+  // lanes 0 .. 32 kStepUnits - 1: unit tid / 32, lse or Delta ((tid / 16) % 2), row tid % 16
   const int unit = (tid >> 5) % kStepUnits;
   const int u = min(kStepUnits * step + unit, nunits - 1);
-  const int t = seg_lo + (rlist[u / a.gpk] & 4095);
-  const int hq = (h * a.gpk + u % a.gpk) * a.gv + min(tid & 15, a.gv - 1);
+  const int t = seg_lo + (rlist[min(row_reader<kPacked>(a, u, tid & 15), nread - 1)] & 4095);
+  const int hq = row_head<kPacked>(a, h, u, tid & 15);
   st.f = ((tid >> 4) & 1 ? a.delta : a.lse)[(tok_base + t) * a.Hq + hq];
 }
 
-template <int D>
-__device__ __forceinline__ void kv_stage_store(const BwdArgs& a, NSA_LDS char* buf, int tid, const KvStage<D>& st) {
+template <int D, bool kPacked>
+__device__ __forceinline__ void kv_stage_store(const BwdArgs& a, const uint16_t* rlist, int nunits, int nread,
+                                               int seg_lo, int kbase, NSA_LDS char* buf, int tid, int step,
+                                               const KvStage<D>& st) {
   using U = KvUnit<D>;
 #pragma unroll
   for (int l = 0; l < U::kLoads; l++) {
@@ -371,21 +487,52 @@ __device__ __forceinline__ void kv_stage_store(const BwdArgs& a, NSA_LDS char* b
     const int rem = gi % (2 * U::kChunks);
     const int row = (rem % U::kChunks) / (D / 8);
     const int ck = rem % (D / 8);
-    // rows of heads past the group are zero (their P and dS are zero too,
-    // and 0 times a stale value could be NaN)
+    const int u = min(kStepUnits * step + unit, nunits - 1);
+    // rows that do not exist are zero (their P and dS are zero too, and 0
+    // times a stale value could be NaN)
     const u32x4 z = {0u, 0u, 0u, 0u};
     // row-major 16-byte chunks XOR-swizzled by row, as in the forward's V
     // slot: the A-operand reads and the transposed reads are conflict-free
     *(NSA_LDS u32x4*)(buf + unit * U::kBytes + (rem < U::kChunks ? 0 : U::kRows) + row * U::kRow +
-                      ((ck ^ v_swizzle<D>(row)) * 16)) = row < a.gv ? st.v[l] : z;
+                      ((ck ^ v_swizzle<D>(row)) * 16)) = row_exists<kPacked>(a, u, row, nread) ? st.v[l] : z;
   }
   if (tid < 32 * kStepUnits) {
     const int unit = tid >> 5;
     const int which = (tid >> 4) & 1;
-    const int j = tid & 15;
-    // a head past the group: lse = +inf makes its P zero, Delta = 0
-    const float val = j < a.gv ? st.f : (which ? 0.f : INFINITY);
-    *(NSA_LDS float*)(buf + unit * U::kBytes + 2 * U::kRows + which * 64 + j * 4) = val;
+    const int r = tid & 15;
+    const int u = min(kStepUnits * step + unit, nunits - 1);
+    // a row that does not exist: lse = +inf makes its P zero, Delta = 0
+    const float val = row_exists<kPacked>(a, u, r, nread) ? st.f : (which ? 0.f : INFINITY);
+    *(NSA_LDS float*)(buf + unit * U::kBytes + U::kLse + which * 64 + r * 4) = val;
+  } else if (kPacked && tid < 128) {
+    // wave 1, 16 lanes per unit: for each row and each block of the chunk,
+    // the offset from the chunk's first key (kbase) of the last key the
+    // row sees, clamped to [-1, 63] (-1: none: the row's reader does not
+    // read that block or the row does not exist); and the unit's header:
+    // the block bits of any of its readers and its last reader's token (the
+    // list is in token order, rows that do not exist hold entry 0)
+    static_assert(kStepUnits <= 4, "16 lanes of wave 1 per unit");
+    const int unit = (tid >> 4) & 3;
+    const int r = tid & 15;
+    const int u = min(kStepUnits * step + unit, nunits - 1);
+    const int e = row_exists<kPacked>(a, u, r, nread) ? (int)rlist[row_reader<kPacked>(a, u, r)] : 0;
+    const uint64_t any0 = __ballot(((e >> 12) & 1) != 0);
+    const uint64_t any1 = __ballot(((e >> 13) & 1) != 0);
+    const int last = rlist[min(row_reader<kPacked>(a, u, 0) + a.tpt, nread) - 1] & 4095;
+    if (unit < kStepUnits) {
+      const int off = row_exists<kPacked>(a, u, r, nread) ? min(max(seg_lo + (e & 4095) - kbase, -1), 63) : -1;
+#pragma unroll
+      for (int tb = 0; tb < 2; tb++)
+        *(NSA_LDS signed char*)(buf + unit * U::kBytes + U::kLim + tb * 16 + r) =
+            (signed char)(((e >> (12 + tb)) & 1) ? off : -1);
+      if (r == 0) {
+        // lanes 16 unit .. 16 unit + 15 of the wave are the unit's rows
+        const int bits = (((any0 >> (16 * unit)) & 0xFFFFull) != 0ull ? 1 : 0) |
+                         (((any1 >> (16 * unit)) & 0xFFFFull) != 0ull ? 2 : 0);
+        *(NSA_LDS int*)(buf + unit * U::kBytes + U::kHdr) = bits;
+        *(NSA_LDS int*)(buf + unit * U::kBytes + U::kHdr + 4) = last;
+      }
+    }
   }
 }
 
@@ -397,7 +544,9 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-template <int D>
+// kPacked: tpt > 1 readers share a unit's 16 rows; each row then carries its
+// own reader's token and block bits
+template <int D, bool kPacked>
 __global__ void __launch_bounds__(64 * kKvTiles) __attribute__((amdgpu_waves_per_eu(2)))
 bwd_dkdv_kernel(BwdArgs a) {
   using U = KvUnit<D>;
@@ -490,7 +639,9 @@ bwd_dkdv_kernel(BwdArgs a) {
     if (lane == 0) nread_s = base;
   }
   __syncthreads();
-  const int nunits = nread_s * a.gpk;          // (reader, head group) pairs, reader-major
+  const int nread = nread_s;
+  // units of tpt readers x one head group, reader-major
+  const int nunits = (nread + a.tpt - 1) / a.tpt * a.gpk;
   const int nsteps = (nunits + kStepUnits - 1) / kStepUnits;
 
   f32x4 dk[DT], dv[DT];
@@ -513,6 +664,7 @@ bwd_dkdv_kernel(BwdArgs a) {
       vf[kk] = *reinterpret_cast<const bf16x8*>(Vp + krow + kk * 32 + g * 8);
     }
     const float sl = a.scale_log2;
+    const int kofs = tile * 16 + c;               // this lane's key, from the chunk's first key
 
     // unit j of a step: unit kStepUnits * step + j, if it exists, reads the
     // tile's block and reaches the tile's first key
@@ -520,11 +672,20 @@ bwd_dkdv_kernel(BwdArgs a) {
       const int slot_unit = j;
       const int u = kStepUnits * step + slot_unit;
       if (u >= nunits) return;
-      const int e = rlist[u / a.gpk];
-      const int t = seg_lo + (e & 4095);
-      if (!active || !((e >> (12 + tblk)) & 1) || key0 > t) return;
       NSA_LDS const char* qs = buf + slot_unit * U::kBytes;
       NSA_LDS const char* ds = qs + U::kRows;
+      // skip the unit if none of its readers reads the tile's block or the
+      // tile starts past its last reader
+      int t = 0;   // the unit's reader (one reader per unit)
+      if constexpr (kPacked) {
+        const int ubits = __builtin_amdgcn_readfirstlane(*(NSA_LDS const int*)(qs + U::kHdr));
+        const int ulast = seg_lo + __builtin_amdgcn_readfirstlane(*(NSA_LDS const int*)(qs + U::kHdr + 4));
+        if (!active || !((ubits >> tblk) & 1) || key0 > ulast) return;
+      } else {
+        const int e = rlist[u / a.gpk];
+        t = seg_lo + (e & 4095);
+        if (!active || !((e >> (12 + tblk)) & 1) || key0 > t) return;
+      }
       // every LDS read of the step goes out first, so their latencies
       // overlap: Q_t, dO_t of the group's heads as A operands (lane (c, g):
       // head c, d = 32 kk + 8 g), lse and Delta of heads 4 g .. 4 g + 3, and
@@ -537,8 +698,10 @@ bwd_dkdv_kernel(BwdArgs a) {
         qa[kk] = *(NSA_LDS const bf16x8*)(qs + c * kRow + ch * 16);
         da[kk] = *(NSA_LDS const bf16x8*)(ds + c * kRow + ch * 16);
       }
-      const f32x4 l4 = *(NSA_LDS const f32x4*)(qs + 2 * U::kRows + g * 16);
-      const f32x4 d4 = *(NSA_LDS const f32x4*)(qs + 2 * U::kRows + 64 + g * 16);
+      const f32x4 l4 = *(NSA_LDS const f32x4*)(qs + U::kLse + g * 16);
+      const f32x4 d4 = *(NSA_LDS const f32x4*)(qs + U::kLse + 64 + g * 16);
+      // rows 4 g .. 4 g + 3: last visible key of the tile's block, from the chunk's first key
+      const int lim4 = kPacked ? *(NSA_LDS const int*)(qs + U::kLim + tblk * 16 + g * 4) : 0;
       bf16x4 qb[DT], db[DT];
 #pragma unroll
       for (int dt = 0; dt < DT; dt++) {
@@ -559,7 +722,8 @@ bwd_dkdv_kernel(BwdArgs a) {
       bf16x4 pa, sa;
 #pragma unroll
       for (int jj = 0; jj < 4; jj++) {
-        const float p = (key > t) ? 0.f : fast_exp2(__builtin_fmaf(sacc[jj], sl, -l4[jj] * 1.4426950408889634f));
+        const bool see = kPacked ? kofs <= (int)(signed char)(lim4 >> (8 * jj)) : key <= t;
+        const float p = see ? fast_exp2(__builtin_fmaf(sacc[jj], sl, -l4[jj] * 1.4426950408889634f)) : 0.f;
         pa[jj] = (__bf16)p;
         sa[jj] = (__bf16)(p * (pacc[jj] - d4[jj]));
       }
@@ -577,20 +741,20 @@ bwd_dkdv_kernel(BwdArgs a) {
     NSA_LDS char* buf0 = (NSA_LDS char*)&slot[0][0];
     NSA_LDS char* buf1 = (NSA_LDS char*)&slot[1][0];
     KvStage<D> s0, s1;
-    kv_stage_load<D>(a, rlist, nunits, seg_lo, tok_base, h, tid, 0, s0);
-    kv_stage_load<D>(a, rlist, nunits, seg_lo, tok_base, h, tid, 1, s1);
-    kv_stage_store<D>(a, buf0, tid, s0);
+    kv_stage_load<D, kPacked>(a, rlist, nunits, nread, seg_lo, tok_base, h, tid, 0, s0);
+    kv_stage_load<D, kPacked>(a, rlist, nunits, nread, seg_lo, tok_base, h, tid, 1, s1);
+    kv_stage_store<D, kPacked>(a, rlist, nunits, nread, seg_lo, chunk * 64, buf0, tid, 0, s0);
     lds_barrier();
     for (int step = 0; step < nsteps; step += 2) {
-      kv_stage_load<D>(a, rlist, nunits, seg_lo, tok_base, h, tid, step + 2, s0);
+      kv_stage_load<D, kPacked>(a, rlist, nunits, nread, seg_lo, tok_base, h, tid, step + 2, s0);
 #pragma unroll
       for (int j = 0; j < kStepUnits; j++) compute(buf0, step, j);
-      kv_stage_store<D>(a, buf1, tid, s1);
+      kv_stage_store<D, kPacked>(a, rlist, nunits, nread, seg_lo, chunk * 64, buf1, tid, step + 1, s1);
       lds_barrier();
-      kv_stage_load<D>(a, rlist, nunits, seg_lo, tok_base, h, tid, step + 3, s1);
+      kv_stage_load<D, kPacked>(a, rlist, nunits, nread, seg_lo, tok_base, h, tid, step + 3, s1);
 #pragma unroll
       for (int j = 0; j < kStepUnits; j++) compute(buf1, step + 1, j);
-      kv_stage_store<D>(a, buf0, tid, s0);
+      kv_stage_store<D, kPacked>(a, rlist, nunits, nread, seg_lo, chunk * 64, buf0, tid, step + 2, s0);
       lds_barrier();
     }
   }
@@ -662,6 +826,8 @@ hipError_t launch_bwd(const BwdPlan& p, const void* q, const void* k, const void
   a.G = p.G;
   a.gv = p.gv;
   a.gpk = p.gpk;
+  a.tpt = bwd_tile_tokens(p);
+  a.gv_magic = bwd_gv_magic(p);
   a.nb = (p.T + p.bs - 1) / p.bs;
   a.nw = (p.T + 31) / 32;
   a.readers = reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(delta) + bwd_delta_bytes(p));
@@ -686,8 +852,13 @@ hipError_t launch_bwd(const BwdPlan& p, const void* q, const void* k, const void
     hipLaunchKernelGGL(red_fn, dim3((unsigned)gr.reduce), dim3(256), 0, stream, a);
     return hipGetLastError();
   };
-  if (p.D == 64) return three(bwd_dq_kernel<64>, bwd_dkdv_kernel<64>, bwd_reduce_kernel<64>);
-  if (p.D == 128) return three(bwd_dq_kernel<128>, bwd_dkdv_kernel<128>, bwd_reduce_kernel<128>);
+  const bool packed = a.tpt > 1;
+  if (p.D == 64)
+    return packed ? three(bwd_dq_kernel<64>, bwd_dkdv_kernel<64, true>, bwd_reduce_kernel<64>)
+                  : three(bwd_dq_kernel<64>, bwd_dkdv_kernel<64, false>, bwd_reduce_kernel<64>);
+  if (p.D == 128)
+    return packed ? three(bwd_dq_kernel<128>, bwd_dkdv_kernel<128, true>, bwd_reduce_kernel<128>)
+                  : three(bwd_dq_kernel<128>, bwd_dkdv_kernel<128, false>, bwd_reduce_kernel<128>);
   return hipErrorInvalidValue;
 }
 

@@ -91,6 +91,15 @@ constexpr int kBwdKvThreads = 256;   // dk/dv workgroup: four 16-key tile waves
 // workgroups; short segments bound the longest workgroup, that of a block every token reads)
 inline int seg_tokens(int T) { return T > 16384 ? 4096 : (T > 8192 ? 2048 : (T > 4096 ? 1024 : 512)); }
 
+// tokens per dq tile, which are also the readers per dk/dv unit: a kv head's
+// query heads (gv of them) fill gv of the 16 MFMA columns (rows), so 16 / gv
+// tokens share one tile; with more than 16 heads per kv head (gpk > 1) a
+// tile is one token's group of 16
+inline int bwd_tile_tokens(const BwdPlan& p) { return p.gpk == 1 ? 16 / p.gv : 1; }
+// r / gv for 0 <= r < 16 as (r * bwd_gv_magic(p)) >> 16 (the kernels split a
+// unit's 16 rows into (reader, head) without an integer division)
+inline int bwd_gv_magic(const BwdPlan& p) { return (1 << 16) / p.gv + 1; }
+
 struct BwdGrids {
   int64_t dq, dkdv, reduce, clear_words;
 };
@@ -99,7 +108,8 @@ inline BwdGrids bwd_grids(const BwdPlan& p) {
   const int64_t seg = seg_tokens(p.T), ns = (p.T + seg - 1) / seg;
   const int64_t nb = (p.T + p.bs - 1) / p.bs, nw = (p.T + 31) / 32;
   BwdGrids g;
-  g.dq = (int64_t)p.B * p.T * p.Hkv * p.gpk;
+  const int64_t tpt = bwd_tile_tokens(p);
+  g.dq = (int64_t)p.B * ((p.T + tpt - 1) / tpt) * p.Hkv * p.gpk;
   g.dkdv = (int64_t)p.B * p.Hkv * ((p.T + 63) / 64) * ns;
   g.reduce = ((int64_t)p.B * p.T * p.Hkv * p.D / 4 + 255) / 256;
   g.clear_words = (int64_t)p.B * p.Hkv * nb * nw;

@@ -63,6 +63,12 @@ void check_bwd(const nsa_dims& d, int bs) {
   const int64_t lim = INT64_C(1) << 32;
   expect(g.dq * nsa::kBwdDqThreads < lim && g.dkdv * nsa::kBwdKvThreads < lim && g.reduce * 256 < lim,
          "bwd grids", d, bs, 0);
+  // a dq tile's tokens (= a dk/dv unit's readers) fill at most the 16 MFMA
+  // columns, and the kernels' division-free row split is exact
+  const int tpt = nsa::bwd_tile_tokens(p);
+  expect(tpt >= 1 && tpt * p.gv <= 16 && (tpt == 1 || p.gpk == 1), "bwd tile tokens", d, bs, 0);
+  for (int r = 0; r < 16; r++) expect(((r * nsa::bwd_gv_magic(p)) >> 16) == r / p.gv, "bwd row split", d, bs, 0);
+  expect(g.dq == (int64_t)p.B * ((p.T + tpt - 1) / tpt) * p.Hkv * p.gpk, "bwd dq grid", d, bs, 0);
   using u128 = unsigned __int128;
   const u128 seg = (u128)nsa::seg_tokens(p.T), T = (u128)p.T, ns = (T + seg - 1) / seg;
   const u128 want = ((u128)p.B * T * p.Hq * 4 + 255) / 256 * 256 +

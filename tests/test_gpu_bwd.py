@@ -123,9 +123,10 @@ def test_bwd_hostile_entries():
     assert np.any(np.all(rq == 0, axis=(-1, -2)))   # some token sees nothing
 
 
-@pytest.mark.parametrize("cfg", [1, 3])
+@pytest.mark.parametrize("cfg", [1, 2, 3])
 def test_bwd_named_workload_full_size(cfg):
-    """Full-size workloads: dq on sampled tokens against the oracle; at every
+    """Full-size workloads (config 2: one query head per kv head, so 16
+    tokens share each MFMA tile in both kernels): dq on sampled tokens against the oracle; at every
     (sequence, kv head, d) the invariants sum_s dV_s = sum over the group's
     (token, head) of dO (rows of P sum to one) and sum_s dK_s = 0 (each row's
     dS sums to zero)."""

@@ -60,8 +60,9 @@ PROFILES = os.path.join(ROOT, "profiles")
 FWD_KERNEL = "fwd_bf16_ring_kernel"   # the attention kernel of the bf16 forward
 
 KERNEL_SOURCES = {
-    # the forward kernel, the helpers it includes and the host code that sizes its tiles
-    "fwd": ("nsa_fwd.hip", "nsa_device.h", "nsa_internal.h", "nsa_plan.h", "nsa_api.hip"),
+    # the forward kernel, the helpers it includes, the host code that sizes its
+    # tiles and the scheduler that orders its work (the order moves its traffic)
+    "fwd": ("nsa_fwd.hip", "nsa_device.h", "nsa_internal.h", "nsa_plan.h", "nsa_api.hip", "nsa_sched.hip"),
     "decode": ("nsa_decode.hip", "nsa_device.h", "nsa_internal.h", "nsa_plan.h"),
 }
 

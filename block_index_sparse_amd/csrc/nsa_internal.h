@@ -6,6 +6,7 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "nsa_bwd_plan.h"
 #include "nsa_plan.h"
 
 namespace nsa {

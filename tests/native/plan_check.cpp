@@ -1,5 +1,5 @@
 // Sanitizer driver for the host-side plan arithmetic of the library
-// (block_index_sparse_amd/csrc/nsa_plan.h), built with the host compiler
+// (block_index_sparse_amd/csrc/nsa_plan.h, nsa_bwd_plan.h), built with the host compiler
 // alone under -fsanitize=address,undefined and run by
 // tests/test_sanitizers.py.  It sweeps hostile dims (sizes at and past the
 // int32 range, S = 1024 and beyond, G = 1024, huge batches and sequence
@@ -11,6 +11,7 @@
 #include <cstdio>
 #include <vector>
 
+#include "nsa_bwd_plan.h"
 #include "nsa_plan.h"
 
 namespace {

@@ -368,14 +368,15 @@ __global__ void __launch_bounds__(256) plan_tokens_kernel(PlanArgs a) {
       }
     };
     // rows are read kRowBatch entries at a time, every load of a batch
-    // issued before any is used
+    // issued before any is used; the first batch does not wait for the
+    // count (every entry of the row is inside the tensor)
     constexpr int kRowBatch = 32;
     if (a.vec4) {
-      for (int32_t i0 = 0; i0 < n; i0 += kRowBatch) {
+      for (int32_t i0 = 0; i0 < n || i0 == 0; i0 += kRowBatch) {
         int4 e[kRowBatch / 4];
 #pragma unroll
         for (int j = 0; j < kRowBatch / 4; j++)
-          if (i0 + 4 * j < n) e[j] = *reinterpret_cast<const int4*>(r + i0 + 4 * j);   // inside the row
+          if (i0 + 4 * j < (i0 == 0 ? a.S : n)) e[j] = *reinterpret_cast<const int4*>(r + i0 + 4 * j);   // inside the row
 #pragma unroll
         for (int j = 0; j < kRowBatch / 4; j++) {
           const int32_t i = i0 + 4 * j;
@@ -386,11 +387,11 @@ __global__ void __launch_bounds__(256) plan_tokens_kernel(PlanArgs a) {
         }
       }
     } else {
-      for (int32_t i0 = 0; i0 < n; i0 += kRowBatch) {
+      for (int32_t i0 = 0; i0 < n || i0 == 0; i0 += kRowBatch) {
         int32_t e[kRowBatch];
 #pragma unroll
         for (int j = 0; j < kRowBatch; j++)
-          if (i0 + j < n) e[j] = r[i0 + j];
+          if (i0 + j < (i0 == 0 ? a.S : n)) e[j] = r[i0 + j];
 #pragma unroll
         for (int j = 0; j < kRowBatch; j++)
           if (i0 + j < n) keep(e[j]);
@@ -497,6 +498,47 @@ __global__ void __launch_bounds__(256) scan_kernel(const int32_t* __restrict__ b
   if (threadIdx.x == 0) total[b] = carry;
 }
 
+// Rank of this lane among the wave's valid lanes holding the same key (lanes
+// below it), and how many hold it: one ballot per distinct key of the wave.
+__device__ __forceinline__ void same_key_rank(int32_t key, bool valid, int32_t& rank, int32_t& count) {
+  uint64_t todo = __ballot(valid);
+  rank = 0;
+  count = 0;
+  while (todo != 0ull) {
+    const int32_t k = __builtin_amdgcn_readlane(key, __builtin_ctzll(todo));
+    const bool mine = valid && key == k;
+    const uint64_t m = __ballot(mine);
+    if (mine) {
+      rank = (int32_t)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+      count = __popcll(m);
+    }
+    todo &= ~m;
+  }
+}
+
+// Exclusive scan over the 64 lanes of a wave.
+__device__ __forceinline__ int32_t wave_exclusive_scan(int32_t v) {
+  int32_t incl = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int32_t y = __shfl_up(incl, o, 64);
+    if ((threadIdx.x & 63) >= (unsigned)o) incl += y;
+  }
+  return incl - v;
+}
+
+// Start of every bucket in the longest-first list (heavier buckets first),
+// from the buckets' totals: one wave, two buckets per lane.
+__device__ __forceinline__ void bucket_bases(const int32_t* tot, int32_t* base) {
+  static_assert(kNumBuckets == 128, "two buckets per lane");
+  const int32_t lane = threadIdx.x & 63;
+  const int32_t b0 = kNumBuckets - 1 - 2 * lane;   // the heavier of the lane's two
+  const int32_t s0 = tot[b0], s1 = tot[b0 - 1];
+  const int32_t excl = wave_exclusive_scan(s0 + s1);
+  base[b0] = excl;
+  base[b0 - 1] = excl + s0;
+}
+
 // One wave per chunk: place every item at
 //   (items of heavier buckets) + (same bucket, earlier chunks) + (same bucket, earlier in chunk).
 __global__ void __launch_bounds__(64) scatter_kernel(const int32_t* __restrict__ bucket,
@@ -505,25 +547,16 @@ __global__ void __launch_bounds__(64) scatter_kernel(const int32_t* __restrict__
                                                      int32_t* __restrict__ worklist, int32_t n_items,
                                                      int32_t n_chunks) {
   __shared__ int32_t base[kNumBuckets];
-  __shared__ int32_t bk[kChunk];
   const int chunk = blockIdx.x;
   const int i = threadIdx.x;
-  if (i == 0) {
-    int32_t acc = 0;
-    for (int b = kNumBuckets - 1; b >= 0; b--) {
-      base[b] = acc;
-      acc += total[b];
-    }
-  }
+  bucket_bases(total, base);
   const int32_t item = chunk * kChunk + i;
-  const int32_t b = item < n_items ? bucket[item] : -1;
-  bk[i] = b;
+  const bool valid = item < n_items;
+  const int32_t b = valid ? bucket[item] : -1;
+  int32_t rank, count;
+  same_key_rank(b, valid, rank, count);
   __syncthreads();
-  if (item < n_items) {
-    int32_t rank = 0;
-    for (int j = 0; j < i; j++) rank += (bk[j] == b) ? 1 : 0;
-    worklist[base[b] + off[(int64_t)b * n_chunks + chunk] + rank] = item;
-  }
+  if (valid) worklist[base[b] + off[(int64_t)b * n_chunks + chunk] + rank] = item;
 }
 
 // The scan and the scatter in one workgroup, for at most kOrderMaxChunks
@@ -537,47 +570,54 @@ __global__ void __launch_bounds__(256) order_kernel(const int32_t* __restrict__ 
                                                     int32_t n_chunks, int32_t* __restrict__ worklist,
                                                     int32_t* __restrict__ err) {
   __shared__ int32_t cnt[kNumBuckets][kOrderMaxChunks];   // count, then start offset inside its bucket
+  __shared__ int32_t tot[kNumBuckets];
   __shared__ int32_t base[kNumBuckets];
-  __shared__ int32_t bk[4][kChunk];
   const int32_t tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   if (tid == 0) *err = 0;
   for (int32_t i = tid; i < kNumBuckets * kOrderMaxChunks; i += 256) (&cnt[0][0])[i] = 0;
   __syncthreads();
-  for (int32_t i = tid; i < n_items; i += 256) atomicAdd(&cnt[bucket[i]][i / kChunk], 1);
+  // chunk c by wave c % 4; every bucket load of the wave goes out at once
+  constexpr int kPerWave = kOrderMaxChunks / 4;
+  int32_t bkt[kPerWave];
+#pragma unroll
+  for (int j = 0; j < kPerWave; j++) {
+    const int32_t item = (wv + 4 * j) * kChunk + lane;
+    bkt[j] = item < n_items ? bucket[item] : -1;
+  }
+  // the first lane of each bucket present in a chunk writes its count
+#pragma unroll
+  for (int j = 0; j < kPerWave; j++) {
+    const int32_t c = wv + 4 * j;
+    if (c >= n_chunks) break;
+    int32_t rank, count;
+    same_key_rank(bkt[j], bkt[j] >= 0, rank, count);
+    if (bkt[j] >= 0 && rank == 0) cnt[bkt[j]][c] = count;
+  }
   __syncthreads();
+  // per bucket, exclusive scan over the chunks (a thread per bucket, the
+  // counts held in registers)
   if (tid < kNumBuckets) {
+    int32_t v[kOrderMaxChunks];
+#pragma unroll
+    for (int32_t c = 0; c < kOrderMaxChunks; c++) v[c] = c < n_chunks ? cnt[tid][c] : 0;
     int32_t run = 0;
-    for (int32_t c = 0; c < n_chunks; c++) {
-      const int32_t v = cnt[tid][c];
-      cnt[tid][c] = run;
-      run += v;
+#pragma unroll
+    for (int32_t c = 0; c < kOrderMaxChunks; c++) {
+      if (c < n_chunks) cnt[tid][c] = run;
+      run += v[c];
     }
-    base[tid] = run;   // the bucket's total, for now
+    tot[tid] = run;
   }
   __syncthreads();
-  if (tid == 0) {
-    int32_t acc = 0;
-    for (int b = kNumBuckets - 1; b >= 0; b--) {
-      const int32_t t = base[b];
-      base[b] = acc;
-      acc += t;
-    }
-  }
+  if (wv == 0) bucket_bases(tot, base);
   __syncthreads();
-  // chunk c is placed by wave c % 4: rank = earlier items of the chunk in the same bucket
-  for (int32_t c = wv; c < n_chunks; c += 4) {
-    const int32_t item = c * kChunk + lane;
-    const int32_t b = item < n_items ? bucket[item] : -1;
-    bk[wv][lane] = b;
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    if (item < n_items) {
-      int32_t rank = 0;
-      for (int j = 0; j < lane; j++) rank += (bk[wv][j] == b) ? 1 : 0;
-      worklist[base[b] + cnt[b][c] + rank] = item;
-    }
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int j = 0; j < kPerWave; j++) {
+    const int32_t c = wv + 4 * j;
+    if (c >= n_chunks) break;
+    int32_t rank, count;
+    same_key_rank(bkt[j], bkt[j] >= 0, rank, count);
+    if (bkt[j] >= 0) worklist[base[bkt[j]] + cnt[bkt[j]][c] + rank] = c * kChunk + lane;
   }
 }
 

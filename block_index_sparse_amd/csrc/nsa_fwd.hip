@@ -157,10 +157,15 @@ __device__ __forceinline__ void lds_release_bump(int* p) {
 
 // Item of round r for workgroup g: each XCD takes a contiguous stretch of
 // the longest-first list per round, so neighbouring items (same head group,
-// adjacent tokens, shared sink/local blocks) meet in one L2.
+// adjacent tokens, shared sink/local blocks) meet in one L2.  Odd rounds
+// walk the round's stretch in reverse (a snake over the workgroups), so the
+// workgroup that drew one of the heaviest items of a round draws one of the
+// lightest of the next: with few rounds (short workloads) the workgroups'
+// totals stay close.
 __device__ __forceinline__ int list_position(int g, int round, int nwg) {
   const int per = nwg / kXcds;
-  return round * nwg + (g % kXcds) * per + g / kXcds;
+  const int p = (g % kXcds) * per + g / kXcds;
+  return round * nwg + ((round & 1) ? nwg - 1 - p : p);
 }
 
 // Item walk shared by every wave of a workgroup: rounds of the

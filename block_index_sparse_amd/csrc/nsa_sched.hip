@@ -569,7 +569,9 @@ constexpr int kOrderMaxChunks = 64;
 __global__ void __launch_bounds__(256) order_kernel(const int32_t* __restrict__ bucket, int32_t n_items,
                                                     int32_t n_chunks, int32_t* __restrict__ worklist,
                                                     int32_t* __restrict__ err) {
-  __shared__ int32_t cnt[kNumBuckets][kOrderMaxChunks];   // count, then start offset inside its bucket
+  // [chunk][bucket]: count, then start offset inside its bucket (a thread
+  // per bucket walks the chunks: consecutive buckets, consecutive banks)
+  __shared__ int32_t cnt[kOrderMaxChunks][kNumBuckets];
   __shared__ int32_t tot[kNumBuckets];
   __shared__ int32_t base[kNumBuckets];
   const int32_t tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -591,19 +593,19 @@ __global__ void __launch_bounds__(256) order_kernel(const int32_t* __restrict__ 
     if (c >= n_chunks) break;
     int32_t rank, count;
     same_key_rank(bkt[j], bkt[j] >= 0, rank, count);
-    if (bkt[j] >= 0 && rank == 0) cnt[bkt[j]][c] = count;
+    if (bkt[j] >= 0 && rank == 0) cnt[c][bkt[j]] = count;
   }
   __syncthreads();
   // per bucket, exclusive scan over the chunks (a thread per bucket, the
-  // counts held in registers)
+  // counts held in registers; chunks past the last hold zeros)
   if (tid < kNumBuckets) {
     int32_t v[kOrderMaxChunks];
 #pragma unroll
-    for (int32_t c = 0; c < kOrderMaxChunks; c++) v[c] = c < n_chunks ? cnt[tid][c] : 0;
+    for (int32_t c = 0; c < kOrderMaxChunks; c++) v[c] = cnt[c][tid];
     int32_t run = 0;
 #pragma unroll
     for (int32_t c = 0; c < kOrderMaxChunks; c++) {
-      if (c < n_chunks) cnt[tid][c] = run;
+      cnt[c][tid] = run;
       run += v[c];
     }
     tot[tid] = run;
@@ -617,7 +619,7 @@ __global__ void __launch_bounds__(256) order_kernel(const int32_t* __restrict__ 
     if (c >= n_chunks) break;
     int32_t rank, count;
     same_key_rank(bkt[j], bkt[j] >= 0, rank, count);
-    if (bkt[j] >= 0) worklist[base[bkt[j]] + cnt[bkt[j]][c] + rank] = c * kChunk + lane;
+    if (bkt[j] >= 0) worklist[base[bkt[j]] + cnt[c][bkt[j]] + rank] = c * kChunk + lane;
   }
 }
 

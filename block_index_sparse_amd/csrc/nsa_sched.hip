@@ -60,7 +60,9 @@ struct PlanArgs {
   uint32_t* masks;      // [n_items * umax][mw]
   uint32_t* units;      // [n_items * umax_units]
   int32_t T, Hkv, S, bs, gpk, tq, num_seqs, n_tiles, n_items, umax, n_chunks;
-  int32_t max_pairs;    // tq * min(S, blocks per sequence): the heaviest possible item
+  int32_t max_pairs;    // tq * min(S, blocks per sequence): the most (block, token) pairs of an item
+  int32_t unit_weight;  // weight of a streamed unit in pairs (item_bucket), 0: pairs alone
+  int32_t max_weight;   // the heaviest possible item's weight
   int32_t kb, nsb, umax_units, tpw;
   int32_t mw;           // token-mask words per merged entry
   int32_t nbw;          // bitmap words per wave: ceil(blocks per sequence / 32)
@@ -69,6 +71,25 @@ struct PlanArgs {
   int32_t nqb;
   int32_t vec4;         // rows are read 16 bytes at a time (S % 4 == 0, indices 16-byte aligned)
 };
+
+// An item's weight for the longest-first order.  The forward streams each
+// of its U merged entries' units once (the loaders' share) and computes
+// each (block, token) pair once (the attention waves' share); a streamed
+// unit costs the loaders about as much as kUnitWeight pairs cost the
+// attention waves (per-unit and per-pair cycle counts of the ring kernel),
+// and the larger share bounds the item.  That weight balances the
+// workgroups best where each draws few items; where each draws many, the
+// pair count alone (equal for most items of a fixed-count workload, so the
+// list keeps token order and neighbouring items share their L2) measured
+// faster, and unit_weight is 0.  Scaled so the heaviest possible item lands
+// in the top bucket.
+constexpr int32_t kUnitWeight = 6;
+constexpr int32_t kUnitWeightRounds = 32;   // the unit-aware weight up to this many items per workgroup
+__device__ __forceinline__ int32_t item_bucket(const PlanArgs& a, int32_t U, int32_t pairs) {
+  const int64_t w = std::max<int64_t>((int64_t)a.unit_weight * U * a.nsb, pairs);
+  const int64_t b = (w * (kNumBuckets - 1) + a.max_weight - 1) / a.max_weight;
+  return b < kNumBuckets ? (int32_t)b : kNumBuckets - 1;
+}
 
 // Sequence s and first position pos0 of token tile `tile` (false past the
 // last tile): closed form for fixed-length sequences, the tile table of
@@ -291,14 +312,10 @@ __global__ void __launch_bounds__(256) plan_kernel(PlanArgs a) {
       a.units[(int64_t)item * a.umax_units + cid * a.nsb + sb] = word;
     }
   }
-  // weight = (block, token) pairs, scaled so the heaviest possible item lands
-  // in the top bucket
   pairs = wave_sum(pairs);
   if (lane == 0) {
     a.hdr[item] = ItemHeader{tok0, pos0, ntok, U};
-    const int64_t wgt = ((int64_t)pairs * (kNumBuckets - 1) + a.max_pairs - 1) / a.max_pairs;
-    const int32_t b = wgt < kNumBuckets ? (int32_t)wgt : kNumBuckets - 1;
-    a.bucket[item] = b;
+    a.bucket[item] = item_bucket(a, U, pairs);
   }
 }
 
@@ -457,9 +474,7 @@ __global__ void __launch_bounds__(256) plan_tokens_kernel(PlanArgs a) {
   __syncthreads();
   if (tid == 0) {
     a.hdr[item] = ItemHeader{tok0, pos0, ntok, U};
-    const int64_t wgt = ((int64_t)s_pairs * (kNumBuckets - 1) + a.max_pairs - 1) / a.max_pairs;
-    const int32_t b = wgt < kNumBuckets ? (int32_t)wgt : kNumBuckets - 1;
-    a.bucket[item] = b;
+    a.bucket[item] = item_bucket(a, U, s_pairs);
   }
 }
 
@@ -651,6 +666,9 @@ hipError_t launch_schedule(const Plan& p, const int32_t* block_indices, const in
   a.umax = p.umax;
   a.n_chunks = p.n_chunks;
   a.max_pairs = p.tq * (p.S < p.nb_max ? p.S : p.nb_max);
+  a.unit_weight = p.n_items <= (int64_t)kUnitWeightRounds * p.nwg ? kUnitWeight : 0;
+  const int64_t max_w = std::max<int64_t>((int64_t)a.unit_weight * p.umax * p.nsb, a.max_pairs);
+  a.max_weight = max_w > INT32_MAX ? INT32_MAX : (int32_t)max_w;
   a.units = reinterpret_cast<uint32_t*>(ws + p.off_units);
   a.kb = p.kb;
   a.nsb = p.nsb;

@@ -46,6 +46,7 @@
 //
 // fp32 kernel: one wave per (item, token group) reading K and V straight
 // from global memory, v_mfma_f32_16x16x4_f32, P kept in fp32.
+#include <cstdlib>
 #include <utility>
 
 #include "nsa.h"
@@ -89,6 +90,7 @@ struct FwdArgs {
   int32_t Hq, Hkv, G, gv, gpk, tpt, tpw, tq, mw, n_tiles, n_items, umax, umax_units, bs, nwg;
   float scale_log2;  // scale * log2(e)
   int32_t split_release;   // attention waves release a slot's K rows after S^T
+  int32_t serial;          // debug: one unit in the ring at a time (NSA_DEBUG=1)
 };
 
 // A header is used only if it stays inside the tensors: a workspace that does
@@ -252,6 +254,7 @@ __global__ void __launch_bounds__(64 * (kConsumers + kProducers), 1) fwd_bf16_ri
   __shared__ int ready[R];
   __shared__ int done_k[R];
   __shared__ int done[R];
+  __shared__ int serial_done;   // debug mode: units fully released so far
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: scalar control flow
@@ -261,6 +264,7 @@ __global__ void __launch_bounds__(64 * (kConsumers + kProducers), 1) fwd_bf16_ri
     done_k[threadIdx.x] = 0;
     done[threadIdx.x] = 0;
   }
+  if (threadIdx.x == 0) serial_done = 0;
   __syncthreads();
 
   const int nsb = a.bs / KB;  // units per listed block
@@ -366,6 +370,12 @@ __global__ void __launch_bounds__(64 * (kConsumers + kProducers), 1) fwd_bf16_ri
 #pragma unroll
       for (int j = 0; j < kOwn; j++) t = (j == js) ? tgt[j] : t;
       NSA_LDS char* kdst = (NSA_LDS char*)&ring[slot][0];
+      // debug mode: unit v_cur enters the ring only once every earlier unit
+      // of the workgroup has been read by all its readers
+      if (a.serial && !wait_free(&serial_done, v_cur)) {
+        stuck = true;
+        break;
+      }
       if (np > 0) {
         // With split releases the K half may be refilled once the readers of
         // the slot's earlier occupants have formed S^T; otherwise the whole
@@ -391,9 +401,17 @@ __global__ void __launch_bounds__(64 * (kConsumers + kProducers), 1) fwd_bf16_ri
         loader_bump(&ready[slot]);
 #pragma unroll
         for (int j = 0; j < kOwn; j++) tgt[j] += (j == js) ? np : 0;
+        if (a.serial) {
+          if (!wait_free(&done[slot], t + np)) {
+            stuck = true;
+            break;
+          }
+          loader_bump(&serial_done);
+        }
       } else {
         loader_bump(&ready_k[slot]);   // no attention wave reads this unit: nothing to load
         loader_bump(&ready[slot]);
+        if (a.serial) loader_bump(&serial_done);
       }
       v_cur += kProducers;
       np = np_n;
@@ -831,6 +849,14 @@ __global__ void __launch_bounds__(256, 2) fwd_f32_kernel(FwdArgs a) {
   }
 }
 
+// NSA_DEBUG=1 (read at every launch): the ring holds one unit at a time, so
+// no load overlaps any read of another unit; results must equal the
+// overlapped ring's bit for bit.
+bool debug_serial() {
+  const char* e = getenv("NSA_DEBUG");
+  return e && e[0] && e[0] != '0';
+}
+
 typedef void (*KernelFn)(FwdArgs);
 
 template <int D, int KB>
@@ -896,6 +922,7 @@ hipError_t launch_fwd(const Plan& p, const void* q, const void* k, const void* v
   // Split releases pay where a unit has few readers (one token per wave);
   // with many readers per unit the second release atomic costs more.
   a.split_release = p.tpw == 1 ? 1 : 0;
+  a.serial = debug_serial() ? 1 : 0;
   KernelFn fn = pick(p.bf16, p.D, p.kb, p.ntpw, a.scale_log2 > 0.f);
   if (!fn) return hipErrorInvalidValue;
   if (p.bf16) {

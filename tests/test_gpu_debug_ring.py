@@ -1,0 +1,62 @@
+"""The forward's debug mode (NSA_DEBUG=1, read at every launch): the LDS
+ring of the bf16 kernel then holds one unit at a time, every unit entering
+only after all readers of every earlier unit have released it, so no load
+overlaps a read.  Every attention wave still walks its units in the same
+order, so the results must equal the overlapped ring's bit for bit; a
+difference would mean a read of a slot raced a load into it (or a load
+raced a read) in the release mode."""
+import os
+import sys
+
+import numpy as np
+import pytest
+
+import nsa_inputs as ni
+from tests._util import to_device
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(w, debug):
+    import block_index_sparse_amd as nsa
+    q, k, v, bi, bc, cu = to_device(w)
+    old = os.environ.get("NSA_DEBUG")
+    try:
+        if debug:
+            os.environ["NSA_DEBUG"] = "1"
+        else:
+            os.environ.pop("NSA_DEBUG", None)
+        f = nsa.Forward(q, k, v, bi, bc, w.block_size, w.scale, cu_seqlens=cu,
+                        index_layout=getattr(w, "index_layout", "token"))
+        out, lse = f.run()
+        assert f.device_status() == 0
+        return out.clone(), lse.clone()
+    finally:
+        if old is None:
+            os.environ.pop("NSA_DEBUG", None)
+        else:
+            os.environ["NSA_DEBUG"] = old
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+def test_serial_ring_equals_overlapped_ring(cfg):
+    import torch
+    w = ni.make_config(cfg)
+    print(f"[debug-ring] {w.name}", flush=True)
+    sys.stdout.flush()
+    o0, l0 = _run(w, False)
+    o1, l1 = _run(w, True)
+    assert torch.equal(o0.view(torch.int16), o1.view(torch.int16)), "out differs between the serial and overlapped ring"
+    assert torch.equal(l0.view(torch.int32), l1.view(torch.int32)), "lse differs between the serial and overlapped ring"
+
+
+def test_serial_ring_hostile_entries():
+    import torch
+    w = ni.make_workload("dbg_hostile", "bf16", [300, 300], 32, 2, 128, 64, 8, "sink_local_random", "uniform", seed=4)
+    rng = np.random.default_rng(4)
+    w.block_indices = rng.integers(-2, 7, size=w.block_indices.shape).astype(np.int32)
+    w.block_counts = rng.integers(-1, 10, size=w.block_counts.shape).astype(np.int32)
+    o0, l0 = _run(w, False)
+    o1, l1 = _run(w, True)
+    assert torch.equal(o0.view(torch.int16), o1.view(torch.int16))
+    assert torch.equal(l0.view(torch.int32), l1.view(torch.int32))

@@ -25,27 +25,22 @@ constexpr int kBufferFlags = 0x00020000;
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Lanes c, c+16, c+32, c+48 hold the same column.  v_permlane16_swap /
-// v_permlane32_swap (gfx950) exchange 16-lane rows between two registers in
-// the VALU: with both operands = v, the pair returned holds v of the lane
-// itself and of its partner 16 (resp. 32) lanes away.
-__device__ __forceinline__ float xor16(float v) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return __uint_as_float((threadIdx.x & 16) ? r[0] : r[1]);
-}
-__device__ __forceinline__ float xor32(float v) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
-}
+// v_permlane32_swap (gfx950) exchange 16-lane (resp. 32-lane) rows between
+// their two registers in the VALU: with both operands = v, every lane gets
+// back its own value and its partner's 16 (resp. 32) lanes away, in one
+// order or the other, which a max or a sum does not mind.
 __device__ __forceinline__ float max_over_groups(float v) {
-  v = fmaxf(v, xor16(v));
-  v = fmaxf(v, xor32(v));
-  return v;
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
 __device__ __forceinline__ float sum_over_groups(float v) {
-  v += xor16(v);
-  v += xor32(v);
-  return v;
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 // 16-byte chunk swizzles of a slot.  K rows are read as ds_read_b128 by

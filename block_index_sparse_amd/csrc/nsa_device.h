@@ -24,6 +24,21 @@ constexpr int kBufferFlags = 0x00020000;
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Maxima without the NaN quieting the compiler wraps around fmaxf for
+// values it cannot prove canonical (MFMA results, lane exchanges): one
+// v_max3_f32 / v_max_f32 each.  The operands are scores or -inf, never
+// signalling NaNs.
+__device__ __forceinline__ float max3_raw(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+__device__ __forceinline__ float max_raw(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
 // Lanes c, c+16, c+32, c+48 hold the same column.  v_permlane16_swap /
 // v_permlane32_swap (gfx950) exchange 16-lane (resp. 32-lane) rows between
 // their two registers in the VALU: with both operands = v, every lane gets
@@ -31,9 +46,9 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // order or the other, which a max or a sum does not mind.
 __device__ __forceinline__ float max_over_groups(float v) {
   auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  v = max_raw(__uint_as_float(r[0]), __uint_as_float(r[1]));
   r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return max_raw(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
 __device__ __forceinline__ float sum_over_groups(float v) {

@@ -592,8 +592,15 @@ __global__ void __launch_bounds__(64 * (kConsumers + kProducers), 1) fwd_bf16_ri
         float mx = -INFINITY;
         const float sc = a.scale_log2;
         if constexpr (kPosScale) {
+          // a v_max3 tree over the lane's 4 MT scores
+          float m3[MT];
 #pragma unroll
-          for (int mt = 0; mt < MT; mt++) mx = fmaxf(mx, fmaxf(fmaxf(s[mt][0], s[mt][1]), fmaxf(s[mt][2], s[mt][3])));
+          for (int mt = 0; mt < MT; mt++) m3[mt] = max3_raw(s[mt][0], s[mt][1], max_raw(s[mt][2], s[mt][3]));
+          if constexpr (MT == 4) {
+            mx = max3_raw(m3[0], m3[1], max_raw(m3[2], m3[3]));
+          } else {
+            mx = max_raw(m3[0], m3[1]);
+          }
           mx = max_over_groups(mx) * sc;
         } else {
 #pragma unroll

@@ -131,6 +131,9 @@ __device__ __forceinline__ uint32_t mask_field(uint32_t word, int first, int cou
 //    (s_waitcnt lgkmcnt(0): its reads of the slot have returned);
 //  * reads of a slot are issued only after the counter that allows them was
 //    observed (control dependence, plus a compiler fence).
+__device__ __forceinline__ uint64_t lds_poll2(int* p) {
+  return __hip_atomic_load(reinterpret_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
 __device__ __forceinline__ int lds_poll(int* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
@@ -210,10 +213,12 @@ __device__ __forceinline__ void next_item(ItemCursor& cs, const FwdArgs& a) {
 // tokens listed the block and the unit's first key is not past the wave's
 // last token; the number of such waves is the unit's participant count,
 // computed by the scheduler into the unit's word.
-//  * ready_k[s] / ready[s] count publications of the K rows / V rows of the
-//    units of slot s (one each per unit, live or not, in unit order): the K
-//    rows of unit v are readable once ready_k[v % R] >= v / R + 1, its V
-//    rows once ready[v % R] >= v / R + 1.
+//  * ready2[s][0] / ready2[s][1] count publications of the K rows / V rows
+//    of the units of slot s (one each per unit, live or not, in unit order):
+//    the K rows of unit v are readable once ready2[v % R][0] >= v / R + 1,
+//    its V rows once ready2[v % R][1] >= v / R + 1.  An attention wave reads
+//    both counters with one 8-byte load when it waits for the K rows, and
+//    polls the V counter again only if the V rows were not yet published.
 //  * done[s] counts participant releases of slot s after their V reads: the
 //    loader may overwrite slot s once done[s] has reached the participant
 //    total of all earlier occupants.  With split releases (few readers per
@@ -250,8 +255,8 @@ __global__ void __launch_bounds__(64 * (kConsumers + kProducers), 1) fwd_bf16_ri
   constexpr int CH = D / 8;    // 16-byte chunks per row
 
   __shared__ __attribute__((aligned(1024))) char ring[R][C::kSlotBytes];
-  __shared__ int ready_k[R];
-  __shared__ int ready[R];
+  // the K and V publication counters of a slot side by side: one 8-byte read polls both
+  __shared__ __attribute__((aligned(8))) int ready2[R][2];
   __shared__ int done_k[R];
   __shared__ int done[R];
   __shared__ int serial_done;   // debug mode: units fully released so far
@@ -259,8 +264,8 @@ __global__ void __launch_bounds__(64 * (kConsumers + kProducers), 1) fwd_bf16_ri
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: scalar control flow
   if (threadIdx.x < R) {
-    ready_k[threadIdx.x] = 0;
-    ready[threadIdx.x] = 0;
+    ready2[threadIdx.x][0] = 0;
+    ready2[threadIdx.x][1] = 0;
     done_k[threadIdx.x] = 0;
     done[threadIdx.x] = 0;
   }
@@ -391,14 +396,14 @@ __global__ void __launch_bounds__(64 * (kConsumers + kProducers), 1) fwd_bf16_ri
       const bool have_n = locate(v_cur + kProducers, np_n, rb_n);
       if (np > 0) {
         wait_vmcnt<0>();   // the K rows have landed
-        loader_bump(&ready_k[slot]);
+        loader_bump(&ready2[slot][0]);
         if (a.split_release && !wait_free(&done[slot], t)) {
           stuck = true;
           break;
         }
         issue_v(rb, kdst + KB * D * 2);
         wait_vmcnt<0>();   // the V rows have landed
-        loader_bump(&ready[slot]);
+        loader_bump(&ready2[slot][1]);
 #pragma unroll
         for (int j = 0; j < kOwn; j++) tgt[j] += (j == js) ? np : 0;
         if (a.serial) {
@@ -409,8 +414,8 @@ __global__ void __launch_bounds__(64 * (kConsumers + kProducers), 1) fwd_bf16_ri
           loader_bump(&serial_done);
         }
       } else {
-        loader_bump(&ready_k[slot]);   // no attention wave reads this unit: nothing to load
-        loader_bump(&ready[slot]);
+        loader_bump(&ready2[slot][0]);   // no attention wave reads this unit: nothing to load
+        loader_bump(&ready2[slot][1]);
         if (a.serial) loader_bump(&serial_done);
       }
       v_cur += kProducers;
@@ -502,13 +507,17 @@ __global__ void __launch_bounds__(64 * (kConsumers + kProducers), 1) fwd_bf16_ri
         const int slot = v % R;
         const int need = v / R + 1;
         int spins = 0;
-        while (lds_poll(&ready_k[slot]) < need) {
+        uint64_t rw = lds_poll2(&ready2[slot][0]);
+        while ((int)(uint32_t)rw < need) {
           __builtin_amdgcn_s_sleep(1);
           if (++spins > kMaxSpin) {
             stuck = true;
             break;
           }
+          rw = lds_poll2(&ready2[slot][0]);
         }
+        // the V rows may already be published with the K rows' counter
+        const bool v_ready = (int)(uint32_t)(rw >> 32) >= need;
         if (stuck) break;
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
         const bool diag = (kstart + KB - 1) > my_tmin;
@@ -664,7 +673,7 @@ __global__ void __launch_bounds__(64 * (kConsumers + kProducers), 1) fwd_bf16_ri
         // the V rows of the unit may land after its K rows (they were issued
         // after them): wait for them only now, after the softmax
         spins = 0;
-        while (lds_poll(&ready[slot]) < need) {
+        while (!v_ready && lds_poll(&ready2[slot][1]) < need) {
           __builtin_amdgcn_s_sleep(1);
           if (++spins > kMaxSpin) {
             stuck = true;

@@ -155,9 +155,12 @@ __device__ __forceinline__ void loader_bump(int* p) {
   if ((threadIdx.x & 63) == 0)
     asm volatile("ds_add_u32 %0, %1" : : "v"(lds_offset(p)), "v"(1) : "memory");
 }
+// An attention wave's release: its LDS reads have returned (release fence),
+// then lane 0 adds one with a plain ds_add (no return value, no lane
+// reduction around it).
 __device__ __forceinline__ void lds_release_bump(int* p) {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  if ((threadIdx.x & 63) == 0) __hip_atomic_fetch_add(p, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  if ((threadIdx.x & 63) == 0) asm volatile("ds_add_u32 %0, %1" : : "v"(lds_offset(p)), "v"(1) : "memory");
 }
 
 // Item of round r for workgroup g: each XCD takes a contiguous stretch of

@@ -489,11 +489,13 @@ __global__ void __launch_bounds__(64 * (kConsumers + kProducers), 1) fwd_bf16_ri
       if (uu < nunits) {
         const int u = uu >> (nsb - 1);   // nsb is 1 or 2
         const int sb = uu & (nsb - 1);
+        // the unit word and the entry's token bits load side by side (both
+        // inside the item's tables), so a new item waits one memory latency
         const uint32_t word = a.units[(int64_t)item * a.umax_units + uu];
+        const uint32_t mk = a.masks[((int64_t)item * a.umax + u) * a.mw + (tok_first >> 5)];
         lj = (int)(word & 0xFFFFFFu);
         const int ks = lj * a.bs + sb * KB;
         if ((word >> 31) != 0u && ks <= my_tmax) {
-          const uint32_t mk = a.masks[((int64_t)item * a.umax + u) * a.mw + (tok_first >> 5)];
           lbits = mask_field(mk, tok_first, tpw);
           part = lbits != 0u;
         }

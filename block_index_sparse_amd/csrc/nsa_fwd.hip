@@ -633,7 +633,9 @@ __global__ void __launch_bounds__(64 * (kConsumers + kProducers), 1) fwd_bf16_ri
         const bool raise = mx > mrun[n] + 8.f;
         const float mnew = raise ? mx : mrun[n];
         const float muse = (mnew == -INFINITY) ? 0.f : mnew;
-        float rsum[4] = {0.f, 0.f, 0.f, 0.f};   // four partial sums: a short dependency chain
+        // four partial sums (a short dependency chain), each starting at its
+        // first term rather than at zero (0 + p costs an add)
+        float rsum[4];
 #pragma unroll
         for (int mt = 0; mt < MT; mt++) {
 #pragma unroll
@@ -641,7 +643,7 @@ __global__ void __launch_bounds__(64 * (kConsumers + kProducers), 1) fwd_bf16_ri
             const float pv = kPosScale ? fast_exp2(__builtin_fmaf(s[mt][jj], sc, -muse))
                                        : fast_exp2(s[mt][jj] - muse);
             s[mt][jj] = pv;
-            rsum[jj] += pv;
+            rsum[jj] = mt == 0 ? pv : rsum[jj] + pv;
           }
         }
         float rs = (rsum[0] + rsum[1]) + (rsum[2] + rsum[3]);

@@ -594,12 +594,13 @@ __global__ void __launch_bounds__(64 * (kConsumers + kProducers), 1) fwd_bf16_ri
         // 16*mt + 4*g + jj of column c.
         const bool need_mask = diag || (tbits != tvalid[n]);
         if (need_mask) {
+          // key kstart + 16 mt + 4 g + jj is visible iff 16 mt + jj <= lim
+          const int lim = sel ? tcol[n] - kstart - g * 4 : -1;
 #pragma unroll
           for (int mt = 0; mt < MT; mt++) {
 #pragma unroll
             for (int jj = 0; jj < 4; jj++) {
-              const int kp = kstart + mt * 16 + g * 4 + jj;
-              if (!sel || kp > tcol[n]) s[mt][jj] = -INFINITY;
+              if (mt * 16 + jj > lim) s[mt][jj] = -INFINITY;
             }
           }
         }

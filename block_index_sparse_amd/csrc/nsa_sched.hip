@@ -514,21 +514,20 @@ __global__ void __launch_bounds__(256) scan_kernel(const int32_t* __restrict__ b
 }
 
 // Rank of this lane among the wave's valid lanes holding the same key (lanes
-// below it), and how many hold it: one ballot per distinct key of the wave.
-__device__ __forceinline__ void same_key_rank(int32_t key, bool valid, int32_t& rank, int32_t& count) {
-  uint64_t todo = __ballot(valid);
-  rank = 0;
-  count = 0;
-  while (todo != 0ull) {
-    const int32_t k = __builtin_amdgcn_readlane(key, __builtin_ctzll(todo));
-    const bool mine = valid && key == k;
-    const uint64_t m = __ballot(mine);
-    if (mine) {
-      rank = (int32_t)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-      count = __popcll(m);
-    }
-    todo &= ~m;
-  }
+// below it), and how many hold it.  Every valid lane ORs its bit into its
+// key's 64-bit word of `sets` (a wave-private LDS table, all zero on entry),
+// then reads the word back: the lanes' LDS operations of one instruction all
+// complete before the wave's next LDS instruction, so the word then holds
+// exactly the lanes that share the key.  The key's lowest lane clears the
+// word again afterwards.  Keys are 0 .. kNumBuckets - 1.
+__device__ __forceinline__ void same_key_rank(int32_t key, bool valid, uint64_t* sets, int32_t& rank,
+                                              int32_t& count) {
+  const uint32_t lane = threadIdx.x & 63;
+  if (valid) __hip_atomic_fetch_or(&sets[key], 1ull << lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  const uint64_t m = valid ? __hip_atomic_load(&sets[key], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) : 0ull;
+  rank = (int32_t)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+  count = __popcll(m);
+  if (valid && rank == 0) __hip_atomic_store(&sets[key], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
 // Exclusive scan over the 64 lanes of a wave.
@@ -562,15 +561,18 @@ __global__ void __launch_bounds__(64) scatter_kernel(const int32_t* __restrict__
                                                      int32_t* __restrict__ worklist, int32_t n_items,
                                                      int32_t n_chunks) {
   __shared__ int32_t base[kNumBuckets];
+  __shared__ uint64_t sets[kNumBuckets];
   const int chunk = blockIdx.x;
   const int i = threadIdx.x;
+  sets[i] = 0ull;
+  sets[i + 64] = 0ull;
   bucket_bases(total, base);
   const int32_t item = chunk * kChunk + i;
   const bool valid = item < n_items;
   const int32_t b = valid ? bucket[item] : -1;
   int32_t rank, count;
-  same_key_rank(b, valid, rank, count);
   __syncthreads();
+  same_key_rank(b, valid, sets, rank, count);
   if (valid) worklist[base[b] + off[(int64_t)b * n_chunks + chunk] + rank] = item;
 }
 
@@ -589,9 +591,11 @@ __global__ void __launch_bounds__(256) order_kernel(const int32_t* __restrict__ 
   __shared__ int32_t cnt[kOrderMaxChunks][kNumBuckets];
   __shared__ int32_t tot[kNumBuckets];
   __shared__ int32_t base[kNumBuckets];
+  __shared__ uint64_t sets[4][kNumBuckets];   // per wave: lanes holding each key
   const int32_t tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   if (tid == 0) *err = 0;
   for (int32_t i = tid; i < kNumBuckets * kOrderMaxChunks; i += 256) (&cnt[0][0])[i] = 0;
+  for (int32_t i = tid; i < 4 * kNumBuckets; i += 256) (&sets[0][0])[i] = 0ull;
   __syncthreads();
   // chunk c by wave c % 4; every bucket load of the wave goes out at once
   constexpr int kPerWave = kOrderMaxChunks / 4;
@@ -607,7 +611,7 @@ __global__ void __launch_bounds__(256) order_kernel(const int32_t* __restrict__ 
     const int32_t c = wv + 4 * j;
     if (c >= n_chunks) break;
     int32_t rank, count;
-    same_key_rank(bkt[j], bkt[j] >= 0, rank, count);
+    same_key_rank(bkt[j], bkt[j] >= 0, sets[wv], rank, count);
     if (bkt[j] >= 0 && rank == 0) cnt[c][bkt[j]] = count;
   }
   __syncthreads();
@@ -633,7 +637,7 @@ __global__ void __launch_bounds__(256) order_kernel(const int32_t* __restrict__ 
     const int32_t c = wv + 4 * j;
     if (c >= n_chunks) break;
     int32_t rank, count;
-    same_key_rank(bkt[j], bkt[j] >= 0, rank, count);
+    same_key_rank(bkt[j], bkt[j] >= 0, sets[wv], rank, count);
     if (bkt[j] >= 0) worklist[base[bkt[j]] + cnt[c][bkt[j]] + rank] = c * kChunk + lane;
   }
 }

@@ -422,8 +422,10 @@ def backward_bench(args):
     ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
     flop = int(10 * w.D * w.G * int(visible_keys_per_row(w).sum()))
 
-    def call():
-        return nsa.bwd(q, k, v, out, lse, dout, bi, bc, w.block_size, w.scale, workspace=ws)
+    def call(check=False):
+        # the device status is read once after the timed steps (reading it
+        # waits for the stream)
+        return nsa.bwd(q, k, v, out, lse, dout, bi, bc, w.block_size, w.scale, workspace=ws, check=check)
 
     for _ in range(args.warmup):
         call()
@@ -436,6 +438,7 @@ def backward_bench(args):
         ev[i][1].record()
     torch.cuda.synchronize()
     ms = [a.elapsed_time(b) for a, b in ev]
+    call(check=True)   # raises if a bounded wait of the dq gather expired
     avg = float(np.mean(ms))
     tf = flop / (avg * 1e-3) / 1e12
     line = {
@@ -445,7 +448,7 @@ def backward_bench(args):
         "config": {"workload": w.name, "B": w.B, "T": w.T, "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D,
                    "block_size": w.block_size, "S": w.S, "useful_flop_per_step": flop,
                    "input_sha256": w.digest()[:16]},
-        "roofline": {"bound": "mfma", "kernel": "bwd_dq_kernel + bwd_dkdv_kernel", "achieved": round(tf, 3),
+        "roofline": {"bound": "mfma", "kernel": "fwd_bf16_ring_kernel (gradient mode: dq) + bwd_dkdv_kernel", "achieved": round(tf, 3),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
                      "traffic": None, "kernel_ms_avg": round(avg, 4), "kernel_ms_min": round(float(np.min(ms)), 4),
                      "algorithmic_flop_per_launch": flop},

@@ -45,8 +45,8 @@ class NsaError(RuntimeError):
 class NsaDeviceError(NsaError):
     """The launch was accepted (the C call returned NSA_SUCCESS) but the
     device status word of the run is not zero: a bounded wait inside the
-    forward kernel expired and out / lse are incomplete.  ``status`` holds
-    the word (bit 0 = NSA_DEVICE_WAIT_EXPIRED)."""
+    forward kernel (or the backward's dq gather) expired and its results are
+    incomplete.  ``status`` holds the word (bit 0 = NSA_DEVICE_WAIT_EXPIRED)."""
 
 
 class NsaDims(ctypes.Structure):
@@ -96,6 +96,8 @@ def load_library():
     lib.nsa_fwd_execute.argtypes = [dp, p, p, p, i32, i32, f32, p, p, p, sz, p]
     lib.nsa_fwd_device_status.restype = ctypes.c_int
     lib.nsa_fwd_device_status.argtypes = [dp, i32, i32, p, sz, p, ctypes.POINTER(i32)]
+    lib.nsa_bwd_device_status.restype = ctypes.c_int
+    lib.nsa_bwd_device_status.argtypes = [dp, i32, p, sz, p, ctypes.POINTER(i32)]
     lib.nsa_status_string.restype = ctypes.c_char_p
     lib.nsa_status_string.argtypes = [ctypes.c_int]
     lib.nsa_abi_version.restype = i32
@@ -413,10 +415,13 @@ def decode(q, k_cache, v_cache, seq_lens, block_indices, block_counts, block_siz
 
 
 def bwd(q, k, v, out, lse, dout, block_indices, block_counts, block_size: int = 64,
-        scale: float | None = None, workspace=None):
+        scale: float | None = None, workspace=None, check: bool = True):
     """Gradients of ``fwd`` (``nsa_bwd``; fixed-length, bf16): returns
     (dq, dk, dv) as float32 tensors shaped like q, k, v.  ``out`` and ``lse``
-    are the forward's results for the same inputs and indices."""
+    are the forward's results for the same inputs and indices.  With
+    ``check`` (the default) the device status word is read after the launch
+    (``nsa_bwd_device_status``: waits for the stream) and a non-zero word
+    raises NsaDeviceError."""
     import torch
     lib = load_library()
     (q, k, v, bi, bc, _, B, T, Hq, Hkv, D, S, code) = _prepare(q, k, v, block_indices, block_counts, None,
@@ -437,7 +442,17 @@ def bwd(q, k, v, out, lse, dout, block_indices, block_counts, block_size: int = 
     dk = torch.empty(k.shape, dtype=torch.float32, device=q.device)
     dv = torch.empty(v.shape, dtype=torch.float32, device=q.device)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    stream = _stream(torch, q.device)
     _check(lib.nsa_bwd(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dout), _ptr(bi),
                        _ptr(bc), int(block_size), scale, _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
-                       workspace.numel() * workspace.element_size(), _stream(torch, q.device)))
+                       ws_bytes, stream))
+    if check:
+        word = ctypes.c_int32(0)
+        _check(lib.nsa_bwd_device_status(ctypes.byref(dims), int(block_size), _ptr(workspace), ws_bytes, stream,
+                                         ctypes.byref(word)))
+        if word.value != 0:
+            raise NsaDeviceError(word.value, f"backward device status {word.value:#x}: a bounded wait inside "
+                                             "the dq gather expired (NSA_DEVICE_WAIT_EXPIRED); dq, dk and dv "
+                                             "are incomplete")
     return dq, dk, dv

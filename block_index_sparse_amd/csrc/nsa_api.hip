@@ -282,7 +282,7 @@ nsa_status nsa_bwd(const nsa_dims* d, const void* q, const void* k, const void* 
                    const int32_t* block_counts, int32_t block_size, float scale, float* dq, float* dk,
                    float* dv, void* workspace, size_t workspace_bytes, void* stream) {
   nsa::BwdPlan p;
-  nsa_status st = make_bwd_plan(d, block_size, &p);
+  nsa_status st = make_bwd_plan(d, block_size, &p, nsa::device_cu_count());
   if (st != NSA_SUCCESS) return st;
   if (!q || !k || !v || !out || !lse || !dout || !block_indices || !block_counts || !dq || !dk || !dv ||
       !workspace)
@@ -295,6 +295,23 @@ nsa_status nsa_bwd(const nsa_dims* d, const void* q, const void* k, const void* 
   if (nsa::launch_bwd(p, q, k, v, out, lse, dout, block_indices, block_counts, scale, dq, dk, dv,
                       reinterpret_cast<float*>(workspace), reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
     return NSA_ERROR_LAUNCH_FAILED;
+  return NSA_SUCCESS;
+}
+
+nsa_status nsa_bwd_device_status(const nsa_dims* dims, int32_t block_size, const void* workspace,
+                                 size_t workspace_bytes, void* stream, int32_t* status) {
+  nsa::BwdPlan p;
+  nsa_status st = make_bwd_plan(dims, block_size, &p);
+  if (st != NSA_SUCCESS) return st;
+  if (!workspace || !status) return NSA_ERROR_INVALID_VALUE;
+  if (workspace_bytes < nsa::bwd_workspace_bytes(p)) return NSA_ERROR_WORKSPACE_TOO_SMALL;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  int32_t word = 0;
+  const char* at = reinterpret_cast<const char*>(workspace) + nsa::bwd_schedule_offset(p) + p.fp.off_err;
+  if (hipMemcpyAsync(&word, at, sizeof(word), hipMemcpyDeviceToHost, s) != hipSuccess ||
+      hipStreamSynchronize(s) != hipSuccess)
+    return NSA_ERROR_LAUNCH_FAILED;
+  *status = word;
   return NSA_SUCCESS;
 }
 

@@ -7,21 +7,11 @@
 //   dK_s  = scale sum_{t, hq} dS_s q,    dV_s = sum_{t, hq} P_s dO
 // (the chain rule through the masked softmax; the forward's lse is reused).
 //
-// dq kernel: one workgroup of kBwdWaves waves per (tile of tpt tokens, kv
-// head, group of <= 16 query heads).  A tile's 16 MFMA columns are its
-// tokens' query heads (tpt = 16 / gv tokens of gv heads each when a kv head
-// has at most 16 query heads, else one token's group of 16), so a gathered
-// unit serves every column whose token kept its block.  The tokens' kept
-// blocks are merged into one ascending list with a token bit set per block
-// and dealt in 32-key units to the waves like the decode kernel: each wave
-// loads a unit's K and V rows whole (every load instruction reads complete
-// rows) into registers one unit ahead, stores them into its LDS slot and
-// reads back the A operands of S^T = K Q^T and dP^T = V dO^T, and K
-// transposed (ds_read_b64_tr_b16) as the A operand of dQ^T += K^T dS^T; a
-// column sees a unit's key iff its token kept the block and the key is not
-// past the token.  The waves' partial dQ are summed through LDS.  The kernel
-// also writes Delta and the reader bitmaps for the dk/dv kernel: per
-// (sequence, kv head, key block) a bit per token that keeps the block (from
+// dQ (with Delta = dO . O and the reader bitmaps of the dk/dv kernel) is the
+// gradient mode of the forward's ring kernel (nsa_fwd.hip), run over the
+// forward's own schedule of the same indices: it gathers every kept unit
+// once per item, as the forward does.  The reader bitmaps hold, per
+// (sequence, kv head, key block), a bit per token that keeps the block (from
 // the row's first clamp(count, 0, S) entries 0 <= j <= own; atomic OR, so
 // repeats and order do not matter).
 //
@@ -53,9 +43,6 @@ namespace {
 
 using namespace dev;
 
-constexpr int kBwdWaves = kBwdDqThreads / 64;
-constexpr int kDqWindow = 2048;      // blocks whose token bits a dq workgroup holds at a time (<= 32 stretches of 64)
-constexpr int kPairsPerThread = (16 * 64 + kBwdDqThreads - 1) / kBwdDqThreads;   // (token, entry) pairs of a tile
 constexpr int kKvTiles = kBwdKvThreads / 64;    // 16-key tiles per dk/dv workgroup (a 64-key chunk)
 constexpr int kStepUnits = 2;  // units of 16 (reader, head) rows per dk/dv step, taken by every tile wave
 constexpr int kSegMax = 4096;   // readers of a chunk are split into token segments of at most this many tokens
@@ -65,332 +52,22 @@ struct BwdArgs {
   const void* q;          // [B, T, Hq, D] bf16
   const void* k;          // [B, T, Hkv, D]
   const void* v;
-  const void* out;        // [B, T, Hq, D] forward output
   const float* lse;       // [B, T, Hq]
   const void* dout;       // [B, T, Hq, D]
-  const int32_t* bi;      // [B, T, Hkv, S]
-  const int32_t* bc;      // [B, T, Hkv]
-  float* dq;              // [B, T, Hq, D]
   float* dk;              // [B, T, Hkv, D]
   float* dv;
   float* delta;           // [B, T, Hq] workspace
   uint32_t* readers;      // [B, Hkv, nb, nw] workspace: bit t of block j = token t reads j
   float* part;            // [ns][2][B, T, Hkv, D] workspace: per token segment, dK (unscaled) and dV
-  int32_t B, T, Hq, Hkv, S, bs, G, gv, gpk, nb, nw, ns, seg;   // seg: tokens per segment
-  int32_t tpt;            // tokens per dq tile = readers per dk/dv unit (16 / gv if gpk == 1, else 1)
+  int32_t B, T, Hq, Hkv, bs, gv, gpk, nb, nw, ns, seg;   // seg: tokens per segment
+  int32_t tpt;            // readers per dk/dv unit (16 / gv if gpk == 1, else 1)
   int32_t gv_magic;       // (1 << 16) / gv + 1: r / gv = (r * gv_magic) >> 16 for 0 <= r < 16
   float scale;
   float scale_log2;
 };
 
 // ---------------------------------------------------------------------------
-// dq (and Delta)
-// ---------------------------------------------------------------------------
-// A workgroup takes a tile of tpt consecutive tokens of one sequence (tpt =
-// 16 / gv when a kv head's query heads fit one 16-column MFMA tile, else 1)
-// and one group of <= 16 query heads: column c of every tile is token
-// c / gv, head c % gv.  The blocks the tile's tokens keep are merged into one
-// ascending list with a token bit set per block (an LDS window of
-// kDqWindow blocks at a time), and each 32-key unit of the list is computed
-// once for all columns, a column seeing the unit's keys iff its token kept
-// the block and the key is not past the token.
-template <int D>
-__global__ void __launch_bounds__(64 * kBwdWaves) __attribute__((amdgpu_waves_per_eu(2)))
-bwd_dq_kernel(BwdArgs a) {
-  constexpr int KB = 32;
-  constexpr int KT = D / 32;
-  constexpr int MT = KB / 16;
-  constexpr int KQ = KB / 32;
-  constexpr int DT = D / 16;
-  constexpr int kHalf = KB * D * 2;
-  static_assert(16 * D * 4 <= kHalf, "the merge buffer fits a slot");
-  // per wave: the unit's K rows, then its V rows (row-major, swizzled)
-  __shared__ __attribute__((aligned(1024))) char kslot[kBwdWaves][2 * kHalf];
-  // token bits of the window's blocks
-  __shared__ uint32_t tmask[kDqWindow];
-  __shared__ uint32_t tnz;   // bit s: some block of the window's stretch s of 64 is kept
-  __shared__ int2 ulist[kBwdWaves][64];   // each wave's units of a stretch (first key, token bits)
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int c = lane & 15;
-  const int g = lane >> 4;
-  const int wg = blockIdx.x;
-  const int grp = wg % a.gpk;
-  const int rest = wg / a.gpk;
-  const int h = rest % a.Hkv;
-  const int rest2 = rest / a.Hkv;
-  const int ntiles = (a.T + a.tpt - 1) / a.tpt;
-  const int b = rest2 / ntiles;
-  const int t0 = (rest2 % ntiles) * a.tpt;         // the tile's first token
-  const int ntok = min(a.tpt, a.T - t0);
-  const int t_last = t0 + ntok - 1;
-  const int nbl = t_last / a.bs + 1;               // blocks up to the last token's own
-  const int nsb = a.bs / KB;
-
-  // the tile's kept entries: pair p = (token p / S, entry p % S), at most
-  // 16 x 64 pairs, kPairsPerThread per thread.  An entry is kept if it is
-  // among the first clamp(count, 0, S) of the row and 0 <= idx <= own
-  // block; repeats are harmless (their bits are OR-ed).  The first head
-  // group's workgroup also sets the token's bit in the reader bitmap of
-  // each kept block, for the dk/dv kernel.
-  int pidx[kPairsPerThread];
-  uint32_t pbit[kPairsPerThread];
-#pragma unroll
-  for (int k = 0; k < kPairsPerThread; k++) {
-    const int pr = k * kBwdDqThreads + tid;
-    pidx[k] = -1;
-    pbit[k] = 0u;
-    if (pr < ntok * a.S) {
-      const int tau = pr / a.S;
-      const int i = pr - tau * a.S;
-      const int t = t0 + tau;
-      const int64_t row = ((int64_t)b * a.T + t) * a.Hkv + h;
-      const int n = min(max(a.bc[row], 0), a.S);
-      const int idx = i < n ? a.bi[row * a.S + i] : -1;
-      if (idx >= 0 && idx <= t / a.bs) {
-        pidx[k] = idx;
-        pbit[k] = 1u << tau;
-        if (grp == 0)
-          atomicOr(a.readers + (((int64_t)b * a.Hkv + h) * a.nb + idx) * a.nw + t / 32, 1u << (t & 31));
-      }
-    }
-  }
-
-  // column c: token t0 + c / gv, head c % gv of the group; Q^T and dO^T
-  // fragments (B operands), Delta and lse of the column
-  const __bf16* __restrict__ Q = reinterpret_cast<const __bf16*>(a.q);
-  const __bf16* __restrict__ dO = reinterpret_cast<const __bf16*>(a.dout);
-  const __bf16* __restrict__ O = reinterpret_cast<const __bf16*>(a.out);
-  const int tau = c / a.gv;
-  const bool cvalid = tau < ntok && c < a.tpt * a.gv;
-  const int tcol = t0 + (cvalid ? tau : 0);                     // the column's token
-  const int64_t btc = (int64_t)b * a.T + tcol;
-  const int hq = (h * a.gpk + grp) * a.gv + (c - tau * a.gv);
-  const int64_t qrow = (btc * a.Hq + (cvalid ? hq : 0)) * D;
-  bf16x8 qf[KT], df[KT];
-  float dpart = 0.f;
-#pragma unroll
-  for (int kk = 0; kk < KT; kk++) {
-    if (cvalid) {
-      qf[kk] = *reinterpret_cast<const bf16x8*>(Q + qrow + kk * 32 + g * 8);
-      df[kk] = *reinterpret_cast<const bf16x8*>(dO + qrow + kk * 32 + g * 8);
-      const bf16x8 of = *reinterpret_cast<const bf16x8*>(O + qrow + kk * 32 + g * 8);
-#pragma unroll
-      for (int e = 0; e < 8; e++) dpart += (float)df[kk][e] * (float)of[e];
-    } else {
-      qf[kk] = bf16x8{0, 0, 0, 0, 0, 0, 0, 0};
-      df[kk] = bf16x8{0, 0, 0, 0, 0, 0, 0, 0};
-    }
-  }
-  const float delta = sum_over_groups(dpart);
-  const float lse2 = cvalid ? a.lse[btc * a.Hq + hq] * 1.4426950408889634f : INFINITY;
-  if (wave == 0 && g == 0 && cvalid) a.delta[btc * a.Hq + hq] = delta;
-
-  const char* __restrict__ Kc = reinterpret_cast<const char*>(a.k);
-  const char* __restrict__ Vc = reinterpret_cast<const char*>(a.v);
-  const int row_bytes = a.Hkv * D * 2;
-  const int64_t kv_bytes = (int64_t)a.B * a.T * row_bytes;
-  // a unit's rows are loaded whole: load l of a lane covers row l * kRpi +
-  // lane / (D / 8), 16-byte chunk lane % (D / 8), so each load instruction
-  // reads kRpi complete rows (full cache lines)
-  constexpr int kRpi = 64 / (D / 8);
-  constexpr int kNl = KB / kRpi;
-  static_assert(kNl == MT * KT, "one register per A fragment");
-  const int lrow = lane / (D / 8);
-  const int lch = lane % (D / 8);
-  const uint32_t loff = (uint32_t)(lrow * row_bytes + lch * 16);
-  auto unit_base = [&](int ks) -> int64_t { return (((int64_t)b * a.T + ks) * a.Hkv + h) * (D * 2); };
-  u32x4 kreg[kNl], vreg[kNl];
-  auto load_rows = [&](const char* base, int64_t rb, u32x4 (&r)[kNl]) {
-    const __amdgpu_buffer_rsrc_t rs = group_rsrc(base, rb, kv_bytes);
-#pragma unroll
-    for (int l = 0; l < kNl; l++)
-      r[l] = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(loff + l * kRpi * row_bytes), 0, 0);
-  };
-  NSA_LDS char* kl = (NSA_LDS char*)&kslot[wave][0];
-  NSA_LDS char* vl = kl + kHalf;
-
-  f32x4 o[DT];
-#pragma unroll
-  for (int dt = 0; dt < DT; dt++) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const float sl = a.scale_log2;
-  int my_ks = 0;        // lane i: first key of the wave's i-th unit of the stretch
-  int my_m = 0;         // lane i: its token bits
-
-  auto step = [&]<bool kMore>(int i) __attribute__((always_inline)) {
-    const int ks = __builtin_amdgcn_readlane(my_ks, i);
-    const uint32_t m = (uint32_t)__builtin_amdgcn_readlane(my_m, i);
-    const int64_t rb_n = kMore ? unit_base(__builtin_amdgcn_readlane(my_ks, i + 1)) : 0;
-    // the unit's K and V rows into the slot, row-major with 16-byte chunks
-    // XOR-swizzled by row (conflict-free writes, A-operand reads and
-    // transposed reads)
-#pragma unroll
-    for (int l = 0; l < kNl; l++) {
-      const int key = l * kRpi + lrow;
-      const int off = key * (D * 2) + ((lch ^ v_swizzle<D>(key)) * 16);
-      *(NSA_LDS u32x4*)(kl + off) = kreg[l];
-      *(NSA_LDS u32x4*)(vl + off) = vreg[l];
-    }
-    // the next unit's loads go out as soon as the registers are free (not
-    // before the stores: the two register sets would not fit)
-    __builtin_amdgcn_sched_barrier(0);
-    if constexpr (kMore) {
-      load_rows(Kc, rb_n, kreg);
-      load_rows(Vc, rb_n, vreg);
-    }
-    // S^T = K Q^T and dP^T = V dO^T; A fragments (lane (c, g): key row
-    // 16 mt + c, 16-byte chunk 4 kk + g) read back from the slot
-    f32x4 s[MT], dp[MT];
-#pragma unroll
-    for (int mt = 0; mt < MT; mt++) {
-      s[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      dp[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const int key = mt * 16 + c;
-#pragma unroll
-      for (int kk = 0; kk < KT; kk++) {
-        const int off = key * (D * 2) + (((kk * 4 + g) ^ v_swizzle<D>(key)) * 16);
-        const bf16x8 ka = *(NSA_LDS const bf16x8*)(kl + off);
-        const bf16x8 va = *(NSA_LDS const bf16x8*)(vl + off);
-        s[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[kk], s[mt], 0, 0, 0);
-        dp[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, df[kk], dp[mt], 0, 0, 0);
-      }
-      // one 16-key tile's fragments live at a time (register budget)
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    // P^T = exp2(S^T sl - lse2), zero where the column's token did not keep
-    // the block or the key is past it; dS^T = P^T (dP^T - Delta)
-    const bool sel = ((m >> tau) & 1u) != 0u;
-#pragma unroll
-    for (int mt = 0; mt < MT; mt++) {
-#pragma unroll
-      for (int jj = 0; jj < 4; jj++) {
-        const int key = ks + mt * 16 + g * 4 + jj;
-        const float p = (!sel || key > tcol) ? 0.f : fast_exp2(__builtin_fmaf(s[mt][jj], sl, -lse2));
-        s[mt][jj] = p * (dp[mt][jj] - delta);
-      }
-    }
-    bf16x8 pf[KQ];
-#pragma unroll
-    for (int kq = 0; kq < KQ; kq++) {
-#pragma unroll
-      for (int jj = 0; jj < 4; jj++) {
-        pf[kq][jj] = (__bf16)s[2 * kq][jj];
-        pf[kq][4 + jj] = (__bf16)s[2 * kq + 1][jj];
-      }
-    }
-    // dQ^T += K^T dS^T, K^T fragments read transposed from the slot
-#pragma unroll
-    for (int dt = 0; dt < DT; dt++) {
-#pragma unroll
-      for (int kq = 0; kq < KQ; kq++) {
-        bf16x8 kf;
-#pragma unroll
-        for (int half = 0; half < 2; half++) {
-          const int key = kq * 32 + half * 16 + g * 4 + (c >> 2);
-          const int d0 = dt * 16 + (c & 3) * 4;
-          const int pc = (d0 >> 3) ^ v_swizzle<D>(key);
-          const s16x4 tv = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (NSA_LDS s16x4*)(kl + key * (D * 2) + pc * 16 + (d0 & 7) * 2));
-          const bf16x4 tb = __builtin_bit_cast(bf16x4, tv);
-#pragma unroll
-          for (int e = 0; e < 4; e++) kf[half * 4 + e] = tb[e];
-        }
-        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, pf[kq], o[dt], 0, 0, 0);
-      }
-    }
-  };
-
-  // The wave's units collect in lanes 0 .. my_n - 1 (my_ks, my_m) across
-  // stretches and windows; 64 of them at most, so a stretch that would
-  // overflow the list first runs the list through the pipelined step loop.
-  int my_n = 0;
-  auto run_list = [&]() {
-    if (my_n > 0) {
-      const int64_t rb0 = unit_base(__builtin_amdgcn_readlane(my_ks, 0));
-      load_rows(Kc, rb0, kreg);
-      load_rows(Vc, rb0, vreg);
-      for (int i = 0; i + 1 < my_n; i++) step.template operator()<true>(i);
-      step.template operator()<false>(my_n - 1);
-      my_n = 0;
-    }
-  };
-  int u_next = 0;   // index of the next unit of the tile (units are dealt round robin to the waves)
-  for (int w0 = 0; w0 < nbl; w0 += kDqWindow) {
-    const int wn = min(kDqWindow, nbl - w0);
-    for (int i = tid; i < wn; i += kBwdDqThreads) tmask[i] = 0u;
-    if (tid == 0) tnz = 0u;
-    __syncthreads();
-#pragma unroll
-    for (int k = 0; k < kPairsPerThread; k++) {
-      if (pidx[k] >= w0 && pidx[k] < w0 + wn) {
-        atomicOr(&tmask[pidx[k] - w0], pbit[k]);
-        atomicOr(&tnz, 1u << ((pidx[k] - w0) >> 6));
-      }
-    }
-    __syncthreads();
-    // the kept stretches of 64 blocks: lane e looks at block w0 + e0 + e,
-    // whose sub-blocks up to the tile's last token are units
-    uint32_t todo = (uint32_t)__builtin_amdgcn_readfirstlane((int)tnz);
-    while (todo != 0u) {
-      const int e0 = __builtin_ctz(todo) * 64;
-      todo &= todo - 1u;
-      const int e = e0 + lane;
-      const uint32_t m = e < wn ? tmask[e] : 0u;
-      const int blk = w0 + e;
-      const int nsub = m != 0u ? min(nsb, (t_last - blk * a.bs) / KB + 1) : 0;
-      int incl = nsub;
-#pragma unroll
-      for (int o2 = 1; o2 < 64; o2 <<= 1) {
-        const int y = __shfl_up(incl, o2, 64);
-        if (lane >= o2) incl += y;
-      }
-      const int first = u_next + incl - nsub;        // the tile index of this lane's first unit
-      const int total = __shfl(incl, 63, 64);
-      // this wave's units of the stretch: tile index u with u % waves == wave,
-      // the k-th of them at list position my_n + k
-      const int u_mine = u_next + ((wave - u_next) % kBwdWaves + kBwdWaves) % kBwdWaves;
-      u_next += total;
-      const int cnt = u_mine < u_next ? (u_next - 1 - u_mine) / kBwdWaves + 1 : 0;   // <= 64
-      if (my_n + cnt > 64) run_list();
-      for (int sb = 0; sb < nsub; sb++) {
-        const int u = first + sb;
-        if (u % kBwdWaves == wave) ulist[wave][my_n + (u - u_mine) / kBwdWaves] = int2{blk * a.bs + sb * KB, (int)m};
-      }
-      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      if (lane >= my_n && lane < my_n + cnt) {
-        const int2 ent = ulist[wave][lane];
-        my_ks = ent.x;
-        my_m = ent.y;
-      }
-      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      my_n += cnt;
-    }
-    __syncthreads();   // every wave is done with the window's bits
-  }
-  run_list();
-
-  // sum the waves' partial dQ^T through LDS ([d tile][lane group][column]
-  // float4s), scale, store fp32
-  float* ow = reinterpret_cast<float*>(&kslot[wave][0]);
-#pragma unroll
-  for (int dt = 0; dt < DT; dt++) *reinterpret_cast<f32x4*>(ow + ((dt * 4 + g) * 16 + c) * 4) = o[dt];
-  __syncthreads();
-  for (int dt = wave; dt < DT; dt += kBwdWaves) {
-    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int w = 0; w < kBwdWaves; w++)
-      acc += *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(&kslot[w][0]) +
-                                             ((dt * 4 + g) * 16 + c) * 4);
-    if (cvalid) *reinterpret_cast<f32x4*>(a.dq + qrow + dt * 16 + g * 4) = acc * a.scale;
-  }
-}
-
-// ---------------------------------------------------------------------------
-// the reader bitmaps start cleared (the dq kernel sets their bits)
+// the reader bitmaps start cleared (the dq ring sets their bits)
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(256) bwd_clear_kernel(uint32_t* __restrict__ p, int64_t n) {
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0u;
@@ -808,12 +485,8 @@ hipError_t launch_bwd(const BwdPlan& p, const void* q, const void* k, const void
   a.q = q;
   a.k = k;
   a.v = v;
-  a.out = out;
   a.lse = lse;
   a.dout = dout;
-  a.bi = block_indices;
-  a.bc = block_counts;
-  a.dq = dq;
   a.dk = dk;
   a.dv = dv;
   a.delta = delta;
@@ -821,9 +494,7 @@ hipError_t launch_bwd(const BwdPlan& p, const void* q, const void* k, const void
   a.T = p.T;
   a.Hq = p.Hq;
   a.Hkv = p.Hkv;
-  a.S = p.S;
   a.bs = p.bs;
-  a.G = p.G;
   a.gv = p.gv;
   a.gpk = p.gpk;
   a.tpt = bwd_tile_tokens(p);
@@ -841,24 +512,28 @@ hipError_t launch_bwd(const BwdPlan& p, const void* q, const void* k, const void
                      dim3(256), 0, stream, a.readers, gr.clear_words);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // a launch that fails leaves the later ones unlaunched
-  auto three = [&](auto dq_fn, auto kv_fn, auto red_fn) -> hipError_t {
-    hipLaunchKernelGGL(dq_fn, dim3((unsigned)gr.dq), dim3(kBwdDqThreads), 0, stream, a);
-    hipError_t r = hipGetLastError();
-    if (r != hipSuccess) return r;
+  // dQ, Delta and the reader bitmaps from the forward's ring over its own
+  // schedule of the indices, then dK / dV and their segment sums; a launch
+  // that fails leaves the later ones unlaunched
+  char* fws = reinterpret_cast<char*>(delta) + bwd_schedule_offset(p);   // delta opens the workspace
+  e = launch_schedule(p.fp, block_indices, block_counts, nullptr, fws, stream);
+  if (e != hipSuccess) return e;
+  e = launch_dq_ring(p.fp, q, k, v, out, lse, dout, scale, dq, delta, a.readers, a.nb, a.nw, fws, stream);
+  if (e != hipSuccess) return e;
+  auto two = [&](auto kv_fn, auto red_fn) -> hipError_t {
     hipLaunchKernelGGL(kv_fn, dim3((unsigned)gr.dkdv), dim3(kBwdKvThreads), 0, stream, a);
-    r = hipGetLastError();
+    hipError_t r = hipGetLastError();
     if (r != hipSuccess) return r;
     hipLaunchKernelGGL(red_fn, dim3((unsigned)gr.reduce), dim3(256), 0, stream, a);
     return hipGetLastError();
   };
   const bool packed = a.tpt > 1;
   if (p.D == 64)
-    return packed ? three(bwd_dq_kernel<64>, bwd_dkdv_kernel<64, true>, bwd_reduce_kernel<64>)
-                  : three(bwd_dq_kernel<64>, bwd_dkdv_kernel<64, false>, bwd_reduce_kernel<64>);
+    return packed ? two(bwd_dkdv_kernel<64, true>, bwd_reduce_kernel<64>)
+                  : two(bwd_dkdv_kernel<64, false>, bwd_reduce_kernel<64>);
   if (p.D == 128)
-    return packed ? three(bwd_dq_kernel<128>, bwd_dkdv_kernel<128, true>, bwd_reduce_kernel<128>)
-                  : three(bwd_dq_kernel<128>, bwd_dkdv_kernel<128, false>, bwd_reduce_kernel<128>);
+    return packed ? two(bwd_dkdv_kernel<128, true>, bwd_reduce_kernel<128>)
+                  : two(bwd_dkdv_kernel<128, false>, bwd_reduce_kernel<128>);
   return hipErrorInvalidValue;
 }
 

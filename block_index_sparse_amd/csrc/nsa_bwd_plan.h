@@ -13,10 +13,13 @@ namespace nsa {
 struct BwdPlan {
   int32_t B, T, Hq, Hkv, D, S, bs, G;
   int32_t gv, gpk;
+  // dQ runs as the gradient mode of the forward's ring kernel, over the
+  // forward's own schedule of the same indices (its plan of the same dims);
+  // the schedule sits in the workspace after the dK / dV partial sums
+  Plan fp;
 };
 
 // Work-items of the backward's kernels.
-constexpr int kBwdDqThreads = 256;   // dq workgroup: four waves
 constexpr int kBwdKvThreads = 256;   // dk/dv workgroup: four 16-key tile waves
 
 // the segment length: 512 tokens up to T = 4096, then 1024, 2048 past 8192 and 4096 past
@@ -24,25 +27,22 @@ constexpr int kBwdKvThreads = 256;   // dk/dv workgroup: four 16-key tile waves
 // workgroups; short segments bound the longest workgroup, that of a block every token reads)
 inline int seg_tokens(int T) { return T > 16384 ? 4096 : (T > 8192 ? 2048 : (T > 4096 ? 1024 : 512)); }
 
-// tokens per dq tile, which are also the readers per dk/dv unit: a kv head's
-// query heads (gv of them) fill gv of the 16 MFMA columns (rows), so 16 / gv
-// tokens share one tile; with more than 16 heads per kv head (gpk > 1) a
-// tile is one token's group of 16
+// readers per dk/dv unit: a kv head's query heads (gv of them) fill gv of
+// the 16 MFMA rows, so 16 / gv tokens share one unit; with more than 16
+// heads per kv head (gpk > 1) a unit is one token's group of 16
 inline int bwd_tile_tokens(const BwdPlan& p) { return p.gpk == 1 ? 16 / p.gv : 1; }
 // r / gv for 0 <= r < 16 as (r * bwd_gv_magic(p)) >> 16 (the kernels split a
 // unit's 16 rows into (reader, head) without an integer division)
 inline int bwd_gv_magic(const BwdPlan& p) { return (1 << 16) / p.gv + 1; }
 
 struct BwdGrids {
-  int64_t dq, dkdv, reduce, clear_words;
+  int64_t dkdv, reduce, clear_words;
 };
 
 inline BwdGrids bwd_grids(const BwdPlan& p) {
   const int64_t seg = seg_tokens(p.T), ns = (p.T + seg - 1) / seg;
   const int64_t nb = (p.T + p.bs - 1) / p.bs, nw = (p.T + 31) / 32;
   BwdGrids g;
-  const int64_t tpt = bwd_tile_tokens(p);
-  g.dq = (int64_t)p.B * ((p.T + tpt - 1) / tpt) * p.Hkv * p.gpk;
   g.dkdv = (int64_t)p.B * p.Hkv * ((p.T + 63) / 64) * ns;
   g.reduce = ((int64_t)p.B * p.T * p.Hkv * p.D / 4 + 255) / 256;
   g.clear_words = (int64_t)p.B * p.Hkv * nb * nw;
@@ -58,12 +58,21 @@ inline size_t bwd_readers_bytes(const BwdPlan& p) {
   return ((size_t)p.B * p.Hkv * nb * nw * sizeof(uint32_t) + 255) / 256 * 256;
 }
 
-inline size_t bwd_workspace_bytes(const BwdPlan& p) {
+inline size_t bwd_part_bytes(const BwdPlan& p) {
   const size_t ns = (size_t)(p.T + seg_tokens(p.T) - 1) / seg_tokens(p.T);
-  return bwd_delta_bytes(p) + bwd_readers_bytes(p) + ns * 2 * (size_t)p.B * p.T * p.Hkv * p.D * sizeof(float);
+  return ns * 2 * (size_t)p.B * p.T * p.Hkv * p.D * sizeof(float);
 }
 
-inline nsa_status make_bwd_plan(const nsa_dims* d, int32_t block_size, BwdPlan* p) {
+// byte offset of the forward's schedule in the backward's workspace
+inline size_t bwd_schedule_offset(const BwdPlan& p) {
+  return bwd_delta_bytes(p) + bwd_readers_bytes(p) + align_up(bwd_part_bytes(p), 256);
+}
+
+inline size_t bwd_workspace_bytes(const BwdPlan& p) { return bwd_schedule_offset(p) + p.fp.bytes; }
+
+// cus: compute units of the device (the forward plan's grid; the layout of
+// the workspace does not depend on it)
+inline nsa_status make_bwd_plan(const nsa_dims* d, int32_t block_size, BwdPlan* p, int cus = 256) {
   if (!d) return NSA_ERROR_INVALID_VALUE;
   if (d->batch <= 0 || d->seqlen <= 0 || d->num_q_heads <= 0 || d->num_kv_heads <= 0 ||
       d->head_dim <= 0 || d->num_selected <= 0 || block_size <= 0)
@@ -96,9 +105,13 @@ inline nsa_status make_bwd_plan(const nsa_dims* d, int32_t block_size, BwdPlan* 
   // every launch of the backward must stay inside the 2^32 work-items a
   // grid dimension holds
   const BwdGrids g = bwd_grids(*p);
-  if (g.dq * kBwdDqThreads >= (INT64_C(1) << 32) || g.dkdv * kBwdKvThreads >= (INT64_C(1) << 32) ||
+  if (g.dkdv * kBwdKvThreads >= (INT64_C(1) << 32) ||
       g.reduce * 256 >= (INT64_C(1) << 32))
     return NSA_ERROR_NOT_SUPPORTED;
+  // the forward's plan of the same call (the backward needs its out and lse)
+  const nsa_status fs = make_plan(d, block_size, 0, false, &p->fp, false, cus);
+  if (fs != NSA_SUCCESS) return fs;
+  if (!p->fp.bf16 || p->fp.ntpw != 1) return NSA_ERROR_NOT_SUPPORTED;
   return NSA_SUCCESS;
 }
 

@@ -91,6 +91,16 @@ struct FwdArgs {
   float scale_log2;  // scale * log2(e)
   int32_t split_release;   // attention waves release a slot's K rows after S^T
   int32_t serial;          // debug: one unit in the ring at a time (NSA_DEBUG=1)
+  // the gradient mode of the ring kernel (dq): its inputs and outputs
+  const void* dout;        // [rows, Hq, D] bf16
+  const void* fwd_out;     // [rows, Hq, D] bf16, the forward's output
+  const float* lse_in;     // [rows, Hq] natural-log lse of the forward
+  float* dq;               // [rows, Hq, D] fp32
+  float* delta;            // [rows, Hq] fp32: dO . O
+  uint32_t* readers;       // [B, Hkv, nb, nw]: bit t of block j = token t keeps j
+  int32_t rd_nb, rd_nw;
+  int32_t T;               // tokens per sequence (fixed-length sequences)
+  float scale;
 };
 
 // A header is used only if it stays inside the tensors: a workspace that does
@@ -245,7 +255,12 @@ struct RingCfg {
 // kPosScale: the softmax scale is > 0, so max(scale * s) = scale * max(s) and
 // masked scores (-inf) stay -inf through the scaling FMA; otherwise each
 // score is scaled and tested on its own.
-template <int D, int KB, int NTPW, bool kPosScale>
+// kDq: the gradient dQ of the same gather (same items, units and ring): per
+// (token, unit) pair S^T = K Q^T, P = 2^(scale log2e S - lse log2e), dP^T =
+// V dO^T, dS = P (dP - Delta), dQ^T += K^T dS^T; the V rows are stored
+// row-swizzled like the K rows (both are read as rows), K is read again
+// transposed for dQ, so a slot is released once, after the last reads.
+template <int D, int KB, int NTPW, bool kPosScale, bool kDq>
 __global__ void __launch_bounds__(64 * (kConsumers + kProducers), 1) fwd_bf16_ring_kernel(FwdArgs a) {
   static_assert(64 * (kConsumers + kProducers) <= 1024, "workgroup size");
   static_assert(NTPW == 1, "the ring kernel runs one 16-column tile per attention wave");
@@ -301,7 +316,7 @@ __global__ void __launch_bounds__(64 * (kConsumers + kProducers), 1) fwd_bf16_ri
     for (int j = 0; j < 4; j++) {
       const int r = j * C::kRowsPerLoad + lane / CH;
       koff[j] = (uint32_t)(r * row_bytes + ((lane % CH) ^ k_swizzle<D>(r)) * 16);
-      voff[j] = (uint32_t)(r * row_bytes + ((lane % CH) ^ v_swizzle<D>(r)) * 16);
+      voff[j] = (uint32_t)(r * row_bytes + ((lane % CH) ^ (kDq ? k_swizzle<D>(r) : v_swizzle<D>(r))) * 16);
     }
     constexpr int kOwn = R / kProducers;    // ring slots each loader owns
     int tgt[kOwn];                          // participant releases owed to each own slot
@@ -454,6 +469,8 @@ __global__ void __launch_bounds__(64 * (kConsumers + kProducers), 1) fwd_bf16_ri
     bf16x8 qf[NTPW][KT];
     f32x4 o[NTPW][DT];
     float mrun[NTPW], lrun[NTPW];
+    bf16x8 dof[NTPW][KT];       // gradient mode: dO^T fragments, like qf
+    float lse2[NTPW], dlt[NTPW];   // gradient mode: per column lse log2e and Delta
 #pragma unroll
     for (int n = 0; n < NTPW; n++) {
       int head;
@@ -478,6 +495,31 @@ __global__ void __launch_bounds__(64 * (kConsumers + kProducers), 1) fwd_bf16_ri
       for (int dt = 0; dt < DT; dt++) o[n][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
       mrun[n] = -INFINITY;
       lrun[n] = 0.f;
+      if constexpr (kDq) {
+        // dO^T fragments; Delta = dO . O of the column (each lane holds 32
+        // of its D products, the four lane groups are summed); the lse in
+        // the log2 domain (0 where the row saw no key: its scores are all
+        // masked, so every P of it is 0)
+        const __bf16* __restrict__ dO = reinterpret_cast<const __bf16*>(a.dout);
+        const __bf16* __restrict__ Ofw = reinterpret_cast<const __bf16*>(a.fwd_out);
+        float part = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < KT; kk++) {
+          if (cvalid[n]) {
+            dof[n][kk] = *reinterpret_cast<const bf16x8*>(dO + qrow + kk * 32 + g * 8);
+            const bf16x8 ov = *reinterpret_cast<const bf16x8*>(Ofw + qrow + kk * 32 + g * 8);
+#pragma unroll
+            for (int e = 0; e < 8; e++) part = __builtin_fmaf((float)dof[n][kk][e], (float)ov[e], part);
+          } else {
+            dof[n][kk] = bf16x8{0, 0, 0, 0, 0, 0, 0, 0};
+          }
+        }
+        dlt[n] = sum_over_groups(part);
+        const int64_t lrow = (int64_t)(hd.tok0 + (cvalid[n] ? tau[n] : 0)) * a.Hq + hq[n];
+        const float lv = cvalid[n] ? a.lse_in[lrow] : 0.f;
+        lse2[n] = (lv == -INFINITY || lv != lv) ? 0.f : lv * 1.4426950408889634f;
+        if (cvalid[n] && g == 0) a.delta[lrow] = dlt[n];
+      }
     }
 
     // find this wave's units 64 at a time: lane i examines unit cbase + i
@@ -531,6 +573,94 @@ __global__ void __launch_bounds__(64 * (kConsumers + kProducers), 1) fwd_bf16_ri
         constexpr int n = 0;   // one 16-column tile per attention wave
         const uint32_t tbits = mine;
         const bool sel = cvalid[n] && ((mine >> (tau[n] - tok_first)) & 1u);
+        if constexpr (kDq) {
+          // the reader bitmap of the dk/dv kernel: this wave's tokens that
+          // keep the block (first sub-block; one head group writes it)
+          if ((uu_b & (nsb - 1)) == 0 && vg % a.gpk == 0 && lane == 0) {
+            const int tt = my_tmin;   // position of the wave's first token
+            const int64_t rbase = ((int64_t)((hd.tok0 - hd.pos0) / a.T) * a.Hkv + vg / a.gpk) * a.rd_nb + j;
+            const uint32_t live = mine & ((1u << my_ntok) - 1u);   // my_ntok <= 16
+            const uint64_t bits = (uint64_t)live << (tt & 31);
+            atomicOr(&a.readers[rbase * a.rd_nw + (tt >> 5)], (uint32_t)bits);
+            if ((uint32_t)(bits >> 32) != 0u) atomicOr(&a.readers[rbase * a.rd_nw + (tt >> 5) + 1], (uint32_t)(bits >> 32));
+          }
+          // rows of K (then of V) one 16-key tile at a time: A operands
+          auto read_rows = [&](NSA_LDS const char* base, bf16x8 (&kf)[KT], int mt) {
+            const int row = mt * 16 + c;
+#pragma unroll
+            for (int kk = 0; kk < KT; kk++) {
+              const int pc = (kk * 4 + g) ^ k_swizzle<D>(row);
+              kf[kk] = *(NSA_LDS const bf16x8*)(base + row * (D * 2) + pc * 16);
+            }
+          };
+          f32x4 s[MT];
+#pragma unroll
+          for (int mt = 0; mt < MT; mt++) {
+            bf16x8 kf[KT];
+            read_rows(kl, kf, mt);
+            s[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < KT; kk++) s[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kk], qf[n][kk], s[mt], 0, 0, 0);
+          }
+          // P = 2^(scale log2e s - lse log2e), 0 where masked
+          const bool need_mask = diag || (tbits != tvalid[n]);
+          const int lim = sel ? tcol[n] - kstart - g * 4 : -1;
+          const float sc = a.scale_log2;
+#pragma unroll
+          for (int mt = 0; mt < MT; mt++)
+#pragma unroll
+            for (int jj = 0; jj < 4; jj++) {
+              const bool vis = !need_mask || (mt * 16 + jj <= lim);
+              s[mt][jj] = vis ? fast_exp2(__builtin_fmaf(s[mt][jj], sc, -lse2[n])) : 0.f;
+            }
+          // the V rows
+          spins = 0;
+          while (!v_ready && lds_poll(&ready2[slot][1]) < need) {
+            __builtin_amdgcn_s_sleep(1);
+            if (++spins > kMaxSpin) {
+              stuck = true;
+              break;
+            }
+          }
+          if (stuck) break;
+          __atomic_signal_fence(__ATOMIC_SEQ_CST);
+          // dP^T = V dO^T one 16-key tile at a time, then dS = P (dP - Delta)
+          // as the bf16 B operand of dQ^T += K^T dS^T
+          bf16x8 dsf[KQ];
+#pragma unroll
+          for (int mt = 0; mt < MT; mt++) {
+            bf16x8 vf[KT];
+            read_rows(vl, vf, mt);
+            f32x4 dp = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < KT; kk++) dp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[kk], dof[n][kk], dp, 0, 0, 0);
+#pragma unroll
+            for (int jj = 0; jj < 4; jj++) dsf[mt >> 1][(mt & 1) * 4 + jj] = (__bf16)(s[mt][jj] * (dp[jj] - dlt[n]));
+          }
+          // dQ^T += K^T dS^T: K read transposed, one 16-row tile of dQ^T at a time
+#pragma unroll
+          for (int dt = 0; dt < DT; dt++) {
+            bf16x8 kt[KQ];
+#pragma unroll
+            for (int kq = 0; kq < KQ; kq++)
+#pragma unroll
+              for (int half = 0; half < 2; half++) {
+                const int key = kq * 32 + half * 16 + g * 4 + (c >> 2);
+                const int d0 = dt * 16 + (c & 3) * 4;
+                const int pc = (d0 >> 3) ^ k_swizzle<D>(key);
+                const s16x4 t = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (NSA_LDS s16x4*)(kl + key * (D * 2) + pc * 16 + (d0 & 7) * 2));
+                const bf16x4 tb = __builtin_bit_cast(bf16x4, t);
+#pragma unroll
+                for (int e = 0; e < 4; e++) kt[kq][half * 4 + e] = tb[e];
+              }
+            if (dt == DT - 1) lds_release_bump(&done[slot]);   // the last reads of the slot have returned
+#pragma unroll
+            for (int kq = 0; kq < KQ; kq++)
+              o[n][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kt[kq], dsf[kq], o[n][dt], 0, 0, 0);
+          }
+          continue;
+        }
         // S^T = K Q^T; K fragments read from the slot half a unit at a time
         // (one LDS round trip per half), then the MFMAs
         f32x4 s[MT];
@@ -704,6 +834,20 @@ __global__ void __launch_bounds__(64 * (kConsumers + kProducers), 1) fwd_bf16_ri
     }
     if (stuck) break;
 
+    if constexpr (kDq) {
+      // dq = scale dQ^T, fp32 rows
+#pragma unroll
+      for (int n = 0; n < NTPW; n++) {
+        if (!cvalid[n]) continue;
+        const int64_t orow = ((int64_t)(hd.tok0 + tau[n]) * a.Hq + hq[n]) * D;
+#pragma unroll
+        for (int dt = 0; dt < DT; dt++)
+          *reinterpret_cast<f32x4*>(a.dq + orow + dt * 16 + g * 4) = o[n][dt] * a.scale;
+      }
+      v_base += nunits;
+      next_item(cs, a);
+      continue;
+    }
     // epilogue: out = O / l (bf16, round to nearest even), lse = ln 2 * (m + log2 l)
 #pragma unroll
     for (int n = 0; n < NTPW; n++) {
@@ -886,7 +1030,8 @@ typedef void (*KernelFn)(FwdArgs);
 template <int D, int KB>
 KernelFn pick_ntpw(bool bf16, int ntpw, bool pos_scale) {
   if (bf16) {
-    if (ntpw == 1) return pos_scale ? fwd_bf16_ring_kernel<D, KB, 1, true> : fwd_bf16_ring_kernel<D, KB, 1, false>;
+    if (ntpw == 1)
+      return pos_scale ? fwd_bf16_ring_kernel<D, KB, 1, true, false> : fwd_bf16_ring_kernel<D, KB, 1, false, false>;
   } else {
     switch (ntpw) {
       case 1: return fwd_f32_kernel<D, KB, 1>;
@@ -955,6 +1100,60 @@ hipError_t launch_fwd(const Plan& p, const void* q, const void* k, const void* v
     const int waves = p.n_items * kConsumers;
     hipLaunchKernelGGL(fn, dim3((waves + 3) / 4), dim3(256), 0, stream, a);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_dq_ring(const Plan& p, const void* q, const void* k, const void* v, const void* out,
+                          const float* lse, const void* dout, float scale, float* dq, float* delta,
+                          uint32_t* readers, int32_t rd_nb, int32_t rd_nw, char* ws, hipStream_t stream) {
+  if (!p.bf16 || p.ntpw != 1) return hipErrorInvalidValue;
+  FwdArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out = nullptr;
+  a.lse = nullptr;
+  a.hdr = reinterpret_cast<const ItemHeader*>(ws + p.off_hdr);
+  a.blocks = reinterpret_cast<const int32_t*>(ws + p.off_blocks);
+  a.masks = reinterpret_cast<const uint32_t*>(ws + p.off_masks);
+  a.units = reinterpret_cast<const uint32_t*>(ws + p.off_units);
+  a.worklist = reinterpret_cast<const int32_t*>(ws + p.off_worklist);
+  a.err = reinterpret_cast<int32_t*>(ws + p.off_err);
+  a.Ttot = p.B * p.T;
+  a.Hq = p.Hq;
+  a.Hkv = p.Hkv;
+  a.G = p.G;
+  a.gv = p.gv;
+  a.gpk = p.gpk;
+  a.tpt = p.tpt;
+  a.tpw = p.tpw;
+  a.tq = p.tq;
+  a.mw = p.mw;
+  a.n_tiles = p.n_tiles;
+  a.n_items = p.n_items;
+  a.umax = p.umax;
+  a.umax_units = p.umax_units;
+  a.bs = p.bs;
+  a.nwg = p.nwg;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.split_release = 0;   // K is read again for dQ: one release per slot
+  a.serial = debug_serial() ? 1 : 0;
+  a.dout = dout;
+  a.fwd_out = out;
+  a.lse_in = lse;
+  a.dq = dq;
+  a.delta = delta;
+  a.readers = readers;
+  a.rd_nb = rd_nb;
+  a.rd_nw = rd_nw;
+  a.T = p.T;
+  a.scale = scale;
+  KernelFn fn = nullptr;
+  if (p.D == 64) fn = p.kb == 32 ? fwd_bf16_ring_kernel<64, 32, 1, true, true> : fwd_bf16_ring_kernel<64, 64, 1, true, true>;
+  if (p.D == 128)
+    fn = p.kb == 32 ? fwd_bf16_ring_kernel<128, 32, 1, true, true> : fwd_bf16_ring_kernel<128, 64, 1, true, true>;
+  if (!fn) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(fn, dim3(p.nwg), dim3(64 * (kConsumers + kProducers)), 0, stream, a);
   return hipGetLastError();
 }
 

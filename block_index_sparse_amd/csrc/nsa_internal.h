@@ -24,6 +24,9 @@ hipError_t launch_schedule(const Plan& p, const int32_t* block_indices, const in
                            const int32_t* cu_seqlens, char* ws, hipStream_t stream);
 hipError_t launch_fwd(const Plan& p, const void* q, const void* k, const void* v, float scale,
                       void* out, float* lse, char* ws, hipStream_t stream);
+hipError_t launch_dq_ring(const Plan& p, const void* q, const void* k, const void* v, const void* out,
+                          const float* lse, const void* dout, float scale, float* dq, float* delta,
+                          uint32_t* readers, int32_t rd_nb, int32_t rd_nw, char* ws, hipStream_t stream);
 hipError_t launch_decode(const DecodePlan& p, const void* q, const void* k, const void* v,
                          const int32_t* seq_lens, const int32_t* block_indices,
                          const int32_t* block_counts, float scale, void* out, float* lse,

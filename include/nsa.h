@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define NSA_ABI_VERSION 2
+#define NSA_ABI_VERSION 3
 
 typedef enum {
   NSA_SUCCESS = 0,
@@ -199,15 +199,19 @@ nsa_status nsa_decode(const nsa_dims* dims, const void* q, const void* k, const 
  *  reader bitmap per key block: B * Hkv * ceil(T / block_size) *
  *  ceil(T / 32) words, and each token segment's partial dK and dV sums:
  *  2 * ceil(T / L) * B * T * Hkv * D float32 with segments of L = 512
- *  tokens up to T = 4096, 1024 up to 8192, 2048 up to 16384, else 4096),
+ *  tokens up to T = 4096, 1024 up to 8192, 2048 up to 16384, else 4096,
+ *  then the forward's schedule of the same indices: dq runs as the
+ *  gradient mode of the forward's gather over it),
  *  256-byte aligned, no initialisation needed.  Past T = 16384 the
  *  segment length stays 4096, so the partial sums grow as T^2: about
  *  1.07 GB at B = 1, T = 32768, Hkv = 4, D = 128, 4.3 GB at T = 65536.
  *  Dims whose kernels would exceed a grid of 2^32 work-items return
  *  NSA_ERROR_NOT_SUPPORTED.
  * dk and dv sum over a block's readers in token order, so results are
- * deterministic.  NSA_ERROR_NOT_SUPPORTED for fp32, S > 64 and
- * the head_dim / block_size / group limits of nsa_fwd.
+ * deterministic.  NSA_ERROR_NOT_SUPPORTED for fp32, S > 64 and wherever
+ * nsa_fwd does not take the same fixed-length dims and block_size.  The
+ * waits of the dq gather are bounded like the forward's: see
+ * nsa_bwd_device_status.
  */
 size_t nsa_bwd_workspace_size(const nsa_dims* dims, int32_t block_size);
 nsa_status nsa_bwd(const nsa_dims* dims, const void* q, const void* k, const void* v,
@@ -272,6 +276,17 @@ nsa_status nsa_fwd_execute(const nsa_dims* dims, const void* q, const void* k, c
 nsa_status nsa_fwd_device_status(const nsa_dims* dims, int32_t block_size, int32_t num_seqs,
                                  const void* workspace, size_t workspace_bytes, void* stream,
                                  int32_t* status);
+
+/*
+ * Device status of the last nsa_bwd call that used `workspace`: bit 0
+ * (NSA_DEVICE_WAIT_EXPIRED) set if a bounded wait of its dq gather expired
+ * (its dq, and the dk / dv that follow from its reader bitmaps, are then
+ * incomplete); 0 if the call completed normally.  dims and block_size must
+ * be those of the call.  Waits for `stream` to finish and copies one word
+ * to the host.
+ */
+nsa_status nsa_bwd_device_status(const nsa_dims* dims, int32_t block_size, const void* workspace,
+                                 size_t workspace_bytes, void* stream, int32_t* status);
 
 /* Human-readable name of a status code (static storage). */
 const char* nsa_status_string(nsa_status status);

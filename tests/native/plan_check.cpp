@@ -62,20 +62,26 @@ void check_bwd(const nsa_dims& d, int bs) {
   bwd_ok++;
   const nsa::BwdGrids g = nsa::bwd_grids(p);
   const int64_t lim = INT64_C(1) << 32;
-  expect(g.dq * nsa::kBwdDqThreads < lim && g.dkdv * nsa::kBwdKvThreads < lim && g.reduce * 256 < lim,
+  expect(g.dkdv * nsa::kBwdKvThreads < lim && g.reduce * 256 < lim,
          "bwd grids", d, bs, 0);
-  // a dq tile's tokens (= a dk/dv unit's readers) fill at most the 16 MFMA
-  // columns, and the kernels' division-free row split is exact
+  // a dk/dv unit's readers fill at most the 16 MFMA rows, and the kernel's
+  // division-free row split is exact
   const int tpt = nsa::bwd_tile_tokens(p);
-  expect(tpt >= 1 && tpt * p.gv <= 16 && (tpt == 1 || p.gpk == 1), "bwd tile tokens", d, bs, 0);
+  expect(tpt >= 1 && tpt * p.gv <= 16 && (tpt == 1 || p.gpk == 1), "bwd unit readers", d, bs, 0);
   for (int r = 0; r < 16; r++) expect(((r * nsa::bwd_gv_magic(p)) >> 16) == r / p.gv, "bwd row split", d, bs, 0);
-  expect(g.dq == (int64_t)p.B * ((p.T + tpt - 1) / tpt) * p.Hkv * p.gpk, "bwd dq grid", d, bs, 0);
   using u128 = unsigned __int128;
   const u128 seg = (u128)nsa::seg_tokens(p.T), T = (u128)p.T, ns = (T + seg - 1) / seg;
   const u128 want = ((u128)p.B * T * p.Hq * 4 + 255) / 256 * 256 +
                     ((u128)p.B * p.Hkv * ((T + p.bs - 1) / p.bs) * ((T + 31) / 32) * 4 + 255) / 256 * 256 +
-                    ns * 2 * (u128)p.B * T * p.Hkv * p.D * 4;
+                    (ns * 2 * (u128)p.B * T * p.Hkv * p.D * 4 + 255) / 256 * 256 + (u128)p.fp.bytes;
   expect((u128)nsa::bwd_workspace_bytes(p) == want, "bwd workspace size", d, bs, 0);
+  // the dq ring runs the forward's plan of the same call: one bf16 column
+  // tile per attention wave
+  {
+    expect(p.fp.bf16 && p.fp.ntpw == 1 && p.fp.tpw * p.fp.gv <= 16 && p.fp.B == p.B && p.fp.T == p.T,
+           "bwd ring plan", d, bs, 0);
+    check_fwd(d, bs, 0, false);
+  }
 }
 
 }  // namespace

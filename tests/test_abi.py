@@ -24,7 +24,7 @@ def test_library_exports_every_declared_symbol():
             "nsa_abi_version", "nsa_fwd_schedule", "nsa_fwd_qblock", "nsa_fwd_schedule_qblock"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.nsa_abi_version() == 2
+    assert lib.nsa_abi_version() == 3
 
 
 def test_status_strings():
@@ -164,6 +164,16 @@ def test_bwd_rejects_bad_arguments():
     assert call(D(), ws_bytes=16) == 3
     assert lib.nsa_bwd_workspace_size(ctypes.byref(D()), 64) > 0
     assert lib.nsa_bwd_workspace_size(ctypes.byref(D(dt=0)), 64) == 0
+    # the forward's limits hold too (dq is the forward's gather in gradient
+    # mode): one head per kv head keeping 64 of 2049 blocks merges more
+    # entries per work item than the forward's planner takes
+    assert call(D(T=2049 * 32, Hq=1, S=64), bs=32) == 2
+    assert call(D(T=2048 * 32, Hq=1, S=64), bs=32, ws_bytes=16) == 3
+    st = ctypes.c_int32(7)
+    assert lib.nsa_bwd_device_status(ctypes.byref(D(Dh=96)), 64, p, 1 << 40, None, ctypes.byref(st)) == 2
+    assert lib.nsa_bwd_device_status(ctypes.byref(D()), 64, None, 1 << 40, None, ctypes.byref(st)) == 1
+    assert lib.nsa_bwd_device_status(ctypes.byref(D()), 64, p, 16, None, ctypes.byref(st)) == 3
+    assert st.value == 7
 
 
 class _StatusLib:

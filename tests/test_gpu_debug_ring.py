@@ -60,3 +60,35 @@ def test_serial_ring_hostile_entries():
     o1, l1 = _run(w, True)
     assert torch.equal(o0.view(torch.int16), o1.view(torch.int16))
     assert torch.equal(l0.view(torch.int32), l1.view(torch.int32))
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3])
+def test_serial_ring_equals_overlapped_ring_backward(cfg):
+    """The backward's dq runs the same ring in its gradient mode: dq (and the
+    dk / dv that follow from its reader bitmaps) must not change bit for bit
+    when the ring holds one unit at a time."""
+    import torch
+    import block_index_sparse_amd as nsa
+    w = ni.make_config(cfg)
+    print(f"[debug-ring] backward {w.name}", flush=True)
+    sys.stdout.flush()
+    q, k, v, bi, bc, _ = to_device(w)
+    out, lse = _run(w, False)
+    x = ni.normal(300 + cfg, 9, w.B * w.T * w.Hq * w.D).reshape(w.B, w.T, w.Hq, w.D)
+    dout = torch.from_numpy(ni.to_bf16_bits(x).view(np.int16)).view(torch.bfloat16).cuda()
+    grads = []
+    old = os.environ.get("NSA_DEBUG")
+    try:
+        for debug in (False, True):
+            if debug:
+                os.environ["NSA_DEBUG"] = "1"
+            else:
+                os.environ.pop("NSA_DEBUG", None)
+            grads.append([g.clone() for g in nsa.bwd(q, k, v, out, lse, dout, bi, bc, w.block_size, w.scale)])
+    finally:
+        if old is None:
+            os.environ.pop("NSA_DEBUG", None)
+        else:
+            os.environ["NSA_DEBUG"] = old
+    for name, a, b in zip(("dq", "dk", "dv"), grads[0], grads[1]):
+        assert torch.equal(a.view(torch.int32), b.view(torch.int32)), f"{name} differs between the serial and overlapped ring"

@@ -109,7 +109,7 @@ inline nsa_status make_bwd_plan(const nsa_dims* d, int32_t block_size, BwdPlan* 
       g.reduce * 256 >= (INT64_C(1) << 32))
     return NSA_ERROR_NOT_SUPPORTED;
   // the forward's plan of the same call (the backward needs its out and lse)
-  const nsa_status fs = make_plan(d, block_size, 0, false, &p->fp, false, cus);
+  const nsa_status fs = make_plan(d, block_size, 0, false, &p->fp, false, cus, true);
   if (fs != NSA_SUCCESS) return fs;
   if (!p->fp.bf16 || p->fp.ntpw != 1) return NSA_ERROR_NOT_SUPPORTED;
   return NSA_SUCCESS;

@@ -574,16 +574,6 @@ __global__ void __launch_bounds__(64 * (kConsumers + kProducers), 1) fwd_bf16_ri
         const uint32_t tbits = mine;
         const bool sel = cvalid[n] && ((mine >> (tau[n] - tok_first)) & 1u);
         if constexpr (kDq) {
-          // the reader bitmap of the dk/dv kernel: this wave's tokens that
-          // keep the block (first sub-block; one head group writes it)
-          if ((uu_b & (nsb - 1)) == 0 && vg % a.gpk == 0 && lane == 0) {
-            const int tt = my_tmin;   // position of the wave's first token
-            const int64_t rbase = ((int64_t)((hd.tok0 - hd.pos0) / a.T) * a.Hkv + vg / a.gpk) * a.rd_nb + j;
-            const uint32_t live = mine & ((1u << my_ntok) - 1u);   // my_ntok <= 16
-            const uint64_t bits = (uint64_t)live << (tt & 31);
-            atomicOr(&a.readers[rbase * a.rd_nw + (tt >> 5)], (uint32_t)bits);
-            if ((uint32_t)(bits >> 32) != 0u) atomicOr(&a.readers[rbase * a.rd_nw + (tt >> 5) + 1], (uint32_t)(bits >> 32));
-          }
           // rows of K (then of V) one 16-key tile at a time: A operands
           auto read_rows = [&](NSA_LDS const char* base, bf16x8 (&kf)[KT], int mt) {
             const int row = mt * 16 + c;
@@ -637,10 +627,9 @@ __global__ void __launch_bounds__(64 * (kConsumers + kProducers), 1) fwd_bf16_ri
 #pragma unroll
             for (int jj = 0; jj < 4; jj++) dsf[mt >> 1][(mt & 1) * 4 + jj] = (__bf16)(s[mt][jj] * (dp[jj] - dlt[n]));
           }
-          // dQ^T += K^T dS^T: K read transposed, one 16-row tile of dQ^T at a time
-#pragma unroll
-          for (int dt = 0; dt < DT; dt++) {
-            bf16x8 kt[KQ];
+          // dQ^T += K^T dS^T: K read transposed, one 16-row tile of dQ^T at a
+          // time, the reads of the next tile issued before the MFMAs of this one
+          auto read_kt = [&](bf16x8 (&kt)[KQ], int dt) {
 #pragma unroll
             for (int kq = 0; kq < KQ; kq++)
 #pragma unroll
@@ -654,10 +643,23 @@ __global__ void __launch_bounds__(64 * (kConsumers + kProducers), 1) fwd_bf16_ri
 #pragma unroll
                 for (int e = 0; e < 4; e++) kt[kq][half * 4 + e] = tb[e];
               }
-            if (dt == DT - 1) lds_release_bump(&done[slot]);   // the last reads of the slot have returned
+          };
+          auto mm = [&](const bf16x8 (&kt)[KQ], int dt) {
 #pragma unroll
             for (int kq = 0; kq < KQ; kq++)
               o[n][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kt[kq], dsf[kq], o[n][dt], 0, 0, 0);
+          };
+          {
+            bf16x8 ka[KQ], kb[KQ];
+            read_kt(ka, 0);
+#pragma unroll
+            for (int dt = 0; dt < DT; dt += 2) {
+              read_kt(kb, dt + 1);
+              mm(ka, dt);
+              if (dt + 2 < DT) read_kt(ka, dt + 2);
+              else lds_release_bump(&done[slot]);   // the last reads of the slot have returned
+              mm(kb, dt + 1);
+            }
           }
           continue;
         }
@@ -830,6 +832,19 @@ __global__ void __launch_bounds__(64 * (kConsumers + kProducers), 1) fwd_bf16_ri
         lds_release_bump(&done[slot]);
         pv(va, 2);
         pv(vb, 3);
+      }
+      if constexpr (kDq) {
+        // the reader bitmap of the dk/dv kernel: this wave's tokens that keep
+        // the lane's block (first sub-block; the first head group of the kv
+        // head writes it), one atomic OR per lane for the chunk
+        if (part && (uu & (nsb - 1)) == 0 && vg % a.gpk == 0) {
+          const int tt = my_tmin;   // position of the wave's first token
+          const int64_t rbase = ((int64_t)((hd.tok0 - hd.pos0) / a.T) * a.Hkv + vg / a.gpk) * a.rd_nb + lj;
+          const uint32_t live = lbits & ((1u << my_ntok) - 1u);   // my_ntok <= 16
+          const uint64_t bits = (uint64_t)live << (tt & 31);
+          atomicOr(&a.readers[rbase * a.rd_nw + (tt >> 5)], (uint32_t)bits);
+          if ((uint32_t)(bits >> 32) != 0u) atomicOr(&a.readers[rbase * a.rd_nw + (tt >> 5) + 1], (uint32_t)(bits >> 32));
+        }
       }
     }
     if (stuck) break;

@@ -86,8 +86,12 @@ inline bool product_le(int64_t a, int64_t b, int64_t c, int64_t limit) {
 }
 
 // Derive tiling and workspace layout.  Returns NSA_SUCCESS or an error.
+// small_units: 32-key units where a block holds 64 keys of D = 128 (the
+// ring then holds 8 units instead of 4; the gradient mode of the ring, whose
+// waves keep a unit longer, gains more from the deeper ring than it loses to
+// the per-unit handshakes, the forward does not).
 inline nsa_status make_plan(const nsa_dims* d, int32_t block_size, int32_t num_seqs, bool varlen, Plan* p,
-                            bool qblock, int cus) {
+                            bool qblock, int cus, bool small_units = false) {
   if (!d) return NSA_ERROR_INVALID_VALUE;
   if (d->batch <= 0 || d->seqlen <= 0 || d->num_q_heads <= 0 || d->num_kv_heads <= 0 ||
       d->head_dim <= 0 || d->num_selected <= 0 || block_size <= 0)
@@ -134,6 +138,7 @@ inline nsa_status make_plan(const nsa_dims* d, int32_t block_size, int32_t num_s
   P.ntpw = P.bf16 ? 1 : ((P.tpt * 2 * kConsumers <= kMaxTileTokensF32) ? 2 : 1);
   P.tpw = P.tpt * P.ntpw;
   P.kb = P.bs < 64 ? P.bs : 64;
+  if (small_units && P.bs == 64 && P.D == 128 && P.bf16) P.kb = 32;
   P.nsb = P.bs / P.kb;
   const int64_t nb_max = (P.T + P.bs - 1) / P.bs;  // a sequence is at most T long
   if (nb_max > (int64_t)kMaxBitmapWords * 32) return NSA_ERROR_NOT_SUPPORTED;

@@ -29,10 +29,10 @@ void expect(bool ok, const char* what, const nsa_dims& d, int bs, int ns) {
 
 bool valid_status(nsa_status s) { return s >= NSA_SUCCESS && s <= NSA_ERROR_LAUNCH_FAILED; }
 
-void check_fwd(const nsa_dims& d, int bs, int ns, bool qblock) {
+void check_fwd(const nsa_dims& d, int bs, int ns, bool qblock, bool small_units = false) {
   const bool varlen = ns > 0;
   nsa::Plan p;
-  const nsa_status st = nsa::make_plan(&d, bs, ns, varlen, &p, qblock, 256);
+  const nsa_status st = nsa::make_plan(&d, bs, ns, varlen, &p, qblock, 256, small_units);
   expect(valid_status(st), "fwd status", d, bs, ns);
   if (st != NSA_SUCCESS) return;
   fwd_ok++;
@@ -80,7 +80,8 @@ void check_bwd(const nsa_dims& d, int bs) {
   {
     expect(p.fp.bf16 && p.fp.ntpw == 1 && p.fp.tpw * p.fp.gv <= 16 && p.fp.B == p.B && p.fp.T == p.T,
            "bwd ring plan", d, bs, 0);
-    check_fwd(d, bs, 0, false);
+    check_fwd(d, bs, 0, false, true);
+    expect(p.fp.kb * p.fp.nsb == p.fp.bs && (p.fp.nsb == 1 || p.fp.nsb == 2), "bwd ring units", d, bs, 0);
   }
 }
 

@@ -126,7 +126,8 @@ def test_bwd_hostile_entries():
 @pytest.mark.parametrize("cfg", [1, 2, 3])
 def test_bwd_named_workload_full_size(cfg):
     """Full-size workloads (config 2: one query head per kv head, so 16
-    tokens share each MFMA tile in both kernels): dq on sampled tokens against the oracle; at every
+    tokens share each MFMA tile in both kernels): dq of about 330 tokens
+    (sampled, edges and a run of 64) against the oracle; at every
     (sequence, kv head, d) the invariants sum_s dV_s = sum over the group's
     (token, head) of dO (rows of P sum to one) and sum_s dK_s = 0 (each row's
     dS sums to zero)."""
@@ -135,7 +136,11 @@ def test_bwd_named_workload_full_size(cfg):
     w = ni.make_config(cfg)
     dout, dbits = _dout(w, 100 + cfg)
     dq, dk, dv = run_bwd(w, dbits)
-    rows = sample_rows(w, 24, seed=cfg)
+    # a seeded sample, sequence starts and ends, block edges, and a run of
+    # 64 consecutive tokens (whole work items of the dq gather and their
+    # boundaries, for items of 12 and of 192 tokens)
+    run0 = int(np.random.default_rng(50 + cfg).integers(0, w.B * w.T - 64))
+    rows = np.union1d(sample_rows(w, 256, seed=cfg), np.arange(run0, run0 + 64))
     rq, mq = obwd.dq_rows(w.q, w.k, w.v, dout, w.block_indices, w.block_counts, w.block_size, w.scale, rows,
                           terms=True)
     check(f"config {cfg} dq rows", dq.reshape(-1, w.Hq, w.D)[rows], rq, mq)

@@ -497,7 +497,7 @@ hipError_t launch_bwd(const BwdPlan& p, const void* q, const void* k, const void
   a.bs = p.bs;
   a.gv = p.gv;
   a.gpk = p.gpk;
-  a.tpt = bwd_tile_tokens(p);
+  a.tpt = bwd_unit_readers(p);
   a.gv_magic = bwd_gv_magic(p);
   a.nb = (p.T + p.bs - 1) / p.bs;
   a.nw = (p.T + 31) / 32;

@@ -30,7 +30,7 @@ inline int seg_tokens(int T) { return T > 16384 ? 4096 : (T > 8192 ? 2048 : (T >
 // readers per dk/dv unit: a kv head's query heads (gv of them) fill gv of
 // the 16 MFMA rows, so 16 / gv tokens share one unit; with more than 16
 // heads per kv head (gpk > 1) a unit is one token's group of 16
-inline int bwd_tile_tokens(const BwdPlan& p) { return p.gpk == 1 ? 16 / p.gv : 1; }
+inline int bwd_unit_readers(const BwdPlan& p) { return p.gpk == 1 ? 16 / p.gv : 1; }
 // r / gv for 0 <= r < 16 as (r * bwd_gv_magic(p)) >> 16 (the kernels split a
 // unit's 16 rows into (reader, head) without an integer division)
 inline int bwd_gv_magic(const BwdPlan& p) { return (1 << 16) / p.gv + 1; }

@@ -66,7 +66,7 @@ void check_bwd(const nsa_dims& d, int bs) {
          "bwd grids", d, bs, 0);
   // a dk/dv unit's readers fill at most the 16 MFMA rows, and the kernel's
   // division-free row split is exact
-  const int tpt = nsa::bwd_tile_tokens(p);
+  const int tpt = nsa::bwd_unit_readers(p);
   expect(tpt >= 1 && tpt * p.gv <= 16 && (tpt == 1 || p.gpk == 1), "bwd unit readers", d, bs, 0);
   for (int r = 0; r < 16; r++) expect(((r * nsa::bwd_gv_magic(p)) >> 16) == r / p.gv, "bwd row split", d, bs, 0);
   using u128 = unsigned __int128;

@@ -62,19 +62,31 @@ def test_serial_ring_hostile_entries():
     assert torch.equal(l0.view(torch.int32), l1.view(torch.int32))
 
 
-@pytest.mark.parametrize("cfg", [1, 2, 3])
+def _hostile_bwd_workload():
+    w = ni.make_workload("dbg_bwd_hostile", "bf16", [300, 300], 64, 2, 128, 64, 8, "sink_local_random", "uniform",
+                         seed=5)
+    rng = np.random.default_rng(5)
+    w.block_indices = rng.integers(-2, 7, size=w.block_indices.shape).astype(np.int32)
+    w.block_counts = rng.integers(-1, 10, size=w.block_counts.shape).astype(np.int32)
+    return w
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, "hostile"])
 def test_serial_ring_equals_overlapped_ring_backward(cfg):
     """The backward's dq runs the same ring in its gradient mode: dq (and the
     dk / dv that follow from its reader bitmaps) must not change bit for bit
-    when the ring holds one unit at a time."""
+    when the ring holds one unit at a time (named workloads, and hostile
+    entries: negative, repeated and out-of-range indices, counts outside
+    [0, S], two head groups per kv head)."""
     import torch
     import block_index_sparse_amd as nsa
-    w = ni.make_config(cfg)
+    w = _hostile_bwd_workload() if cfg == "hostile" else ni.make_config(cfg)
+    seed = 300 + (cfg if isinstance(cfg, int) else 9)
     print(f"[debug-ring] backward {w.name}", flush=True)
     sys.stdout.flush()
     q, k, v, bi, bc, _ = to_device(w)
     out, lse = _run(w, False)
-    x = ni.normal(300 + cfg, 9, w.B * w.T * w.Hq * w.D).reshape(w.B, w.T, w.Hq, w.D)
+    x = ni.normal(seed, 9, w.B * w.T * w.Hq * w.D).reshape(w.B, w.T, w.Hq, w.D)
     dout = torch.from_numpy(ni.to_bf16_bits(x).view(np.int16)).view(torch.bfloat16).cuda()
     grads = []
     old = os.environ.get("NSA_DEBUG")

@@ -12,7 +12,7 @@ the launch stream around that kernel inside every timed step).  The CPU
 baseline times the fp64 oracle on a bounded token sample of the same
 workload on the host's cores.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 3] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 3] [--no-cpu-baseline] [--cold]
 
 --config 0..4 selects the other named workloads (parity cases, not the
 headline); --config 5 is the same long-context shape with one index row per
@@ -466,6 +466,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cold", action="store_true",
+                    help="also time the headline steps with 1 GiB of scratch written before each (cold L2 and MALL)")
     ap.add_argument("--decode", action="store_true", help="measure the decode step instead")
     ap.add_argument("--backward", action="store_true", help="measure the backward pass on --config")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -522,6 +524,9 @@ def main():
     print(f"[bench] {w.name}: generated in {gen_s:.1f} s", file=sys.stderr, flush=True)
     flop = useful_flops(w)
     tm = time_forward(w, dev, args.warmup, args.steps)
+    # the cold variant (--cold; reported beside the headline, never as its
+    # value): the same steps with L2 and MALL flushed before each one
+    tmc = time_forward(w, dev, 2, args.steps, cold=True) if args.cold else None
     step_ms = tm["window_ms"] / args.steps
     kern_avg = tm["kernel_ms"]["mean"]
 
@@ -568,6 +573,9 @@ def main():
             "algorithmic_bytes_per_launch": algorithmic_bytes(w),
         },
     }
+    if tmc is not None:
+        line["timing_cold"] = {"step_ms": tmc["step_ms"], "kernel_ms": tmc["kernel_ms"],
+                               "scratch_bytes_written_before_each_step": COLD_SCRATCH_BYTES}
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a token sample", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(w, seconds_target=args.cpu_seconds)
@@ -599,10 +607,15 @@ def _stats(xs) -> dict:
             "p90": round(float(np.percentile(a, 90)), 4), "mean": round(float(a.mean()), 4)}
 
 
-def time_forward(w, dev, warmup, steps):
+COLD_SCRATCH_BYTES = 1 << 30   # written between steps of the cold variant (beyond L2 and MALL)
+
+
+def time_forward(w, dev, warmup, steps, cold=False):
     """`warmup` untimed steps, then `steps` timed ones; a step is the whole
     call (scheduler, then the attention kernel).  HIP events on the launch
-    stream bracket every step, every kernel and the whole timed window."""
+    stream bracket every step, every kernel and the whole timed window.
+    With `cold`, 1 GiB of scratch is written before each timed step (outside
+    its events), so every step starts with no input in L2 or MALL."""
     import torch
     import block_index_sparse_amd as nsa
     import nsa_inputs as ni
@@ -615,10 +628,13 @@ def time_forward(w, dev, warmup, steps):
     torch.cuda.synchronize()
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
     e_start, e_stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    scratch = torch.empty(COLD_SCRATCH_BYTES // 4, dtype=torch.int32, device=dev) if cold else None
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     e_start.record()
     for i in range(steps):
+        if cold:
+            scratch.fill_(i)
         ev[i][0].record()
         f.schedule()
         ev[i][1].record()
@@ -634,7 +650,7 @@ def time_forward(w, dev, warmup, steps):
     out = {"window_ms": e_start.elapsed_time(e_stop), "wall_s": wall,
            "step_ms": _stats([a.elapsed_time(c) for a, _, c in ev]),
            "kernel_ms": _stats([b.elapsed_time(c) for _, b, c in ev])}
-    del f, q, k, v, bi, bc, cu
+    del f, q, k, v, bi, bc, cu, scratch
     torch.cuda.empty_cache()
     return out
 

@@ -267,6 +267,18 @@ def _oracle_threads() -> int:
     return _THREADS[0]
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (first `model name` of /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, seconds_target=12.0, seed=0):
     """Time the fp64 oracle on a seeded token sample sized to ~seconds_target."""
     import oracle
@@ -288,7 +300,7 @@ def cpu_baseline(w, seconds_target=12.0, seed=0):
     return {"value": fl / used / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"{len(rows)} of {total} tokens (seeded uniform sample, all {w.Hq} query heads), "
                       f"{used:.2f} s fp64 on {threads} OpenMP threads",
-            "seconds": used, "tokens": int(len(rows))}
+            "seconds": used, "tokens": int(len(rows)), "cpu_model": cpu_model(), "host_cpus": os.cpu_count()}
 
 
 def bwd_cpu_baseline(w, dout, seconds_target=12.0, seed=0):

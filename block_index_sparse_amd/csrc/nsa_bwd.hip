@@ -45,7 +45,7 @@ using namespace dev;
 
 constexpr int kKvTiles = kBwdKvThreads / 64;    // 16-key tiles per dk/dv workgroup (a 64-key chunk)
 constexpr int kStepUnits = 2;  // units of 16 (reader, head) rows per dk/dv step, taken by every tile wave
-constexpr int kSegMax = 4096;   // readers of a chunk are split into token segments of at most this many tokens
+constexpr int kSegMax = kBwdSegMax;   // readers of a chunk are split into token segments of at most this many tokens
 
 
 struct BwdArgs {
@@ -438,9 +438,13 @@ bwd_dkdv_kernel(BwdArgs a) {
   if (!active) return;
 
   // the segment's partial sum dS^T Q and P^T dO; lane (c, g) holds keys 4 g + jj at d = 16 dt + c
+  // (with one segment the sums are final: dK = scale dS^T Q, dV = P^T dO
+  // go straight to the outputs)
   const int64_t plane = (int64_t)a.B * a.T * a.Hkv * D;
-  float* pk = a.part + (int64_t)seg * 2 * plane;
-  float* pv = pk + plane;
+  const bool whole = a.ns == 1;
+  float* pk = whole ? a.dk : a.part + (int64_t)seg * 2 * plane;
+  float* pv = whole ? a.dv : pk + plane;
+  const float ks = whole ? a.scale : 1.f;
 #pragma unroll
   for (int jj = 0; jj < 4; jj++) {
     const int kr = key0 + g * 4 + jj;
@@ -448,7 +452,7 @@ bwd_dkdv_kernel(BwdArgs a) {
     const int64_t o = ((tok_base + kr) * a.Hkv + h) * D;
 #pragma unroll
     for (int dt = 0; dt < DT; dt++) {
-      pk[o + dt * 16 + c] = dk[dt][jj];
+      pk[o + dt * 16 + c] = dk[dt][jj] * ks;
       pv[o + dt * 16 + c] = dv[dt][jj];
     }
   }
@@ -503,8 +507,8 @@ hipError_t launch_bwd(const BwdPlan& p, const void* q, const void* k, const void
   a.nw = (p.T + 31) / 32;
   a.readers = reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(delta) + bwd_delta_bytes(p));
   a.part = reinterpret_cast<float*>(reinterpret_cast<char*>(a.readers) + bwd_readers_bytes(p));
-  a.seg = seg_tokens(p.T);
-  a.ns = (p.T + a.seg - 1) / a.seg;
+  a.seg = bwd_seg_tokens(p);
+  a.ns = bwd_segments(p);
   a.scale = scale;
   a.scale_log2 = scale * 1.4426950408889634f;
   const BwdGrids gr = bwd_grids(p);   // make_bwd_plan kept every grid inside 2^32 work-items
@@ -523,7 +527,7 @@ hipError_t launch_bwd(const BwdPlan& p, const void* q, const void* k, const void
   auto two = [&](auto kv_fn, auto red_fn) -> hipError_t {
     hipLaunchKernelGGL(kv_fn, dim3((unsigned)gr.dkdv), dim3(kBwdKvThreads), 0, stream, a);
     hipError_t r = hipGetLastError();
-    if (r != hipSuccess) return r;
+    if (r != hipSuccess || a.ns == 1) return r;   // one segment: dk, dv are written already
     hipLaunchKernelGGL(red_fn, dim3((unsigned)gr.reduce), dim3(256), 0, stream, a);
     return hipGetLastError();
   };

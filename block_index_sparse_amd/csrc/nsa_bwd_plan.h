@@ -22,15 +22,27 @@ struct BwdPlan {
 // Work-items of the backward's kernels.
 constexpr int kBwdKvThreads = 256;   // dk/dv workgroup: four 16-key tile waves
 
-// the segment length: 512 tokens up to T = 4096, then 1024, 2048 past 8192 and 4096 past
-// 16384 tokens (fewer workgroups and partial sums where every segment still has many
-// workgroups; short segments bound the longest workgroup, that of a block every token reads)
-inline int seg_tokens(int T) { return T > 16384 ? 4096 : (T > 8192 ? 2048 : (T > 4096 ? 1024 : 512)); }
-
 // readers per dk/dv unit: a kv head's query heads (gv of them) fill gv of
 // the 16 MFMA rows, so 16 / gv tokens share one unit; with more than 16
 // heads per kv head (gpk > 1) a unit is one token's group of 16
 inline int bwd_unit_readers(const BwdPlan& p) { return p.gpk == 1 ? 16 / p.gv : 1; }
+
+constexpr int kBwdSegMax = 4096;   // tokens of one segment (the dk/dv kernel's LDS reader list)
+
+// The token segment of a dk/dv workgroup: 512 tokens up to T = 4096, then
+// 1024, 2048 past 8192 and 4096 past 16384 (fewer workgroups and partial sums
+// where every segment still has many workgroups; short segments bound the
+// longest workgroup, that of a block every token reads), times the readers
+// per unit (a workgroup's work follows its units, not its tokens), at most
+// kBwdSegMax and at most T.  One segment (ns = 1): the dk/dv kernel writes
+// the final sums itself and no partial sums are kept.
+inline int seg_tokens(int T, int readers_per_unit) {
+  const int64_t base = T > 16384 ? 4096 : (T > 8192 ? 2048 : (T > 4096 ? 1024 : 512));
+  return (int)std::min<int64_t>(std::min<int64_t>(base * readers_per_unit, kBwdSegMax), std::max(T, 1));
+}
+inline int bwd_seg_tokens(const BwdPlan& p) { return seg_tokens(p.T, bwd_unit_readers(p)); }
+inline int bwd_segments(const BwdPlan& p) { return (p.T + bwd_seg_tokens(p) - 1) / bwd_seg_tokens(p); }
+
 // r / gv for 0 <= r < 16 as (r * bwd_gv_magic(p)) >> 16 (the kernels split a
 // unit's 16 rows into (reader, head) without an integer division)
 inline int bwd_gv_magic(const BwdPlan& p) { return (1 << 16) / p.gv + 1; }
@@ -40,7 +52,7 @@ struct BwdGrids {
 };
 
 inline BwdGrids bwd_grids(const BwdPlan& p) {
-  const int64_t seg = seg_tokens(p.T), ns = (p.T + seg - 1) / seg;
+  const int64_t ns = bwd_segments(p);
   const int64_t nb = (p.T + p.bs - 1) / p.bs, nw = (p.T + 31) / 32;
   BwdGrids g;
   g.dkdv = (int64_t)p.B * p.Hkv * ((p.T + 63) / 64) * ns;
@@ -59,8 +71,8 @@ inline size_t bwd_readers_bytes(const BwdPlan& p) {
 }
 
 inline size_t bwd_part_bytes(const BwdPlan& p) {
-  const size_t ns = (size_t)(p.T + seg_tokens(p.T) - 1) / seg_tokens(p.T);
-  return ns * 2 * (size_t)p.B * p.T * p.Hkv * p.D * sizeof(float);
+  const size_t ns = (size_t)bwd_segments(p);
+  return ns > 1 ? ns * 2 * (size_t)p.B * p.T * p.Hkv * p.D * sizeof(float) : 0;
 }
 
 // byte offset of the forward's schedule in the backward's workspace

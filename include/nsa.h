@@ -200,6 +200,8 @@ nsa_status nsa_decode(const nsa_dims* dims, const void* q, const void* k, const 
  *  ceil(T / 32) words, and each token segment's partial dK and dV sums:
  *  2 * ceil(T / L) * B * T * Hkv * D float32 with segments of L = 512
  *  tokens up to T = 4096, 1024 up to 8192, 2048 up to 16384, else 4096,
+ *  times 16 / G where G = Hq / Hkv <= 16, at most 4096 and at most T (none
+ *  when one segment covers T: dk and dv are then written directly),
  *  then the forward's schedule of the same indices: dq runs as the
  *  gradient mode of the forward's gather over it),
  *  256-byte aligned, no initialisation needed.  Past T = 16384 the

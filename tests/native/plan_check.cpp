@@ -70,10 +70,14 @@ void check_bwd(const nsa_dims& d, int bs) {
   expect(tpt >= 1 && tpt * p.gv <= 16 && (tpt == 1 || p.gpk == 1), "bwd unit readers", d, bs, 0);
   for (int r = 0; r < 16; r++) expect(((r * nsa::bwd_gv_magic(p)) >> 16) == r / p.gv, "bwd row split", d, bs, 0);
   using u128 = unsigned __int128;
-  const u128 seg = (u128)nsa::seg_tokens(p.T), T = (u128)p.T, ns = (T + seg - 1) / seg;
+  // segment: the base length for T times the unit's readers, at most 4096 and T
+  const int64_t base = p.T > 16384 ? 4096 : (p.T > 8192 ? 2048 : (p.T > 4096 ? 1024 : 512));
+  const int64_t segl = std::min<int64_t>(std::min<int64_t>(base * tpt, 4096), p.T);
+  expect(nsa::bwd_seg_tokens(p) == segl && segl >= 1, "bwd segment length", d, bs, 0);
+  const u128 seg = (u128)segl, T = (u128)p.T, ns = (T + seg - 1) / seg;
   const u128 want = ((u128)p.B * T * p.Hq * 4 + 255) / 256 * 256 +
                     ((u128)p.B * p.Hkv * ((T + p.bs - 1) / p.bs) * ((T + 31) / 32) * 4 + 255) / 256 * 256 +
-                    (ns * 2 * (u128)p.B * T * p.Hkv * p.D * 4 + 255) / 256 * 256 + (u128)p.fp.bytes;
+                    (ns > 1 ? (ns * 2 * (u128)p.B * T * p.Hkv * p.D * 4 + 255) / 256 * 256 : 0) + (u128)p.fp.bytes;
   expect((u128)nsa::bwd_workspace_bytes(p) == want, "bwd workspace size", d, bs, 0);
   // the dq ring runs the forward's plan of the same call: one bf16 column
   // tile per attention wave

@@ -29,8 +29,9 @@
 // is not past the reader), and accumulates dV += P^T dO and dK += dS^T Q
 // with 16x16x16 MFMAs whose B operands (dO and Q, rows x d) are read
 // transposed from the buffer.  The segments' partial sums are added in
-// segment order by the reduce kernel.  Every key row gets written (zeros
-// where no token reads the block).
+// segment order by the reduce kernel; where one segment covers the sequence
+// the kernel writes the final dK and dV itself and no reduce runs.  Every
+// key row gets written (zeros where no token reads the block).
 #include <utility>
 
 #include "nsa.h"

@@ -201,3 +201,38 @@ def test_bwd_segments_deterministic():
     dq2, dk2, dv2 = run_bwd(w, dbits)
     assert torch.equal(dq, dq2) and torch.equal(dk, dk2) and torch.equal(dv, dv2)
     _check_blocks(w, dout, dk, dv, [(0, 0, 0), (0, 0, 1), (0, 0, 15), (0, 0, 20), (0, 0, 39)], "bwd_seg")
+
+
+def test_bwd_dirty_workspace():
+    """The workspace needs no initialisation: a workspace filled with 0xFF
+    bytes (and one reused after a call on other dims) gives bit-identical
+    gradients to a fresh one (the reader bitmaps are cleared and the dq
+    gather's schedule is written by every call)."""
+    import ctypes
+    import torch
+    import block_index_sparse_amd as nsa
+    _say("[bwd] dirty workspace")
+    w = ni.make_workload("bwd_dirty", "bf16", [700, 700], 32, 2, 128, 64, 6, "sink_local_random", "uniform", seed=23)
+    dout, dbits = _dout(w, 23)
+    q, k, v, bi, bc, _ = to_device(w)
+    f = nsa.Forward(q, k, v, bi, bc, w.block_size, w.scale)
+    out, lse = f.run()
+    dO = torch.from_numpy(np.ascontiguousarray(dbits).view(np.int16)).view(torch.bfloat16).cuda()
+    lib = nsa.load_library()
+    need = lib.nsa_bwd_workspace_size(ctypes.byref(nsa._dims(w.B, w.T, w.Hq, w.Hkv, w.D, w.S, nsa.DTYPE_BF16)),
+                                      w.block_size)
+    ref = [g.clone() for g in nsa.bwd(q, k, v, out, lse, dO, bi, bc, w.block_size, w.scale)]
+    ws = torch.full((need + 4096,), 255, dtype=torch.uint8, device="cuda")
+    got = nsa.bwd(q, k, v, out, lse, dO, bi, bc, w.block_size, w.scale, workspace=ws)
+    for name, a, b in zip(("dq", "dk", "dv"), got, ref):
+        assert torch.equal(a.view(torch.int32), b.view(torch.int32)), f"{name}: dirty workspace changed the result"
+    # the same workspace after a call on other dims (one sequence, T = 300)
+    w2 = ni.make_workload("bwd_dirty2", "bf16", [300], 32, 2, 128, 64, 6, "local_random", "uniform", seed=24)
+    _, d2 = _dout(w2, 24)
+    q2, k2, v2, bi2, bc2, _ = to_device(w2)
+    o2, l2 = nsa.Forward(q2, k2, v2, bi2, bc2, w2.block_size, w2.scale).run()
+    dO2 = torch.from_numpy(np.ascontiguousarray(d2).view(np.int16)).view(torch.bfloat16).cuda()
+    nsa.bwd(q2, k2, v2, o2, l2, dO2, bi2, bc2, w2.block_size, w2.scale, workspace=ws)
+    got = nsa.bwd(q, k, v, out, lse, dO, bi, bc, w.block_size, w.scale, workspace=ws)
+    for name, a, b in zip(("dq", "dk", "dv"), got, ref):
+        assert torch.equal(a.view(torch.int32), b.view(torch.int32)), f"{name}: reused workspace changed the result"
